@@ -1,0 +1,116 @@
+"""Seeded synthetic inputs for the attention forward pass.
+
+This module holds no attention arithmetic.  It is the only code shared by the
+GPU path's tests/bench and the oracle's callers: both sides read the exact
+fp16 values produced here.
+
+Workloads: the FlashAttention evaluation of PipeThreader runs LLaMA3-8B and
+LLaMA3-70B head shapes at sequence lengths 512..8k and batch sizes 1 and 64
+(page "PipeThreader ... (OSDI 2025)" summary, section "实验与结果", citing the
+paper's section 6.2 / Fig.12).  No dataset is involved; the heads enter only as
+shapes: D = 128, Hq/Hkv = 32/8 (8B) or 64/8 (70B).
+
+Recipe: for tensor t in {Q: 0, K: 1, V: 2} and batch entry b, a CPU
+torch.Generator seeded with base * 1_000_003 + t * 65_537 + b draws
+torch.randn((S, H_t, D), float32), which is rounded to fp16 (round to nearest
+even).  Seeding per (tensor, batch entry) lets a checker regenerate any batch
+slice on its own, and lets slices be generated in parallel.
+"""
+from __future__ import annotations
+
+import struct
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass
+
+import torch
+
+Q, K, V = 0, 1, 2
+
+# fp32 value of 1/sqrt(128), the softmax scale every workload uses.
+SCALE_D128 = struct.unpack("<f", struct.pack("<I", 0x3DB504F3))[0]
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    S: int
+    Hq: int
+    Hkv: int
+    D: int
+    causal: bool
+    seed: int
+    scale: float = SCALE_D128
+
+    @property
+    def flops(self) -> float:
+        """Metric FLOPs: 2 * B * Hq * S^2 * D (QK^T and PV over the causal half)."""
+        return 2.0 * self.B * self.Hq * self.S * self.S * self.D
+
+    def heads(self, t: int) -> int:
+        return self.Hq if t == Q else self.Hkv
+
+    def describe(self) -> dict:
+        return {"workload": self.name, "B": self.B, "S": self.S, "Hq": self.Hq, "Hkv": self.Hkv, "D": self.D,
+                "causal": self.causal, "layout": "[B,S,H,D] fp16 in/out, LSE [B,Hq,S] fp32",
+                "scale": self.scale, "seed": self.seed}
+
+
+WORKLOADS = [
+    Workload("llama3-8b_b1_s512", 1, 512, 32, 8, 128, True, 1),
+    Workload("llama3-8b_b1_s8192", 1, 8192, 32, 8, 128, True, 2),
+    Workload("llama3-70b_b1_s8192", 1, 8192, 64, 8, 128, True, 3),
+    Workload("llama3-8b_b64_s2048", 64, 2048, 32, 8, 128, True, 4),
+    Workload("llama3-70b_b64_s8192", 64, 8192, 64, 8, 128, True, 5),
+]
+BY_NAME = {w.name: w for w in WORKLOADS}
+
+
+def slice_seed(base: int, tensor: int, b: int) -> int:
+    return base * 1_000_003 + tensor * 65_537 + b
+
+
+def make_slice(S: int, H: int, D: int, base: int, tensor: int, b: int) -> torch.Tensor:
+    """One batch entry of one tensor: CPU fp16 [S, H, D], N(0,1) rounded to fp16."""
+    g = torch.Generator(device="cpu").manual_seed(slice_seed(base, tensor, b))
+    return torch.randn((S, H, D), generator=g, dtype=torch.float32).to(torch.float16)
+
+
+def _threads() -> int:
+    import os
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def make_tensor(B: int, S: int, H: int, D: int, base: int, tensor: int, device="cpu") -> torch.Tensor:
+    """Full [B, S, H, D] fp16 tensor, batch slices generated in parallel and written into place."""
+    out = torch.empty((B, S, H, D), dtype=torch.float16, device=device)
+
+    def fill(b):
+        x = make_slice(S, H, D, base, tensor, b)
+        out[b].copy_(x, non_blocking=False)
+        return b
+
+    if B == 1:
+        fill(0)
+    else:
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(fill, range(B)))
+    return out
+
+
+def make_inputs(w: Workload, device="cpu"):
+    """(q, k, v) for a workload on `device` ([B,S,Hq,D], [B,S,Hkv,D], [B,S,Hkv,D] fp16)."""
+    q = make_tensor(w.B, w.S, w.Hq, w.D, w.seed, Q, device)
+    k = make_tensor(w.B, w.S, w.Hkv, w.D, w.seed, K, device)
+    v = make_tensor(w.B, w.S, w.Hkv, w.D, w.seed, V, device)
+    return q, k, v
+
+
+def make_batch_cpu(w: Workload, b: int):
+    """(q, k, v) of batch entry b on the CPU: [S,Hq,D], [S,Hkv,D], [S,Hkv,D] fp16."""
+    return (make_slice(w.S, w.Hq, w.D, w.seed, Q, b), make_slice(w.S, w.Hkv, w.D, w.seed, K, b),
+            make_slice(w.S, w.Hkv, w.D, w.seed, V, b))
