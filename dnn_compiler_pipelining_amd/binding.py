@@ -1,0 +1,126 @@
+"""Python binding of libattn: argument marshalling only.
+
+The functions carry the names of the C entry points in include/attn.h
+(attn_fwd, attn_fwd_stream, attn_status_string, attn_version) and forward to
+them through ctypes; every step of the computation runs in the HIP kernel.
+`forward()` is a convenience that allocates the outputs with torch and checks
+the tensors first.  There is no fallback: if libattn.so is missing or fails to
+load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libattn.so")
+
+ATTN_OK = 0
+ATTN_ERR_NULL = 1
+ATTN_ERR_SHAPE = 2
+ATTN_ERR_UNSUPPORTED = 3
+ATTN_ERR_ALIGN = 4
+ATTN_ERR_HIP = 5
+ATTN_ERR_OVERLAP = 6
+
+EXPORTS = ("attn_fwd", "attn_fwd_stream", "attn_status_string", "attn_version")
+
+_lock = threading.Lock()
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int):
+        super().__init__("libattn status %d: %s" % (status, attn_status_string(status)))
+        self.status = status
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libattn.so.  Raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(path):
+                raise FileNotFoundError(
+                    "libattn.so not built at %s: run `python -c 'import __graft_entry__ as g; g.build()'`" % path)
+            lib = ctypes.CDLL(path)
+            vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+            lib.attn_fwd.restype = i
+            lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f]
+            lib.attn_fwd_stream.restype = i
+            lib.attn_fwd_stream.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
+            lib.attn_status_string.restype = ctypes.c_char_p
+            lib.attn_status_string.argtypes = [i]
+            lib.attn_version.restype = i
+            lib.attn_version.argtypes = []
+            _lib = lib
+        return _lib
+
+
+def _ptr(x) -> int:
+    if x is None:
+        return 0
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def attn_fwd(q, k, v, o, lse, B: int, S: int, Hq: int, Hkv: int, D: int, causal: int, scale: float) -> int:
+    """C attn_fwd on the null stream.  Tensors or raw device addresses (int); lse may be None."""
+    return load().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, S, Hq, Hkv, D, int(causal),
+                           float(scale))
+
+
+def attn_fwd_stream(q, k, v, o, lse, B: int, S: int, Hq: int, Hkv: int, D: int, causal: int, scale: float,
+                    stream) -> int:
+    """C attn_fwd_stream.  `stream` is a torch.cuda.Stream, a raw hipStream_t (int) or None."""
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else (stream or 0)
+    return load().attn_fwd_stream(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, S, Hq, Hkv, D, int(causal),
+                                  float(scale), handle)
+
+
+def attn_status_string(status: int) -> str:
+    return load().attn_status_string(int(status)).decode()
+
+
+def attn_version() -> int:
+    return load().attn_version()
+
+
+def forward(q, k, v, causal: bool = True, scale: float | None = None, out=None, lse=None, want_lse: bool = True,
+            stream=None):
+    """Run the kernel on torch tensors q [B,S,Hq,D], k/v [B,S,Hkv,D] (fp16, contiguous, same GPU).
+
+    Returns (o, lse) with o [B,S,Hq,D] fp16 and lse [B,Hq,S] fp32 (None if not wanted).  Enqueues on
+    `stream` (default: torch's current stream) and does not synchronise.
+    """
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.float16 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous float16 tensor on a GPU" % name)
+        if t.dim() != 4:
+            raise ValueError("%s must be [B, S, H, D]" % name)
+    B, S, Hq, D = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[1] != S or k.shape[3] != D:
+        raise ValueError("shape mismatch: q %s k %s v %s" % (tuple(q.shape), tuple(k.shape), tuple(v.shape)))
+    if q.device != k.device or q.device != v.device:
+        raise ValueError("q, k, v must be on the same device")
+    Hkv = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if want_lse and lse is None:
+        lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (B, Hq, S)):
+        raise ValueError("lse must be a contiguous float32 [B, Hq, S] tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    with torch.cuda.device(q.device):
+        st = attn_fwd_stream(q, k, v, out, lse, B, S, Hq, Hkv, D, int(bool(causal)), float(scale), stream)
+    if st != ATTN_OK:
+        raise AttnError(st)
+    return out, lse

@@ -1,0 +1,43 @@
+"""Build libattn.so (gfx950) in-tree with hipcc."""
+from __future__ import annotations
+
+import os
+import subprocess
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libattn.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+SOURCES = [os.path.join(CSRC, "attn_fwd.hip"), os.path.join(CSRC, "attn_api.cpp")]
+
+# Packed fp32 VALU forms are switched off for all device code.
+HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-I" + INCLUDE, "-I" + CSRC]
+
+
+def build(out: str = LIB, extra_flags=()) -> str:
+    """Compile libattn.so (always recompiles).  Returns the library path."""
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, *HIP_FLAGS, *extra_flags, *SOURCES, "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed (%d):\n%s\n%s" % (res.returncode, " ".join(cmd), res.stderr))
+    os.replace(tmp, out)
+    return out
+
+
+def device_asm(out: str) -> str:
+    """Write the gfx950 assembly of the kernel (for register/LDS/scratch inspection)."""
+    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-S", "--cuda-device-only",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-I" + INCLUDE, "-I" + CSRC,
+           SOURCES[0], "-o", out]
+    subprocess.run(cmd, check=True, capture_output=True)
+    return out
+
+
+if __name__ == "__main__":
+    print(build())

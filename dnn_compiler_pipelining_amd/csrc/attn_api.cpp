@@ -1,0 +1,98 @@
+// attn_api.cpp -- the extern "C" boundary of libattn (declared in include/attn.h).
+//
+// Validation runs before any HIP call, so every error path is reachable
+// without a GPU.  Valid calls enqueue exactly one kernel and return.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "attn.h"
+#include "attn_kernel.h"
+
+namespace {
+
+constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+bool overlaps(const void* a, uint64_t a_bytes, const void* b, uint64_t b_bytes) {
+  if (!a || !b || a_bytes == 0 || b_bytes == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + b_bytes && b0 < a0 + a_bytes;
+}
+
+int validate(const void* q, const void* k, const void* v, const void* o, const float* lse, int B, int S, int Hq,
+             int Hkv, int D, int causal, float scale) {
+  if (!q || !k || !v || !o) return ATTN_ERR_NULL;
+  if (B < 1 || S < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_ERR_SHAPE;
+  if (causal != 0 && causal != 1) return ATTN_ERR_SHAPE;
+  if (!std::isfinite(scale)) return ATTN_ERR_SHAPE;
+  if (D != 128) return ATTN_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned16(lse)))
+    return ATTN_ERR_ALIGN;
+  const uint64_t q_bytes = (uint64_t)B * S * Hq * D * 2;
+  const uint64_t kv_bytes = (uint64_t)B * S * Hkv * D * 2;
+  const uint64_t lse_bytes = (uint64_t)B * Hq * S * 4;
+  if (overlaps(o, q_bytes, q, q_bytes) || overlaps(o, q_bytes, k, kv_bytes) || overlaps(o, q_bytes, v, kv_bytes) ||
+      overlaps(o, q_bytes, lse, lse_bytes))
+    return ATTN_ERR_OVERLAP;
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd_stream(const void* q, const void* k, const void* v, void* o, float* lse, int B, int S, int Hq, int Hkv,
+                    int D, int causal, float scale, void* stream) {
+  const int st = validate(q, k, v, o, lse, B, S, Hq, Hkv, D, causal, scale);
+  if (st != ATTN_OK) return st;
+
+  libattn::Params p;
+  p.q = static_cast<const _Float16*>(q);
+  p.k = static_cast<const _Float16*>(k);
+  p.v = static_cast<const _Float16*>(v);
+  p.o = static_cast<_Float16*>(o);
+  p.lse = lse;
+  p.q_sstride = (int64_t)Hq * D;
+  p.q_bstride = (int64_t)S * p.q_sstride;
+  p.kv_sstride = (int64_t)Hkv * D;
+  p.kv_bstride = (int64_t)S * p.kv_sstride;
+  p.B = B;
+  p.S = S;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.g = Hq / Hkv;
+  p.pairs = (p.g + 1) / 2;
+  p.n_qt = (S + 127) / 128;
+  p.causal = causal;
+  p.neg = scale < 0.f ? 1 : 0;
+  p.cs = std::fabs(scale) * 1.44269504088896340736f;
+  if (libattn::grid_blocks(p) < 0) return ATTN_ERR_SHAPE;
+
+  const hipError_t e = libattn::launch_attn_fwd(p, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int S, int Hq, int Hkv, int D,
+             int causal, float scale) {
+  return attn_fwd_stream(q, k, v, o, lse, B, S, Hq, Hkv, D, causal, scale, nullptr);
+}
+
+const char* attn_status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULL: return "a required pointer is NULL";
+    case ATTN_ERR_SHAPE: return "invalid shape, causal flag or scale";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported head dimension (D must be 128)";
+    case ATTN_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case ATTN_ERR_HIP: return "HIP launch error";
+    case ATTN_ERR_OVERLAP: return "output overlaps an input";
+    default: return "unknown status";
+  }
+}
+
+int attn_version(void) { return kVersion; }
+
+}  // extern "C"

@@ -1,0 +1,74 @@
+/*
+ * attn.h -- C ABI of libattn: fused grouped-query softmax attention, forward
+ * pass, for AMD Instinct MI355X (gfx950).
+ *
+ * The operation.  PipeThreader's FlashAttention workload (page "PipeThreader:
+ * Software-Defined Pipelining for Efficient DNN Execution (OSDI 2025)"
+ * summary, section "实验与结果", citing the paper's section 6.2 / Fig.12:
+ * LLaMA3-8B/70B head shapes, sequence 512..8k, batch 1/64) is the attention
+ * forward pass, which that page splits into load, mma and softmax sTasks
+ * (section "核心方法").  For every batch entry b, query head h and query row i:
+ *
+ *   c = h / (Hq / Hkv)                         query head h reads KV head c
+ *   allowed keys j: 0..i if causal, else 0..S-1 (top-left causal mask, Sq == Sk)
+ *   s_j = scale * dot(q[b,i,h,:], k[b,j,c,:])
+ *   o[b,i,h,:]  = sum_j softmax(s)_j * v[b,j,c,:]
+ *   lse[b,h,i]  = log(sum_j exp(s_j))          natural log of the scaled scores
+ *
+ * Tensors (all device memory, owned and allocated by the caller, contiguous):
+ *   q   fp16 [B][S][Hq][D]     k, v  fp16 [B][S][Hkv][D]
+ *   o   fp16 [B][S][Hq][D]     (written; must not overlap q, k, v or lse)
+ *   lse fp32 [B][Hq][S]        (written; may be NULL when not wanted)
+ * Every pointer must be 16-byte aligned.  fp16 is IEEE binary16; o is rounded
+ * to nearest even from fp32.  Internal offsets are 64-bit, so tensors larger
+ * than 4 GiB are supported.
+ *
+ * Scalars: B, S, Hq, Hkv >= 1; Hq % Hkv == 0; D == 128 (other head sizes
+ * return ATTN_ERR_UNSUPPORTED); causal is 0 or 1; scale is any finite float.
+ *
+ * Execution: the call validates its arguments, then enqueues one kernel on
+ * the given HIP stream (attn_fwd uses the null stream) and returns without
+ * waiting.  Faults during execution surface at the caller's next
+ * synchronisation.  The library allocates no memory, keeps no state between
+ * calls, is thread-safe, and gives bitwise identical results run to run.
+ *
+ * Errors: on invalid arguments nothing is launched and a nonzero ATTN_ERR_*
+ * code is returned; a failed launch returns ATTN_ERR_HIP.  No exception
+ * crosses the ABI and nothing is printed.  attn_status_string() names a code.
+ */
+#ifndef LIBATTN_ATTN_H
+#define LIBATTN_ATTN_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = 1,        /* a required pointer is NULL */
+  ATTN_ERR_SHAPE = 2,       /* B, S, Hq, Hkv < 1, Hq % Hkv != 0, causal not 0/1, or scale not finite */
+  ATTN_ERR_UNSUPPORTED = 3, /* D other than 128 */
+  ATTN_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
+  ATTN_ERR_HIP = 5,         /* the HIP runtime reported an error at launch */
+  ATTN_ERR_OVERLAP = 6      /* o overlaps q, k, v or lse */
+};
+
+/* Forward pass on the null stream.  Returns ATTN_OK or an ATTN_ERR_* code. */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int S, int Hq, int Hkv, int D,
+             int causal, float scale);
+
+/* Same as attn_fwd, enqueued on `stream` (a hipStream_t; NULL means the null stream). */
+int attn_fwd_stream(const void* q, const void* k, const void* v, void* o, float* lse, int B, int S, int Hq, int Hkv,
+                    int D, int causal, float scale, void* stream);
+
+/* Static, NUL-terminated description of a status code ("unknown status" for others). */
+const char* attn_status_string(int status);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBATTN_ATTN_H */

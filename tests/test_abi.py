@@ -1,0 +1,108 @@
+"""CPU tests of the C ABI: the library builds, loads, exports what include/attn.h declares,
+and rejects invalid arguments before touching the GPU (fake pointers are never dereferenced)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from dnn_compiler_pipelining_amd import binding as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+# Aligned, distinct, never-dereferenced fake device addresses (validation fails before use).
+QP, KP, VP, OP, LP = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(attn_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        from dnn_compiler_pipelining_amd import build
+        build.build()
+    return L.load()
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted(L.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT\s+(\w+)$", out, flags=re.M))
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_version_and_status_strings(lib):
+    assert L.attn_version() >= 10000
+    assert L.attn_status_string(L.ATTN_OK) == "ok"
+    for code in range(1, 7):
+        s = L.attn_status_string(code)
+        assert s and s != "unknown status"
+    assert L.attn_status_string(99) == "unknown status"
+
+
+def call(q=QP, k=KP, v=VP, o=OP, lse=LP, B=1, S=64, Hq=8, Hkv=2, D=128, causal=1, scale=0.088):
+    return L.attn_fwd(q, k, v, o, lse, B, S, Hq, Hkv, D, causal, scale)
+
+
+def test_null_pointers(lib):
+    assert call(q=0) == L.ATTN_ERR_NULL
+    assert call(k=0) == L.ATTN_ERR_NULL
+    assert call(v=0) == L.ATTN_ERR_NULL
+    assert call(o=0) == L.ATTN_ERR_NULL
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(S=0), dict(Hq=0), dict(Hkv=0), dict(Hq=6, Hkv=4), dict(causal=2),
+                                dict(causal=-1), dict(scale=float("inf")), dict(scale=float("nan")), dict(B=-3)])
+def test_bad_shapes(lib, kw):
+    assert call(**kw) == L.ATTN_ERR_SHAPE
+
+
+@pytest.mark.parametrize("D", [64, 256, 127, 0 + 1])
+def test_unsupported_head_dim(lib, D):
+    assert call(D=D) == L.ATTN_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "o", "lse"])
+def test_misaligned(lib, which):
+    kw = {which: {"q": QP, "k": KP, "v": VP, "o": OP, "lse": LP}[which] + 8}
+    assert call(**kw) == L.ATTN_ERR_ALIGN
+
+
+def test_overlap(lib):
+    assert call(o=QP) == L.ATTN_ERR_OVERLAP
+    assert call(o=KP + 4096) == L.ATTN_ERR_OVERLAP  # o starts inside k
+    assert call(o=LP - 4096) == L.ATTN_ERR_OVERLAP  # o runs into lse
+    assert call(o=VP, lse=0) == L.ATTN_ERR_OVERLAP
+
+
+def test_validation_order(lib):
+    # a null pointer is reported before a bad shape, a bad shape before an unsupported D
+    assert call(q=0, B=0) == L.ATTN_ERR_NULL
+    assert call(B=0, D=64) == L.ATTN_ERR_SHAPE
+    assert call(D=64, q=QP + 8) == L.ATTN_ERR_UNSUPPORTED
+
+
+def test_stream_entry_point_validates_too(lib):
+    st = L.attn_fwd_stream(QP, KP, VP, OP, LP, 1, 64, 8, 3, 128, 1, 0.1, None)
+    assert st == L.ATTN_ERR_SHAPE
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    saved = L._lib
+    try:
+        L._lib = None
+        with pytest.raises(FileNotFoundError):
+            L.load(str(tmp_path / "missing.so"))
+    finally:
+        L._lib = saved
