@@ -1,0 +1,325 @@
+#!/usr/bin/env python3
+"""Benchmark of libattn's causal GQA attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME | --all] [--no-cpu-baseline]
+
+A step is one forward pass (one kernel launch) over the whole workload: the
+LLaMA3-70B-shaped B=64 S=8192 Hq=64 Hkv=8 D=128 causal configuration by
+default, inputs seeded N(0,1) fp16 and resident in HBM before timing.  W
+untimed steps, then exactly K steps between two device synchronisations.
+Rank 0 prints one JSON line per workload:
+
+  value      whole-job TFLOP/s = metric FLOPs (2*B*Hq*S^2*D) * K / wall time
+  roofline   the kernel against the MFMA roofline: metric FLOPs per launch over
+             the average launch duration from HIP events on the launch stream,
+             against MI355X's published dense fp16 MFMA peak (2.5 PFLOP/s);
+             traffic = HBM bytes per launch from the committed rocprofv3
+             counter summary (null if that summary is for another kernel build)
+  cpu_baseline  the fp64 CPU oracle timed on the host on a bounded sample of
+             rows of the same workload (a baseline, not a target)
+
+`--pmc-copy BYTES` also launches a plain elementwise copy (negation) kernel that
+reads and writes BYTES bytes after the timed region (counter calibration for the HBM traffic figure), and
+`--summarize-traffic FETCH_DIR WRITE_DIR` turns two rocprofv3 --pmc runs
+(FETCH_SIZE, then WRITE_SIZE) into the traffic summary under profiles/, and
+`--summarize-kernel-trace TRACE_DIR COMMAND` writes the kernel-trace summary.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "causal attention fwd TFLOP/s (fp16) + % of MFMA peak, LLaMA3 shapes"
+PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, published
+DEFAULT_WORKLOAD = "llama3-70b_b64_s8192"
+KERNEL_NAME = "attn_fwd_kernel"
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_fingerprint() -> str:
+    """sha256 over the kernel sources and build flags: identifies the measured kernel build."""
+    from dnn_compiler_pipelining_amd import build as hipbuild
+
+    h = hashlib.sha256()
+    for path in hipbuild.SOURCES + [os.path.join(hipbuild.CSRC, "attn_kernel.h")]:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    h.update(" ".join(hipbuild.HIP_FLAGS[:9]).encode())
+    return h.hexdigest()[:16]
+
+
+def traffic_path(workload: str) -> str:
+    return os.path.join(PROFILES, "hbm_traffic_%s.json" % workload)
+
+
+def load_traffic(workload: str):
+    path = traffic_path(workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_fingerprint") != kernel_fingerprint():
+        return None
+    return t
+
+
+# ------------------------------------------------------------------ GPU timing
+
+def time_workload(w, steps: int, warmup: int, pmc_copy: int = 0):
+    import torch
+
+    from dnn_compiler_pipelining_amd import binding, inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log("[bench] %s: generating seeded inputs" % w.name)
+    q, k, v = inputs.make_inputs(w, dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.S), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    torch.cuda.synchronize()
+
+    def step():
+        binding.forward(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream)
+
+    log("[bench] %s: %d warmup steps" % (w.name, warmup))
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    log("[bench] %s: %d timed steps" % (w.name, steps))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall_ms = (t1 - t0) * 1e3 / steps
+    kernel_ms = e0.elapsed_time(e1) / steps
+    ok = bool(torch.isfinite(o[-1, -1]).all().item()) and bool(torch.isfinite(lse[-1, -1]).all().item())
+    if pmc_copy:
+        n = pmc_copy // 2
+        src = torch.ones(n, dtype=torch.float16, device=dev)
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)  # one elementwise kernel: reads and writes `pmc_copy` bytes each
+        torch.cuda.synchronize()
+        log("[bench] calibration copy of %d bytes done" % (2 * n))
+        del src, dst
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
+    return wall_ms, kernel_ms, ok
+
+
+# ------------------------------------------------------------------ CPU oracle baseline
+
+def cpu_baseline(w, target_s: float = 15.0):
+    """Times the fp64 oracle on rows of batch entry 0 (uniformly random rows, all heads)."""
+    import numpy as np
+
+    from dnn_compiler_pipelining_amd import inputs
+    from oracle import oracle as oracle_mod
+
+    threads = oracle_mod.default_threads()
+    qb, kb, vb = inputs.make_batch_cpu(w, 0)
+    qn, kn, vn = qb.numpy(), kb.numpy(), vb.numpy()
+    rng = np.random.default_rng(12345)
+
+    def run(nrows):
+        heads = rng.integers(0, w.Hq, nrows).astype(np.int32)
+        rows = rng.integers(0, w.S, nrows).astype(np.int32)
+        keys = (rows.astype(np.float64) + 1.0) if w.causal else np.full(nrows, float(w.S))
+        flops = float(4.0 * w.D * keys.sum())  # QK^T and PV over the allowed keys of each row
+        t = time.perf_counter()
+        oracle_mod.attn_rows(qn, kn, vn, heads, rows, w.causal, w.scale, nthreads=threads)
+        return flops, time.perf_counter() - t
+
+    f0, t0 = run(256 * threads)  # calibration (includes widening K/V of the batch entry once)
+    rate = f0 / max(t0, 1e-6)
+    avg_row = 4.0 * w.D * ((w.S + 1) / 2.0 if w.causal else w.S)
+    n = int(min(max(rate * max(target_s - t0, 1.0) / avg_row, 64), 4_000_000))
+    log("[bench] cpu oracle: %d threads, %.2f GFLOP/s calibration, timing %d rows" % (threads, rate / 1e9, n))
+    f1, t1 = run(n)
+    flops, secs = f0 + f1, t0 + t1
+    return {"value": round(flops / secs / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "%d (head,row) outputs of batch entry 0 of %s (rows uniform in [0,S), heads uniform), "
+                      "fp64, %.1f s wall; FLOPs = 4*D*(allowed keys) per row" % (256 * threads + n, w.name, secs)}
+
+
+# ------------------------------------------------------------------ traffic summary from rocprofv3 --pmc runs
+
+def _db_files(d: str):
+    files = glob.glob(os.path.join(d, "**", "*_results.db"), recursive=True)
+    if not files:
+        raise FileNotFoundError("no rocprofv3 *_results.db under %s" % d)
+    return files
+
+
+def _per_dispatch(d: str, counter: str):
+    """{(kernel_name, dispatch_id): value} for one counter of a rocprofv3 --pmc run (rocpd SQLite output)."""
+    import sqlite3
+
+    out = {}
+    for f in _db_files(d):
+        con = sqlite3.connect(f)
+        for name, disp, val in con.execute(
+                "select kernel_name, dispatch_id, value from counters_collection where counter_name = ?", (counter,)):
+            out[(name, disp)] = out.get((name, disp), 0.0) + float(val)
+        con.close()
+    return out
+
+
+def summarize_kernel_trace(d: str, workload: str, command: str):
+    """Markdown summary of a rocprofv3 --kernel-trace --stats run, written under profiles/."""
+    import sqlite3
+
+    lines = ["# rocprofv3 kernel trace: %s" % workload, "", "Command (from the repository root):", "",
+             "    " + command, "", "| kernel | calls | average us | total us | share % |", "|---|---|---|---|---|"]
+    info = None
+    for f in _db_files(d):
+        con = sqlite3.connect(f)
+        for name, calls, total, avg, pct in con.execute(
+                "select name, total_calls, total_duration, average, percentage from top_kernels"):
+            short = name if len(name) < 70 else name[:67] + "..."
+            lines.append("| `%s` | %d | %.1f | %.1f | %.3f |" % (short, calls, avg, total, pct))
+        row = con.execute("select grid_x, workgroup_x, lds_size, scratch_size, vgpr_count, accum_vgpr_count, "
+                          "sgpr_count from kernels where name like ? limit 1", ("%" + KERNEL_NAME + "%",)).fetchone()
+        if row:
+            info = row
+        con.close()
+    if info:
+        lines += ["", "%s dispatch: grid %d work-items, workgroup %d, LDS %d B, scratch %d B, vgpr_count %d, "
+                      "accum_vgpr_count %d, sgpr_count %d (as the trace reports them)" % ((KERNEL_NAME,) + tuple(info))]
+    lines += ["", "Kernel source fingerprint: %s" % kernel_fingerprint(), ""]
+    os.makedirs(PROFILES, exist_ok=True)
+    out = os.path.join(PROFILES, "%s_%s_kernel_trace.md" % (KERNEL_NAME, workload))
+    with open(out, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+
+
+def summarize_traffic(fetch_dir: str, write_dir: str, workload: str, copy_bytes: int):
+    res = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        vals = _per_dispatch(d, counter)
+        attn = [v for (kn, _), v in vals.items() if KERNEL_NAME in kn]
+        other = [(kn, v) for (kn, _), v in vals.items() if KERNEL_NAME not in kn]
+        if not attn:
+            raise RuntimeError("no %s dispatches in %s" % (KERNEL_NAME, d))
+        # the calibration copy is the largest non-attention dispatch
+        copy_kib = max(v for _, v in other) if other else 0.0
+        factor = copy_bytes / (copy_kib * 1024.0) if copy_kib else None
+        raw = sum(attn) / len(attn) * 1024.0
+        res[counter] = {"kib_per_launch": raw / 1024.0, "launches": len(attn), "copy_kib": copy_kib,
+                        "copy_bytes": copy_bytes, "factor": factor,
+                        "bytes_per_launch": raw * factor if factor else None}
+    total = None
+    if res["FETCH_SIZE"]["bytes_per_launch"] and res["WRITE_SIZE"]["bytes_per_launch"]:
+        total = res["FETCH_SIZE"]["bytes_per_launch"] + res["WRITE_SIZE"]["bytes_per_launch"]
+    from dnn_compiler_pipelining_amd import inputs
+
+    w = inputs.BY_NAME[workload]
+    algo = 2 * (2 * w.B * w.S * w.Hq * w.D + 2 * w.B * w.S * w.Hkv * w.D) + 4 * w.B * w.Hq * w.S
+    cmd = ("rocprofv3 --pmc %s -d <dir> -o <name> -- python3 bench.py --workload %s --steps 2 --warmup 1 "
+           "--no-cpu-baseline --pmc-copy %d")
+    out = {"workload": workload, "kernel": KERNEL_NAME, "kernel_fingerprint": kernel_fingerprint(),
+           "hbm_bytes_per_launch": total, "algorithmic_bytes_per_launch": algo,
+           "commands": [cmd % ("FETCH_SIZE", workload, copy_bytes), cmd % ("WRITE_SIZE", workload, copy_bytes),
+                        "python3 bench.py --workload %s --pmc-copy %d --summarize-traffic <fetch dir> <write dir>"
+                        % (workload, copy_bytes)],
+           "calibration": "each counter is scaled by copy_bytes / (its reading for an elementwise kernel that "
+                          "reads and writes copy_bytes bytes, launched in the same run)",
+           "counters": res}
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(traffic_path(workload), "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
+# ------------------------------------------------------------------ main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--all", action="store_true", help="one line per workload (parity-test configurations too)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--pmc-copy", type=int, default=0)
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-kernel-trace", nargs=2, metavar=("TRACE_DIR", "COMMAND"))
+    args = ap.parse_args()
+
+    from dnn_compiler_pipelining_amd import inputs
+
+    if args.summarize_kernel_trace:
+        summarize_kernel_trace(args.summarize_kernel_trace[0], args.workload, args.summarize_kernel_trace[1])
+        return 0
+    if args.summarize_traffic:
+        summarize_traffic(args.summarize_traffic[0], args.summarize_traffic[1], args.workload, args.pmc_copy)
+        return 0
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: this build measures one MI355X's share of the workload; "
+              "--gpus %d (WORLD_SIZE %d) is not supported" % (args.gpus, world), file=sys.stderr)
+        return 2
+
+    names = [w.name for w in inputs.WORKLOADS] if args.all else [args.workload]
+    for name in names:
+        w = inputs.BY_NAME[name]
+        wall_ms, kernel_ms, ok = time_workload(w, args.steps, args.warmup, args.pmc_copy)
+        if not ok:
+            log("[bench] non-finite output")
+            return 1
+        value = w.flops / (wall_ms * 1e-3) / 1e12
+        achieved = w.flops / (kernel_ms * 1e-3) / 1e12
+        traffic = load_traffic(w.name)
+        line = {
+            "metric": METRIC,
+            "value": round(value, 2),
+            "unit": "TFLOP/s",
+            "n_gpus": 1,
+            "steps": args.steps,
+            "warmup": args.warmup,
+            "ms_per_step": round(wall_ms, 4),
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": "f16",
+            "data": "synthetic: seeded i.i.d. N(0,1) fp16 Q/K/V",
+            "pct_of_mfma_peak": round(100.0 * value / PEAK_TFLOPS, 2),
+            "config": w.describe(),
+            "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(achieved / PEAK_TFLOPS, 4),
+                         "traffic": (round(traffic["hbm_bytes_per_launch"])
+                                     if traffic and traffic.get("hbm_bytes_per_launch") else None),
+                         "kernel": KERNEL_NAME, "kernel_ms": round(kernel_ms, 4),
+                         "flops_per_launch": w.flops},
+        }
+        if not args.no_cpu_baseline and not args.all:
+            line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

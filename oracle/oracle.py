@@ -62,11 +62,15 @@ def load(path: str = LIB) -> ctypes.CDLL:
         return _libs[path]
 
 
+MAX_THREADS = 16  # a one-GPU job's share of host cores
+
+
 def default_threads() -> int:
     try:
-        return max(1, len(os.sched_getaffinity(0)))
+        n = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
-        return max(1, os.cpu_count() or 1)
+        n = os.cpu_count() or 1
+    return max(1, min(MAX_THREADS, n))
 
 
 def _u16(a) -> np.ndarray:
