@@ -6,6 +6,8 @@
 
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
+#include <cstring>
 
 #include "attn.h"
 #include "attn_kernel.h"
@@ -13,6 +15,14 @@
 namespace {
 
 constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
+
+// LIBATTN_SCHEDULE=serial selects the serial tile schedule, a cross-check of
+// the default ping-pong schedule that computes bitwise identical results.
+// Read on every call so a test can switch it inside one process.
+int schedule_from_env() {
+  const char* s = std::getenv("LIBATTN_SCHEDULE");
+  return (s && std::strcmp(s, "serial") == 0) ? libattn::SCHEDULE_SERIAL : libattn::SCHEDULE_PINGPONG;
+}
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
@@ -69,6 +79,7 @@ int attn_fwd_stream(const void* q, const void* k, const void* v, void* o, float*
   p.causal = causal;
   p.neg = scale < 0.f ? 1 : 0;
   p.cs = std::fabs(scale) * 1.44269504088896340736f;
+  p.schedule = schedule_from_env();
   if (libattn::grid_blocks(p) < 0) return ATTN_ERR_SHAPE;
 
   const hipError_t e = libattn::launch_attn_fwd(p, static_cast<hipStream_t>(stream));

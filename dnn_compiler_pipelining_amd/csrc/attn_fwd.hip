@@ -72,6 +72,15 @@ __device__ __forceinline__ float wave_pair_sum(float x) {
   return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
 
+// Workgroup barrier that orders LDS accesses only: global loads issued before
+// it stay in flight (a full __syncthreads would wait for them).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+template <bool kPingPong>
 __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) _Float16 k_smem[2 * TILE];
   __shared__ __attribute__((aligned(16))) _Float16 v_smem[2 * TILE];
@@ -137,29 +146,37 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(Params p) {
     }
   }
 
-  // ---- global -> register staging of one K/V tile (2 + 2 chunks per thread)
+  // ---- K/V staging: global -> registers -> swizzled LDS.  K and V each have
+  // a two-slot ring (tile t lives in slot t & 1).  Every thread moves 2 K and
+  // 2 V chunks of 16 B per staging step: of the whole tile in the serial
+  // schedule, of its group's half of the tile in the ping-pong schedule.
+  const int st_base = kPingPong ? grp * (TILE / 16) : 0;
+  const int st_lt = kPingPong ? (tid & (NTHREADS / 2 - 1)) : tid;
+  const int st_stride = kPingPong ? NTHREADS / 2 : NTHREADS;
   u32x4 kreg[2], vreg[2];
-  auto fetch = [&](int tile) {
+  auto fetch = [&](int tk, int tv) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int x = tid + NTHREADS * u;
+      const int x = st_base + st_lt + st_stride * u;
       const int row = x >> 4, ch = x & 15;
-      const int key = tile * BN + row;
+      const int kkey = tk * BN + row, vkey = tv * BN + row;
       kreg[u] = u32x4{0, 0, 0, 0};
       vreg[u] = u32x4{0, 0, 0, 0};
-      if (key < S) {
-        kreg[u] = *reinterpret_cast<const u32x4*>(kb_ + (int64_t)key * p.kv_sstride + ch * 8);
-        vreg[u] = *reinterpret_cast<const u32x4*>(vb_ + (int64_t)key * p.kv_sstride + ch * 8);
-      }
+      if (tk < n_tiles && kkey < S)
+        kreg[u] = *reinterpret_cast<const u32x4*>(kb_ + (int64_t)kkey * p.kv_sstride + ch * 8);
+      if (tv < n_tiles && vkey < S)
+        vreg[u] = *reinterpret_cast<const u32x4*>(vb_ + (int64_t)vkey * p.kv_sstride + ch * 8);
     }
   };
-  auto stash = [&](int buf) {
+  auto stash = [&](int tk, int tv) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int x = tid + NTHREADS * u;
+      const int x = st_base + st_lt + st_stride * u;
       const int row = x >> 4, ch = x & 15;
-      *(LDS u32x4*)(&k_lds[buf * TILE + row * HD + ((ch ^ swz_k(row)) << 3)]) = kreg[u];
-      *(LDS u32x4*)(&v_lds[buf * TILE + row * HD + ((ch ^ swz_v(row)) << 3)]) = vreg[u];
+      if (tk < n_tiles)
+        *(LDS u32x4*)(&k_lds[(tk & 1) * TILE + row * HD + ((ch ^ swz_k(row)) << 3)]) = kreg[u];
+      if (tv < n_tiles)
+        *(LDS u32x4*)(&v_lds[(tv & 1) * TILE + row * HD + ((ch ^ swz_v(row)) << 3)]) = vreg[u];
     }
   };
 
@@ -169,104 +186,148 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(Params p) {
   float m_run = M_INIT;  // running max of the log2-scaled scores of query n
   float l_run = 0.f;     // running sum of exp2(score - m_run)
   const float cs = p.cs;
+  f32x16 s[2];           // S^T of the current tile
+  f16x8 pf[4];           // P^T of the current tile (PV operand)
 
-  fetch(0);
-  stash(0);
-  __syncthreads();
+  // a wave skips every tile that lies wholly above its causal diagonal
+  auto skip = [&](int j) { return !active || (p.causal && j * BN > qw + 31); };
 
-  for (int j = 0; j < n_tiles; ++j) {
-    const int buf = j & 1;
-    const bool has_next = j + 1 < n_tiles;
-    if (has_next) fetch(j + 1);
-
-    const int kj = j * BN;
-    const bool skip = !active || (p.causal && kj > qw + 31);
-    if (!skip) {
-      const LDS _Float16* ks = k_lds + buf * TILE;
-      const LDS _Float16* vs = v_lds + buf * TILE;
-      // ---- mma: S^T[key][query] for the 64 keys of the tile, two 32-key blocks
-      f32x16 s[2];
+  // ---- mma sTask 1: S^T[key][query] for the 64 keys of tile j, two 32-key blocks
+  auto mma_qk = [&](int j) {
+    const LDS _Float16* ks = k_lds + (j & 1) * TILE;
+    s[0] = f32x16{};
+    s[1] = f32x16{};
+    // the two 32-key blocks are independent accumulator chains: interleave them
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const int ch = 2 * kk + hh;
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb) {
-        s[sb] = f32x16{};
         const int row = 32 * sb + n;
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-          const int ch = 2 * kk + hh;
-          const f16x8 kf = *(const LDS f16x8*)(&ks[row * HD + ((ch ^ swz_k(row)) << 3)]);
-          s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[kk], s[sb], 0, 0, 0);
-        }
-      }
-
-      // ---- softmax (online, log2 domain)
-      const bool need_mask = (p.causal && kj + BN - 1 > qw) || (kj + BN > S);
-      const int query = qw + n;
-      uint32_t keep = 0xffffffffu;  // bit (16*sb + r): key allowed
-      if (need_mask) {
-        keep = 0;
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kj + 32 * sb + 8 * (r >> 2) + 4 * hh + (r & 3);
-            const bool ok = key < S && (!p.causal || key <= query);
-            keep |= (ok ? 1u : 0u) << (16 * sb + r);
-          }
-      }
-      float mt = NEG_INF;
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float x = ((keep >> (16 * sb + r)) & 1u) ? s[sb][r] : NEG_INF;
-          mt = fmaxf(mt, x);
-        }
-      mt = wave_pair_max(mt);
-      const float mts = (mt == NEG_INF) ? NEG_INF : mt * cs;
-      const float m_new = fmaxf(m_run, mts);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-
-      float rs = 0.f;
-      f16x8 pf[4];
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][r], cs, -m_new));
-          e = ((keep >> (16 * sb + r)) & 1u) ? e : 0.f;
-          rs += e;
-          pf[2 * sb + (r >> 3)][r & 7] = (_Float16)e;
-        }
-      rs = wave_pair_sum(rs);
-      l_run = l_run * alpha + rs;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) o_acc[db] *= alpha;
-
-      // ---- mma: O^T[d][query] += V^T[d][key] P^T[key][query]
-      const int G = lane >> 4, sl = lane & 15;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int row1 = 16 * kk + 4 * (G >> 1) + (sl >> 2);
-        const int row2 = row1 + 8;
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const int ch = 4 * db + 2 * (G & 1) + ((sl & 3) >> 1);
-          const int within = (sl & 1) << 2;
-          const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (LDS i16x4*)&vs[row1 * HD + ((ch ^ swz_v(row1)) << 3) + within]);
-          const i16x4 a2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (LDS i16x4*)&vs[row2 * HD + ((ch ^ swz_v(row2)) << 3) + within]);
-          const f16x4 h1 = __builtin_bit_cast(f16x4, a1);
-          const f16x4 h2 = __builtin_bit_cast(f16x4, a2);
-          const f16x8 vf = {h1[0], h1[1], h1[2], h1[3], h2[0], h2[1], h2[2], h2[3]};
-          o_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[kk], o_acc[db], 0, 0, 0);
-        }
+        const f16x8 kf = *(const LDS f16x8*)(&ks[row * HD + ((ch ^ swz_k(row)) << 3)]);
+        s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[kk], s[sb], 0, 0, 0);
       }
     }
+  };
 
-    if (has_next) stash(buf ^ 1);
-    __syncthreads();
+  // ---- softmax sTask: online softmax of tile j in the log2 domain
+  auto softmax = [&](int j) {
+    const int kj = j * BN;
+    const bool need_mask = (p.causal && kj + BN - 1 > qw) || (kj + BN > S);
+    const int query = qw + n;
+    uint32_t keep = 0xffffffffu;  // bit (16*sb + r): key allowed
+    if (need_mask) {
+      keep = 0;
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kj + 32 * sb + 8 * (r >> 2) + 4 * hh + (r & 3);
+          const bool ok = key < S && (!p.causal || key <= query);
+          keep |= (ok ? 1u : 0u) << (16 * sb + r);
+        }
+    }
+    float mt = NEG_INF;
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float x = ((keep >> (16 * sb + r)) & 1u) ? s[sb][r] : NEG_INF;
+        mt = fmaxf(mt, x);
+      }
+    mt = wave_pair_max(mt);
+    const float mts = (mt == NEG_INF) ? NEG_INF : mt * cs;
+    const float m_new = fmaxf(m_run, mts);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+
+    float rs = 0.f;
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][r], cs, -m_new));
+        e = ((keep >> (16 * sb + r)) & 1u) ? e : 0.f;
+        rs += e;
+        pf[2 * sb + (r >> 3)][r & 7] = (_Float16)e;
+      }
+    rs = wave_pair_sum(rs);
+    l_run = l_run * alpha + rs;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) o_acc[db] *= alpha;
+  };
+
+  // ---- mma sTask 2: O^T[d][query] += V^T[d][key] P^T[key][query] for tile j
+  auto mma_pv = [&](int j) {
+    const LDS _Float16* vs = v_lds + (j & 1) * TILE;
+    const int G = lane >> 4, sl = lane & 15;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int row1 = 16 * kk + 4 * (G >> 1) + (sl >> 2);
+      const int row2 = row1 + 8;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const int ch = 4 * db + 2 * (G & 1) + ((sl & 3) >> 1);
+        const int within = (sl & 1) << 2;
+        const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (LDS i16x4*)&vs[row1 * HD + ((ch ^ swz_v(row1)) << 3) + within]);
+        const i16x4 a2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (LDS i16x4*)&vs[row2 * HD + ((ch ^ swz_v(row2)) << 3) + within]);
+        const f16x4 h1 = __builtin_bit_cast(f16x4, a1);
+        const f16x4 h2 = __builtin_bit_cast(f16x4, a2);
+        const f16x8 vf = {h1[0], h1[1], h1[2], h1[3], h2[0], h2[1], h2[2], h2[3]};
+        o_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[kk], o_acc[db], 0, 0, 0);
+      }
+    }
+  };
+
+  if constexpr (!kPingPong) {
+    // ---- serial schedule: every wave runs load-next / QK / softmax / PV per tile
+    fetch(0, 0);
+    stash(0, 0);
+    lds_barrier();
+    for (int j = 0; j < n_tiles; ++j) {
+      fetch(j + 1, j + 1);
+      if (!skip(j)) {
+        mma_qk(j);
+        softmax(j);
+        mma_pv(j);
+      }
+      stash(j + 1, j + 1);
+      lds_barrier();
+    }
+  } else {
+    // ---- ping-pong schedule.  Time is cut into half-steps by workgroup
+    // barriers.  Each wave alternates an mma block (PV of tile j-1, then QK
+    // of tile j) and a softmax block (tile j); group 1 runs one half-step
+    // behind group 0, so on every SIMD one wave keeps the matrix core busy
+    // while the other runs softmax on the VALU.  Group 0 stages its half of
+    // (K_{j+1}, V_j) during its softmax block j, group 1 its half of
+    // (K_{j+2}, V_{j+1}) during its softmax block j; every slot is rewritten
+    // only after both groups have read it.
+    fetch(0, n_tiles);
+    stash(0, n_tiles);
+    if (grp == 1) fetch(1, 0);
+    lds_barrier();
+    for (int hs = 0; hs < 2 * n_tiles + 2; ++hs) {
+      const int ph = hs - grp;
+      if (ph == -1) {
+        stash(1, 0);
+      } else if (ph <= 2 * n_tiles) {
+        const int j = ph >> 1;
+        if ((ph & 1) == 0) {
+          fetch(j + 1 + grp, j + grp);
+          __builtin_amdgcn_s_setprio(1);
+          if (j >= 1 && !skip(j - 1)) mma_pv(j - 1);
+          if (j < n_tiles && !skip(j)) mma_qk(j);
+          __builtin_amdgcn_s_setprio(0);
+        } else {
+          if (!skip(j)) softmax(j);
+          stash(j + 1 + grp, j + grp);
+        }
+      }
+      lds_barrier();
+    }
   }
 
   // ---- epilogue: O = O^T / l (fp16, round to nearest even), LSE in natural log
@@ -298,7 +359,10 @@ int64_t grid_blocks(const Params& p) {
 hipError_t launch_attn_fwd(const Params& p, hipStream_t stream) {
   const int64_t nb = grid_blocks(p);
   if (nb <= 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(attn_fwd_kernel, dim3((unsigned)nb), dim3(NTHREADS), 0, stream, p);
+  if (p.schedule == SCHEDULE_SERIAL)
+    hipLaunchKernelGGL(attn_fwd_kernel<false>, dim3((unsigned)nb), dim3(NTHREADS), 0, stream, p);
+  else
+    hipLaunchKernelGGL(attn_fwd_kernel<true>, dim3((unsigned)nb), dim3(NTHREADS), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -7,6 +7,11 @@
 
 namespace libattn {
 
+// Tile schedules of the kernel.  Both compute bitwise identical results; the
+// serial one exists to cross-check the ping-pong one (an LDS race in either
+// would make them differ).
+enum Schedule { SCHEDULE_PINGPONG = 0, SCHEDULE_SERIAL = 1 };
+
 // Launch parameters.  Pointers are device pointers; strides are in elements.
 struct Params {
   const _Float16* q;
@@ -25,6 +30,7 @@ struct Params {
   int causal;
   int neg;           // scale < 0: the kernel negates Q and uses |scale|
   float cs;          // |scale| * log2(e)
+  int schedule;      // Schedule
 };
 
 // Grid size for p (number of workgroups), or -1 if it does not fit an int.

@@ -32,6 +32,10 @@
  * synchronisation.  The library allocates no memory, keeps no state between
  * calls, is thread-safe, and gives bitwise identical results run to run.
  *
+ * The environment variable LIBATTN_SCHEDULE=serial (read at each call)
+ * selects a serial tile schedule instead of the default ping-pong one; both
+ * give bitwise identical results, so it serves as a cross-check.
+ *
  * Errors: on invalid arguments nothing is launched and a nonzero ATTN_ERR_*
  * code is returned; a failed launch returns ATTN_ERR_HIP.  No exception
  * crosses the ABI and nothing is printed.  attn_status_string() names a code.

@@ -167,3 +167,18 @@ def test_gpu_validation_errors_launch_nothing():
     assert st == binding.ATTN_ERR_UNSUPPORTED
     torch.cuda.synchronize()
     assert bool(torch.isnan(o).all().item())
+
+
+@pytest.mark.parametrize("B,S,Hq,Hkv,causal", [(1, 1000, 8, 2, 1), (2, 333, 16, 4, 0), (1, 257, 6, 2, 1),
+                                               (1, 8192, 64, 8, 1)], ids=str)
+def test_schedules_bitwise_identical(monkeypatch, B, S, Hq, Hkv, causal):
+    """The ping-pong schedule against the serial one: same arithmetic per accumulator, so any LDS
+    race (a slot rewritten while another wave still reads it) would show up as a difference."""
+    q, k, v = cpu_qkv(B, S, Hq, Hkv, seed=90 + S)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    monkeypatch.delenv("LIBATTN_SCHEDULE", raising=False)
+    o1, l1 = U.run(qd, kd, vd, bool(causal), SC)
+    monkeypatch.setenv("LIBATTN_SCHEDULE", "serial")
+    o2, l2 = U.run(qd, kd, vd, bool(causal), SC)
+    monkeypatch.delenv("LIBATTN_SCHEDULE")
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
