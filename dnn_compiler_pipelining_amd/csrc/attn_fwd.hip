@@ -8,11 +8,11 @@
 // The tile loop follows the load / mma / softmax sTask split of PipeThreader
 // (page "PipeThreader: Software-Defined Pipelining ... (OSDI 2025)" summary,
 // section "核心方法"), mapped onto gfx950 units:
-//   load    : K/V tiles of 64 keys, global -> registers -> swizzled LDS, one
-//             tile ahead of the compute (double-buffered LDS ring; the
-//             prologue / steady state / epilogue pattern of software
-//             pipelining with ping-pong buffers, page "AI编译器融合技术 -- 5.
-//             并行性与分布式融合", section 5.4.2)
+//   load    : K/V tiles of 64 keys, global -> registers -> padded LDS rows,
+//             staged ahead of the compute in two-slot rings (the prologue /
+//             steady state / epilogue pattern of software pipelining with
+//             ping-pong buffers, page "AI编译器融合技术 -- 5. 并行性与分布式融合",
+//             section 5.4.2)
 //   mma     : S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_32x32x16_f16,
 //             fp16 operands and fp32 accumulation (same page, section 5.2.2:
 //             map the contraction onto the matrix instruction and conform the
@@ -21,6 +21,8 @@
 //             need one cross-lane step (v_permlane32_swap) because the S^T
 //             layout keeps each query in one lane pair (same page, section
 //             5.2.1: subgroup reductions by lane exchange instead of LDS)
+// and the two wave groups are offset by half a tile so that one group's
+// softmax runs on the VALU while the other's MFMAs run on the matrix core.
 //
 // Layout facts this file relies on (checked on gfx950 with a lane probe):
 //   mfma 32x32x16 f16, lane l, element i of the 8-half operands and r of the
@@ -32,42 +34,65 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "attn_kernel.h"
 
 namespace libattn {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 #define LDS __attribute__((address_space(3)))
 
-constexpr int HD = 128;                 // head dim
-constexpr int BM = 128;                 // query rows per wave group
-constexpr int BN = 64;                  // keys per KV tile
-constexpr int NTHREADS = 512;           // 8 wavefronts
-constexpr int TILE = BN * HD;           // halves per K or V tile (16 KiB)
+constexpr int HD = 128;          // head dim
+constexpr int BM = 128;          // query rows per wave group
+constexpr int BN = 64;           // keys per KV tile
+constexpr int NTHREADS = 512;    // 8 wavefronts
 constexpr float NEG_INF = -__builtin_inff();
-constexpr float M_INIT = -1e30f;        // finite start for the running max
+constexpr float M_INIT = -1e30f; // finite start for the running max
 constexpr float LN2 = 0.693147180559945309f;
+// Lazy rescaling: the running max (log2 units) is only raised when a tile's
+// max exceeds it by more than TAU, so P = 2^(s - m) stays below 2^TAU; the
+// final O / l and LSE = m + log2(l) are exact for any m.
+constexpr float TAU = 8.0f;
 
-// 16-byte chunk swizzles (a row of a tile is 256 B = 16 chunks).
-// K is read with ds_read_b128 by 32 consecutive rows per chunk column: XOR by
-// row&7 spreads each 8-lane pass over 8 distinct 16-byte bank groups.
-// V is read with ds_read_b64_tr_b16 in 4-row groups covering 4 chunks: XOR by
-// 4*(row&3) keeps every 16- and 32-lane pass on distinct bank groups.
-__device__ __forceinline__ int swz_k(int row) { return row & 7; }
-__device__ __forceinline__ int swz_v(int row) { return (row & 3) << 2; }
+// LDS layouts (bytes).  Both tiles are staged through registers so that the
+// global loads of a tile can stay in flight across a barrier.
+//  K: 64 key rows of 256 + 16 B.  The 8 lanes of a ds_read_b128 pass (8
+//    consecutive keys, same 16-byte column) fall 16 B apart in bank space and
+//    a 16-lane pass covers all 64 banks once; every K fragment read is a
+//    compile-time offset from one per-lane base.
+//  V: stored transposed, V^T[d][key]: 128 d rows of 64 keys (128 B) + 16 B,
+//    so a PV fragment (8 keys of one d) is one ds_read_b128 instead of two
+//    transpose reads.  Inside each group of 16 keys the columns are ordered
+//    0-3, 8-11, 4-7, 12-15: lane half h of the MFMA B operand P^T holds keys
+//    {4h..4h+3, 8+4h..8+4h+3} of the group (the accumulator layout of S^T), and
+//    reads exactly those 8 keys as 16 contiguous bytes.
+constexpr int K_ROWB = 2 * HD + 16;     // 272
+constexpr int K_TILEB = BN * K_ROWB;    // 17408
+constexpr int VT_ROWB = 2 * BN + 16;    // 144
+constexpr int VT_TILEB = HD * VT_ROWB;  // 18432
+static_assert(2 * (K_TILEB + VT_TILEB) <= 160 * 1024, "two K and two V^T slots fit the 160 KiB LDS");
+__host__ __device__ constexpr int vt_col(int key) {  // column of key (0..63) in a V^T row
+  return (key & ~15) | (key & 3) | (((key >> 3) & 1) << 2) | (((key >> 2) & 1) << 3);
+}
+// Depth of the fragment prefetch ring of the mma block.
+#ifndef ATTN_RING
+#define ATTN_RING 4
+#endif
+constexpr int RING = ATTN_RING;
 
-__device__ __forceinline__ float wave_pair_max(float x) {
+__device__ __forceinline__ float pair_max(float x) {
   // lanes l and l^32 hold the same query: combine their partial results
   auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
 }
-__device__ __forceinline__ float wave_pair_sum(float x) {
+__device__ __forceinline__ float pair_sum(float x) {
   auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
@@ -80,12 +105,42 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Compile-time loop: f(std::integral_constant<int, i>) for i = 0..N-1.
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Steps of an mma block.  A QK step (kk, x = sb) adds K[32sb.., 16kk..] x
+// Q^T[16kk.., :] into S^T block sb; a PV step (kk, x = db) adds
+// V^T[32db.., 16kk..] x P^T[16kk.., :] into O^T block db.  Mode 0 runs PV of
+// tile j-1 and QK of tile j with the two kinds alternating, so consecutive
+// MFMAs of one accumulator are >= 4 steps apart: per group g the order is
+// PV(g,0) QK(2g,0) PV(g,1) QK(2g,1) PV(g,2) QK(2g+1,0) PV(g,3) QK(2g+1,1).
+// Mode 1 is PV only, mode 2 QK only.
+struct Step {
+  bool pv;
+  int kk, x;
+};
+__host__ __device__ constexpr Step step_of(int mode, int i) {
+  return mode == 1   ? Step{true, i >> 2, i & 3}
+         : mode == 2 ? Step{false, i >> 1, i & 1}
+         : ((i & 7) & 1) == 0 ? Step{true, i >> 3, (i & 7) >> 1}
+                              : Step{false, 2 * (i >> 3) + ((i & 7) >> 2), ((i & 7) >> 1) & 1};
+}
+constexpr int steps_of(int mode) { return mode == 0 ? 32 : 16; }
+constexpr int reads_of(int, int) { return 1; }  // LDS reads per fragment
+
 template <bool kPingPong>
 __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(Params p) {
-  __shared__ __attribute__((aligned(16))) _Float16 k_smem[2 * TILE];
-  __shared__ __attribute__((aligned(16))) _Float16 v_smem[2 * TILE];
-  LDS _Float16* const k_lds = (LDS _Float16*)k_smem;
-  LDS _Float16* const v_lds = (LDS _Float16*)v_smem;
+  __shared__ __attribute__((aligned(1024))) char k_smem[2 * K_TILEB];
+  __shared__ __attribute__((aligned(1024))) char v_smem[2 * VT_TILEB];
+  LDS char* const k_lds = (LDS char*)k_smem;
+  LDS char* const v_lds = (LDS char*)v_smem;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -146,45 +201,79 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(Params p) {
     }
   }
 
-  // ---- K/V staging: global -> registers -> swizzled LDS.  K and V each have
-  // a two-slot ring (tile t lives in slot t & 1).  Every thread moves 2 K and
-  // 2 V chunks of 16 B per staging step: of the whole tile in the serial
-  // schedule, of its group's half of the tile in the ping-pong schedule.
-  const int st_base = kPingPong ? grp * (TILE / 16) : 0;
-  const int st_lt = kPingPong ? (tid & (NTHREADS / 2 - 1)) : tid;
-  const int st_stride = kPingPong ? NTHREADS / 2 : NTHREADS;
-  u32x4 kreg[2], vreg[2];
-  auto fetch = [&](int tk, int tv) {
+  // ---- K/V staging through registers.  K_t and V_t live in slot t & 1 of
+  // their rings.  Group 0 stages K tiles, group 1 V tiles; each of the 256
+  // threads of a group moves 4 chunks of 16 B per tile.  Rows past the end of
+  // the sequence are loaded from row S-1 (finite data whose scores and weights
+  // are masked to zero).  Loads use a wave-uniform tile base plus a constant
+  // per-thread 32-bit offset.
+  const int gt = tid & (NTHREADS / 2 - 1);
+  const uint32_t row_bytes = (uint32_t)p.kv_sstride * 2;
+  // K: chunk x = gt + 256u -> key row x / 16, column chunk x % 16
+  const int k_row0 = gt >> 4, k_ch = gt & 15;
+  // V: key quad vq = gt % 16 (keys 4vq..4vq+3), d chunk vc = gt / 16 (d 8vc..8vc+7)
+  const int vq = gt & 15, vc = gt >> 4;
+  // row of chunk u = st_row0 + u * st_drow; byte offset = st_off0 + u * st_doff
+  const int st_row0 = grp == 0 ? k_row0 : 4 * vq;
+  const int st_drow = grp == 0 ? 16 : 1;
+  const uint32_t st_col = (uint32_t)(grp == 0 ? k_ch : vc) * 16u;
+  const uint32_t st_off0 = (uint32_t)st_row0 * row_bytes + st_col;
+  const uint32_t st_doff = (uint32_t)st_drow * row_bytes;
+  const char* st_src;
+  {  // wave-uniform source pointer, so the tile base below lives in SGPRs
+    const uintptr_t a = (uintptr_t)(grp == 0 ? (const char*)kb_ : (const char*)vb_);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    st_src = (const char*)(((uintptr_t)hi << 32) | lo);
+  }
+  u32x4 stg[4];
+  auto stage_load = [&](int tile) {  // global -> registers (this group's tensor)
+    tile = __builtin_amdgcn_readfirstlane(tile);
+    if (tile >= n_tiles) return;
+    if ((tile + 1) * BN <= S) {
+      const char* base = st_src + (int64_t)tile * BN * row_bytes;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int x = st_base + st_lt + st_stride * u;
-      const int row = x >> 4, ch = x & 15;
-      const int kkey = tk * BN + row, vkey = tv * BN + row;
-      kreg[u] = u32x4{0, 0, 0, 0};
-      vreg[u] = u32x4{0, 0, 0, 0};
-      if (tk < n_tiles && kkey < S)
-        kreg[u] = *reinterpret_cast<const u32x4*>(kb_ + (int64_t)kkey * p.kv_sstride + ch * 8);
-      if (tv < n_tiles && vkey < S)
-        vreg[u] = *reinterpret_cast<const u32x4*>(vb_ + (int64_t)vkey * p.kv_sstride + ch * 8);
+      for (int u = 0; u < 4; ++u) stg[u] = *reinterpret_cast<const u32x4*>(base + (st_off0 + u * st_doff));
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int key = min(tile * BN + st_row0 + u * st_drow, S - 1);
+        stg[u] = *reinterpret_cast<const u32x4*>(st_src + (int64_t)key * row_bytes + st_col);
+      }
     }
   };
-  auto stash = [&](int tk, int tv) {
+  auto stage_store = [&](int tile) {  // registers -> LDS slot tile & 1
+    if (tile >= n_tiles) return;
+    if (grp == 0) {
+      LDS char* dst = k_lds + (tile & 1) * K_TILEB + k_row0 * K_ROWB + k_ch * 16;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int x = st_base + st_lt + st_stride * u;
-      const int row = x >> 4, ch = x & 15;
-      if (tk < n_tiles)
-        *(LDS u32x4*)(&k_lds[(tk & 1) * TILE + row * HD + ((ch ^ swz_k(row)) << 3)]) = kreg[u];
-      if (tv < n_tiles)
-        *(LDS u32x4*)(&v_lds[(tv & 1) * TILE + row * HD + ((ch ^ swz_v(row)) << 3)]) = vreg[u];
+      for (int u = 0; u < 4; ++u) *(LDS u32x4*)(dst + 16 * u * K_ROWB) = stg[u];
+    } else {
+      // transpose: for each of the 8 d values of the chunk, the 4 keys of the
+      // quad become one 8-byte word of V^T row d
+      LDS char* dst = v_lds + (tile & 1) * VT_TILEB + vc * 8 * VT_ROWB + 2 * vt_col(4 * vq);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const uint32_t lo0 = __builtin_amdgcn_perm(stg[1][m], stg[0][m], 0x05040100u);
+        const uint32_t lo1 = __builtin_amdgcn_perm(stg[3][m], stg[2][m], 0x05040100u);
+        const uint32_t hi0 = __builtin_amdgcn_perm(stg[1][m], stg[0][m], 0x07060302u);
+        const uint32_t hi1 = __builtin_amdgcn_perm(stg[3][m], stg[2][m], 0x07060302u);
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        *(LDS u32x2*)(dst + (2 * m) * VT_ROWB) = u32x2{lo0, lo1};
+        *(LDS u32x2*)(dst + (2 * m + 1) * VT_ROWB) = u32x2{hi0, hi1};
+      }
     }
   };
+
+  // per-lane fragment bases (bytes); everything else is a compile-time offset
+  const int k_frag = n * K_ROWB + 16 * hh;    // A operand of QK^T: key row n, d column 8*hh
+  const int v_frag = n * VT_ROWB + 16 * hh;   // A operand of PV: V^T row n, key columns of lane half hh
 
   f32x16 o_acc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) o_acc[db] = f32x16{};
-  float m_run = M_INIT;  // running max of the log2-scaled scores of query n
-  float l_run = 0.f;     // running sum of exp2(score - m_run)
+  float m_run = M_INIT;  // running max (log2 units) of the scores of query n
+  float l_run = 0.f;     // running sum of 2^(score - m_run), from the fp16 P
   const float cs = p.cs;
   f32x16 s[2];           // S^T of the current tile
   f16x8 pf[4];           // P^T of the current tile (PV operand)
@@ -192,31 +281,62 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(Params p) {
   // a wave skips every tile that lies wholly above its causal diagonal
   auto skip = [&](int j) { return !active || (p.causal && j * BN > qw + 31); };
 
-  // ---- mma sTask 1: S^T[key][query] for the 64 keys of tile j, two 32-key blocks
-  auto mma_qk = [&](int j) {
-    const LDS _Float16* ks = k_lds + (j & 1) * TILE;
-    s[0] = f32x16{};
-    s[1] = f32x16{};
-    // the two 32-key blocks are independent accumulator chains: interleave them
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const int ch = 2 * kk + hh;
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
-        const int row = 32 * sb + n;
-        const f16x8 kf = *(const LDS f16x8*)(&ks[row * HD + ((ch ^ swz_k(row)) << 3)]);
-        s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[kk], s[sb], 0, 0, 0);
-      }
-    }
+  // ---- mma sTasks
+  auto frag_qk = [&](int j, int kk, int sb) -> f16x8 {
+    return *(const LDS f16x8*)(k_lds + (j & 1) * K_TILEB + k_frag + 32 * sb * K_ROWB + 32 * kk);
+  };
+  auto frag_pv = [&](int j, int kk, int db) -> f16x8 {
+    return *(const LDS f16x8*)(v_lds + (j & 1) * VT_TILEB + v_frag + 32 * db * VT_ROWB + 32 * kk);
+  };
+  // One mma block: the fragments of the next RING steps are always in
+  // flight; the scheduler is pinned to "MFMA i, then the LDS reads of step
+  // i + RING" so the matrix core never waits on a just-issued read.
+  auto mma_block = [&](int j, auto mode_c) {
+    constexpr int mode = decltype(mode_c)::value;  // 0: PV(j-1)+QK(j), 1: PV(j-1), 2: QK(j)
+    constexpr int nsteps = steps_of(mode);
+    auto load = [&](auto ic) -> f16x8 {
+      constexpr Step st = step_of(mode, decltype(ic)::value);
+      if constexpr (st.pv) return frag_pv(j - 1, st.kk, st.x);
+      else return frag_qk(j, st.kk, st.x);
+    };
+    f16x8 fr[RING];
+    static_for<RING>([&](auto ic) { fr[decltype(ic)::value] = load(ic); });
+    static_for<nsteps>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      constexpr Step st = step_of(mode, i);
+      const f16x8 a = fr[i % RING];
+      if constexpr (i + RING < nsteps) fr[i % RING] = load(std::integral_constant<int, i + RING>{});
+      if constexpr (st.pv)
+        o_acc[st.x] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[st.kk], o_acc[st.x], 0, 0, 0);
+      else if constexpr (st.kk == 0)
+        s[st.x] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[0], f32x16{}, 0, 0, 0);
+      else
+        s[st.x] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[st.kk], s[st.x], 0, 0, 0);
+    });
+    static_for<RING>([&](auto ic) {
+      __builtin_amdgcn_sched_group_barrier(0x100, reads_of(mode, decltype(ic)::value), 0);
+    });
+    static_for<nsteps>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if constexpr (i + RING < nsteps) __builtin_amdgcn_sched_group_barrier(0x100, reads_of(mode, i + RING), 0);
+    });
+  };
+  auto mma = [&](int j) {  // PV of tile j-1 and QK of tile j, whichever this wave needs
+    const bool do_pv = j >= 1 && !skip(j - 1);
+    const bool do_qk = j < n_tiles && !skip(j);
+    if (do_pv && do_qk) mma_block(j, std::integral_constant<int, 0>{});
+    else if (do_pv) mma_block(j, std::integral_constant<int, 1>{});
+    else if (do_qk) mma_block(j, std::integral_constant<int, 2>{});
   };
 
   // ---- softmax sTask: online softmax of tile j in the log2 domain
-  auto softmax = [&](int j) {
-    const int kj = j * BN;
-    const bool need_mask = (p.causal && kj + BN - 1 > qw) || (kj + BN > S);
-    const int query = qw + n;
+  auto softmax = [&](int j, auto masked) {
+    constexpr bool kMasked = decltype(masked)::value;
     uint32_t keep = 0xffffffffu;  // bit (16*sb + r): key allowed
-    if (need_mask) {
+    if constexpr (kMasked) {
+      const int kj = j * BN;
+      const int query = qw + n;
       keep = 0;
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
@@ -227,103 +347,99 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(Params p) {
           keep |= (ok ? 1u : 0u) << (16 * sb + r);
         }
     }
+    auto kept = [&](int sb, int r) { return !kMasked || ((keep >> (16 * sb + r)) & 1u); };
+
     float mt = NEG_INF;
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float x = ((keep >> (16 * sb + r)) & 1u) ? s[sb][r] : NEG_INF;
-        mt = fmaxf(mt, x);
-      }
-    mt = wave_pair_max(mt);
+      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, kept(sb, r) ? s[sb][r] : NEG_INF);
+    mt = pair_max(mt);
     const float mts = (mt == NEG_INF) ? NEG_INF : mt * cs;
-    const float m_new = fmaxf(m_run, mts);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
+    if (__builtin_amdgcn_ballot_w64(mts > m_run + TAU)) {  // wave-uniform: rescale only when needed
+      const float m_new = fmaxf(m_run, mts);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o_acc[db] *= alpha;
+    }
 
-    float rs = 0.f;
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][r], cs, -m_new));
-        e = ((keep >> (16 * sb + r)) & 1u) ? e : 0.f;
-        rs += e;
+        float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][r], cs, -m_run));
+        if constexpr (kMasked) e = kept(sb, r) ? e : 0.f;
         pf[2 * sb + (r >> 3)][r & 7] = (_Float16)e;
       }
-    rs = wave_pair_sum(rs);
-    l_run = l_run * alpha + rs;
+    // row sum of the fp16 P actually fed to PV: 16 dot2 products against (1, 1)
+    float rs = 0.f;
+    const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
-    for (int db = 0; db < 4; ++db) o_acc[db] *= alpha;
-  };
-
-  // ---- mma sTask 2: O^T[d][query] += V^T[d][key] P^T[key][query] for tile j
-  auto mma_pv = [&](int j) {
-    const LDS _Float16* vs = v_lds + (j & 1) * TILE;
-    const int G = lane >> 4, sl = lane & 15;
+    for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int row1 = 16 * kk + 4 * (G >> 1) + (sl >> 2);
-      const int row2 = row1 + 8;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const int ch = 4 * db + 2 * (G & 1) + ((sl & 3) >> 1);
-        const int within = (sl & 1) << 2;
-        const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (LDS i16x4*)&vs[row1 * HD + ((ch ^ swz_v(row1)) << 3) + within]);
-        const i16x4 a2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (LDS i16x4*)&vs[row2 * HD + ((ch ^ swz_v(row2)) << 3) + within]);
-        const f16x4 h1 = __builtin_bit_cast(f16x4, a1);
-        const f16x4 h2 = __builtin_bit_cast(f16x4, a2);
-        const f16x8 vf = {h1[0], h1[1], h1[2], h1[3], h2[0], h2[1], h2[2], h2[3]};
-        o_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[kk], o_acc[db], 0, 0, 0);
+      for (int e = 0; e < 4; ++e) {
+        const f16x2 pr = {pf[kk][2 * e], pf[kk][2 * e + 1]};
+        rs = __builtin_amdgcn_fdot2(pr, ones, rs, false);
       }
-    }
+    l_run += pair_sum(rs);
+  };
+  auto softmax_tile = [&](int j) {
+    const int kj = j * BN;
+    if ((p.causal && kj + BN - 1 > qw) || kj + BN > S)
+      softmax(j, std::true_type{});
+    else
+      softmax(j, std::false_type{});
   };
 
   if constexpr (!kPingPong) {
-    // ---- serial schedule: every wave runs load-next / QK / softmax / PV per tile
-    fetch(0, 0);
-    stash(0, 0);
+    // ---- serial schedule: every wave runs load-next / QK / store-next /
+    // softmax / PV per tile (group 0 moves K tiles, group 1 V tiles)
+    stage_load(0);
+    stage_store(0);
     lds_barrier();
     for (int j = 0; j < n_tiles; ++j) {
-      fetch(j + 1, j + 1);
+      stage_load(j + 1);  // slot (j+1) & 1 was last read in iteration j-1
+      if (!skip(j)) mma_block(j, std::integral_constant<int, 2>{});
+      stage_store(j + 1);
       if (!skip(j)) {
-        mma_qk(j);
-        softmax(j);
-        mma_pv(j);
+        softmax_tile(j);
+        mma_block(j + 1, std::integral_constant<int, 1>{});
       }
-      stash(j + 1, j + 1);
       lds_barrier();
     }
   } else {
     // ---- ping-pong schedule.  Time is cut into half-steps by workgroup
-    // barriers.  Each wave alternates an mma block (PV of tile j-1, then QK
-    // of tile j) and a softmax block (tile j); group 1 runs one half-step
-    // behind group 0, so on every SIMD one wave keeps the matrix core busy
-    // while the other runs softmax on the VALU.  Group 0 stages its half of
-    // (K_{j+1}, V_j) during its softmax block j, group 1 its half of
-    // (K_{j+2}, V_{j+1}) during its softmax block j; every slot is rewritten
-    // only after both groups have read it.
-    fetch(0, n_tiles);
-    stash(0, n_tiles);
-    if (grp == 1) fetch(1, 0);
+    // barriers.  Each wave alternates an mma block (PV of tile j-1 and QK of
+    // tile j) and a softmax block (tile j); group 1 runs one half-step behind
+    // group 0, so on every SIMD one wave keeps the matrix core busy while the
+    // other runs softmax on the VALU.  Staging: group 0 loads K_{j+1} during
+    // its mma block j (half-step 2j) and stores it during its softmax block j
+    // (2j+1); group 1 loads V_j during its mma block j-1 (2j-1) and stores it
+    // during its softmax block j-1 (2j).  The slot a store overwrites was last
+    // read in half-step 2j-1, and the tile is first read in half-step 2j+2.
+    if (grp == 0) {
+      stage_load(0);
+      stage_store(0);
+    } else {
+      stage_load(0);
+    }
     lds_barrier();
     for (int hs = 0; hs < 2 * n_tiles + 2; ++hs) {
       const int ph = hs - grp;
       if (ph == -1) {
-        stash(1, 0);
+        stage_store(0);  // group 1: V_0
       } else if (ph <= 2 * n_tiles) {
         const int j = ph >> 1;
         if ((ph & 1) == 0) {
-          fetch(j + 1 + grp, j + grp);
+          stage_load(j + 1);  // group 0: K_{j+1}; group 1: V_{j+1}
           __builtin_amdgcn_s_setprio(1);
-          if (j >= 1 && !skip(j - 1)) mma_pv(j - 1);
-          if (j < n_tiles && !skip(j)) mma_qk(j);
+          mma(j);
           __builtin_amdgcn_s_setprio(0);
         } else {
-          if (!skip(j)) softmax(j);
-          stash(j + 1 + grp, j + grp);
+          stage_store(j + 1);
+          if (!skip(j)) softmax_tile(j);
         }
       }
       lds_barrier();
