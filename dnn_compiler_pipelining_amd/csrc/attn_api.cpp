@@ -16,12 +16,14 @@ namespace {
 
 constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
 
-// LIBATTN_SCHEDULE=serial selects the serial tile schedule, a cross-check of
-// the default ping-pong schedule that computes bitwise identical results.
-// Read on every call so a test can switch it inside one process.
+// LIBATTN_SCHEDULE=serial|pingpong selects another tile schedule than the
+// default (overlap); all compute bitwise identical results, so they
+// cross-check each other.  Read on every call so a test can switch it.
 int schedule_from_env() {
   const char* s = std::getenv("LIBATTN_SCHEDULE");
-  return (s && std::strcmp(s, "serial") == 0) ? libattn::SCHEDULE_SERIAL : libattn::SCHEDULE_PINGPONG;
+  if (s && std::strcmp(s, "serial") == 0) return libattn::SCHEDULE_SERIAL;
+  if (s && std::strcmp(s, "pingpong") == 0) return libattn::SCHEDULE_PINGPONG;
+  return libattn::SCHEDULE_OVERLAP;
 }
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }

@@ -8,11 +8,11 @@
 // The tile loop follows the load / mma / softmax sTask split of PipeThreader
 // (page "PipeThreader: Software-Defined Pipelining ... (OSDI 2025)" summary,
 // section "核心方法"), mapped onto gfx950 units:
-//   load    : K/V tiles of 64 keys, global -> registers -> padded LDS rows,
-//             staged ahead of the compute in two-slot rings (the prologue /
-//             steady state / epilogue pattern of software pipelining with
-//             ping-pong buffers, page "AI编译器融合技术 -- 5. 并行性与分布式融合",
-//             section 5.4.2)
+//   load    : K/V tiles of 64 keys, global -> LDS by direct loads
+//             (global_load_lds_dwordx4), staged ahead of the compute in
+//             two-slot rings (the prologue / steady state / epilogue pattern
+//             of software pipelining with ping-pong buffers, page "AI编译器融合
+//             技术 -- 5. 并行性与分布式融合", section 5.4.2)
 //   mma     : S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_32x32x16_f16,
 //             fp16 operands and fp32 accumulation (same page, section 5.2.2:
 //             map the contraction onto the matrix instruction and conform the
@@ -21,8 +21,9 @@
 //             need one cross-lane step (v_permlane32_swap) because the S^T
 //             layout keeps each query in one lane pair (same page, section
 //             5.2.1: subgroup reductions by lane exchange instead of LDS)
-// and the two wave groups are offset by half a tile so that one group's
-// softmax runs on the VALU while the other's MFMAs run on the matrix core.
+// Three tile schedules (see Schedule in attn_kernel.h) order these tasks; the
+// default one overlaps, inside every wave, the softmax of tile j with the
+// MFMAs of QK^T(j+1) and PV(j-1).
 //
 // Layout facts this file relies on (checked on gfx950 with a lane probe):
 //   mfma 32x32x16 f16, lane l, element i of the 8-half operands and r of the
@@ -31,10 +32,12 @@
 //   ds_read_b64_tr_b16: within each 16-lane group, result element j of lane i
 //   is element i%4 of the 8 bytes addressed by lane 4*j + i/4 of the group.
 //   v_permlane32_swap(x, y): x's upper 32 lanes trade places with y's lower 32.
+//   global_load_lds_dwordx4: lane l writes its 16 bytes at LDS M0 + 16*l.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "attn_kernel.h"
 
@@ -48,6 +51,9 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 #define LDS __attribute__((address_space(3)))
+// Lambdas of the kernel body are always inlined: an outlined softmax would
+// pass its register arrays through scratch memory.
+#define INL __attribute__((always_inline))
 
 constexpr int HD = 128;          // head dim
 constexpr int BM = 128;          // query rows per wave group
@@ -61,27 +67,27 @@ constexpr float LN2 = 0.693147180559945309f;
 // final O / l and LSE = m + log2(l) are exact for any m.
 constexpr float TAU = 8.0f;
 
-// LDS layouts (bytes).  Both tiles are staged through registers so that the
-// global loads of a tile can stay in flight across a barrier.
+// LDS layouts (bytes).  A tile slot is a run of 1 KiB DMA instructions.
 //  K: 64 key rows of 256 + 16 B.  The 8 lanes of a ds_read_b128 pass (8
 //    consecutive keys, same 16-byte column) fall 16 B apart in bank space and
 //    a 16-lane pass covers all 64 banks once; every K fragment read is a
-//    compile-time offset from one per-lane base.
-//  V: stored transposed, V^T[d][key]: 128 d rows of 64 keys (128 B) + 16 B,
-//    so a PV fragment (8 keys of one d) is one ds_read_b128 instead of two
-//    transpose reads.  Inside each group of 16 keys the columns are ordered
-//    0-3, 8-11, 4-7, 12-15: lane half h of the MFMA B operand P^T holds keys
-//    {4h..4h+3, 8+4h..8+4h+3} of the group (the accumulator layout of S^T), and
-//    reads exactly those 8 keys as 16 contiguous bytes.
-constexpr int K_ROWB = 2 * HD + 16;     // 272
-constexpr int K_TILEB = BN * K_ROWB;    // 17408
-constexpr int VT_ROWB = 2 * BN + 16;    // 144
-constexpr int VT_TILEB = HD * VT_ROWB;  // 18432
-static_assert(2 * (K_TILEB + VT_TILEB) <= 160 * 1024, "two K and two V^T slots fit the 160 KiB LDS");
-__host__ __device__ constexpr int vt_col(int key) {  // column of key (0..63) in a V^T row
-  return (key & ~15) | (key & 3) | (((key >> 3) & 1) << 2) | (((key >> 2) & 1) << 3);
-}
-// Depth of the fragment prefetch ring of the mma block.
+//    compile-time offset from one per-lane base.  17 DMA instructions per
+//    tile (one 16-byte lane slot per row lands in the padding).
+//  V: 64 key rows of 256 B whose 16-byte chunks are XOR-swizzled by
+//    4*(row & 3).  A ds_read_b64_tr_b16 group reads 4 consecutive rows x 32 B;
+//    the swizzle puts the 4 rows of two groups (4 rows x 64 B) on all 64 banks
+//    once.  Across the four 32-wide d blocks the per-lane address changes by
+//    an XOR with 64*db.  16 DMA instructions per tile.
+constexpr int K_ROWB = 2 * HD + 16;
+constexpr int K_TILEB = BN * K_ROWB;   // 17408
+constexpr int V_TILEB = BN * 2 * HD;   // 16384
+constexpr int K_DMA = K_TILEB / 1024;  // 17
+constexpr int V_DMA = V_TILEB / 1024;  // 16
+constexpr int K_DMA_PER_WAVE = (K_DMA + 7) / 8;  // 3: wave w issues K instructions w, w+8, w+16
+static_assert(K_TILEB % 1024 == 0 && V_TILEB % 1024 == 0, "tile slots are whole DMA instructions");
+static_assert(V_DMA == 16, "wave w issues V instructions w and w+8");
+static_assert(2 * (K_TILEB + V_TILEB) <= 160 * 1024, "two K and two V slots fit the 160 KiB LDS");
+// Depth of the fragment prefetch ring of the mma steps.
 #ifndef ATTN_RING
 #define ATTN_RING 4
 #endif
@@ -105,6 +111,24 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// One direct global -> LDS load of 16 B per lane: lane l writes LDS byte
+// address lds_base + 16*l with the 16 bytes at base + off.  Issued as inline
+// assembly so the compiler does not add conservative waits before unrelated
+// LDS reads; the caller waits with dma_wait() before the barrier that
+// publishes the tile.  M0 is restored afterwards.
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(off), "s"(base), "s"(lds_base)
+      : "memory");
+}
+__device__ __forceinline__ void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // Compile-time loop: f(std::integral_constant<int, i>) for i = 0..N-1.
 template <typename F, int... Is>
 __device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
@@ -117,11 +141,15 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 // Steps of an mma block.  A QK step (kk, x = sb) adds K[32sb.., 16kk..] x
 // Q^T[16kk.., :] into S^T block sb; a PV step (kk, x = db) adds
-// V^T[32db.., 16kk..] x P^T[16kk.., :] into O^T block db.  Mode 0 runs PV of
-// tile j-1 and QK of tile j with the two kinds alternating, so consecutive
-// MFMAs of one accumulator are >= 4 steps apart: per group g the order is
-// PV(g,0) QK(2g,0) PV(g,1) QK(2g,1) PV(g,2) QK(2g+1,0) PV(g,3) QK(2g+1,1).
-// Mode 1 is PV only, mode 2 QK only.
+// V^T[32db.., 16kk..] x P^T[16kk.., :] into O^T block db.
+//   mode 0: PV and QK steps alternate, so consecutive MFMAs of one
+//           accumulator are >= 4 steps apart: per group g the order is
+//           PV(g,0) QK(2g,0) PV(g,1) QK(2g,1) PV(g,2) QK(2g+1,0) PV(g,3)
+//           QK(2g+1,1)
+//   mode 1: PV only;  mode 2: QK only
+//   mode 3: all PV steps (P^T consumed in kk order), then the QK steps of S^T
+//           block 0, then of block 1 -- the order in which a softmax running
+//           alongside frees the old P^T and S^T registers
 struct Step {
   bool pv;
   int kk, x;
@@ -129,16 +157,17 @@ struct Step {
 __host__ __device__ constexpr Step step_of(int mode, int i) {
   return mode == 1   ? Step{true, i >> 2, i & 3}
          : mode == 2 ? Step{false, i >> 1, i & 1}
+         : mode == 3 ? (i < 16 ? Step{true, i >> 2, i & 3} : Step{false, (i - 16) & 7, (i - 16) >> 3})
          : ((i & 7) & 1) == 0 ? Step{true, i >> 3, (i & 7) >> 1}
                               : Step{false, 2 * (i >> 3) + ((i & 7) >> 2), ((i & 7) >> 1) & 1};
 }
-constexpr int steps_of(int mode) { return mode == 0 ? 32 : 16; }
-constexpr int reads_of(int, int) { return 1; }  // LDS reads per fragment
+constexpr int steps_of(int mode) { return (mode == 0 || mode == 3) ? 32 : 16; }
+constexpr int reads_of(int mode, int i) { return step_of(mode, i).pv ? 2 : 1; }  // LDS reads per fragment
 
-template <bool kPingPong>
+template <int kSched>
 __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(Params p) {
   __shared__ __attribute__((aligned(1024))) char k_smem[2 * K_TILEB];
-  __shared__ __attribute__((aligned(1024))) char v_smem[2 * VT_TILEB];
+  __shared__ __attribute__((aligned(1024))) char v_smem[2 * V_TILEB];
   LDS char* const k_lds = (LDS char*)k_smem;
   LDS char* const v_lds = (LDS char*)v_smem;
 
@@ -201,73 +230,65 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(Params p) {
     }
   }
 
-  // ---- K/V staging through registers.  K_t and V_t live in slot t & 1 of
-  // their rings.  Group 0 stages K tiles, group 1 V tiles; each of the 256
-  // threads of a group moves 4 chunks of 16 B per tile.  Rows past the end of
-  // the sequence are loaded from row S-1 (finite data whose scores and weights
-  // are masked to zero).  Loads use a wave-uniform tile base plus a constant
-  // per-thread 32-bit offset.
-  const int gt = tid & (NTHREADS / 2 - 1);
+  // ---- K/V staging by direct global -> LDS loads.  K_t and V_t live in slot
+  // t & 1 of their rings.  Wave w issues K instructions w, w+8, w+16 and V
+  // instructions w, w+8 of a tile: 33 per tile over the 8 waves.  The lane
+  // offsets relative to a tile's first row are fixed; rows past the end of
+  // the sequence are loaded from row S-1 (finite data whose scores and
+  // weights are masked to zero).
   const uint32_t row_bytes = (uint32_t)p.kv_sstride * 2;
-  // K: chunk x = gt + 256u -> key row x / 16, column chunk x % 16
-  const int k_row0 = gt >> 4, k_ch = gt & 15;
-  // V: key quad vq = gt % 16 (keys 4vq..4vq+3), d chunk vc = gt / 16 (d 8vc..8vc+7)
-  const int vq = gt & 15, vc = gt >> 4;
-  // row of chunk u = st_row0 + u * st_drow; byte offset = st_off0 + u * st_doff
-  const int st_row0 = grp == 0 ? k_row0 : 4 * vq;
-  const int st_drow = grp == 0 ? 16 : 1;
-  const uint32_t st_col = (uint32_t)(grp == 0 ? k_ch : vc) * 16u;
-  const uint32_t st_off0 = (uint32_t)st_row0 * row_bytes + st_col;
-  const uint32_t st_doff = (uint32_t)st_drow * row_bytes;
-  const char* st_src;
-  {  // wave-uniform source pointer, so the tile base below lives in SGPRs
-    const uintptr_t a = (uintptr_t)(grp == 0 ? (const char*)kb_ : (const char*)vb_);
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-    st_src = (const char*)(((uintptr_t)hi << 32) | lo);
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t k_lds_base = (uint32_t)(uintptr_t)k_lds, v_lds_base = (uint32_t)(uintptr_t)v_lds;
+  int k_row[K_DMA_PER_WAVE];
+  uint32_t k_col[K_DMA_PER_WAVE];
+#pragma unroll
+  for (int u = 0; u < K_DMA_PER_WAVE; ++u) {
+    const int o = 64 * (wave + 8 * u) + lane;  // 16-byte lane slot inside the tile
+    k_row[u] = o / (K_ROWB / 16);
+    const int cb = o - k_row[u] * (K_ROWB / 16);
+    k_col[u] = 16u * (uint32_t)(cb < 16 ? cb : 15);  // padding slot: any in-bounds chunk of the row
   }
-  u32x4 stg[4];
-  auto stage_load = [&](int tile) {  // global -> registers (this group's tensor)
-    tile = __builtin_amdgcn_readfirstlane(tile);
-    if (tile >= n_tiles) return;
-    if ((tile + 1) * BN <= S) {
-      const char* base = st_src + (int64_t)tile * BN * row_bytes;
+  const int v_rowl = lane >> 4;                                    // + 4 * instruction
+  const uint32_t v_col = 16u * (uint32_t)((lane & 15) ^ (v_rowl << 2));  // chunk stored at slot lane & 15
+  auto stage = [&](int tk, int tv) INL {  // issue this wave's DMA for K tile tk and V tile tv
+    tk = __builtin_amdgcn_readfirstlane(tk);
+    tv = __builtin_amdgcn_readfirstlane(tv);
+    if (tk < n_tiles) {
+      const char* base = (const char*)kb_ + (int64_t)tk * BN * row_bytes;
+      const bool full = (tk + 1) * BN <= S;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) stg[u] = *reinterpret_cast<const u32x4*>(base + (st_off0 + u * st_doff));
-    } else {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int key = min(tile * BN + st_row0 + u * st_drow, S - 1);
-        stg[u] = *reinterpret_cast<const u32x4*>(st_src + (int64_t)key * row_bytes + st_col);
+      for (int u = 0; u < K_DMA_PER_WAVE; ++u) {
+        const int i = wave_s + 8 * u;
+        if (i < K_DMA) {
+          const int row = full ? k_row[u] : min(k_row[u], S - 1 - tk * BN);
+          dma16(base, (uint32_t)row * row_bytes + k_col[u], k_lds_base + (tk & 1) * K_TILEB + 1024 * i);
+        }
       }
     }
-  };
-  auto stage_store = [&](int tile) {  // registers -> LDS slot tile & 1
-    if (tile >= n_tiles) return;
-    if (grp == 0) {
-      LDS char* dst = k_lds + (tile & 1) * K_TILEB + k_row0 * K_ROWB + k_ch * 16;
+    if (tv < n_tiles) {
+      const char* base = (const char*)vb_ + (int64_t)tv * BN * row_bytes;
+      const bool full = (tv + 1) * BN <= S;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) *(LDS u32x4*)(dst + 16 * u * K_ROWB) = stg[u];
-    } else {
-      // transpose: for each of the 8 d values of the chunk, the 4 keys of the
-      // quad become one 8-byte word of V^T row d
-      LDS char* dst = v_lds + (tile & 1) * VT_TILEB + vc * 8 * VT_ROWB + 2 * vt_col(4 * vq);
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const uint32_t lo0 = __builtin_amdgcn_perm(stg[1][m], stg[0][m], 0x05040100u);
-        const uint32_t lo1 = __builtin_amdgcn_perm(stg[3][m], stg[2][m], 0x05040100u);
-        const uint32_t hi0 = __builtin_amdgcn_perm(stg[1][m], stg[0][m], 0x07060302u);
-        const uint32_t hi1 = __builtin_amdgcn_perm(stg[3][m], stg[2][m], 0x07060302u);
-        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-        *(LDS u32x2*)(dst + (2 * m) * VT_ROWB) = u32x2{lo0, lo1};
-        *(LDS u32x2*)(dst + (2 * m + 1) * VT_ROWB) = u32x2{hi0, hi1};
+      for (int u = 0; u < 2; ++u) {
+        const int i = wave_s + 8 * u;
+        const int row0 = 4 * i + v_rowl;
+        const int row = full ? row0 : min(row0, S - 1 - tv * BN);
+        dma16(base, (uint32_t)row * row_bytes + v_col, v_lds_base + (tv & 1) * V_TILEB + 1024 * i);
       }
     }
   };
 
   // per-lane fragment bases (bytes); everything else is a compile-time offset
-  const int k_frag = n * K_ROWB + 16 * hh;    // A operand of QK^T: key row n, d column 8*hh
-  const int v_frag = n * VT_ROWB + 16 * hh;   // A operand of PV: V^T row n, key columns of lane half hh
+  const int k_frag = n * K_ROWB + 16 * hh;  // A operand of QK^T: key row n, d column 8*hh
+  int v_frag[4];                            // transpose reads of V, one base per 32-wide d block
+  {
+    const int vg = lane >> 4, vsl = lane & 15;
+    const int r0 = 4 * (vg >> 1) + (vsl >> 2);
+    const int c0 = 2 * (vg & 1) + ((vsl & 3) >> 1);
+    const int f0 = r0 * 2 * HD + ((c0 ^ ((r0 & 3) << 2)) << 4) + ((vsl & 1) << 3);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) v_frag[db] = f0 ^ (64 * db);
+  }
 
   f32x16 o_acc[4];
 #pragma unroll
@@ -275,43 +296,125 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(Params p) {
   float m_run = M_INIT;  // running max (log2 units) of the scores of query n
   float l_run = 0.f;     // running sum of 2^(score - m_run), from the fp16 P
   const float cs = p.cs;
-  f32x16 s[2];           // S^T of the current tile
-  f16x8 pf[4];           // P^T of the current tile (PV operand)
 
-  // a wave skips every tile that lies wholly above its causal diagonal
-  auto skip = [&](int j) { return !active || (p.causal && j * BN > qw + 31); };
+  // A wave skips every tile that lies wholly above its causal diagonal.  The
+  // tests take wave-uniform copies so that they compile to scalar branches.
+  const int qw_u = __builtin_amdgcn_readfirstlane(qw);
+  const bool active_u = __builtin_amdgcn_readfirstlane(active ? 1 : 0) != 0;
+  auto skip = [&](int j) INL { return !active_u || (p.causal && j * BN > qw_u + 31); };
+  auto is_masked = [&](int j) INL { return (p.causal && j * BN + BN - 1 > qw_u) || j * BN + BN > S; };
 
-  // ---- mma sTasks
-  auto frag_qk = [&](int j, int kk, int sb) -> f16x8 {
+  // ---- fragments of the mma sTasks
+  auto frag_qk = [&](int j, int kk, int sb) INL -> f16x8 {
     return *(const LDS f16x8*)(k_lds + (j & 1) * K_TILEB + k_frag + 32 * sb * K_ROWB + 32 * kk);
   };
-  auto frag_pv = [&](int j, int kk, int db) -> f16x8 {
-    return *(const LDS f16x8*)(v_lds + (j & 1) * VT_TILEB + v_frag + 32 * db * VT_ROWB + 32 * kk);
+  auto frag_pv = [&](int j, int kk, int db) INL -> f16x8 {
+    const LDS char* a = v_lds + (j & 1) * V_TILEB + v_frag[db] + 16 * kk * 2 * HD;
+    const f16x4 h1 = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS i16x4*)a));
+    const f16x4 h2 = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS i16x4*)(a + 8 * 2 * HD)));
+    return f16x8{h1[0], h1[1], h1[2], h1[3], h2[0], h2[1], h2[2], h2[3]};
   };
-  // One mma block: the fragments of the next RING steps are always in
-  // flight; the scheduler is pinned to "MFMA i, then the LDS reads of step
-  // i + RING" so the matrix core never waits on a just-issued read.
-  auto mma_block = [&](int j, auto mode_c) {
-    constexpr int mode = decltype(mode_c)::value;  // 0: PV(j-1)+QK(j), 1: PV(j-1), 2: QK(j)
+
+  // ---- softmax sTask: online softmax of tile j (scores sc) in the log2
+  // domain, P^T into pd.  Returns the rescale factor of O and whether any
+  // lane needs it (wave-uniform); the caller applies O *= alpha once the PV of
+  // the previous tile has been accumulated.
+  struct Rescale {
+    bool any;
+    float alpha;
+  };
+  auto softmax = [&](int j, f32x16 (&sc)[2], f16x8 (&pd)[4], auto masked) INL -> Rescale {
+    constexpr bool kMasked = decltype(masked)::value;
+    // Key (sb, r) of this lane is kj + 32sb + 8(r/4) + 4hh + r%4; it is
+    // allowed iff it is below end = min(S, query + 1) (causal) or S, i.e. iff
+    // the compile-time part 32sb + 8(r/4) + r%4 is below lim.
+    int lim = 0;
+    if constexpr (kMasked) {
+      const int query = qw + n;
+      const int end = p.causal ? min(S, query + 1) : S;
+      lim = end - j * BN - 4 * hh;
+    }
+    auto kept = [&](int sb, int r) INL { return !kMasked || 32 * sb + 8 * (r >> 2) + (r & 3) < lim; };
+
+    // tile max: four independent chains, then combined
+    float mq[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      mq[q] = NEG_INF;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int sb = q >> 1, r = 8 * (q & 1) + e;
+        mq[q] = fmaxf(mq[q], kept(sb, r) ? sc[sb][r] : NEG_INF);
+      }
+    }
+    const float mt = pair_max(fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3])));
+    const float mts = (mt == NEG_INF) ? NEG_INF : mt * cs;
+    Rescale rz;
+    rz.any = __builtin_amdgcn_ballot_w64(mts > m_run + TAU) != 0;  // wave-uniform
+    const float m_new = rz.any ? fmaxf(m_run, mts) : m_run;
+    rz.alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    l_run *= rz.alpha;
+
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[sb][r], cs, -m_run));
+        if constexpr (kMasked) e = kept(sb, r) ? e : 0.f;
+        pd[2 * sb + (r >> 3)][r & 7] = (_Float16)e;
+      }
+    // row sum of the fp16 P actually fed to PV: dot2 products against (1, 1)
+    float rq[2] = {0.f, 0.f};
+    const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const f16x2 pr = {pd[kk][2 * e], pd[kk][2 * e + 1]};
+        rq[kk & 1] = __builtin_amdgcn_fdot2(pr, ones, rq[kk & 1], false);
+      }
+    l_run += pair_sum(rq[0] + rq[1]);
+    return rz;
+  };
+  auto rescale_o = [&](const Rescale& rz) INL {
+    if (rz.any) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o_acc[db] *= rz.alpha;
+    }
+  };
+
+  // ---- one block of mma steps, optionally fused with a softmax in the same
+  // basic block.  QK steps read K tile jq into sd; PV steps read V tile jv
+  // with P^T from ps.  The fragments of the next RING steps are always in
+  // flight; the scheduler is pinned to "MFMA i, LDS reads of step i + RING,
+  // then a share of the softmax VALU work", so the matrix core, the LDS and
+  // the VALU stay busy together.
+  struct NoSoftmax {};
+  auto block = [&](auto mode_c, int jq, f32x16 (&sd)[2], int jv, f16x8 (&ps)[4], auto sm) INL -> Rescale {
+    constexpr int mode = decltype(mode_c)::value;
     constexpr int nsteps = steps_of(mode);
-    auto load = [&](auto ic) -> f16x8 {
+    constexpr bool kSoftmax = !std::is_same_v<decltype(sm), NoSoftmax>;
+    auto load = [&](auto ic) INL -> f16x8 {
       constexpr Step st = step_of(mode, decltype(ic)::value);
-      if constexpr (st.pv) return frag_pv(j - 1, st.kk, st.x);
-      else return frag_qk(j, st.kk, st.x);
+      if constexpr (st.pv) return frag_pv(jv, st.kk, st.x);
+      else return frag_qk(jq, st.kk, st.x);
     };
     f16x8 fr[RING];
     static_for<RING>([&](auto ic) { fr[decltype(ic)::value] = load(ic); });
+    Rescale rz{false, 1.f};
+    if constexpr (kSoftmax) rz = sm();
     static_for<nsteps>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
       constexpr Step st = step_of(mode, i);
       const f16x8 a = fr[i % RING];
       if constexpr (i + RING < nsteps) fr[i % RING] = load(std::integral_constant<int, i + RING>{});
       if constexpr (st.pv)
-        o_acc[st.x] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[st.kk], o_acc[st.x], 0, 0, 0);
+        o_acc[st.x] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, ps[st.kk], o_acc[st.x], 0, 0, 0);
       else if constexpr (st.kk == 0)
-        s[st.x] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[0], f32x16{}, 0, 0, 0);
+        sd[st.x] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[0], f32x16{}, 0, 0, 0);
       else
-        s[st.x] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[st.kk], s[st.x], 0, 0, 0);
+        sd[st.x] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[st.kk], sd[st.x], 0, 0, 0);
     });
     static_for<RING>([&](auto ic) {
       __builtin_amdgcn_sched_group_barrier(0x100, reads_of(mode, decltype(ic)::value), 0);
@@ -320,130 +423,155 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(Params p) {
       constexpr int i = decltype(ic)::value;
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       if constexpr (i + RING < nsteps) __builtin_amdgcn_sched_group_barrier(0x100, reads_of(mode, i + RING), 0);
+      // VALU incl. transcendental; nsteps x share stays below the unmasked softmax's ~130 VALU
+      if constexpr (kSoftmax) __builtin_amdgcn_sched_group_barrier(0x402, 128 / nsteps, 0);
     });
+    return rz;
   };
-  auto mma = [&](int j) {  // PV of tile j-1 and QK of tile j, whichever this wave needs
-    const bool do_pv = j >= 1 && !skip(j - 1);
-    const bool do_qk = j < n_tiles && !skip(j);
-    if (do_pv && do_qk) mma_block(j, std::integral_constant<int, 0>{});
-    else if (do_pv) mma_block(j, std::integral_constant<int, 1>{});
-    else if (do_qk) mma_block(j, std::integral_constant<int, 2>{});
-  };
-
-  // ---- softmax sTask: online softmax of tile j in the log2 domain
-  auto softmax = [&](int j, auto masked) {
-    constexpr bool kMasked = decltype(masked)::value;
-    uint32_t keep = 0xffffffffu;  // bit (16*sb + r): key allowed
-    if constexpr (kMasked) {
-      const int kj = j * BN;
-      const int query = qw + n;
-      keep = 0;
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kj + 32 * sb + 8 * (r >> 2) + 4 * hh + (r & 3);
-          const bool ok = key < S && (!p.causal || key <= query);
-          keep |= (ok ? 1u : 0u) << (16 * sb + r);
-        }
-    }
-    auto kept = [&](int sb, int r) { return !kMasked || ((keep >> (16 * sb + r)) & 1u); };
-
-    float mt = NEG_INF;
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, kept(sb, r) ? s[sb][r] : NEG_INF);
-    mt = pair_max(mt);
-    const float mts = (mt == NEG_INF) ? NEG_INF : mt * cs;
-    if (__builtin_amdgcn_ballot_w64(mts > m_run + TAU)) {  // wave-uniform: rescale only when needed
-      const float m_new = fmaxf(m_run, mts);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) o_acc[db] *= alpha;
-    }
-
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][r], cs, -m_run));
-        if constexpr (kMasked) e = kept(sb, r) ? e : 0.f;
-        pf[2 * sb + (r >> 3)][r & 7] = (_Float16)e;
-      }
-    // row sum of the fp16 P actually fed to PV: 16 dot2 products against (1, 1)
-    float rs = 0.f;
-    const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const f16x2 pr = {pf[kk][2 * e], pf[kk][2 * e + 1]};
-        rs = __builtin_amdgcn_fdot2(pr, ones, rs, false);
-      }
-    l_run += pair_sum(rs);
-  };
-  auto softmax_tile = [&](int j) {
-    const int kj = j * BN;
-    if ((p.causal && kj + BN - 1 > qw) || kj + BN > S)
-      softmax(j, std::true_type{});
-    else
-      softmax(j, std::false_type{});
+  using M_BOTH = std::integral_constant<int, 0>;
+  using M_PV = std::integral_constant<int, 1>;
+  using M_QK = std::integral_constant<int, 2>;
+  using M_FUSED = std::integral_constant<int, 3>;
+  f16x8 pf[4];  // P^T of the tile whose softmax ran last
+  f32x16 s[2];  // S^T of the tile whose QK^T ran last
+  auto softmax_tile = [&](int j) INL {
+    const Rescale rz = is_masked(j) ? softmax(j, s, pf, std::true_type{}) : softmax(j, s, pf, std::false_type{});
+    rescale_o(rz);
   };
 
-  if constexpr (!kPingPong) {
-    // ---- serial schedule: every wave runs load-next / QK / store-next /
-    // softmax / PV per tile (group 0 moves K tiles, group 1 V tiles)
-    stage_load(0);
-    stage_store(0);
+  if constexpr (kSched == SCHEDULE_SERIAL) {
+    // ---- serial schedule: every wave runs stage-next / QK / softmax / PV per
+    // tile; slot (j+1) & 1 was last read in iteration j-1
+    stage(0, 0);
+    dma_wait();
     lds_barrier();
     for (int j = 0; j < n_tiles; ++j) {
-      stage_load(j + 1);  // slot (j+1) & 1 was last read in iteration j-1
-      if (!skip(j)) mma_block(j, std::integral_constant<int, 2>{});
-      stage_store(j + 1);
+      stage(j + 1, j + 1);
       if (!skip(j)) {
+        block(M_QK{}, j, s, 0, pf, NoSoftmax{});
         softmax_tile(j);
-        mma_block(j + 1, std::integral_constant<int, 1>{});
+        block(M_PV{}, 0, s, j, pf, NoSoftmax{});
       }
+      dma_wait();
       lds_barrier();
     }
-  } else {
+  } else if constexpr (kSched == SCHEDULE_PINGPONG) {
     // ---- ping-pong schedule.  Time is cut into half-steps by workgroup
     // barriers.  Each wave alternates an mma block (PV of tile j-1 and QK of
     // tile j) and a softmax block (tile j); group 1 runs one half-step behind
     // group 0, so on every SIMD one wave keeps the matrix core busy while the
-    // other runs softmax on the VALU.  Staging: group 0 loads K_{j+1} during
-    // its mma block j (half-step 2j) and stores it during its softmax block j
-    // (2j+1); group 1 loads V_j during its mma block j-1 (2j-1) and stores it
-    // during its softmax block j-1 (2j).  The slot a store overwrites was last
-    // read in half-step 2j-1, and the tile is first read in half-step 2j+2.
-    if (grp == 0) {
-      stage_load(0);
-      stage_store(0);
-    } else {
-      stage_load(0);
-    }
+    // other runs softmax on the VALU.  In half-step 2j all waves issue the
+    // loads of K_{j+1} and V_j, whose slots were last read in half-step 2j-1,
+    // and wait for them at the end of half-step 2j+1; the tiles are first read
+    // in half-step 2j+2.
+    stage(0, n_tiles);
+    dma_wait();
     lds_barrier();
     for (int hs = 0; hs < 2 * n_tiles + 2; ++hs) {
       const int ph = hs - grp;
-      if (ph == -1) {
-        stage_store(0);  // group 1: V_0
-      } else if (ph <= 2 * n_tiles) {
+      if ((hs & 1) == 0) stage((hs >> 1) + 1, hs >> 1);
+      if (ph >= 0 && ph <= 2 * n_tiles) {
         const int j = ph >> 1;
         if ((ph & 1) == 0) {
-          stage_load(j + 1);  // group 0: K_{j+1}; group 1: V_{j+1}
+          const bool do_pv = j >= 1 && !skip(j - 1);
+          const bool do_qk = j < n_tiles && !skip(j);
           __builtin_amdgcn_s_setprio(1);
-          mma(j);
+          if (do_pv && do_qk) block(M_BOTH{}, j, s, j - 1, pf, NoSoftmax{});
+          else if (do_pv) block(M_PV{}, j, s, j - 1, pf, NoSoftmax{});
+          else if (do_qk) block(M_QK{}, j, s, j - 1, pf, NoSoftmax{});
           __builtin_amdgcn_s_setprio(0);
-        } else {
-          stage_store(j + 1);
-          if (!skip(j)) softmax_tile(j);
+        } else if (!skip(j)) {
+          softmax_tile(j);
         }
       }
+      if (hs & 1) dma_wait();
       lds_barrier();
     }
+  } else {
+    // ---- overlap schedule: all eight waves run the same phases, and the
+    // overlap of MFMA and VALU work happens inside each wave.  Iteration j is
+    // one block -- PV of tile j-1 and QK^T of tile j+1 on the matrix core,
+    // the softmax of tile j on the VALU alongside -- then O *= alpha_j, then
+    // a barrier.  Iteration j reads K_{j+1} and V_{j-1} and loads K_{j+2} and
+    // V_j into the slots that K_j and V_{j-2} left in iteration j-1.  Per
+    // accumulator the operations are those of the serial schedule in the same
+    // order (O is rescaled between PV(j-1) and PV(j) in both).
+    //
+    // No wave skips a tile here: the steady-state loop has one code path per
+    // mask case, so O, S and P each keep a single set of registers.  A tile
+    // wholly above a wave's diagonal (only ever the last one) is computed with
+    // every key masked, which is an exact no-op: the tile max is -inf, so
+    // alpha = 1 and the running max stays, every P is 0, l gains 0 and PV adds
+    // zeros.  Waves of a missing odd head (hl == g) compute head h of the pair
+    // and store nothing.
+    // S^T and P^T alternate between two register sets (sa/sb, pa/pb) from
+    // one iteration to the next, so the loops are unrolled twice.  On entry
+    // to each loop S^T of the current tile is in sa and P^T of the previous
+    // tile in pa.
+    f32x16 sa[2], sb[2];
+    f16x8 pa[4], pb[4];
+    auto iter = [&](int j, auto with_pv, auto with_qk, auto masked, f32x16 (&sc)[2], f32x16 (&sn)[2],
+                    f16x8 (&pp)[4], f16x8 (&pc)[4]) INL {
+      constexpr bool kPV = decltype(with_pv)::value, kQK = decltype(with_qk)::value;
+      stage(j + 2, j);
+      auto sm = [&]() INL { return softmax(j, sc, pc, masked); };
+      Rescale rz;
+      if constexpr (kPV && kQK) rz = block(M_FUSED{}, j + 1, sn, j - 1, pp, sm);
+      else if constexpr (kQK) rz = block(M_QK{}, j + 1, sn, j - 1, pp, sm);
+      else if constexpr (kPV) rz = block(M_PV{}, j + 1, sn, j - 1, pp, sm);
+      else rz = sm();
+      rescale_o(rz);
+      dma_wait();
+      lds_barrier();
+    };
+    auto to_a = [&]() INL {  // back to the loop-entry convention
+#pragma unroll
+      for (int i = 0; i < 2; ++i) sa[i] = sb[i];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pa[i] = pb[i];
+    };
+    // Tiles below j_ms need no mask for any wave of the workgroup; the
+    // steady-state loop is split there so that each loop has one code path.
+    // The first and the last iteration always take the masked path (with no
+    // key masked it computes the same values).
+    const int j_ms = min(n_tiles, p.causal ? min(q0, S) / BN : S / BN);
+    using T = std::true_type;
+    using F = std::false_type;
+    stage(0, n_tiles);
+    stage(1, n_tiles);
+    dma_wait();
+    lds_barrier();
+    block(M_QK{}, 0, sa, 0, pa, NoSoftmax{});
+    lds_barrier();  // everyone has read K_0 before iteration 0 reloads its slot
+    if (n_tiles == 1) {
+      iter(0, F{}, F{}, T{}, sa, sb, pa, pb);
+    } else {
+      iter(0, F{}, T{}, T{}, sa, sb, pa, pb);
+      to_a();
+      int j = 1;
+      const int j_u = min(j_ms, n_tiles - 1);  // unmasked iterations: [1, j_u)
+      for (; j + 1 < j_u; j += 2) {
+        iter(j, T{}, T{}, F{}, sa, sb, pa, pb);
+        iter(j + 1, T{}, T{}, F{}, sb, sa, pb, pa);
+      }
+      if (j < j_u) {
+        iter(j, T{}, T{}, F{}, sa, sb, pa, pb);
+        to_a();
+        ++j;
+      }
+      for (; j + 1 < n_tiles - 1; j += 2) {
+        iter(j, T{}, T{}, T{}, sa, sb, pa, pb);
+        iter(j + 1, T{}, T{}, T{}, sb, sa, pb, pa);
+      }
+      if (j < n_tiles - 1) {
+        iter(j, T{}, T{}, T{}, sa, sb, pa, pb);
+        to_a();
+        ++j;
+      }
+      iter(j, T{}, F{}, T{}, sa, sb, pa, pb);
+    }
+    // PV of the last tile, whose P^T the last iteration left in pb
+    block(M_PV{}, 0, sa, n_tiles - 1, pb, NoSoftmax{});
   }
 
   // ---- epilogue: O = O^T / l (fp16, round to nearest even), LSE in natural log
@@ -476,9 +604,11 @@ hipError_t launch_attn_fwd(const Params& p, hipStream_t stream) {
   const int64_t nb = grid_blocks(p);
   if (nb <= 0) return hipErrorInvalidValue;
   if (p.schedule == SCHEDULE_SERIAL)
-    hipLaunchKernelGGL(attn_fwd_kernel<false>, dim3((unsigned)nb), dim3(NTHREADS), 0, stream, p);
+    hipLaunchKernelGGL(attn_fwd_kernel<SCHEDULE_SERIAL>, dim3((unsigned)nb), dim3(NTHREADS), 0, stream, p);
+  else if (p.schedule == SCHEDULE_PINGPONG)
+    hipLaunchKernelGGL(attn_fwd_kernel<SCHEDULE_PINGPONG>, dim3((unsigned)nb), dim3(NTHREADS), 0, stream, p);
   else
-    hipLaunchKernelGGL(attn_fwd_kernel<true>, dim3((unsigned)nb), dim3(NTHREADS), 0, stream, p);
+    hipLaunchKernelGGL(attn_fwd_kernel<SCHEDULE_OVERLAP>, dim3((unsigned)nb), dim3(NTHREADS), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -7,10 +7,13 @@
 
 namespace libattn {
 
-// Tile schedules of the kernel.  Both compute bitwise identical results; the
-// serial one exists to cross-check the ping-pong one (an LDS race in either
-// would make them differ).
-enum Schedule { SCHEDULE_PINGPONG = 0, SCHEDULE_SERIAL = 1 };
+// Tile schedules of the kernel.  All compute bitwise identical results (each
+// accumulator sees the same operations in the same order), so running one
+// against another cross-checks them: an LDS race in any would show up.
+//   OVERLAP : every wave overlaps its own softmax with the next tile's MFMAs
+//   PINGPONG: two wave groups offset by half a tile alternate MFMA and softmax
+//   SERIAL  : one barrier per tile, no overlap (the reference order)
+enum Schedule { SCHEDULE_OVERLAP = 0, SCHEDULE_PINGPONG = 1, SCHEDULE_SERIAL = 2 };
 
 // Launch parameters.  Pointers are device pointers; strides are in elements.
 struct Params {

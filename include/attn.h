@@ -32,9 +32,10 @@
  * synchronisation.  The library allocates no memory, keeps no state between
  * calls, is thread-safe, and gives bitwise identical results run to run.
  *
- * The environment variable LIBATTN_SCHEDULE=serial (read at each call)
- * selects a serial tile schedule instead of the default ping-pong one; both
- * give bitwise identical results, so it serves as a cross-check.
+ * The environment variable LIBATTN_SCHEDULE (read at each call) selects the
+ * kernel's tile schedule: "overlap", "pingpong" or "serial"; unset or any
+ * other value gives the default.  All schedules give bitwise identical
+ * results, so each serves as a cross-check of the others.
  *
  * Errors: on invalid arguments nothing is launched and a nonzero ATTN_ERR_*
  * code is returned; a failed launch returns ATTN_ERR_HIP.  No exception
