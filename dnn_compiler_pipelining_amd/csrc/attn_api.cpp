@@ -16,14 +16,14 @@ namespace {
 
 constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
 
-// LIBATTN_SCHEDULE=serial|pingpong selects another tile schedule than the
-// default (overlap); all compute bitwise identical results, so they
+// LIBATTN_SCHEDULE=overlap|pingpong selects another tile schedule than the
+// default (serial); all compute bitwise identical results, so they
 // cross-check each other.  Read on every call so a test can switch it.
 int schedule_from_env() {
   const char* s = std::getenv("LIBATTN_SCHEDULE");
-  if (s && std::strcmp(s, "serial") == 0) return libattn::SCHEDULE_SERIAL;
+  if (s && std::strcmp(s, "overlap") == 0) return libattn::SCHEDULE_OVERLAP;
   if (s && std::strcmp(s, "pingpong") == 0) return libattn::SCHEDULE_PINGPONG;
-  return libattn::SCHEDULE_OVERLAP;
+  return libattn::SCHEDULE_SERIAL;
 }
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }

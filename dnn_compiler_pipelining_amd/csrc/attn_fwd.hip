@@ -21,9 +21,10 @@
 //             need one cross-lane step (v_permlane32_swap) because the S^T
 //             layout keeps each query in one lane pair (same page, section
 //             5.2.1: subgroup reductions by lane exchange instead of LDS)
-// Three tile schedules (see Schedule in attn_kernel.h) order these tasks; the
-// default one overlaps, inside every wave, the softmax of tile j with the
-// MFMAs of QK^T(j+1) and PV(j-1).
+// Three tile schedules (see Schedule in attn_kernel.h) order these tasks and
+// give the same bits: serial (the default), an overlap schedule that fuses the
+// softmax of tile j with the MFMAs of QK^T(j+1) and PV(j-1) in every wave,
+// and a ping-pong schedule of two wave groups offset by half a tile.
 //
 // Layout facts this file relies on (checked on gfx950 with a lane probe):
 //   mfma 32x32x16 f16, lane l, element i of the 8-half operands and r of the
@@ -86,7 +87,11 @@ constexpr int V_DMA = V_TILEB / 1024;  // 16
 constexpr int K_DMA_PER_WAVE = (K_DMA + 7) / 8;  // 3: wave w issues K instructions w, w+8, w+16
 static_assert(K_TILEB % 1024 == 0 && V_TILEB % 1024 == 0, "tile slots are whole DMA instructions");
 static_assert(V_DMA == 16, "wave w issues V instructions w and w+8");
-static_assert(2 * (K_TILEB + V_TILEB) <= 160 * 1024, "two K and two V slots fit the 160 KiB LDS");
+// K tiles rotate through three slots, V tiles through two: K_t stays in LDS
+// for the whole iteration after its QK^T, so a softmax that has to be redone
+// can recompute S^T from it.
+constexpr int K_SLOTS = 3, V_SLOTS = 2;
+static_assert(K_SLOTS * K_TILEB + V_SLOTS * V_TILEB <= 160 * 1024, "the K and V rings fit the 160 KiB LDS");
 // Depth of the fragment prefetch ring of the mma steps.
 #ifndef ATTN_RING
 #define ATTN_RING 4
@@ -146,18 +151,19 @@ __device__ __forceinline__ void static_for(F&& f) {
 //           accumulator are >= 4 steps apart: per group g the order is
 //           PV(g,0) QK(2g,0) PV(g,1) QK(2g,1) PV(g,2) QK(2g+1,0) PV(g,3)
 //           QK(2g+1,1)
-//   mode 1: PV only;  mode 2: QK only
-//   mode 3: all PV steps (P^T consumed in kk order), then the QK steps of S^T
-//           block 0, then of block 1 -- the order in which a softmax running
-//           alongside frees the old P^T and S^T registers
+//   mode 1: PV only, k-major over the four O^T blocks
+//   mode 2: QK only, S^T block 0 first (so it is complete half-way)
+//   mode 3: the QK steps of mode 2, then the PV steps of mode 1
+// Each accumulator sees its k steps in increasing order in every mode, so all
+// modes give the same bits.
 struct Step {
   bool pv;
   int kk, x;
 };
 __host__ __device__ constexpr Step step_of(int mode, int i) {
   return mode == 1   ? Step{true, i >> 2, i & 3}
-         : mode == 2 ? Step{false, i >> 1, i & 1}
-         : mode == 3 ? (i < 16 ? Step{true, i >> 2, i & 3} : Step{false, (i - 16) & 7, (i - 16) >> 3})
+         : mode == 2 ? Step{false, i & 7, i >> 3}
+         : mode == 3 ? (i < 16 ? Step{false, i & 7, i >> 3} : Step{true, (i - 16) >> 2, (i - 16) & 3})
          : ((i & 7) & 1) == 0 ? Step{true, i >> 3, (i & 7) >> 1}
                               : Step{false, 2 * (i >> 3) + ((i & 7) >> 2), ((i & 7) >> 1) & 1};
 }
@@ -166,8 +172,8 @@ constexpr int reads_of(int mode, int i) { return step_of(mode, i).pv ? 2 : 1; } 
 
 template <int kSched>
 __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(Params p) {
-  __shared__ __attribute__((aligned(1024))) char k_smem[2 * K_TILEB];
-  __shared__ __attribute__((aligned(1024))) char v_smem[2 * V_TILEB];
+  __shared__ __attribute__((aligned(1024))) char k_smem[K_SLOTS * K_TILEB];
+  __shared__ __attribute__((aligned(1024))) char v_smem[V_SLOTS * V_TILEB];
   LDS char* const k_lds = (LDS char*)k_smem;
   LDS char* const v_lds = (LDS char*)v_smem;
 
@@ -261,7 +267,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(Params p) {
         const int i = wave_s + 8 * u;
         if (i < K_DMA) {
           const int row = full ? k_row[u] : min(k_row[u], S - 1 - tk * BN);
-          dma16(base, (uint32_t)row * row_bytes + k_col[u], k_lds_base + (tk & 1) * K_TILEB + 1024 * i);
+          dma16(base, (uint32_t)row * row_bytes + k_col[u], k_lds_base + (tk % K_SLOTS) * K_TILEB + 1024 * i);
         }
       }
     }
@@ -306,7 +312,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(Params p) {
 
   // ---- fragments of the mma sTasks
   auto frag_qk = [&](int j, int kk, int sb) INL -> f16x8 {
-    return *(const LDS f16x8*)(k_lds + (j & 1) * K_TILEB + k_frag + 32 * sb * K_ROWB + 32 * kk);
+    return *(const LDS f16x8*)(k_lds + (j % K_SLOTS) * K_TILEB + k_frag + 32 * sb * K_ROWB + 32 * kk);
   };
   auto frag_pv = [&](int j, int kk, int db) INL -> f16x8 {
     const LDS char* a = v_lds + (j & 1) * V_TILEB + v_frag[db] + 16 * kk * 2 * HD;
@@ -316,82 +322,146 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(Params p) {
   };
 
   // ---- softmax sTask: online softmax of tile j (scores sc) in the log2
-  // domain, P^T into pd.  Returns the rescale factor of O and whether any
-  // lane needs it (wave-uniform); the caller applies O *= alpha once the PV of
-  // the previous tile has been accumulated.
+  // domain, P^T into pd.  It yields the rescale factor alpha of O and whether
+  // any lane needs it (wave-uniform); the caller applies O *= alpha once the
+  // PV of the previous tile has been accumulated.
+  //
+  // The work is cut into parts with compile-time indices so that a fused mma
+  // block can place each part between two MFMAs:
+  //   X0..X7  tile max: four chains of 8 scores, half a chain per part
+  //   X8, X9  lane-pair max, tile max in log2 units, ballot of the lazy
+  //           rescale test (is the tile max more than TAU above m?)
+  //   D       new running max m, alpha = 2^(m_old - m), -m for the exponents
+  //   E0..E31 P = 2^(s*cs - m) for score e; every second part also packs an
+  //           earlier pair to fp16 and adds it to the row sum (dot2 against
+  //           (1, 1)), one pair behind to hide the exponential's latency
+  //   E32     packs the last pair
+  //   E33     row sum across the lane pair
+  //   F       l = l * alpha + row sum (one fused multiply-add)
+  // In order X, D, E, F this is the textbook online softmax.  The fused
+  // blocks of the overlap schedule run the E parts speculatively with the
+  // current m alongside the X parts, and D after the block; only when the
+  // test fires (in practice on a row's first tiles) are the E parts run
+  // again with the new m.  Either way P is computed with the final m, so
+  // every schedule produces the same bits.
   struct Rescale {
     bool any;
     float alpha;
   };
-  auto softmax = [&](int j, f32x16 (&sc)[2], f16x8 (&pd)[4], auto masked) INL -> Rescale {
-    constexpr bool kMasked = decltype(masked)::value;
-    // Key (sb, r) of this lane is kj + 32sb + 8(r/4) + 4hh + r%4; it is
-    // allowed iff it is below end = min(S, query + 1) (causal) or S, i.e. iff
-    // the compile-time part 32sb + 8(r/4) + r%4 is below lim.
-    int lim = 0;
-    if constexpr (kMasked) {
+  struct SmState {
+    float mq[4];     // chain maxima
+    float sw[2];     // the lane pair's combined maxima after the swap
+    float mts;       // tile max, log2 units
+    float negm;      // -(running max) used by the exponentials
+    float t[2][2];   // exponentials of the last two pairs
+    float rq[2];     // row-sum partials
+    float rs;        // row sum of the tile
+    int lim;         // masked tiles: compile-time key offsets below lim are allowed
+    Rescale rz;
+  };
+  // Key (sb, r) of this lane is j*BN + 32sb + 8(r/4) + 4hh + r%4; it is
+  // allowed iff it is below end = min(S, query + 1) (causal) or S, i.e. iff
+  // the compile-time part 32sb + 8(r/4) + r%4 is below lim.
+  auto sm_init = [&](int j, auto masked, SmState& st) INL {
+    if constexpr (decltype(masked)::value) {
       const int query = qw + n;
       const int end = p.causal ? min(S, query + 1) : S;
-      lim = end - j * BN - 4 * hh;
+      st.lim = end - j * BN - 4 * hh;
     }
-    auto kept = [&](int sb, int r) INL { return !kMasked || 32 * sb + 8 * (r >> 2) + (r & 3) < lim; };
-
-    // tile max: four independent chains, then combined
-    float mq[4];
+    st.negm = -m_run;
+    st.rq[0] = 0.f;
+    st.rq[1] = 0.f;
+  };
+  auto sm_x = [&](auto kc, f32x16 (&sc)[2], auto masked, SmState& st) INL {  // parts X0..X9
+    constexpr int k = decltype(kc)::value;
+    constexpr bool kMasked = decltype(masked)::value;
+    auto kept = [&](int sb, int r) INL { return !kMasked || 32 * sb + 8 * (r >> 2) + (r & 3) < st.lim; };
+    if constexpr (k < 8) {
+      constexpr int q = k & 3, half = k >> 2;
+      if constexpr (half == 0) st.mq[q] = NEG_INF;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      mq[q] = NEG_INF;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
+      for (int e = 4 * half; e < 4 * half + 4; ++e) {
         const int sb = q >> 1, r = 8 * (q & 1) + e;
-        mq[q] = fmaxf(mq[q], kept(sb, r) ? sc[sb][r] : NEG_INF);
+        st.mq[q] = fmaxf(st.mq[q], kept(sb, r) ? sc[sb][r] : NEG_INF);
       }
+    } else if constexpr (k == 8) {
+      const float m4 = fmaxf(fmaxf(st.mq[0], st.mq[1]), fmaxf(st.mq[2], st.mq[3]));
+      // lanes l and l^32 hold the same query: combine their partial maxima
+      auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(m4), __float_as_uint(m4), false, false);
+      st.sw[0] = __uint_as_float(x[0]);
+      st.sw[1] = __uint_as_float(x[1]);
+    } else {
+      static_assert(k == 9, "max part index");
+      const float mt = fmaxf(st.sw[0], st.sw[1]);
+      st.mts = (mt == NEG_INF) ? NEG_INF : mt * cs;
+      st.rz.any = __builtin_amdgcn_ballot_w64(st.mts > m_run + TAU) != 0;  // wave-uniform
     }
-    const float mt = pair_max(fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3])));
-    const float mts = (mt == NEG_INF) ? NEG_INF : mt * cs;
-    Rescale rz;
-    rz.any = __builtin_amdgcn_ballot_w64(mts > m_run + TAU) != 0;  // wave-uniform
-    const float m_new = rz.any ? fmaxf(m_run, mts) : m_run;
-    rz.alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+  };
+  auto sm_d = [&](SmState& st) INL {  // part D
+    const float m_new = st.rz.any ? fmaxf(m_run, st.mts) : m_run;
+    st.rz.alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
-    l_run *= rz.alpha;
-
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[sb][r], cs, -m_run));
-        if constexpr (kMasked) e = kept(sb, r) ? e : 0.f;
-        pd[2 * sb + (r >> 3)][r & 7] = (_Float16)e;
-      }
-    // row sum of the fp16 P actually fed to PV: dot2 products against (1, 1)
-    float rq[2] = {0.f, 0.f};
-    const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const f16x2 pr = {pd[kk][2 * e], pd[kk][2 * e + 1]};
-        rq[kk & 1] = __builtin_amdgcn_fdot2(pr, ones, rq[kk & 1], false);
-      }
-    l_run += pair_sum(rq[0] + rq[1]);
-    return rz;
+    st.negm = -m_run;
+  };
+  auto sm_e = [&](auto kc, f32x16 (&sc)[2], f16x8 (&pd)[4], auto masked, SmState& st) INL {  // E0..E33
+    constexpr int e = decltype(kc)::value;
+    constexpr bool kMasked = decltype(masked)::value;
+    auto kept = [&](int sb, int r) INL { return !kMasked || 32 * sb + 8 * (r >> 2) + (r & 3) < st.lim; };
+    auto pack = [&](auto pc) INL {  // pair pp to fp16 P^T and into the row sum
+      constexpr int pp = decltype(pc)::value, kk = pp >> 2, c = 2 * (pp & 3);
+      pd[kk][c] = (_Float16)st.t[pp & 1][0];
+      pd[kk][c + 1] = (_Float16)st.t[pp & 1][1];
+      const f16x2 pr = {pd[kk][c], pd[kk][c + 1]};
+      const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+      st.rq[kk & 1] = __builtin_amdgcn_fdot2(pr, ones, st.rq[kk & 1], false);
+    };
+    if constexpr (e < 32) {  // score e = pair e/2, element e%2: (sb, r)
+      constexpr int pair = e >> 1, u = e & 1, sb = pair >> 3, r = 2 * (pair & 7) + u;
+      float x = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[sb][r], cs, st.negm));
+      if constexpr (kMasked) x = kept(sb, r) ? x : 0.f;
+      st.t[pair & 1][u] = x;
+      if constexpr (u == 1 && pair >= 1) pack(std::integral_constant<int, pair - 1>{});
+    } else if constexpr (e == 32) {
+      pack(std::integral_constant<int, 15>{});
+    } else {
+      static_assert(e == 33, "exp part index");
+      st.rs = pair_sum(st.rq[0] + st.rq[1]);
+    }
+  };
+  auto sm_f = [&](SmState& st) INL { l_run = __builtin_fmaf(l_run, st.rz.alpha, st.rs); };  // part F
+  constexpr int SM_X = 10, SM_E = 34;
+  constexpr int SM_ORDERED = SM_X + 1 + SM_E + 1;  // X, D, E, F
+  // part k of the ordered sequence
+  auto sm_ordered = [&](auto kc, f32x16 (&sc)[2], f16x8 (&pd)[4], auto masked, SmState& st) INL {
+    constexpr int k = decltype(kc)::value;
+    if constexpr (k < SM_X) sm_x(kc, sc, masked, st);
+    else if constexpr (k == SM_X) sm_d(st);
+    else if constexpr (k < SM_X + 1 + SM_E) sm_e(std::integral_constant<int, k - SM_X - 1>{}, sc, pd, masked, st);
+    else sm_f(st);
+  };
+  auto softmax = [&](int j, f32x16 (&sc)[2], f16x8 (&pd)[4], auto masked) INL -> Rescale {
+    SmState st;
+    sm_init(j, masked, st);
+    static_for<SM_ORDERED>([&](auto kc) INL { sm_ordered(kc, sc, pd, masked, st); });
+    return st.rz;
   };
   auto rescale_o = [&](const Rescale& rz) INL {
-    if (rz.any) {
+    if (__builtin_expect(rz.any, 0)) {  // rare after a row's first tiles
 #pragma unroll
       for (int db = 0; db < 4; ++db) o_acc[db] *= rz.alpha;
     }
   };
 
-  // ---- one block of mma steps, optionally fused with a softmax in the same
-  // basic block.  QK steps read K tile jq into sd; PV steps read V tile jv
-  // with P^T from ps.  The fragments of the next RING steps are always in
-  // flight; the scheduler is pinned to "MFMA i, LDS reads of step i + RING,
-  // then a share of the softmax VALU work", so the matrix core, the LDS and
-  // the VALU stay busy together.
+  // ---- one block of mma steps, optionally fused with a softmax.  QK steps
+  // read K tile jq into sd; PV steps read V tile jv with P^T from ps.  The
+  // fragments of the next RING steps are always in flight.  Without a
+  // softmax the scheduler is pinned to "MFMA i, then the LDS reads of step
+  // i + RING".  With one, step i is fixed by
+  // hand as "the softmax parts placed there (sm(i)), MFMA i, LDS reads of
+  // step i + RING" and nothing moves across steps, so each wave keeps the
+  // matrix core, the LDS and the VALU busy together.
   struct NoSoftmax {};
-  auto block = [&](auto mode_c, int jq, f32x16 (&sd)[2], int jv, f16x8 (&ps)[4], auto sm) INL -> Rescale {
+  auto block = [&](auto mode_c, int jq, f32x16 (&sd)[2], int jv, f16x8 (&ps)[4], auto sm) INL {
     constexpr int mode = decltype(mode_c)::value;
     constexpr int nsteps = steps_of(mode);
     constexpr bool kSoftmax = !std::is_same_v<decltype(sm), NoSoftmax>;
@@ -401,10 +471,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(Params p) {
       else return frag_qk(jq, st.kk, st.x);
     };
     f16x8 fr[RING];
-    static_for<RING>([&](auto ic) { fr[decltype(ic)::value] = load(ic); });
-    Rescale rz{false, 1.f};
-    if constexpr (kSoftmax) rz = sm();
-    static_for<nsteps>([&](auto ic) {
+    static_for<RING>([&](auto ic) INL { fr[decltype(ic)::value] = load(ic); });
+    auto step = [&](auto ic) INL {
       constexpr int i = decltype(ic)::value;
       constexpr Step st = step_of(mode, i);
       const f16x8 a = fr[i % RING];
@@ -415,18 +483,24 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(Params p) {
         sd[st.x] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[0], f32x16{}, 0, 0, 0);
       else
         sd[st.x] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[st.kk], sd[st.x], 0, 0, 0);
-    });
-    static_for<RING>([&](auto ic) {
-      __builtin_amdgcn_sched_group_barrier(0x100, reads_of(mode, decltype(ic)::value), 0);
-    });
-    static_for<nsteps>([&](auto ic) {
-      constexpr int i = decltype(ic)::value;
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if constexpr (i + RING < nsteps) __builtin_amdgcn_sched_group_barrier(0x100, reads_of(mode, i + RING), 0);
-      // VALU incl. transcendental; nsteps x share stays below the unmasked softmax's ~130 VALU
-      if constexpr (kSoftmax) __builtin_amdgcn_sched_group_barrier(0x402, 128 / nsteps, 0);
-    });
-    return rz;
+    };
+    if constexpr (!kSoftmax) {
+      static_for<nsteps>(step);
+      static_for<RING>([&](auto ic) INL {
+        __builtin_amdgcn_sched_group_barrier(0x100, reads_of(mode, decltype(ic)::value), 0);
+      });
+      static_for<nsteps>([&](auto ic) INL {
+        constexpr int i = decltype(ic)::value;
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if constexpr (i + RING < nsteps) __builtin_amdgcn_sched_group_barrier(0x100, reads_of(mode, i + RING), 0);
+      });
+    } else {
+      static_for<nsteps>([&](auto ic) INL {
+        sm(ic);  // the softmax parts placed before MFMA i
+        step(ic);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    }
   };
   using M_BOTH = std::integral_constant<int, 0>;
   using M_PV = std::integral_constant<int, 1>;
@@ -489,13 +563,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(Params p) {
     }
   } else {
     // ---- overlap schedule: all eight waves run the same phases, and the
-    // overlap of MFMA and VALU work happens inside each wave.  Iteration j is
-    // one block -- PV of tile j-1 and QK^T of tile j+1 on the matrix core,
-    // the softmax of tile j on the VALU alongside -- then O *= alpha_j, then
-    // a barrier.  Iteration j reads K_{j+1} and V_{j-1} and loads K_{j+2} and
-    // V_j into the slots that K_j and V_{j-2} left in iteration j-1.  Per
-    // accumulator the operations are those of the serial schedule in the same
-    // order (O is rescaled between PV(j-1) and PV(j) in both).
+    // overlap of MFMA and VALU work happens inside each wave.  The softmax is
+    // pipelined across iterations.  Iteration j is one block of 32 MFMAs --
+    // QK^T of tile j+1, then PV of tile j-1 -- with, between them, the
+    // exponentials and row sum of tile j (whose running max was fixed in
+    // iteration j-1) and, once S^T of tile j+1 is complete, the max of tile
+    // j+1 and the new running max; then O *= alpha_j and a barrier.
+    // Iteration j reads K_{j+1} and V_{j-1} and loads K_{j+2} and V_j into
+    // the slots that K_{j-1} and V_{j-2} left.  Per tile the softmax runs the
+    // same parts in the same order as the serial schedule, and per
+    // accumulator the MFMAs are the same, so the results are the same bits.
     //
     // No wave skips a tile here: the steady-state loop has one code path per
     // mask case, so O, S and P each keep a single set of registers.  A tile
@@ -504,23 +581,75 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(Params p) {
     // alpha = 1 and the running max stays, every P is 0, l gains 0 and PV adds
     // zeros.  Waves of a missing odd head (hl == g) compute head h of the pair
     // and store nothing.
+    //
     // S^T and P^T alternate between two register sets (sa/sb, pa/pb) from
     // one iteration to the next, so the loops are unrolled twice.  On entry
     // to each loop S^T of the current tile is in sa and P^T of the previous
-    // tile in pa.
+    // tile in pa; cur holds the softmax state of the current tile.
     f32x16 sa[2], sb[2];
     f16x8 pa[4], pb[4];
-    auto iter = [&](int j, auto with_pv, auto with_qk, auto masked, f32x16 (&sc)[2], f32x16 (&sn)[2],
-                    f16x8 (&pp)[4], f16x8 (&pc)[4]) INL {
+    SmState cur;
+    auto set_lim = [&](int j, auto masked, SmState& st) INL {
+      if constexpr (decltype(masked)::value) {
+        const int query = qw + n;
+        const int end = p.causal ? min(S, query + 1) : S;
+        st.lim = end - j * BN - 4 * hh;
+      }
+    };
+    // One iteration.  with_pv / with_qk: whether PV(j-1) / QK(j+1) exist;
+    // mask_e / mask_x: whether tile j / tile j+1 need the key mask.
+    auto iter = [&](int j, auto with_pv, auto with_qk, auto mask_e, auto mask_x, f32x16 (&sc)[2],
+                    f32x16 (&sn)[2], f16x8 (&pp)[4], f16x8 (&pc)[4]) INL {
       constexpr bool kPV = decltype(with_pv)::value, kQK = decltype(with_qk)::value;
       stage(j + 2, j);
-      auto sm = [&]() INL { return softmax(j, sc, pc, masked); };
-      Rescale rz;
-      if constexpr (kPV && kQK) rz = block(M_FUSED{}, j + 1, sn, j - 1, pp, sm);
-      else if constexpr (kQK) rz = block(M_QK{}, j + 1, sn, j - 1, pp, sm);
-      else if constexpr (kPV) rz = block(M_PV{}, j + 1, sn, j - 1, pp, sm);
-      else rz = sm();
-      rescale_o(rz);
+      SmState nx;  // tile j+1
+      if constexpr (kQK) set_lim(j + 1, mask_x, nx);
+      cur.rq[0] = 0.f;
+      cur.rq[1] = 0.f;
+      // Placement of the softmax parts before the MFMAs of the block:
+      // E part e before MFMA floor(e * (nsteps - 1) / 33), F after E33; the
+      // max parts of tile j+1 read S^T block 0 (chains 0, 1) from MFMA 10 on
+      // and block 1 (chains 2, 3) from MFMA 18 on (mode 3; with QK^T alone
+      // the block-1 chains, X8, X9 and D follow the block).
+      constexpr int nsteps = kQK ? steps_of(kPV ? 3 : 2) : steps_of(1);
+      auto part_x = [&](auto kc) INL { sm_x(kc, sn, mask_x, nx); };
+      auto x_at = [&](auto ic) INL {
+        constexpr int i = decltype(ic)::value;
+        if constexpr (i == 10) part_x(std::integral_constant<int, 0>{});
+        if constexpr (i == 11) part_x(std::integral_constant<int, 1>{});
+        if constexpr (i == 12) part_x(std::integral_constant<int, 4>{});
+        if constexpr (i == 13) part_x(std::integral_constant<int, 5>{});
+        if constexpr (i == 18) part_x(std::integral_constant<int, 2>{});
+        if constexpr (i == 19) part_x(std::integral_constant<int, 3>{});
+        if constexpr (i == 20) part_x(std::integral_constant<int, 6>{});
+        if constexpr (i == 21) part_x(std::integral_constant<int, 7>{});
+        if constexpr (i == 23) part_x(std::integral_constant<int, 8>{});
+        if constexpr (i == 25) part_x(std::integral_constant<int, 9>{});
+        if constexpr (i == 27) sm_d(nx);
+      };
+      auto sm = [&](auto ic) INL {
+        constexpr int i = decltype(ic)::value;
+        static_for<SM_E>([&](auto ec) INL {
+          if constexpr (decltype(ec)::value * (nsteps - 1) / (SM_E - 1) == i) sm_e(ec, sc, pc, mask_e, cur);
+        });
+        if constexpr (i == nsteps - 1) sm_f(cur);
+        if constexpr (kQK) x_at(ic);
+      };
+      if constexpr (kPV && kQK) {
+        block(M_FUSED{}, j + 1, sn, j - 1, pp, sm);
+      } else if constexpr (kQK) {
+        block(M_QK{}, j + 1, sn, j - 1, pp, sm);
+        static_for<32>([&](auto ic) INL {  // the max parts placed beyond MFMA 15
+          if constexpr (decltype(ic)::value >= 16) x_at(ic);
+        });
+      } else if constexpr (kPV) {
+        block(M_PV{}, j + 1, sn, j - 1, pp, sm);
+      } else {
+        static_for<SM_E>([&](auto ec) INL { sm_e(ec, sc, pc, mask_e, cur); });
+        sm_f(cur);
+      }
+      rescale_o(cur.rz);
+      if constexpr (kQK) cur = nx;
       dma_wait();
       lds_barrier();
     };
@@ -531,9 +660,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(Params p) {
       for (int i = 0; i < 4; ++i) pa[i] = pb[i];
     };
     // Tiles below j_ms need no mask for any wave of the workgroup; the
-    // steady-state loop is split there so that each loop has one code path.
-    // The first and the last iteration always take the masked path (with no
-    // key masked it computes the same values).
+    // steady-state loop is split so that each loop has one code path.  The
+    // first and the last iteration always take the masked path (with no key
+    // masked it computes the same values).
     const int j_ms = min(n_tiles, p.causal ? min(q0, S) / BN : S / BN);
     using T = std::true_type;
     using F = std::false_type;
@@ -541,35 +670,41 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(Params p) {
     stage(1, n_tiles);
     dma_wait();
     lds_barrier();
+    // prologue: S^T of tile 0, its max and the first running max (K_0 keeps
+    // its slot while iteration 0 loads K_2, so no barrier is needed here)
     block(M_QK{}, 0, sa, 0, pa, NoSoftmax{});
-    lds_barrier();  // everyone has read K_0 before iteration 0 reloads its slot
-    if (n_tiles == 1) {
-      iter(0, F{}, F{}, T{}, sa, sb, pa, pb);
-    } else {
-      iter(0, F{}, T{}, T{}, sa, sb, pa, pb);
+    set_lim(0, T{}, cur);
+    static_for<SM_X>([&](auto kc) INL { sm_x(kc, sa, T{}, cur); });
+    sm_d(cur);
+    int j = 0;
+    if (n_tiles > 1) {
+      iter(0, F{}, T{}, T{}, T{}, sa, sb, pa, pb);
       to_a();
-      int j = 1;
-      const int j_u = min(j_ms, n_tiles - 1);  // unmasked iterations: [1, j_u)
+      j = 1;
+      // iterations with tiles j and j+1 both unmasked: [1, j_u)
+      const int j_u = min(j_ms - 1, n_tiles - 1);
       for (; j + 1 < j_u; j += 2) {
-        iter(j, T{}, T{}, F{}, sa, sb, pa, pb);
-        iter(j + 1, T{}, T{}, F{}, sb, sa, pb, pa);
+        iter(j, T{}, T{}, F{}, F{}, sa, sb, pa, pb);
+        iter(j + 1, T{}, T{}, F{}, F{}, sb, sa, pb, pa);
       }
       if (j < j_u) {
-        iter(j, T{}, T{}, F{}, sa, sb, pa, pb);
+        iter(j, T{}, T{}, F{}, F{}, sa, sb, pa, pb);
         to_a();
         ++j;
       }
       for (; j + 1 < n_tiles - 1; j += 2) {
-        iter(j, T{}, T{}, T{}, sa, sb, pa, pb);
-        iter(j + 1, T{}, T{}, T{}, sb, sa, pb, pa);
+        iter(j, T{}, T{}, T{}, T{}, sa, sb, pa, pb);
+        iter(j + 1, T{}, T{}, T{}, T{}, sb, sa, pb, pa);
       }
       if (j < n_tiles - 1) {
-        iter(j, T{}, T{}, T{}, sa, sb, pa, pb);
+        iter(j, T{}, T{}, T{}, T{}, sa, sb, pa, pb);
         to_a();
         ++j;
       }
-      iter(j, T{}, F{}, T{}, sa, sb, pa, pb);
     }
+    // the last tile (j = n_tiles - 1): with PV of the tile before if there is one
+    if (j > 0) iter(j, T{}, F{}, T{}, T{}, sa, sb, pa, pb);
+    else iter(j, F{}, F{}, T{}, T{}, sa, sb, pa, pb);
     // PV of the last tile, whose P^T the last iteration left in pb
     block(M_PV{}, 0, sa, n_tiles - 1, pb, NoSoftmax{});
   }
@@ -603,12 +738,12 @@ int64_t grid_blocks(const Params& p) {
 hipError_t launch_attn_fwd(const Params& p, hipStream_t stream) {
   const int64_t nb = grid_blocks(p);
   if (nb <= 0) return hipErrorInvalidValue;
-  if (p.schedule == SCHEDULE_SERIAL)
-    hipLaunchKernelGGL(attn_fwd_kernel<SCHEDULE_SERIAL>, dim3((unsigned)nb), dim3(NTHREADS), 0, stream, p);
+  if (p.schedule == SCHEDULE_OVERLAP)
+    hipLaunchKernelGGL(attn_fwd_kernel<SCHEDULE_OVERLAP>, dim3((unsigned)nb), dim3(NTHREADS), 0, stream, p);
   else if (p.schedule == SCHEDULE_PINGPONG)
     hipLaunchKernelGGL(attn_fwd_kernel<SCHEDULE_PINGPONG>, dim3((unsigned)nb), dim3(NTHREADS), 0, stream, p);
   else
-    hipLaunchKernelGGL(attn_fwd_kernel<SCHEDULE_OVERLAP>, dim3((unsigned)nb), dim3(NTHREADS), 0, stream, p);
+    hipLaunchKernelGGL(attn_fwd_kernel<SCHEDULE_SERIAL>, dim3((unsigned)nb), dim3(NTHREADS), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -10,10 +10,16 @@ namespace libattn {
 // Tile schedules of the kernel.  All compute bitwise identical results (each
 // accumulator sees the same operations in the same order), so running one
 // against another cross-checks them: an LDS race in any would show up.
-//   OVERLAP : every wave overlaps its own softmax with the next tile's MFMAs
+//   SERIAL  : per tile, one wave runs QK^T, softmax and PV back to back; the
+//             two waves that share a SIMD overlap each other's MFMA and VALU
+//             work (the default: fastest measured, see below)
+//   OVERLAP : every wave overlaps, inside one instruction stream, the softmax
+//             of tile j with the MFMAs of QK^T(j+1) and PV(j-1)
 //   PINGPONG: two wave groups offset by half a tile alternate MFMA and softmax
-//   SERIAL  : one barrier per tile, no overlap (the reference order)
-enum Schedule { SCHEDULE_OVERLAP = 0, SCHEDULE_PINGPONG = 1, SCHEDULE_SERIAL = 2 };
+// Measured on MI355X all three land within a few percent of each other: the
+// kernel runs at the chip's power limit, where the clock, not the issue
+// order, sets the rate.
+enum Schedule { SCHEDULE_SERIAL = 0, SCHEDULE_OVERLAP = 1, SCHEDULE_PINGPONG = 2 };
 
 // Launch parameters.  Pointers are device pointers; strides are in elements.
 struct Params {
