@@ -22,7 +22,9 @@ Rank 0 prints one JSON line per workload:
 reads and writes BYTES bytes after the timed region (counter calibration for the HBM traffic figure), and
 `--summarize-traffic FETCH_DIR WRITE_DIR` turns two rocprofv3 --pmc runs
 (FETCH_SIZE, then WRITE_SIZE) into the traffic summary under profiles/, and
-`--summarize-kernel-trace TRACE_DIR COMMAND` writes the kernel-trace summary.
+`--summarize-kernel-trace TRACE_DIR COMMAND` writes the kernel-trace summary,
+and `--summarize-counters DIR [DIR ...]` the summary of rocprofv3 --pmc runs of
+SQ/GRBM counters (MFMA busy fraction, VALU/MFMA co-execution, LDS activity).
 """
 from __future__ import annotations
 
@@ -252,6 +254,57 @@ def summarize_traffic(fetch_dir: str, write_dir: str, workload: str, copy_bytes:
     print(json.dumps(out, indent=1))
 
 
+def summarize_counters(dirs, workload: str):
+    """Markdown summary of rocprofv3 --pmc runs of SQ/GRBM counters for the attention kernel.
+
+    Per-dispatch averages of each counter (summed over the device), plus derived figures:
+    per-SIMD MFMA busy fraction = SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs * GRBM_GUI_ACTIVE / XCDs),
+    co-execution share = SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES.
+    """
+    import sqlite3
+
+    n_xcd, n_simd = 8, 256 * 4
+    vals, cmds = {}, []
+    for d in dirs:
+        names = set()
+        for f in _db_files(d):
+            con = sqlite3.connect(f)
+            for name, counter, val, n in con.execute(
+                    "select kernel_name, counter_name, sum(value), count(distinct dispatch_id) from counters_collection "
+                    "where kernel_name like ? group by kernel_name, counter_name", ("%" + KERNEL_NAME + "%",)):
+                vals[counter] = val / max(n, 1)
+                names.add(counter)
+            con.close()
+        cmds.append("rocprofv3 --pmc %s -d <dir> -o <name> -- python3 bench.py --workload %s --steps 2 --warmup 1 "
+                    "--no-cpu-baseline" % (" ".join(sorted(names)), workload))
+    lines = ["# rocprofv3 counters: %s, %s" % (KERNEL_NAME, workload), "", "Commands (from the repository root; one "
+             "--pmc pass per line, counters grouped within the per-block limits):", ""]
+    lines += ["    " + c for c in cmds]
+    lines += ["", "Values are per dispatch of the attention kernel, summed over the device.", "",
+              "| counter | per dispatch |", "|---|---|"]
+    for k in sorted(vals):
+        lines.append("| %s | %.4g |" % (k, vals[k]))
+    gui = vals.get("GRBM_GUI_ACTIVE")
+    if gui:
+        cyc = gui / n_xcd
+        lines += ["", "Derived:", "", "- active cycles per XCD: %.4g" % cyc]
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in vals:
+            lines.append("- MFMA busy per SIMD: %.1f %% of active cycles" %
+                         (100.0 * vals["SQ_VALU_MFMA_BUSY_CYCLES"] / (n_simd * cyc)))
+        if "SQ_VALU_MFMA_COEXEC_CYCLES" in vals and vals.get("SQ_VALU_MFMA_BUSY_CYCLES"):
+            lines.append("- VALU issued during MFMA busy cycles: %.1f %% of MFMA busy cycles" %
+                         (100.0 * vals["SQ_VALU_MFMA_COEXEC_CYCLES"] / vals["SQ_VALU_MFMA_BUSY_CYCLES"]))
+        if "SQ_LDS_IDX_ACTIVE" in vals:
+            lines.append("- LDS indexed-access active: %.1f %% of active cycles per CU" %
+                         (100.0 * vals["SQ_LDS_IDX_ACTIVE"] / (256 * cyc)))
+    lines += ["", "Kernel source fingerprint: %s" % kernel_fingerprint(), ""]
+    os.makedirs(PROFILES, exist_ok=True)
+    out = os.path.join(PROFILES, "%s_%s_counters.md" % (KERNEL_NAME, workload))
+    with open(out, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+
+
 # ------------------------------------------------------------------ main
 
 def main():
@@ -266,10 +319,14 @@ def main():
     ap.add_argument("--pmc-copy", type=int, default=0)
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-kernel-trace", nargs=2, metavar=("TRACE_DIR", "COMMAND"))
+    ap.add_argument("--summarize-counters", nargs="+", metavar="DIR")
     args = ap.parse_args()
 
     from dnn_compiler_pipelining_amd import inputs
 
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.workload)
+        return
     if args.summarize_kernel_trace:
         summarize_kernel_trace(args.summarize_kernel_trace[0], args.workload, args.summarize_kernel_trace[1])
         return 0
