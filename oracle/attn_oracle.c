@@ -17,7 +17,7 @@
  * rescaling:
  *
  *   g = Hq / Hkv,  c = floor(h / g)        (query head h reads KV head c)
- *   A(i) = {0..i} if causal else {0..S-1}  (key j allowed for query i)
+ *   A(i) = {0..i+Sk-Sq} if causal else {0..Sk-1}  (key j allowed for query i)
  *   s_j  = scale * sum_{d ascending} q[b,i,h,d] * k[b,j,c,d]      j in A(i)
  *   m    = max_j s_j
  *   w_j  = exp(s_j - m)
@@ -25,14 +25,16 @@
  *   O[b,i,h,:] = (sum_{j ascending} w_j * v[b,j,c,:]) / l
  *   LSE[b,h,i] = m + log(l)                (natural log of the scaled scores)
  *
- * The readings it takes where the pages are silent (GQA head map, causal
- * alignment with Sq == Sk, natural-log LSE of the scaled scores, the scale as
- * the fp32 value the GPU receives) are stated in the comments above.  All
+ * The readings it takes where the pages are silent (GQA head map; causal
+ * alignment at the bottom right, so query i sits at key position i + Sk - Sq
+ * and the square case Sq == Sk is the usual j <= i; natural-log LSE of the
+ * scaled scores; the scale as the fp32 value the GPU receives) are stated in
+ * the comments above.  Causal needs Sq <= Sk, so every row has a key.  All
  * arithmetic is IEEE binary64 from the exact fp16 input values; it is built
  * with -O2 -ffp-contract=off so every sum runs in the order written.
  *
  * Layouts (row-major, contiguous): one batch entry at a time,
- *   q [S][Hq][D], k [S][Hkv][D], v [S][Hkv][D] as raw fp16 bit patterns.
+ *   q [Sq][Hq][D], k [Sk][Hkv][D], v [Sk][Hkv][D] as raw fp16 bit patterns.
  * Output per requested (head, row) item n: o[n*D .. n*D+D-1], lse[n].
  */
 #include <math.h>
@@ -60,9 +62,9 @@ double oracle_half_to_double(uint16_t h) {
 
 typedef struct {
   const uint16_t* q;
-  const double* kd; /* widened k, [S][Hkv][D] */
-  const double* vd; /* widened v, [S][Hkv][D] */
-  int S, Hq, Hkv, D, causal;
+  const double* kd; /* widened k, [Sk][Hkv][D] */
+  const double* vd; /* widened v, [Sk][Hkv][D] */
+  int Sq, Sk, Hq, Hkv, D, causal;
   double sigma;
   const int32_t* heads;
   const int32_t* rows;
@@ -74,12 +76,13 @@ typedef struct {
 } job_t;
 
 static void one_row(const job_t* J, int64_t item, double* scores, double* qrow, double* acc) {
-  const int S = J->S, Hq = J->Hq, Hkv = J->Hkv, D = J->D;
+  const int Sk = J->Sk, Hq = J->Hq, Hkv = J->Hkv, D = J->D;
+  const int off = J->Sk - J->Sq; /* key position of query row 0, bottom-right alignment */
   const int h = J->heads[item];
   const int i = J->rows[item];
   const int g = Hq / Hkv;
   const int c = h / g;
-  const int nkeys = J->causal ? i + 1 : S;
+  const int nkeys = J->causal ? i + 1 + off : Sk;
 
   for (int d = 0; d < D; ++d) qrow[d] = oracle_half_to_double(J->q[((int64_t)i * Hq + h) * D + d]);
 
@@ -108,7 +111,7 @@ static void one_row(const job_t* J, int64_t item, double* scores, double* qrow, 
 
 static void* worker(void* arg) {
   job_t* J = (job_t*)arg;
-  double* scores = (double*)malloc(sizeof(double) * (size_t)J->S);
+  double* scores = (double*)malloc(sizeof(double) * (size_t)J->Sk);
   double* qrow = (double*)malloc(sizeof(double) * (size_t)J->D);
   double* acc = (double*)malloc(sizeof(double) * (size_t)J->D);
   if (!scores || !qrow || !acc) {
@@ -126,21 +129,23 @@ static void* worker(void* arg) {
   return NULL;
 }
 
-/* Computes n output rows of one batch entry.
- * Returns 0 on success, 1 on invalid arguments, 2 on allocation/thread failure. */
-int oracle_attn_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v, int S, int Hq, int Hkv, int D,
-                     int causal, float scale, const int32_t* heads, const int32_t* rows, int64_t n, double* o,
-                     double* lse, int nthreads) {
+/* Computes n output rows of one batch entry with Sq query rows and Sk keys.
+ * Returns 0 on success, 1 on invalid arguments (including causal with
+ * Sq > Sk), 2 on allocation/thread failure. */
+int oracle_attn_rows_ex(const uint16_t* q, const uint16_t* k, const uint16_t* v, int Sq, int Sk, int Hq, int Hkv,
+                        int D, int causal, float scale, const int32_t* heads, const int32_t* rows, int64_t n,
+                        double* o, double* lse, int nthreads) {
   if (!q || !k || !v || !heads || !rows || !o || !lse) return 1;
-  if (S < 1 || Hq < 1 || Hkv < 1 || D < 1 || Hq % Hkv != 0 || n < 0) return 1;
+  if (Sq < 1 || Sk < 1 || Hq < 1 || Hkv < 1 || D < 1 || Hq % Hkv != 0 || n < 0) return 1;
   if (causal != 0 && causal != 1) return 1;
+  if (causal && Sq > Sk) return 1;
   for (int64_t t = 0; t < n; ++t)
-    if (heads[t] < 0 || heads[t] >= Hq || rows[t] < 0 || rows[t] >= S) return 1;
+    if (heads[t] < 0 || heads[t] >= Hq || rows[t] < 0 || rows[t] >= Sq) return 1;
   if (n == 0) return 0;
   if (nthreads < 1) nthreads = 1;
   if ((int64_t)nthreads > n) nthreads = (int)n;
 
-  const int64_t kv_elems = (int64_t)S * Hkv * D;
+  const int64_t kv_elems = (int64_t)Sk * Hkv * D;
   double* kd = (double*)malloc(sizeof(double) * (size_t)kv_elems);
   double* vd = (double*)malloc(sizeof(double) * (size_t)kv_elems);
   if (!kd || !vd) {
@@ -158,7 +163,8 @@ int oracle_attn_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v, in
   J.q = q;
   J.kd = kd;
   J.vd = vd;
-  J.S = S;
+  J.Sq = Sq;
+  J.Sk = Sk;
   J.Hq = Hq;
   J.Hkv = Hkv;
   J.D = D;
@@ -188,4 +194,11 @@ int oracle_attn_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v, in
   free(kd);
   free(vd);
   return rc;
+}
+
+/* The square case Sq == Sk == S. */
+int oracle_attn_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v, int S, int Hq, int Hkv, int D,
+                     int causal, float scale, const int32_t* heads, const int32_t* rows, int64_t n, double* o,
+                     double* lse, int nthreads) {
+  return oracle_attn_rows_ex(q, k, v, S, S, Hq, Hkv, D, causal, scale, heads, rows, n, o, lse, nthreads);
 }

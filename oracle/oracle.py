@@ -45,6 +45,10 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_attn_rows.argtypes = [u16p, u16p, u16p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                      ctypes.c_int, ctypes.c_float, i32p, i32p, ctypes.c_int64, f64p, f64p,
                                      ctypes.c_int]
+    lib.oracle_attn_rows_ex.restype = ctypes.c_int
+    lib.oracle_attn_rows_ex.argtypes = [u16p, u16p, u16p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_float, i32p, i32p, ctypes.c_int64, f64p,
+                                        f64p, ctypes.c_int]
     lib.oracle_half_to_double.restype = ctypes.c_double
     lib.oracle_half_to_double.argtypes = [ctypes.c_uint16]
     return lib
@@ -98,7 +102,8 @@ class Oracle:
     def rows(self, q, k, v, heads, rows, causal: bool, scale: float, nthreads: int | None = None):
         """O rows and LSE for one batch entry.
 
-        q: [S, Hq, D] fp16; k, v: [S, Hkv, D] fp16; heads, rows: int sequences of equal length n.
+        q: [Sq, Hq, D] fp16; k, v: [Sk, Hkv, D] fp16 (Sk may differ from Sq; causal then aligns the last
+        query row with the last key, and needs Sq <= Sk); heads, rows: int sequences of equal length n.
         Returns (o [n, D] float64, lse [n] float64).
         """
         qb, kb, vb = _u16(q), _u16(k), _u16(v)
@@ -106,7 +111,7 @@ class Oracle:
             raise ValueError("expected [S, H, D] arrays for one batch entry")
         S, Hq, D = qb.shape
         Sk, Hkv, Dk = kb.shape
-        if kb.shape != vb.shape or Sk != S or Dk != D:
+        if kb.shape != vb.shape or Dk != D:
             raise ValueError("shape mismatch q %s k %s v %s" % (qb.shape, kb.shape, vb.shape))
         hs = np.ascontiguousarray(np.asarray(heads, dtype=np.int32).reshape(-1))
         rs = np.ascontiguousarray(np.asarray(rows, dtype=np.int32).reshape(-1))
@@ -115,16 +120,17 @@ class Oracle:
         n = hs.shape[0]
         o = np.empty((n, D), dtype=np.float64)
         lse = np.empty((n,), dtype=np.float64)
-        rc = self.lib.oracle_attn_rows(_p(qb, ctypes.c_uint16), _p(kb, ctypes.c_uint16), _p(vb, ctypes.c_uint16),
-                                       S, Hq, Hkv, D, int(bool(causal)), float(scale), _p(hs, ctypes.c_int32),
-                                       _p(rs, ctypes.c_int32), n, _p(o, ctypes.c_double),
-                                       _p(lse, ctypes.c_double), int(nthreads or default_threads()))
+        rc = self.lib.oracle_attn_rows_ex(_p(qb, ctypes.c_uint16), _p(kb, ctypes.c_uint16),
+                                          _p(vb, ctypes.c_uint16), S, Sk, Hq, Hkv, D, int(bool(causal)),
+                                          float(scale), _p(hs, ctypes.c_int32), _p(rs, ctypes.c_int32), n,
+                                          _p(o, ctypes.c_double), _p(lse, ctypes.c_double),
+                                          int(nthreads or default_threads()))
         if rc != 0:
             raise RuntimeError("oracle_attn_rows failed with code %d" % rc)
         return o, lse
 
     def full(self, q, k, v, causal: bool, scale: float, nthreads: int | None = None):
-        """Whole-tensor oracle: q [B,S,Hq,D], k/v [B,S,Hkv,D] fp16 -> (O [B,S,Hq,D], LSE [B,Hq,S]) float64."""
+        """Whole-tensor oracle: q [B,Sq,Hq,D], k/v [B,Sk,Hkv,D] fp16 -> (O [B,Sq,Hq,D], LSE [B,Hq,Sq]) float64."""
         qn, kn, vn = _u16(q), _u16(k), _u16(v)
         B, S, Hq, D = qn.shape
         O = np.empty((B, S, Hq, D), dtype=np.float64)

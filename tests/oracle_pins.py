@@ -256,5 +256,124 @@ def pin_brute_force(orc, seed=19):
             np.testing.assert_allclose(L, Lb, rtol=1e-12, atol=1e-13)
 
 
+# ---------------------------------------------------------------- Sq != Sk (bottom-right causal alignment)
+
+def rand_qkv_rect(rng, B, Sq, Sk, Hq, Hkv, D):
+    q = rng.standard_normal((B, Sq, Hq, D)).astype(np.float16)
+    k = rng.standard_normal((B, Sk, Hkv, D)).astype(np.float16)
+    v = rng.standard_normal((B, Sk, Hkv, D)).astype(np.float16)
+    return q, k, v
+
+
+def torch_reference_rect(q, k, v, causal, scale):
+    """float64 torch for Sq != Sk: scaled_dot_product_attention with an explicit boolean mask (query i
+    may attend key j iff j <= i + Sk - Sq when causal), and logsumexp of the masked scaled scores."""
+    B, Sq, Hq, D = q.shape
+    Sk, Hkv = k.shape[1], k.shape[2]
+    g = Hq // Hkv
+    qt = torch.from_numpy(q.astype(np.float64)).permute(0, 2, 1, 3)
+    kt = torch.from_numpy(k.astype(np.float64)).permute(0, 2, 1, 3).repeat_interleave(g, dim=1)
+    vt = torch.from_numpy(v.astype(np.float64)).permute(0, 2, 1, 3).repeat_interleave(g, dim=1)
+    allowed = torch.ones(Sq, Sk, dtype=torch.bool)
+    if causal:
+        allowed = torch.arange(Sk)[None, :] <= torch.arange(Sq)[:, None] + (Sk - Sq)
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=allowed, scale=float(scale))
+    s = torch.matmul(qt, kt.transpose(-1, -2).contiguous()) * float(scale)
+    lse = torch.logsumexp(s.masked_fill(~allowed, float("-inf")), dim=-1)
+    return o.permute(0, 2, 1, 3).numpy(), lse.numpy()
+
+
+RECT_SHAPES = [
+    # B, Sq, Sk, Hq, Hkv, D
+    (1, 1, 7, 2, 1, 8),
+    (2, 3, 17, 4, 2, 16),
+    (1, 16, 64, 8, 2, 128),
+    (1, 33, 100, 4, 4, 64),
+]
+
+
+def pin_torch_sdpa_rect(orc, seed=21):
+    rng = np.random.default_rng(seed)
+    for B, Sq, Sk, Hq, Hkv, D in RECT_SHAPES:
+        for causal in (True, False):
+            q, k, v = rand_qkv_rect(rng, B, Sq, Sk, Hq, Hkv, D)
+            scale = f32(float(rng.uniform(0.05, 0.6)))
+            O, L = orc.full(q, k, v, causal, scale)
+            Ot, Lt = torch_reference_rect(q, k, v, causal, scale)
+            tag = "B%d Sq%d Sk%d Hq%d Hkv%d D%d causal%d" % (B, Sq, Sk, Hq, Hkv, D, causal)
+            np.testing.assert_allclose(O, Ot, rtol=1e-10, atol=1e-11, err_msg=tag)
+            np.testing.assert_allclose(L, Lt, rtol=1e-10, atol=1e-11, err_msg=tag)
+    # more query rows than keys, non-causal
+    q, k, v = rand_qkv_rect(rng, 1, 9, 4, 2, 1, 8)
+    O, L = orc.full(q, k, v, False, f32(0.3))
+    Ot, Lt = torch_reference_rect(q, k, v, False, f32(0.3))
+    np.testing.assert_allclose(O, Ot, rtol=1e-10, atol=1e-11)
+    np.testing.assert_allclose(L, Lt, rtol=1e-10, atol=1e-11)
+
+
+def pin_zero_q_rect(orc, seed=22):
+    """Q = 0 with Sq < Sk, causal: query row i averages V over keys 0..i+Sk-Sq; LSE = ln(i+1+Sk-Sq)."""
+    rng = np.random.default_rng(seed)
+    B, Sq, Sk, Hq, Hkv, D = 1, 6, 15, 4, 2, 8
+    _, k, v = rand_qkv_rect(rng, B, Sq, Sk, Hq, Hkv, D)
+    q = np.zeros((B, Sq, Hq, D), dtype=np.float16)
+    O, L = orc.full(q, k, v, True, 0.5)
+    vd = v.astype(np.float64)
+    g = Hq // Hkv
+    for i in range(Sq):
+        n = i + 1 + Sk - Sq
+        mean = vd[0, :n].mean(axis=0)
+        for h in range(Hq):
+            np.testing.assert_allclose(O[0, i, h], mean[h // g], rtol=0, atol=1e-14)
+            assert abs(L[0, h, i] - math.log(n)) < 1e-14
+
+
+def pin_suffix_of_square(orc, seed=23):
+    """Causal with Sq < Sk equals the last Sq rows of the square Sk x Sk problem whose last Sq query
+    rows are the given ones (the square case is pinned on its own above)."""
+    rng = np.random.default_rng(seed)
+    B, Sq, Sk, Hq, Hkv, D = 2, 5, 21, 4, 2, 16
+    q, k, v = rand_qkv_rect(rng, B, Sq, Sk, Hq, Hkv, D)
+    qfull = np.concatenate([rng.standard_normal((B, Sk - Sq, Hq, D)).astype(np.float16), q], axis=1)
+    O, L = orc.full(q, k, v, True, 0.35)
+    Of, Lf = orc.full(qfull, k, v, True, 0.35)
+    np.testing.assert_allclose(O, Of[:, Sk - Sq:], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(L, Lf[:, :, Sk - Sq:], rtol=0, atol=1e-14)
+
+
+def brute_force_rect(q, k, v, causal, scale):
+    """brute_force for Sq != Sk (bottom-right causal alignment)."""
+    B, Sq, Hq, D = q.shape
+    Sk, Hkv = k.shape[1], k.shape[2]
+    g = Hq // Hkv
+    O = np.zeros((B, Sq, Hq, D))
+    L = np.zeros((B, Hq, Sq))
+    qd, kd, vd = q.astype(np.float64), k.astype(np.float64), v.astype(np.float64)
+    for b in range(B):
+        for h in range(Hq):
+            c = h // g
+            for i in range(Sq):
+                keys = range(i + 1 + Sk - Sq) if causal else range(Sk)
+                w = [math.exp(scale * math.fsum(qd[b, i, h, d] * kd[b, j, c, d] for d in range(D))) for j in keys]
+                tot = math.fsum(w)
+                for d in range(D):
+                    O[b, i, h, d] = math.fsum(wj * vd[b, j, c, d] for wj, j in zip(w, keys)) / tot
+                L[b, h, i] = math.log(tot)
+    return O, L
+
+
+def pin_brute_force_rect(orc, seed=24):
+    rng = np.random.default_rng(seed)
+    for B, Sq, Sk, Hq, Hkv, D in ((1, 1, 3, 1, 1, 2), (1, 4, 9, 2, 1, 8), (2, 3, 5, 4, 2, 4)):
+        q, k, v = rand_qkv_rect(rng, B, Sq, Sk, Hq, Hkv, D)
+        for causal in (True, False):
+            scale = f32(float(rng.uniform(0.05, 0.5)))
+            O, L = orc.full(q, k, v, causal, scale)
+            Ob, Lb = brute_force_rect(q, k, v, causal, scale)
+            np.testing.assert_allclose(O, Ob, rtol=1e-12, atol=1e-13)
+            np.testing.assert_allclose(L, Lb, rtol=1e-12, atol=1e-13)
+
+
 ALL_PINS = [pin_handworked, pin_torch_sdpa, pin_constant_v, pin_zero_q, pin_first_causal_row, pin_gqa_constant_heads,
-            pin_large_scale_argmax, pin_causal_is_prefix, pin_key_shift, pin_brute_force]
+            pin_large_scale_argmax, pin_causal_is_prefix, pin_key_shift, pin_brute_force, pin_torch_sdpa_rect,
+            pin_zero_q_rect, pin_suffix_of_square, pin_brute_force_rect]

@@ -58,3 +58,14 @@ def test_rejects_bad_arguments(orc):
         orc.rows(q[0], k[0], v[0], [2], [0], True, 0.1)  # head out of range
     with pytest.raises(RuntimeError):
         orc.rows(q[0], k[0], v[0], [0], [4], True, 0.1)  # row out of range
+
+
+def test_rejects_causal_with_more_queries_than_keys(orc):
+    """Bottom-right causal alignment needs Sq <= Sk (every row keeps a key); non-causal allows any."""
+    rng = np.random.default_rng(4)
+    q = rng.standard_normal((5, 2, 8)).astype(np.float16)
+    k = rng.standard_normal((3, 1, 8)).astype(np.float16)
+    with pytest.raises(RuntimeError):
+        orc.rows(q, k, k, [0], [0], True, 0.5)
+    o, lse = orc.rows(q, k, k, [0, 1], [4, 0], False, 0.5)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()

@@ -12,17 +12,19 @@ from tests import oracle_pins as P
 
 MUTANTS = {
     "gqa_map_modulo": ("const int c = h / g;", "const int c = h % Hkv;"),
-    "causal_excludes_diagonal": ("J->causal ? i + 1 : S", "J->causal ? (i > 0 ? i : 1) : S"),
-    "causal_one_key_too_many": ("J->causal ? i + 1 : S", "J->causal ? (i + 2 < S ? i + 2 : S) : S"),
+    "causal_excludes_diagonal": ("J->causal ? i + 1 + off : Sk", "J->causal ? (i + off > 0 ? i + off : 1) : Sk"),
+    "causal_one_key_too_many": ("J->causal ? i + 1 + off : Sk", "J->causal ? (i + 2 + off < Sk ? i + 2 + off : Sk) : Sk"),
+    "causal_offset_dropped": ("J->causal ? i + 1 + off : Sk", "J->causal ? i + 1 : Sk"),
+    "causal_offset_sign": ("const int off = J->Sk - J->Sq;", "const int off = J->Sq - J->Sk;"),
     "scale_dropped": ("scores[j] = J->sigma * dot;", "scores[j] = dot;"),
     "lse_without_max": ("J->lse[item] = m + log(l);", "J->lse[item] = log(l);"),
     "k_and_v_swapped": ("const double* kr = J->kd +", "const double* kr = J->vd +"),
     "no_normaliser": ("out[d] = acc[d] / l;", "out[d] = acc[d];"),
     "wrong_sign_in_exp": ("exp(scores[j] - m)", "exp(m - scores[j])"),
-    "q_index_transposed": ("J->q[((int64_t)i * Hq + h) * D + d]", "J->q[((int64_t)h * S + i) * D + d]"),
+    "q_index_transposed": ("J->q[((int64_t)i * Hq + h) * D + d]", "J->q[((int64_t)h * J->Sq + i) * D + d]"),
     "dropped_first_d_term": ("for (int d = 0; d < D; ++d) dot +=", "for (int d = 1; d < D; ++d) dot +="),
     "v_row_off_by_one": ("const double* vr = J->vd + ((int64_t)j * Hkv + c) * D;",
-                         "const double* vr = J->vd + ((int64_t)(j + 1 < S ? j + 1 : j) * Hkv + c) * D;"),
+                         "const double* vr = J->vd + ((int64_t)(j + 1 < Sk ? j + 1 : j) * Hkv + c) * D;"),
 }
 
 
