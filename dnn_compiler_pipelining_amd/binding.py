@@ -25,7 +25,7 @@ ATTN_ERR_ALIGN = 4
 ATTN_ERR_HIP = 5
 ATTN_ERR_OVERLAP = 6
 
-EXPORTS = ("attn_fwd", "attn_fwd_stream", "attn_status_string", "attn_version")
+EXPORTS = ("attn_fwd", "attn_fwd_stream", "attn_fwd_ex", "attn_status_string", "attn_version")
 
 _lock = threading.Lock()
 _lib = None
@@ -51,6 +51,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
             lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f]
             lib.attn_fwd_stream.restype = i
             lib.attn_fwd_stream.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
+            lib.attn_fwd_ex.restype = i
+            lib.attn_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
             lib.attn_status_string.restype = ctypes.c_char_p
             lib.attn_status_string.argtypes = [i]
             lib.attn_version.restype = i
@@ -81,6 +83,14 @@ def attn_fwd_stream(q, k, v, o, lse, B: int, S: int, Hq: int, Hkv: int, D: int, 
                                   float(scale), handle)
 
 
+def attn_fwd_ex(q, k, v, o, lse, B: int, Sq: int, Sk: int, Hq: int, Hkv: int, D: int, causal: int, scale: float,
+                stream) -> int:
+    """C attn_fwd_ex (Sq query rows, Sk keys).  `stream` as for attn_fwd_stream."""
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else (stream or 0)
+    return load().attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Sq, Sk, Hq, Hkv, D, int(causal),
+                              float(scale), handle)
+
+
 def attn_status_string(status: int) -> str:
     return load().attn_status_string(int(status)).decode()
 
@@ -91,9 +101,10 @@ def attn_version() -> int:
 
 def forward(q, k, v, causal: bool = True, scale: float | None = None, out=None, lse=None, want_lse: bool = True,
             stream=None):
-    """Run the kernel on torch tensors q [B,S,Hq,D], k/v [B,S,Hkv,D] (fp16, contiguous, same GPU).
+    """Run the kernel on torch tensors q [B,Sq,Hq,D], k/v [B,Sk,Hkv,D] (fp16, contiguous, same GPU).
 
-    Returns (o, lse) with o [B,S,Hq,D] fp16 and lse [B,Hq,S] fp32 (None if not wanted).  Enqueues on
+    Sk may differ from Sq (causal then aligns the last query row with the last key; see attn_fwd_ex).
+    Returns (o, lse) with o [B,Sq,Hq,D] fp16 and lse [B,Hq,Sq] fp32 (None if not wanted).  Enqueues on
     `stream` (default: torch's current stream) and does not synchronise.
     """
     import torch
@@ -104,7 +115,8 @@ def forward(q, k, v, causal: bool = True, scale: float | None = None, out=None, 
         if t.dim() != 4:
             raise ValueError("%s must be [B, S, H, D]" % name)
     B, S, Hq, D = q.shape
-    if k.shape != v.shape or k.shape[0] != B or k.shape[1] != S or k.shape[3] != D:
+    Sk = k.shape[1]
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != D:
         raise ValueError("shape mismatch: q %s k %s v %s" % (tuple(q.shape), tuple(k.shape), tuple(v.shape)))
     if q.device != k.device or q.device != v.device:
         raise ValueError("q, k, v must be on the same device")
@@ -120,7 +132,10 @@ def forward(q, k, v, causal: bool = True, scale: float | None = None, out=None, 
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     with torch.cuda.device(q.device):
-        st = attn_fwd_stream(q, k, v, out, lse, B, S, Hq, Hkv, D, int(bool(causal)), float(scale), stream)
+        if Sk == S:
+            st = attn_fwd_stream(q, k, v, out, lse, B, S, Hq, Hkv, D, int(bool(causal)), float(scale), stream)
+        else:
+            st = attn_fwd_ex(q, k, v, out, lse, B, S, Sk, Hq, Hkv, D, int(bool(causal)), float(scale), stream)
     if st != ATTN_OK:
         raise AttnError(st)
     return out, lse

@@ -14,7 +14,8 @@
 
 namespace {
 
-constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
+constexpr int kVersion = 1 * 10000 + 1 * 100 + 0;
+constexpr int kMaxSeq = 1 << 30;  // sequence lengths up to 2^30 keep all tile arithmetic in int
 
 // LIBATTN_SCHEDULE=overlap|pingpong selects another tile schedule than the
 // default (serial); all compute bitwise identical results, so they
@@ -34,18 +35,21 @@ bool overlaps(const void* a, uint64_t a_bytes, const void* b, uint64_t b_bytes) 
   return a0 < b0 + b_bytes && b0 < a0 + a_bytes;
 }
 
-int validate(const void* q, const void* k, const void* v, const void* o, const float* lse, int B, int S, int Hq,
-             int Hkv, int D, int causal, float scale) {
+int validate(const void* q, const void* k, const void* v, const void* o, const float* lse, int B, int Sq, int Sk,
+             int Hq, int Hkv, int D, int causal, float scale) {
   if (!q || !k || !v || !o) return ATTN_ERR_NULL;
-  if (B < 1 || S < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_ERR_SHAPE;
+  if (B < 1 || Sq < 1 || Sk < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_ERR_SHAPE;
+  if (Sq > kMaxSeq || Sk > kMaxSeq) return ATTN_ERR_SHAPE;
   if (causal != 0 && causal != 1) return ATTN_ERR_SHAPE;
+  if (causal && Sq > Sk) return ATTN_ERR_SHAPE;
   if (!std::isfinite(scale)) return ATTN_ERR_SHAPE;
   if (D != 128) return ATTN_ERR_UNSUPPORTED;
+  if ((int64_t)Hkv * D * 2 * 64 > 0xffffffffLL) return ATTN_ERR_UNSUPPORTED;  // 64 K/V rows must span < 4 GiB
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned16(lse)))
     return ATTN_ERR_ALIGN;
-  const uint64_t q_bytes = (uint64_t)B * S * Hq * D * 2;
-  const uint64_t kv_bytes = (uint64_t)B * S * Hkv * D * 2;
-  const uint64_t lse_bytes = (uint64_t)B * Hq * S * 4;
+  const uint64_t q_bytes = (uint64_t)B * Sq * Hq * D * 2;
+  const uint64_t kv_bytes = (uint64_t)B * Sk * Hkv * D * 2;
+  const uint64_t lse_bytes = (uint64_t)B * Hq * Sq * 4;
   if (overlaps(o, q_bytes, q, q_bytes) || overlaps(o, q_bytes, k, kv_bytes) || overlaps(o, q_bytes, v, kv_bytes) ||
       overlaps(o, q_bytes, lse, lse_bytes))
     return ATTN_ERR_OVERLAP;
@@ -56,9 +60,9 @@ int validate(const void* q, const void* k, const void* v, const void* o, const f
 
 extern "C" {
 
-int attn_fwd_stream(const void* q, const void* k, const void* v, void* o, float* lse, int B, int S, int Hq, int Hkv,
-                    int D, int causal, float scale, void* stream) {
-  const int st = validate(q, k, v, o, lse, B, S, Hq, Hkv, D, causal, scale);
+int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Sq, int Sk, int Hq,
+                int Hkv, int D, int causal, float scale, void* stream) {
+  const int st = validate(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, D, causal, scale);
   if (st != ATTN_OK) return st;
 
   libattn::Params p;
@@ -68,16 +72,18 @@ int attn_fwd_stream(const void* q, const void* k, const void* v, void* o, float*
   p.o = static_cast<_Float16*>(o);
   p.lse = lse;
   p.q_sstride = (int64_t)Hq * D;
-  p.q_bstride = (int64_t)S * p.q_sstride;
+  p.q_bstride = (int64_t)Sq * p.q_sstride;
   p.kv_sstride = (int64_t)Hkv * D;
-  p.kv_bstride = (int64_t)S * p.kv_sstride;
+  p.kv_bstride = (int64_t)Sk * p.kv_sstride;
   p.B = B;
-  p.S = S;
+  p.Sq = Sq;
+  p.Sk = Sk;
   p.Hq = Hq;
   p.Hkv = Hkv;
+  p.off = causal ? Sk - Sq : 0;
   p.g = Hq / Hkv;
   p.pairs = (p.g + 1) / 2;
-  p.n_qt = (S + 127) / 128;
+  p.n_qt = (Sq + 127) / 128;
   p.causal = causal;
   p.neg = scale < 0.f ? 1 : 0;
   p.cs = std::fabs(scale) * 1.44269504088896340736f;
@@ -86,6 +92,11 @@ int attn_fwd_stream(const void* q, const void* k, const void* v, void* o, float*
 
   const hipError_t e = libattn::launch_attn_fwd(p, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+int attn_fwd_stream(const void* q, const void* k, const void* v, void* o, float* lse, int B, int S, int Hq, int Hkv,
+                    int D, int causal, float scale, void* stream) {
+  return attn_fwd_ex(q, k, v, o, lse, B, S, S, Hq, Hkv, D, causal, scale, stream);
 }
 
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int S, int Hq, int Hkv, int D,

@@ -210,11 +210,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(Params p) {
   const bool active = hl < p.g;
   const int h = c * p.g + (active ? hl : 0);
 
-  const int S = p.S;
+  const int Sq = p.Sq, Sk = p.Sk;
+  const int off = p.off;        // causal: query row i attends keys j <= i + off
   const int q0 = t * BM;
   const int qw = q0 + 32 * wq;  // first query row of this wave
-  const int kv_tiles_all = (S + BN - 1) / BN;
-  const int n_tiles = p.causal ? min(kv_tiles_all, (q0 + BM + BN - 1) / BN) : kv_tiles_all;
+  const int kv_tiles_all = (Sk + BN - 1) / BN;
+  const int n_tiles = p.causal ? min(kv_tiles_all, (q0 + off + BM + BN - 1) / BN) : kv_tiles_all;
 
   const _Float16* qb = p.q + (int64_t)b * p.q_bstride + (int64_t)h * HD;
   const _Float16* kb_ = p.k + (int64_t)b * p.kv_bstride + (int64_t)c * HD;
@@ -224,7 +225,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(Params p) {
   f16x8 qf[8];
   {
     const int qrow = qw + n;
-    const bool ok = active && qrow < S;
+    const bool ok = active && qrow < Sq;
     const uint32_t flip = p.neg ? 0x80008000u : 0u;
     const _Float16* src = qb + (int64_t)qrow * p.q_sstride + 8 * hh;
 #pragma unroll
@@ -240,7 +241,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(Params p) {
   // t & 1 of their rings.  Wave w issues K instructions w, w+8, w+16 and V
   // instructions w, w+8 of a tile: 33 per tile over the 8 waves.  The lane
   // offsets relative to a tile's first row are fixed; rows past the end of
-  // the sequence are loaded from row S-1 (finite data whose scores and
+  // the keys are loaded from row Sk-1 (finite data whose scores and
   // weights are masked to zero).
   const uint32_t row_bytes = (uint32_t)p.kv_sstride * 2;
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
@@ -261,24 +262,24 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(Params p) {
     tv = __builtin_amdgcn_readfirstlane(tv);
     if (tk < n_tiles) {
       const char* base = (const char*)kb_ + (int64_t)tk * BN * row_bytes;
-      const bool full = (tk + 1) * BN <= S;
+      const bool full = (tk + 1) * BN <= Sk;
 #pragma unroll
       for (int u = 0; u < K_DMA_PER_WAVE; ++u) {
         const int i = wave_s + 8 * u;
         if (i < K_DMA) {
-          const int row = full ? k_row[u] : min(k_row[u], S - 1 - tk * BN);
+          const int row = full ? k_row[u] : min(k_row[u], Sk - 1 - tk * BN);
           dma16(base, (uint32_t)row * row_bytes + k_col[u], k_lds_base + (tk % K_SLOTS) * K_TILEB + 1024 * i);
         }
       }
     }
     if (tv < n_tiles) {
       const char* base = (const char*)vb_ + (int64_t)tv * BN * row_bytes;
-      const bool full = (tv + 1) * BN <= S;
+      const bool full = (tv + 1) * BN <= Sk;
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int i = wave_s + 8 * u;
         const int row0 = 4 * i + v_rowl;
-        const int row = full ? row0 : min(row0, S - 1 - tv * BN);
+        const int row = full ? row0 : min(row0, Sk - 1 - tv * BN);
         dma16(base, (uint32_t)row * row_bytes + v_col, v_lds_base + (tv & 1) * V_TILEB + 1024 * i);
       }
     }
@@ -307,8 +308,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(Params p) {
   // tests take wave-uniform copies so that they compile to scalar branches.
   const int qw_u = __builtin_amdgcn_readfirstlane(qw);
   const bool active_u = __builtin_amdgcn_readfirstlane(active ? 1 : 0) != 0;
-  auto skip = [&](int j) INL { return !active_u || (p.causal && j * BN > qw_u + 31); };
-  auto is_masked = [&](int j) INL { return (p.causal && j * BN + BN - 1 > qw_u) || j * BN + BN > S; };
+  auto skip = [&](int j) INL { return !active_u || (p.causal && j * BN > qw_u + 31 + off); };
+  auto is_masked = [&](int j) INL { return (p.causal && j * BN + BN - 1 > qw_u + off) || j * BN + BN > Sk; };
 
   // ---- fragments of the mma sTasks
   auto frag_qk = [&](int j, int kk, int sb) INL -> f16x8 {
@@ -360,12 +361,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(Params p) {
     Rescale rz;
   };
   // Key (sb, r) of this lane is j*BN + 32sb + 8(r/4) + 4hh + r%4; it is
-  // allowed iff it is below end = min(S, query + 1) (causal) or S, i.e. iff
+  // allowed iff it is below end = min(Sk, query + off + 1) (causal) or Sk, i.e. iff
   // the compile-time part 32sb + 8(r/4) + r%4 is below lim.
   auto sm_init = [&](int j, auto masked, SmState& st) INL {
     if constexpr (decltype(masked)::value) {
       const int query = qw + n;
-      const int end = p.causal ? min(S, query + 1) : S;
+      const int end = p.causal ? min(Sk, query + off + 1) : Sk;
       st.lim = end - j * BN - 4 * hh;
     }
     st.negm = -m_run;
@@ -592,7 +593,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(Params p) {
     auto set_lim = [&](int j, auto masked, SmState& st) INL {
       if constexpr (decltype(masked)::value) {
         const int query = qw + n;
-        const int end = p.causal ? min(S, query + 1) : S;
+        const int end = p.causal ? min(Sk, query + off + 1) : Sk;
         st.lim = end - j * BN - 4 * hh;
       }
     };
@@ -663,7 +664,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(Params p) {
     // steady-state loop is split so that each loop has one code path.  The
     // first and the last iteration always take the masked path (with no key
     // masked it computes the same values).
-    const int j_ms = min(n_tiles, p.causal ? min(q0, S) / BN : S / BN);
+    const int j_ms = min(n_tiles, p.causal ? min(q0 + off, Sk) / BN : Sk / BN);
     using T = std::true_type;
     using F = std::false_type;
     stage(0, n_tiles);
@@ -712,7 +713,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(Params p) {
   // ---- epilogue: O = O^T / l (fp16, round to nearest even), LSE in natural log
   if (active) {
     const int qrow = qw + n;
-    if (qrow < S) {
+    if (qrow < Sq) {
       const float inv = 1.0f / l_run;
       _Float16* dst = p.o + (int64_t)b * p.q_bstride + (int64_t)qrow * p.q_sstride + (int64_t)h * HD;
 #pragma unroll
@@ -725,7 +726,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(Params p) {
           *reinterpret_cast<f16x4*>(dst + 32 * db + 8 * r4 + 4 * hh) = hv;
         }
       if (p.lse && hh == 0)
-        p.lse[((int64_t)b * p.Hq + h) * S + qrow] = (m_run + log2f(l_run)) * LN2;
+        p.lse[((int64_t)b * p.Hq + h) * Sq + qrow] = (m_run + log2f(l_run)) * LN2;
     }
   }
 }

@@ -28,14 +28,15 @@ struct Params {
   const _Float16* v;
   _Float16* o;
   float* lse;        // may be null
-  int64_t q_bstride;  // S * Hq * D
+  int64_t q_bstride;  // Sq * Hq * D
   int64_t q_sstride;  // Hq * D
-  int64_t kv_bstride; // S * Hkv * D
+  int64_t kv_bstride; // Sk * Hkv * D
   int64_t kv_sstride; // Hkv * D
-  int B, S, Hq, Hkv;
+  int B, Sq, Sk, Hq, Hkv;
+  int off;           // causal: Sk - Sq (query row i may attend keys j <= i + off); 0 otherwise
   int g;             // Hq / Hkv
   int pairs;         // ceil(g / 2): head pairs per KV head
-  int n_qt;          // query tiles per head
+  int n_qt;          // query tiles per head (over Sq)
   int causal;
   int neg;           // scale < 0: the kernel negates Q and uses |scale|
   float cs;          // |scale| * log2(e)

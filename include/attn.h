@@ -10,7 +10,7 @@
  * (section "核心方法").  For every batch entry b, query head h and query row i:
  *
  *   c = h / (Hq / Hkv)                         query head h reads KV head c
- *   allowed keys j: 0..i if causal, else 0..S-1 (top-left causal mask, Sq == Sk)
+ *   allowed keys j: 0..i if causal, else 0..S-1
  *   s_j = scale * dot(q[b,i,h,:], k[b,j,c,:])
  *   o[b,i,h,:]  = sum_j softmax(s)_j * v[b,j,c,:]
  *   lse[b,h,i]  = log(sum_j exp(s_j))          natural log of the scaled scores
@@ -23,8 +23,17 @@
  * to nearest even from fp32.  Internal offsets are 64-bit, so tensors larger
  * than 4 GiB are supported.
  *
- * Scalars: B, S, Hq, Hkv >= 1; Hq % Hkv == 0; D == 128 (other head sizes
- * return ATTN_ERR_UNSUPPORTED); causal is 0 or 1; scale is any finite float.
+ * Scalars: B, S, Hq, Hkv >= 1; S <= 2^30; Hq % Hkv == 0; D == 128 (other
+ * head sizes return ATTN_ERR_UNSUPPORTED, and so does Hkv * D * 2 * 64 >=
+ * 2^32, i.e. a 64-row K/V tile spanning 4 GiB or more); causal is 0 or 1;
+ * scale is any finite float.
+ *
+ * attn_fwd_ex takes different query and key lengths (chunked prefill): q and
+ * o are [B][Sq][Hq][D], k and v [B][Sk][Hkv][D], lse [B][Hq][Sq].  With
+ * causal = 1 the mask is aligned at the bottom right: query row i sits at key
+ * position i + Sk - Sq and attends keys 0..i + Sk - Sq, so the last query row
+ * sees every key (Sq == Sk gives the square mask above); causal needs
+ * Sq <= Sk, else ATTN_ERR_SHAPE.  Without causal any Sq, Sk >= 1 is allowed.
  *
  * Execution: the call validates its arguments, then enqueues one kernel on
  * the given HIP stream (attn_fwd uses the null stream) and returns without
@@ -51,7 +60,7 @@ extern "C" {
 enum {
   ATTN_OK = 0,
   ATTN_ERR_NULL = 1,        /* a required pointer is NULL */
-  ATTN_ERR_SHAPE = 2,       /* B, S, Hq, Hkv < 1, Hq % Hkv != 0, causal not 0/1, or scale not finite */
+  ATTN_ERR_SHAPE = 2,       /* a size < 1 or > 2^30, Hq % Hkv != 0, causal not 0/1, causal with Sq > Sk, scale not finite */
   ATTN_ERR_UNSUPPORTED = 3, /* D other than 128 */
   ATTN_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
   ATTN_ERR_HIP = 5,         /* the HIP runtime reported an error at launch */
@@ -65,6 +74,11 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
 /* Same as attn_fwd, enqueued on `stream` (a hipStream_t; NULL means the null stream). */
 int attn_fwd_stream(const void* q, const void* k, const void* v, void* o, float* lse, int B, int S, int Hq, int Hkv,
                     int D, int causal, float scale, void* stream);
+
+/* Sq query rows against Sk keys (see above), enqueued on `stream`.  attn_fwd_stream(..., S, ...) is
+ * attn_fwd_ex(..., S, S, ...). */
+int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Sq, int Sk, int Hq,
+                int Hkv, int D, int causal, float scale, void* stream);
 
 /* Static, NUL-terminated description of a status code ("unknown status" for others). */
 const char* attn_status_string(int status);

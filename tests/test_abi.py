@@ -106,3 +106,26 @@ def test_binding_fails_loudly_without_library(tmp_path):
             L.load(str(tmp_path / "missing.so"))
     finally:
         L._lib = saved
+
+
+def call_ex(**kw):
+    a = dict(q=QP, k=KP, v=VP, o=OP, lse=LP, B=1, Sq=64, Sk=64, Hq=8, Hkv=2, D=128, causal=1, scale=0.1, stream=None)
+    a.update(kw)
+    return L.attn_fwd_ex(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Sq"], a["Sk"], a["Hq"], a["Hkv"], a["D"],
+                         a["causal"], a["scale"], a["stream"])
+
+
+@pytest.mark.parametrize("kw", [dict(Sq=0), dict(Sk=0), dict(Sq=65, Sk=64), dict(Sq=(1 << 30) + 1, Sk=(1 << 30) + 1),
+                                dict(Sk=(1 << 30) + 1, causal=0), dict(Hq=9, Hkv=2)], ids=str)
+def test_ex_bad_shapes(lib, kw):
+    """attn_fwd_ex: causal needs Sq <= Sk; sizes are 1..2^30 (nothing is launched on an error)."""
+    assert call_ex(**kw) == L.ATTN_ERR_SHAPE
+
+
+def test_ex_limits_and_order(lib):
+    assert call_ex(D=64) == L.ATTN_ERR_UNSUPPORTED
+    # 64 rows of K/V must span less than 4 GiB: Hkv * 128 * 2 * 64 >= 2^32 is refused
+    assert call_ex(Hq=262144, Hkv=262144) == L.ATTN_ERR_UNSUPPORTED
+    assert call_ex(q=0, Sq=65) == L.ATTN_ERR_NULL
+    assert call_ex(Sq=65, D=64) == L.ATTN_ERR_SHAPE
+    assert call_ex(o=KP + 4096, Sq=16, Sk=64) == L.ATTN_ERR_OVERLAP
