@@ -57,7 +57,8 @@ def kernel_fingerprint() -> str:
     from dnn_compiler_pipelining_amd import build as hipbuild
 
     h = hashlib.sha256()
-    for path in hipbuild.SOURCES + [os.path.join(hipbuild.CSRC, "attn_kernel.h")]:
+    for path in hipbuild.SOURCES + [os.path.join(hipbuild.CSRC, n) for n in ("attn_kernel.h", "variant.h",
+                                                                           "tuned_table.h")]:
         with open(path, "rb") as f:
             h.update(f.read())
     h.update(" ".join(hipbuild.HIP_FLAGS[:9]).encode())

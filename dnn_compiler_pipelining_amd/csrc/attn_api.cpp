@@ -17,14 +17,29 @@ namespace {
 constexpr int kVersion = 1 * 10000 + 1 * 100 + 0;
 constexpr int kMaxSeq = 1 << 30;  // sequence lengths up to 2^30 keep all tile arithmetic in int
 
-// LIBATTN_SCHEDULE=overlap|pingpong selects another tile schedule than the
-// default (serial); all compute bitwise identical results, so they
-// cross-check each other.  Read on every call so a test can switch it.
-int schedule_from_env() {
-  const char* s = std::getenv("LIBATTN_SCHEDULE");
-  if (s && std::strcmp(s, "overlap") == 0) return libattn::SCHEDULE_OVERLAP;
-  if (s && std::strcmp(s, "pingpong") == 0) return libattn::SCHEDULE_PINGPONG;
-  return libattn::SCHEDULE_SERIAL;
+// The variant for a shape: the tuned choice (variant.h), unless the
+// environment overrides a field.  LIBATTN_SCHEDULE=serial|overlap|pingpong,
+// LIBATTN_RING=2|4, LIBATTN_XCD=0|1 and LIBATTN_LPT=0|1 are read on every
+// call, so tests and the schedule search can switch them; all variants give
+// bitwise identical results.
+libattn::Variant choose_variant(int B, int Sq, int Sk, int Hq, int Hkv) {
+  libattn::Variant v = libattn::tuned_variant(B, Sq, Sk, Hq, Hkv);
+  if (const char* s = std::getenv("LIBATTN_SCHEDULE")) {
+    if (std::strcmp(s, "serial") == 0) v.schedule = libattn::SCHEDULE_SERIAL;
+    if (std::strcmp(s, "overlap") == 0) v.schedule = libattn::SCHEDULE_OVERLAP;
+    if (std::strcmp(s, "pingpong") == 0) v.schedule = libattn::SCHEDULE_PINGPONG;
+  }
+  auto flag = [](const char* name, int& field, int lo, int hi) {
+    if (const char* s = std::getenv(name)) {
+      const int x = std::atoi(s);
+      if (x == lo || x == hi) field = x;
+    }
+  };
+  flag("LIBATTN_RING", v.ring, 2, 4);
+  flag("LIBATTN_XCD", v.xcd, 0, 1);
+  flag("LIBATTN_LPT", v.lpt, 0, 1);
+  if (!libattn::variant_valid(v)) v = libattn::Variant{libattn::SCHEDULE_SERIAL, 4, 1, 1};
+  return v;
 }
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
@@ -87,7 +102,11 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
   p.causal = causal;
   p.neg = scale < 0.f ? 1 : 0;
   p.cs = std::fabs(scale) * 1.44269504088896340736f;
-  p.schedule = schedule_from_env();
+  const libattn::Variant var = choose_variant(B, Sq, Sk, Hq, Hkv);
+  p.schedule = var.schedule;
+  p.ring = var.ring;
+  p.xcd = var.xcd;
+  p.lpt = var.lpt;
   if (libattn::grid_blocks(p) < 0) return ATTN_ERR_SHAPE;
 
   const hipError_t e = libattn::launch_attn_fwd(p, static_cast<hipStream_t>(stream));

@@ -92,11 +92,6 @@ static_assert(V_DMA == 16, "wave w issues V instructions w and w+8");
 // can recompute S^T from it.
 constexpr int K_SLOTS = 3, V_SLOTS = 2;
 static_assert(K_SLOTS * K_TILEB + V_SLOTS * V_TILEB <= 160 * 1024, "the K and V rings fit the 160 KiB LDS");
-// Depth of the fragment prefetch ring of the mma steps.
-#ifndef ATTN_RING
-#define ATTN_RING 4
-#endif
-constexpr int RING = ATTN_RING;
 
 __device__ __forceinline__ float pair_max(float x) {
   // lanes l and l^32 hold the same query: combine their partial results
@@ -170,7 +165,9 @@ __host__ __device__ constexpr Step step_of(int mode, int i) {
 constexpr int steps_of(int mode) { return (mode == 0 || mode == 3) ? 32 : 16; }
 constexpr int reads_of(int mode, int i) { return step_of(mode, i).pv ? 2 : 1; }  // LDS reads per fragment
 
-template <int kSched>
+// kSched: tile schedule; kRing: depth of the fragment prefetch ring of the mma
+// steps (how many steps ahead the LDS reads run).
+template <int kSched, int kRing>
 __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(Params p) {
   __shared__ __attribute__((aligned(1024))) char k_smem[K_SLOTS * K_TILEB];
   __shared__ __attribute__((aligned(1024))) char v_smem[V_SLOTS * V_TILEB];
@@ -186,15 +183,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(Params p) {
   const int hh = lane >> 5;   // lane half
 
   // ---- workgroup -> (batch, kv head, head pair, query tile)
-  // Workgroups are dealt round-robin to the 8 XCDs; give each XCD whole
-  // (batch, kv head) groups so that co-resident workgroups share K/V in that
-  // XCD's L2, and within a group run the longest causal tiles first.
+  // Workgroups are dealt round-robin to the 8 XCDs.  With p.xcd, give each XCD
+  // whole (batch, kv head) groups so that co-resident workgroups share K/V in
+  // that XCD's L2; with p.lpt, run the longest causal tiles of a group first.
   const int items = p.pairs * p.n_qt;  // workgroups per (b, c) group
   const int ngroups = p.B * p.Hkv;
   int group, item;
   {
     const int bid = blockIdx.x;
-    if ((ngroups & 7) == 0) {
+    if (p.xcd && (ngroups & 7) == 0) {
       const int x = bid & 7, y = bid >> 3;
       group = (y / items) * 8 + x;
       item = y % items;
@@ -205,7 +202,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(Params p) {
   }
   const int b = group / p.Hkv;
   const int c = group % p.Hkv;
-  const int t = p.n_qt - 1 - item / p.pairs;
+  const int t = p.lpt ? p.n_qt - 1 - item / p.pairs : item / p.pairs;
   const int hl = 2 * (item % p.pairs) + grp;  // head index inside the KV group
   const bool active = hl < p.g;
   const int h = c * p.g + (active ? hl : 0);
@@ -455,11 +452,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(Params p) {
 
   // ---- one block of mma steps, optionally fused with a softmax.  QK steps
   // read K tile jq into sd; PV steps read V tile jv with P^T from ps.  The
-  // fragments of the next RING steps are always in flight.  Without a
+  // fragments of the next kRing steps are always in flight.  Without a
   // softmax the scheduler is pinned to "MFMA i, then the LDS reads of step
-  // i + RING".  With one, step i is fixed by
+  // i + kRing".  With one, step i is fixed by
   // hand as "the softmax parts placed there (sm(i)), MFMA i, LDS reads of
-  // step i + RING" and nothing moves across steps, so each wave keeps the
+  // step i + kRing" and nothing moves across steps, so each wave keeps the
   // matrix core, the LDS and the VALU busy together.
   struct NoSoftmax {};
   auto block = [&](auto mode_c, int jq, f32x16 (&sd)[2], int jv, f16x8 (&ps)[4], auto sm) INL {
@@ -471,13 +468,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(Params p) {
       if constexpr (st.pv) return frag_pv(jv, st.kk, st.x);
       else return frag_qk(jq, st.kk, st.x);
     };
-    f16x8 fr[RING];
-    static_for<RING>([&](auto ic) INL { fr[decltype(ic)::value] = load(ic); });
+    f16x8 fr[kRing];
+    static_for<kRing>([&](auto ic) INL { fr[decltype(ic)::value] = load(ic); });
     auto step = [&](auto ic) INL {
       constexpr int i = decltype(ic)::value;
       constexpr Step st = step_of(mode, i);
-      const f16x8 a = fr[i % RING];
-      if constexpr (i + RING < nsteps) fr[i % RING] = load(std::integral_constant<int, i + RING>{});
+      const f16x8 a = fr[i % kRing];
+      if constexpr (i + kRing < nsteps) fr[i % kRing] = load(std::integral_constant<int, i + kRing>{});
       if constexpr (st.pv)
         o_acc[st.x] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, ps[st.kk], o_acc[st.x], 0, 0, 0);
       else if constexpr (st.kk == 0)
@@ -487,13 +484,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(Params p) {
     };
     if constexpr (!kSoftmax) {
       static_for<nsteps>(step);
-      static_for<RING>([&](auto ic) INL {
+      static_for<kRing>([&](auto ic) INL {
         __builtin_amdgcn_sched_group_barrier(0x100, reads_of(mode, decltype(ic)::value), 0);
       });
       static_for<nsteps>([&](auto ic) INL {
         constexpr int i = decltype(ic)::value;
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if constexpr (i + RING < nsteps) __builtin_amdgcn_sched_group_barrier(0x100, reads_of(mode, i + RING), 0);
+        if constexpr (i + kRing < nsteps) __builtin_amdgcn_sched_group_barrier(0x100, reads_of(mode, i + kRing), 0);
       });
     } else {
       static_for<nsteps>([&](auto ic) INL {
@@ -739,12 +736,21 @@ int64_t grid_blocks(const Params& p) {
 hipError_t launch_attn_fwd(const Params& p, hipStream_t stream) {
   const int64_t nb = grid_blocks(p);
   if (nb <= 0) return hipErrorInvalidValue;
-  if (p.schedule == SCHEDULE_OVERLAP)
-    hipLaunchKernelGGL(attn_fwd_kernel<SCHEDULE_OVERLAP>, dim3((unsigned)nb), dim3(NTHREADS), 0, stream, p);
-  else if (p.schedule == SCHEDULE_PINGPONG)
-    hipLaunchKernelGGL(attn_fwd_kernel<SCHEDULE_PINGPONG>, dim3((unsigned)nb), dim3(NTHREADS), 0, stream, p);
-  else
-    hipLaunchKernelGGL(attn_fwd_kernel<SCHEDULE_SERIAL>, dim3((unsigned)nb), dim3(NTHREADS), 0, stream, p);
+  const dim3 grid((unsigned)nb), block(NTHREADS);
+#define LIBATTN_LAUNCH(S, R) hipLaunchKernelGGL((attn_fwd_kernel<S, R>), grid, block, 0, stream, p)
+  if (p.ring != 2 && p.ring != 4) return hipErrorInvalidValue;
+  const bool r2 = p.ring == 2;
+  if (p.schedule == SCHEDULE_OVERLAP) {
+    if (r2) LIBATTN_LAUNCH(SCHEDULE_OVERLAP, 2);
+    else LIBATTN_LAUNCH(SCHEDULE_OVERLAP, 4);
+  } else if (p.schedule == SCHEDULE_PINGPONG) {
+    if (r2) LIBATTN_LAUNCH(SCHEDULE_PINGPONG, 2);
+    else LIBATTN_LAUNCH(SCHEDULE_PINGPONG, 4);
+  } else {
+    if (r2) LIBATTN_LAUNCH(SCHEDULE_SERIAL, 2);
+    else LIBATTN_LAUNCH(SCHEDULE_SERIAL, 4);
+  }
+#undef LIBATTN_LAUNCH
   return hipGetLastError();
 }
 

@@ -5,21 +5,13 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "variant.h"
+
 namespace libattn {
 
-// Tile schedules of the kernel.  All compute bitwise identical results (each
-// accumulator sees the same operations in the same order), so running one
-// against another cross-checks them: an LDS race in any would show up.
-//   SERIAL  : per tile, one wave runs QK^T, softmax and PV back to back; the
-//             two waves that share a SIMD overlap each other's MFMA and VALU
-//             work (the default: fastest measured, see below)
-//   OVERLAP : every wave overlaps, inside one instruction stream, the softmax
-//             of tile j with the MFMAs of QK^T(j+1) and PV(j-1)
-//   PINGPONG: two wave groups offset by half a tile alternate MFMA and softmax
-// Measured on MI355X all three land within a few percent of each other: the
-// kernel runs at the chip's power limit, where the clock, not the issue
-// order, sets the rate.
-enum Schedule { SCHEDULE_SERIAL = 0, SCHEDULE_OVERLAP = 1, SCHEDULE_PINGPONG = 2 };
+// Tile schedules and the variant choice: variant.h.  Measured on MI355X all
+// three schedules land within a few percent of each other: the kernel runs at
+// the chip's power limit, where the clock, not the issue order, sets the rate.
 
 // Launch parameters.  Pointers are device pointers; strides are in elements.
 struct Params {
@@ -41,6 +33,9 @@ struct Params {
   int neg;           // scale < 0: the kernel negates Q and uses |scale|
   float cs;          // |scale| * log2(e)
   int schedule;      // Schedule
+  int ring;          // fragment prefetch depth of the mma steps: 2 or 4
+  int xcd;           // 1: give each XCD whole (batch, kv head) groups
+  int lpt;           // 1: longest causal query tiles of a group first
 };
 
 // Grid size for p (number of workgroups), or -1 if it does not fit an int.

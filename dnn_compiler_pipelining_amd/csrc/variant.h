@@ -1,0 +1,68 @@
+// variant.h -- the kernel variants libattn can launch and the choice among
+// them per problem shape.  Host-only and free of HIP, so that the selection
+// logic can be compiled and tested on its own.
+//
+// A variant is a point of the schedule space that the search in
+// dnn_compiler_pipelining_amd/tune.py explores: the tile schedule, the depth
+// of the fragment prefetch ring, and two workgroup-order switches.  Every
+// variant computes bitwise identical results; they differ only in speed.
+// PipeThreader searches such a space of task orders with a validity check
+// and profile feedback (page "PipeThreader: Software-Defined Pipelining ...
+// (OSDI 2025)" summary, section "核心方法"); tuned_table.h is the outcome of
+// that search for a set of measured shapes.
+#pragma once
+
+#include <cmath>
+
+namespace libattn {
+
+// Tile schedules (see attn_fwd.hip).  All compute bitwise identical results.
+//   SERIAL  : per tile, one wave runs QK^T, softmax and PV back to back; the
+//             two waves that share a SIMD overlap each other's MFMA and VALU
+//             work
+//   OVERLAP : every wave overlaps, inside one instruction stream, the softmax
+//             of tile j with the MFMAs of QK^T(j+1) and PV(j-1)
+//   PINGPONG: two wave groups offset by half a tile alternate MFMA and softmax
+enum Schedule { SCHEDULE_SERIAL = 0, SCHEDULE_OVERLAP = 1, SCHEDULE_PINGPONG = 2 };
+
+struct Variant {
+  int schedule;  // Schedule
+  int ring;      // fragment prefetch depth of the mma steps: 2 or 4
+  int xcd;       // 1: each XCD gets whole (batch, kv head) groups
+  int lpt;       // 1: longest causal query tiles of a group first
+};
+
+// One measured shape and the fastest variant found for it.
+struct TunedEntry {
+  int B, Sq, Sk, Hq, Hkv;
+  Variant v;
+  double tflops;  // measured rate of that variant (documentation only)
+};
+
+#include "tuned_table.h"  // kTuned[], kTunedCount
+
+inline bool variant_valid(const Variant& v) {
+  return v.schedule >= SCHEDULE_SERIAL && v.schedule <= SCHEDULE_PINGPONG && (v.ring == 2 || v.ring == 4) &&
+         (v.xcd == 0 || v.xcd == 1) && (v.lpt == 0 || v.lpt == 1);
+}
+
+// The variant tuned for the measured shape nearest to (B, Sq, Sk, Hq, Hkv):
+// distance = sum of |log2| ratios of B, Sq, Sk and the GQA ratio Hq/Hkv, plus
+// half that of Hkv.  The first entry wins ties.
+inline Variant tuned_variant(int B, int Sq, int Sk, int Hq, int Hkv) {
+  auto lr = [](double a, double b) { return std::fabs(std::log2(a / b)); };
+  const double g = (double)Hq / Hkv;
+  int best = 0;
+  double best_d = 1e300;
+  for (int i = 0; i < kTunedCount; ++i) {
+    const TunedEntry& e = kTuned[i];
+    const double d = lr(B, e.B) + lr(Sq, e.Sq) + lr(Sk, e.Sk) + lr(g, (double)e.Hq / e.Hkv) + 0.5 * lr(Hkv, e.Hkv);
+    if (d < best_d) {
+      best_d = d;
+      best = i;
+    }
+  }
+  return kTuned[best].v;
+}
+
+}  // namespace libattn

@@ -1,0 +1,227 @@
+"""Schedule-space search for libattn.
+
+PipeThreader schedules an operator by searching the space of task orders on
+the hardware's units under a resource check, with measured feedback (page
+"PipeThreader: Software-Defined Pipelining ... (OSDI 2025)" summary, section
+"核心方法").  This module does that for libattn's space of kernel variants
+(csrc/variant.h): tile schedule x fragment-prefetch depth (compile time) x
+two workgroup-order switches (run time).  Every variant computes the same bits,
+so the search only trades speed.
+
+    python -m dnn_compiler_pipelining_amd.tune --check
+        validity of every compiled variant from the code-object metadata (CPU)
+    python -m dnn_compiler_pipelining_amd.tune --search OUT_DIR [--workload NAME ...]
+        greedy coordinate search with measured feedback per workload (GPU);
+        writes OUT_DIR/schedule_search.json
+    python -m dnn_compiler_pipelining_amd.tune --emit SEARCH_JSON
+        turns a search record into csrc/tuned_table.h and profiles/schedule_search.json (CPU)
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import re
+import sys
+import tempfile
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+TABLE = os.path.join(PKG, "csrc", "tuned_table.h")
+PROFILE = os.path.join(ROOT, "profiles", "schedule_search.json")
+
+SCHEDULES = ("serial", "overlap", "pingpong")  # Schedule enum order in csrc/variant.h
+RINGS = (2, 4)
+SWITCHES = (0, 1)
+SEED = {"schedule": "serial", "ring": 4, "xcd": 1, "lpt": 1}
+
+# resource budget of one variant: 8 waves per workgroup at 2 waves per SIMD
+MAX_VGPR = 256
+MAX_LDS = 160 * 1024
+
+
+def kernel_resources(asm_path: str):
+    """{(schedule, ring): {vgpr, agpr, vgpr_spill, scratch, lds}} from the AMDGPU metadata of a device asm file."""
+    text = open(asm_path).read()
+    meta = text[text.index("amdhsa.kernels:"):]
+    out = {}
+    for block in re.split(r"\n  - ", meta)[1:]:
+        m = re.search(r"\.name:\s+\S*attn_fwd_kernelILi(\d)ELi(\d)E", block)
+        if not m:
+            continue
+
+        def num(key):
+            mm = re.search(r"\." + key + r":\s+(\d+)", block)
+            return int(mm.group(1)) if mm else 0
+
+        out[(SCHEDULES[int(m.group(1))], int(m.group(2)))] = dict(
+            vgpr=num("vgpr_count"), agpr=num("agpr_count"), vgpr_spill=num("vgpr_spill_count"),
+            scratch=num("private_segment_fixed_size"), lds=num("group_segment_fixed_size"))
+    return out
+
+
+def check_valid(res: dict) -> tuple[bool, str]:
+    """A variant is valid when it fits 2 waves per SIMD with no spills and no scratch, and its LDS fits a CU."""
+    if res["vgpr"] + res["agpr"] > MAX_VGPR:
+        return False, "%d VGPRs > %d" % (res["vgpr"] + res["agpr"], MAX_VGPR)
+    if res["vgpr_spill"] or res["scratch"]:
+        return False, "spills %d VGPRs / %d B scratch" % (res["vgpr_spill"], res["scratch"])
+    if res["lds"] > MAX_LDS:
+        return False, "%d B LDS > %d" % (res["lds"], MAX_LDS)
+    return True, "ok"
+
+
+def valid_variants(asm_path: str | None = None):
+    """{(schedule, ring): (valid, reason, resources)} for the current sources."""
+    from dnn_compiler_pipelining_amd import build
+
+    if asm_path is None:
+        fd, asm_path = tempfile.mkstemp(suffix=".s")
+        os.close(fd)
+        build.device_asm(asm_path)
+    res = kernel_resources(asm_path)
+    return {k: check_valid(v) + (v,) for k, v in res.items()}
+
+
+# ------------------------------------------------------------------ search (GPU)
+
+def _time(fn, reps: int) -> float:
+    import torch
+
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def measure(w, point: dict, q, k, v, o, lse) -> float:
+    """TFLOP/s of one variant on one workload (median of three timed batches)."""
+    from dnn_compiler_pipelining_amd import binding
+
+    os.environ["LIBATTN_SCHEDULE"] = point["schedule"]
+    os.environ["LIBATTN_RING"] = str(point["ring"])
+    os.environ["LIBATTN_XCD"] = str(point["xcd"])
+    os.environ["LIBATTN_LPT"] = str(point["lpt"])
+    reps = max(2, min(50, int(0.15 / max(w.flops / 1e15, 1e-6))))  # about 0.15 s per batch at 1 PFLOP/s
+    ms = sorted(_time(lambda: binding.forward(q, k, v, w.causal, w.scale, o, lse), reps) for _ in range(3))[1]
+    return w.flops / ms / 1e9
+
+
+def search_workload(w, valid, log=print):
+    """Greedy coordinate search from the seed variant: change one field at a time, keep a change only when it
+    is more than 1% faster (measurement noise on one box is about that), repeat until nothing improves."""
+    from dnn_compiler_pipelining_amd import inputs
+
+    q, k, v = inputs.make_inputs(w, "cuda")
+    import torch
+
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.S), dtype=torch.float32, device=q.device)
+    seen = {}
+
+    def rate(pt):
+        key = (pt["schedule"], pt["ring"], pt["xcd"], pt["lpt"])
+        if key not in seen:
+            seen[key] = measure(w, pt, q, k, v, o, lse)
+            log("  %-26s %-9s ring %d xcd %d lpt %d: %7.1f TFLOP/s" % (w.name, *key, seen[key]))
+        return seen[key]
+
+    axes = [("schedule", SCHEDULES), ("ring", RINGS), ("xcd", SWITCHES), ("lpt", SWITCHES)]
+    best = dict(SEED)
+    best_rate = rate(best)
+    improved = True
+    while improved:
+        improved = False
+        for field, values in axes:
+            for val in values:
+                if val == best[field]:
+                    continue
+                cand = dict(best, **{field: val})
+                if not valid.get((cand["schedule"], cand["ring"]), (False,))[0]:
+                    continue
+                r = rate(cand)
+                if r > best_rate * 1.01:
+                    best, best_rate, improved = cand, r, True
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
+    for key in ("LIBATTN_SCHEDULE", "LIBATTN_RING", "LIBATTN_XCD", "LIBATTN_LPT"):
+        os.environ.pop(key, None)
+    return {"workload": w.name, "B": w.B, "Sq": w.S, "Sk": w.S, "Hq": w.Hq, "Hkv": w.Hkv, "best": best,
+            "best_tflops": round(best_rate, 1),
+            "measured": [{"schedule": s, "ring": r, "xcd": x, "lpt": l, "tflops": round(t, 1)}
+                         for (s, r, x, l), t in seen.items()]}
+
+
+def search(out_dir: str, names=None):
+    from dnn_compiler_pipelining_amd import inputs
+
+    valid = valid_variants()
+    for (s, r), (ok, why, _) in sorted(valid.items()):
+        print("variant %-9s ring %d: %s" % (s, r, why), flush=True)
+    rec = {"valid": {"%s/%d" % k: dict(ok=v[0], reason=v[1], **v[2]) for k, v in valid.items()},
+           "rule": "greedy coordinate search from %s; a change is kept when > 1%% faster" % json.dumps(SEED),
+           "results": []}
+    for w in inputs.WORKLOADS:
+        if names and w.name not in names:
+            continue
+        print("search %s" % w.name, flush=True)
+        rec["results"].append(search_workload(w, valid, log=lambda *a: print(*a, flush=True)))
+    os.makedirs(out_dir, exist_ok=True)
+    path = os.path.join(out_dir, "schedule_search.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print("wrote", path)
+    return rec
+
+
+# ------------------------------------------------------------------ emit the table (CPU)
+
+def emit(search_json: str, table: str = TABLE, profile: str | None = PROFILE):
+    rec = json.load(open(search_json))
+    enum = {"serial": "SCHEDULE_SERIAL", "overlap": "SCHEDULE_OVERLAP", "pingpong": "SCHEDULE_PINGPONG"}
+    lines = ["// tuned_table.h -- generated by `python -m dnn_compiler_pipelining_amd.tune --emit`",
+             "// from the measured schedule search (profiles/schedule_search.json); do not edit by hand.",
+             "#pragma once", "static const TunedEntry kTuned[] = {"]
+    for r in rec["results"]:
+        b = r["best"]
+        lines.append("    {%d, %d, %d, %d, %d, {%s, %d, %d, %d}, %.1f},  // %s" % (
+            r["B"], r["Sq"], r["Sk"], r["Hq"], r["Hkv"], enum[b["schedule"]], b["ring"], b["xcd"], b["lpt"],
+            r["best_tflops"], r["workload"]))
+    lines += ["};", "static const int kTunedCount = sizeof(kTuned) / sizeof(kTuned[0]);", ""]
+    with open(table, "w") as f:
+        f.write("\n".join(lines))
+    rec["commands"] = ["python -m dnn_compiler_pipelining_amd.tune --search <out dir>   (on the GPU)",
+                       "python -m dnn_compiler_pipelining_amd.tune --emit <out dir>/schedule_search.json"]
+    if profile:
+        os.makedirs(os.path.dirname(profile), exist_ok=True)
+        with open(profile, "w") as f:
+            json.dump(rec, f, indent=1)
+    print("\n".join(lines))
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--check", action="store_true")
+    ap.add_argument("--search", metavar="OUT_DIR")
+    ap.add_argument("--workload", action="append")
+    ap.add_argument("--emit", metavar="SEARCH_JSON")
+    args = ap.parse_args(argv)
+    if ROOT not in sys.path:
+        sys.path.insert(0, ROOT)
+    if args.check:
+        for (s, r), (ok, why, res) in sorted(valid_variants().items()):
+            print("%-9s ring %d: %-5s %s  %s" % (s, r, ok, why, res))
+    if args.search:
+        search(args.search, args.workload)
+    if args.emit:
+        emit(args.emit)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

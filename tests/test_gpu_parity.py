@@ -184,3 +184,24 @@ def test_schedules_bitwise_identical(monkeypatch, B, S, Hq, Hkv, causal):
         o2, l2 = U.run(qd, kd, vd, bool(causal), SC)
         assert torch.equal(o1, o2) and torch.equal(l1, l2), sched
     monkeypatch.delenv("LIBATTN_SCHEDULE")
+
+
+@pytest.mark.parametrize("B,S,Hq,Hkv,causal", [(1, 700, 8, 2, 1), (2, 257, 12, 3, 0)], ids=str)
+def test_all_variants_bitwise_identical(monkeypatch, B, S, Hq, Hkv, causal):
+    """Every point of the searched variant space (schedule x prefetch depth x workgroup order) gives the
+    same bits as the default."""
+    q, k, v = cpu_qkv(B, S, Hq, Hkv, seed=95 + S)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    for key in ("LIBATTN_SCHEDULE", "LIBATTN_RING", "LIBATTN_XCD", "LIBATTN_LPT"):
+        monkeypatch.delenv(key, raising=False)
+    o1, l1 = U.run(qd, kd, vd, bool(causal), SC)
+    for sched in ("serial", "overlap", "pingpong"):
+        for ring in ("2", "4"):
+            for xcd in ("0", "1"):
+                for lpt in ("0", "1"):
+                    monkeypatch.setenv("LIBATTN_SCHEDULE", sched)
+                    monkeypatch.setenv("LIBATTN_RING", ring)
+                    monkeypatch.setenv("LIBATTN_XCD", xcd)
+                    monkeypatch.setenv("LIBATTN_LPT", lpt)
+                    o2, l2 = U.run(qd, kd, vd, bool(causal), SC)
+                    assert torch.equal(o1, o2) and torch.equal(l1, l2), (sched, ring, xcd, lpt)

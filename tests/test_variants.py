@@ -1,0 +1,88 @@
+"""CPU tests of the variant space and its selection (csrc/variant.h, dnn_compiler_pipelining_amd/tune.py)."""
+import json
+import os
+import shutil
+import subprocess
+
+import pytest
+
+from dnn_compiler_pipelining_amd import tune
+
+CSRC = os.path.join(tune.PKG, "csrc")
+
+
+def test_every_compiled_variant_is_valid():
+    vs = tune.valid_variants()
+    assert set(vs) == {(s, r) for s in tune.SCHEDULES for r in tune.RINGS}
+    for key, (ok, why, res) in vs.items():
+        assert ok, (key, why, res)
+        assert res["lds"] > 0 and res["vgpr"] > 0
+
+
+@pytest.mark.parametrize("res,reason", [
+    (dict(vgpr=257, agpr=0, vgpr_spill=0, scratch=0, lds=1024), "VGPRs"),
+    (dict(vgpr=200, agpr=64, vgpr_spill=0, scratch=0, lds=1024), "VGPRs"),
+    (dict(vgpr=200, agpr=0, vgpr_spill=3, scratch=12, lds=1024), "spills"),
+    (dict(vgpr=200, agpr=0, vgpr_spill=0, scratch=16, lds=1024), "spills"),
+    (dict(vgpr=200, agpr=0, vgpr_spill=0, scratch=0, lds=160 * 1024 + 16), "LDS"),
+])
+def test_check_valid_rejects_over_budget(res, reason):
+    ok, why = tune.check_valid(res)
+    assert not ok and reason in why
+
+
+LOOKUP_MAIN = r'''
+#include <cstdio>
+#include "variant.h"
+int main(int argc, char** argv) {
+  int B, Sq, Sk, Hq, Hkv;
+  while (std::scanf("%d %d %d %d %d", &B, &Sq, &Sk, &Hq, &Hkv) == 5) {
+    libattn::Variant v = libattn::tuned_variant(B, Sq, Sk, Hq, Hkv);
+    std::printf("%d %d %d %d %d\n", v.schedule, v.ring, v.xcd, v.lpt, libattn::variant_valid(v) ? 1 : 0);
+  }
+  return 0;
+}
+'''
+
+
+def lookup(tmp_path, table_dir, shapes):
+    # variant.h includes "tuned_table.h" from its own directory, so it is compiled next to the table under test
+    if os.path.abspath(str(table_dir)) != os.path.abspath(CSRC):
+        shutil.copy(os.path.join(CSRC, "variant.h"), str(table_dir))
+    src = tmp_path / "lookup.cpp"
+    src.write_text(LOOKUP_MAIN)
+    exe = tmp_path / "lookup"
+    subprocess.run(["g++", "-std=c++17", "-O1", "-I", str(table_dir), str(src), "-o", str(exe)], check=True)
+    inp = "\n".join(" ".join(str(x) for x in s) for s in shapes) + "\n"
+    out = subprocess.run([str(exe)], input=inp, capture_output=True, text=True, check=True).stdout.split("\n")
+    return [tuple(int(x) for x in line.split()) for line in out if line.strip()]
+
+
+def test_committed_table_picks_its_own_entries(tmp_path):
+    text = open(os.path.join(CSRC, "tuned_table.h")).read()
+    import re
+    enum = {"SCHEDULE_SERIAL": 0, "SCHEDULE_OVERLAP": 1, "SCHEDULE_PINGPONG": 2}
+    rows = re.findall(r"\{(\d+), (\d+), (\d+), (\d+), (\d+), \{(SCHEDULE_\w+), (\d), (\d), (\d)\}", text)
+    assert rows
+    got = lookup(tmp_path, CSRC, [r[:5] for r in rows])
+    for r, g in zip(rows, got):
+        assert g == (enum[r[5]], int(r[6]), int(r[7]), int(r[8]), 1), (r, g)
+
+
+def test_emit_and_nearest_shape(tmp_path):
+    """A search record becomes a table; a shape takes the variant of the nearest measured shape."""
+    rec = {"results": [
+        {"workload": "small", "B": 1, "Sq": 512, "Sk": 512, "Hq": 32, "Hkv": 8, "best_tflops": 90.0,
+         "best": {"schedule": "overlap", "ring": 2, "xcd": 0, "lpt": 1}},
+        {"workload": "big", "B": 64, "Sq": 8192, "Sk": 8192, "Hq": 64, "Hkv": 8, "best_tflops": 990.0,
+         "best": {"schedule": "pingpong", "ring": 4, "xcd": 1, "lpt": 0}},
+    ]}
+    js = tmp_path / "search.json"
+    js.write_text(json.dumps(rec))
+    tdir = tmp_path / "tbl"
+    tdir.mkdir()
+    tune.emit(str(js), table=str(tdir / "tuned_table.h"), profile=None)
+    got = lookup(tmp_path, tdir, [(1, 600, 600, 32, 8), (48, 8192, 8192, 64, 8), (1, 2048, 8192, 64, 8)])
+    assert got[0] == (1, 2, 0, 1, 1)
+    assert got[1] == (2, 4, 1, 0, 1)
+    assert got[2] in ((1, 2, 0, 1, 1), (2, 4, 1, 0, 1))
