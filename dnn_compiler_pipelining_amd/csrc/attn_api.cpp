@@ -58,7 +58,7 @@ int validate(const void* q, const void* k, const void* v, const void* o, const f
   if (causal != 0 && causal != 1) return ATTN_ERR_SHAPE;
   if (causal && Sq > Sk) return ATTN_ERR_SHAPE;
   if (!std::isfinite(scale)) return ATTN_ERR_SHAPE;
-  if (D != 128) return ATTN_ERR_UNSUPPORTED;
+  if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
   if ((int64_t)Hkv * D * 2 * 64 > 0xffffffffLL) return ATTN_ERR_UNSUPPORTED;  // 64 K/V rows must span < 4 GiB
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned16(lse)))
     return ATTN_ERR_ALIGN;
@@ -103,7 +103,8 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
   p.neg = scale < 0.f ? 1 : 0;
   p.cs = std::fabs(scale) * 1.44269504088896340736f;
   const libattn::Variant var = choose_variant(B, Sq, Sk, Hq, Hkv);
-  p.schedule = var.schedule;
+  p.hd = D;
+  p.schedule = D == 128 ? var.schedule : libattn::SCHEDULE_SERIAL;  // HD 64: serial schedule only
   p.ring = var.ring;
   p.xcd = var.xcd;
   p.lpt = var.lpt;
@@ -128,7 +129,7 @@ const char* attn_status_string(int status) {
     case ATTN_OK: return "ok";
     case ATTN_ERR_NULL: return "a required pointer is NULL";
     case ATTN_ERR_SHAPE: return "invalid shape, causal flag or scale";
-    case ATTN_ERR_UNSUPPORTED: return "unsupported head dimension (D must be 128)";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported head dimension (D must be 64 or 128) or K/V heads too wide";
     case ATTN_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case ATTN_ERR_HIP: return "HIP launch error";
     case ATTN_ERR_OVERLAP: return "output overlaps an input";

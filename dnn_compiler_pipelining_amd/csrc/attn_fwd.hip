@@ -56,7 +56,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // pass its register arrays through scratch memory.
 #define INL __attribute__((always_inline))
 
-constexpr int HD = 128;          // head dim
 constexpr int BM = 128;          // query rows per wave group
 constexpr int BN = 64;           // keys per KV tile
 constexpr int NTHREADS = 512;    // 8 wavefronts
@@ -68,30 +67,46 @@ constexpr float LN2 = 0.693147180559945309f;
 // final O / l and LSE = m + log2(l) are exact for any m.
 constexpr float TAU = 8.0f;
 
-// LDS layouts (bytes).  A tile slot is a run of 1 KiB DMA instructions.
-//  K: 64 key rows of 256 + 16 B.  The 8 lanes of a ds_read_b128 pass (8
-//    consecutive keys, same 16-byte column) fall 16 B apart in bank space and
-//    a 16-lane pass covers all 64 banks once; every K fragment read is a
-//    compile-time offset from one per-lane base.  17 DMA instructions per
-//    tile (one 16-byte lane slot per row lands in the padding).
-//  V: 64 key rows of 256 B whose 16-byte chunks are XOR-swizzled by
-//    4*(row & 3).  A ds_read_b64_tr_b16 group reads 4 consecutive rows x 32 B;
-//    the swizzle puts the 4 rows of two groups (4 rows x 64 B) on all 64 banks
-//    once.  Across the four 32-wide d blocks the per-lane address changes by
-//    an XOR with 64*db.  16 DMA instructions per tile.
-constexpr int K_ROWB = 2 * HD + 16;
-constexpr int K_TILEB = BN * K_ROWB;   // 17408
-constexpr int V_TILEB = BN * 2 * HD;   // 16384
-constexpr int K_DMA = K_TILEB / 1024;  // 17
-constexpr int V_DMA = V_TILEB / 1024;  // 16
-constexpr int K_DMA_PER_WAVE = (K_DMA + 7) / 8;  // 3: wave w issues K instructions w, w+8, w+16
-static_assert(K_TILEB % 1024 == 0 && V_TILEB % 1024 == 0, "tile slots are whole DMA instructions");
-static_assert(V_DMA == 16, "wave w issues V instructions w and w+8");
+// LDS layouts (bytes), per head dimension HD (64 or 128).  A tile slot is a
+// run of 1 KiB DMA instructions.
+//  K: 64 key rows of 2*HD + 16 B.  Consecutive keys fall 68 (HD 128) or 36
+//    (HD 64) banks apart, so the 16 keys of a ds_read_b128 pass at one
+//    16-byte column cover all 64 banks once; every K fragment read is a
+//    compile-time offset from one per-lane base.  One 16-byte lane slot per
+//    row lands in the padding.
+//  V: 64 key rows of 2*HD B whose 16-byte chunks are XOR-swizzled: by
+//    4*(row & 3) for HD 128, by 4*((row >> 1) & 1) for HD 64.  A
+//    ds_read_b64_tr_b16 group reads 4 consecutive rows x 32 B; with the
+//    swizzle the 4 rows of the two groups of a half-wave (4 rows x 64 B) hit
+//    all 64 banks once.  Across the 32-wide d blocks the per-lane address
+//    changes by an XOR with 64*db.
+template <int kHD>
+struct Geo {
+  static_assert(kHD == 64 || kHD == 128, "head dimension");
+  static constexpr int HD = kHD;
+  static constexpr int KC = kHD / 8;                 // 16-byte chunks per K/V row
+  static constexpr int K_ROWB = 2 * kHD + 16;
+  static constexpr int K_TILEB = BN * K_ROWB;        // 17408 | 9216
+  static constexpr int K_DMA = K_TILEB / 1024;       // 17 | 9
+  static constexpr int K_DMA_PER_WAVE = (K_DMA + 7) / 8;  // wave w issues K instructions w, w+8, ...
+  static constexpr int V_ROWB = 2 * kHD;
+  static constexpr int V_TILEB = BN * V_ROWB;        // 16384 | 8192
+  static constexpr int V_DMA = V_TILEB / 1024;       // 16 | 8
+  static constexpr int V_DMA_PER_WAVE = V_DMA / 8;   // wave w issues V instructions w, w+8, ...
+  static constexpr int V_ROWS_PER_DMA = 1024 / V_ROWB;
+  static constexpr int NKK = kHD / 16;               // 16-wide d steps of QK^T
+  static constexpr int NDB = kHD / 32;               // 32-wide d blocks of O^T
+  static_assert(K_TILEB % 1024 == 0 && V_TILEB % 1024 == 0, "tile slots are whole DMA instructions");
+  static_assert(V_DMA % 8 == 0, "every wave issues the same number of V instructions");
+  // physical 16-byte chunk of logical chunk c in V row r is c ^ vswz(r)
+  __host__ __device__ static constexpr int vswz(int r) { return kHD == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+};
 // K tiles rotate through three slots, V tiles through two: K_t stays in LDS
 // for the whole iteration after its QK^T, so a softmax that has to be redone
 // can recompute S^T from it.
 constexpr int K_SLOTS = 3, V_SLOTS = 2;
-static_assert(K_SLOTS * K_TILEB + V_SLOTS * V_TILEB <= 160 * 1024, "the K and V rings fit the 160 KiB LDS");
+static_assert(K_SLOTS * Geo<128>::K_TILEB + V_SLOTS * Geo<128>::V_TILEB <= 160 * 1024,
+              "the K and V rings fit the 160 KiB LDS");
 
 __device__ __forceinline__ float pair_max(float x) {
   // lanes l and l^32 hold the same query: combine their partial results
@@ -139,14 +154,15 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-// Steps of an mma block.  A QK step (kk, x = sb) adds K[32sb.., 16kk..] x
+// Steps of an mma block, for NKK = HD/16 k steps of QK^T and NDB = HD/32
+// blocks of O^T.  A QK step (kk, x = sb) adds K[32sb.., 16kk..] x
 // Q^T[16kk.., :] into S^T block sb; a PV step (kk, x = db) adds
 // V^T[32db.., 16kk..] x P^T[16kk.., :] into O^T block db.
 //   mode 0: PV and QK steps alternate, so consecutive MFMAs of one
 //           accumulator are >= 4 steps apart: per group g the order is
 //           PV(g,0) QK(2g,0) PV(g,1) QK(2g,1) PV(g,2) QK(2g+1,0) PV(g,3)
-//           QK(2g+1,1)
-//   mode 1: PV only, k-major over the four O^T blocks
+//           QK(2g+1,1)  (HD 128 only)
+//   mode 1: PV only, k-major over the O^T blocks
 //   mode 2: QK only, S^T block 0 first (so it is complete half-way)
 //   mode 3: the QK steps of mode 2, then the PV steps of mode 1
 // Each accumulator sees its k steps in increasing order in every mode, so all
@@ -155,20 +171,28 @@ struct Step {
   bool pv;
   int kk, x;
 };
-__host__ __device__ constexpr Step step_of(int mode, int i) {
-  return mode == 1   ? Step{true, i >> 2, i & 3}
-         : mode == 2 ? Step{false, i & 7, i >> 3}
-         : mode == 3 ? (i < 16 ? Step{false, i & 7, i >> 3} : Step{true, (i - 16) >> 2, (i - 16) & 3})
+__host__ __device__ constexpr Step step_of(int mode, int i, int nkk, int ndb) {
+  return mode == 1   ? Step{true, i / ndb, i % ndb}
+         : mode == 2 ? Step{false, i % nkk, i / nkk}
+         : mode == 3 ? (i < 2 * nkk ? Step{false, i % nkk, i / nkk} : Step{true, (i - 2 * nkk) / ndb, (i - 2 * nkk) % ndb})
          : ((i & 7) & 1) == 0 ? Step{true, i >> 3, (i & 7) >> 1}
                               : Step{false, 2 * (i >> 3) + ((i & 7) >> 2), ((i & 7) >> 1) & 1};
 }
-constexpr int steps_of(int mode) { return (mode == 0 || mode == 3) ? 32 : 16; }
-constexpr int reads_of(int mode, int i) { return step_of(mode, i).pv ? 2 : 1; }  // LDS reads per fragment
+constexpr int steps_of(int mode, int nkk, int ndb) {
+  return mode == 1 ? 4 * ndb : mode == 2 ? 2 * nkk : 2 * nkk + 4 * ndb;
+}
+constexpr int reads_of(int mode, int i, int nkk, int ndb) { return step_of(mode, i, nkk, ndb).pv ? 2 : 1; }
 
 // kSched: tile schedule; kRing: depth of the fragment prefetch ring of the mma
-// steps (how many steps ahead the LDS reads run).
-template <int kSched, int kRing>
+// steps (how many steps ahead the LDS reads run); kHD: head dimension.  The
+// overlap and ping-pong schedules are written for HD 128.
+template <int kSched, int kRing, int kHD>
 __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(Params p) {
+  using G = Geo<kHD>;
+  static_assert(kHD == 128 || kSched == SCHEDULE_SERIAL, "HD 64 runs the serial schedule");
+  constexpr int HD = G::HD, NKK = G::NKK, NDB = G::NDB;
+  constexpr int K_ROWB = G::K_ROWB, K_TILEB = G::K_TILEB, K_DMA = G::K_DMA, K_DMA_PER_WAVE = G::K_DMA_PER_WAVE;
+  constexpr int V_ROWB = G::V_ROWB, V_TILEB = G::V_TILEB;
   __shared__ __attribute__((aligned(1024))) char k_smem[K_SLOTS * K_TILEB];
   __shared__ __attribute__((aligned(1024))) char v_smem[V_SLOTS * V_TILEB];
   LDS char* const k_lds = (LDS char*)k_smem;
@@ -219,14 +243,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(Params p) {
   const _Float16* vb_ = p.v + (int64_t)b * p.kv_bstride + (int64_t)c * HD;
 
   // ---- Q^T fragments (B operand of S^T = K Q^T), resident for the whole loop
-  f16x8 qf[8];
+  f16x8 qf[NKK];
   {
     const int qrow = qw + n;
     const bool ok = active && qrow < Sq;
     const uint32_t flip = p.neg ? 0x80008000u : 0u;
     const _Float16* src = qb + (int64_t)qrow * p.q_sstride + 8 * hh;
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
+    for (int kk = 0; kk < NKK; ++kk) {
       u32x4 u = {0, 0, 0, 0};
       if (ok) u = *reinterpret_cast<const u32x4*>(src + 16 * kk);
       u ^= flip;
@@ -250,10 +274,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(Params p) {
     const int o = 64 * (wave + 8 * u) + lane;  // 16-byte lane slot inside the tile
     k_row[u] = o / (K_ROWB / 16);
     const int cb = o - k_row[u] * (K_ROWB / 16);
-    k_col[u] = 16u * (uint32_t)(cb < 16 ? cb : 15);  // padding slot: any in-bounds chunk of the row
+    k_col[u] = 16u * (uint32_t)(cb < G::KC ? cb : G::KC - 1);  // padding slot: any in-bounds chunk of the row
   }
-  const int v_rowl = lane >> 4;                                    // + 4 * instruction
-  const uint32_t v_col = 16u * (uint32_t)((lane & 15) ^ (v_rowl << 2));  // chunk stored at slot lane & 15
+  const int v_rowl = lane / G::KC;  // row inside the instruction's rows (V_ROWS_PER_DMA * i + v_rowl)
+  // chunk stored at slot lane % KC; the swizzle depends on row bits the
+  // instruction base (a multiple of V_ROWS_PER_DMA >= 4) does not touch
+  const uint32_t v_col = 16u * (uint32_t)((lane % G::KC) ^ G::vswz(v_rowl));
   auto stage = [&](int tk, int tv) INL {  // issue this wave's DMA for K tile tk and V tile tv
     tk = __builtin_amdgcn_readfirstlane(tk);
     tv = __builtin_amdgcn_readfirstlane(tv);
@@ -273,9 +299,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(Params p) {
       const char* base = (const char*)vb_ + (int64_t)tv * BN * row_bytes;
       const bool full = (tv + 1) * BN <= Sk;
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int u = 0; u < G::V_DMA_PER_WAVE; ++u) {
         const int i = wave_s + 8 * u;
-        const int row0 = 4 * i + v_rowl;
+        const int row0 = G::V_ROWS_PER_DMA * i + v_rowl;
         const int row = full ? row0 : min(row0, Sk - 1 - tv * BN);
         dma16(base, (uint32_t)row * row_bytes + v_col, v_lds_base + (tv & 1) * V_TILEB + 1024 * i);
       }
@@ -284,19 +310,19 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(Params p) {
 
   // per-lane fragment bases (bytes); everything else is a compile-time offset
   const int k_frag = n * K_ROWB + 16 * hh;  // A operand of QK^T: key row n, d column 8*hh
-  int v_frag[4];                            // transpose reads of V, one base per 32-wide d block
+  int v_frag[NDB];                          // transpose reads of V, one base per 32-wide d block
   {
     const int vg = lane >> 4, vsl = lane & 15;
     const int r0 = 4 * (vg >> 1) + (vsl >> 2);
     const int c0 = 2 * (vg & 1) + ((vsl & 3) >> 1);
-    const int f0 = r0 * 2 * HD + ((c0 ^ ((r0 & 3) << 2)) << 4) + ((vsl & 1) << 3);
+    const int f0 = r0 * V_ROWB + ((c0 ^ G::vswz(r0)) << 4) + ((vsl & 1) << 3);
 #pragma unroll
-    for (int db = 0; db < 4; ++db) v_frag[db] = f0 ^ (64 * db);
+    for (int db = 0; db < NDB; ++db) v_frag[db] = f0 ^ (64 * db);
   }
 
-  f32x16 o_acc[4];
+  f32x16 o_acc[NDB];
 #pragma unroll
-  for (int db = 0; db < 4; ++db) o_acc[db] = f32x16{};
+  for (int db = 0; db < NDB; ++db) o_acc[db] = f32x16{};
   float m_run = M_INIT;  // running max (log2 units) of the scores of query n
   float l_run = 0.f;     // running sum of 2^(score - m_run), from the fp16 P
   const float cs = p.cs;
@@ -313,9 +339,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(Params p) {
     return *(const LDS f16x8*)(k_lds + (j % K_SLOTS) * K_TILEB + k_frag + 32 * sb * K_ROWB + 32 * kk);
   };
   auto frag_pv = [&](int j, int kk, int db) INL -> f16x8 {
-    const LDS char* a = v_lds + (j & 1) * V_TILEB + v_frag[db] + 16 * kk * 2 * HD;
+    const LDS char* a = v_lds + (j & 1) * V_TILEB + v_frag[db] + 16 * kk * V_ROWB;
     const f16x4 h1 = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS i16x4*)a));
-    const f16x4 h2 = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS i16x4*)(a + 8 * 2 * HD)));
+    const f16x4 h2 = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS i16x4*)(a + 8 * V_ROWB)));
     return f16x8{h1[0], h1[1], h1[2], h1[3], h2[0], h2[1], h2[2], h2[3]};
   };
 
@@ -446,7 +472,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(Params p) {
   auto rescale_o = [&](const Rescale& rz) INL {
     if (__builtin_expect(rz.any, 0)) {  // rare after a row's first tiles
 #pragma unroll
-      for (int db = 0; db < 4; ++db) o_acc[db] *= rz.alpha;
+      for (int db = 0; db < NDB; ++db) o_acc[db] *= rz.alpha;
     }
   };
 
@@ -461,10 +487,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(Params p) {
   struct NoSoftmax {};
   auto block = [&](auto mode_c, int jq, f32x16 (&sd)[2], int jv, f16x8 (&ps)[4], auto sm) INL {
     constexpr int mode = decltype(mode_c)::value;
-    constexpr int nsteps = steps_of(mode);
+    constexpr int nsteps = steps_of(mode, NKK, NDB);
     constexpr bool kSoftmax = !std::is_same_v<decltype(sm), NoSoftmax>;
     auto load = [&](auto ic) INL -> f16x8 {
-      constexpr Step st = step_of(mode, decltype(ic)::value);
+      constexpr Step st = step_of(mode, decltype(ic)::value, NKK, NDB);
       if constexpr (st.pv) return frag_pv(jv, st.kk, st.x);
       else return frag_qk(jq, st.kk, st.x);
     };
@@ -472,7 +498,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(Params p) {
     static_for<kRing>([&](auto ic) INL { fr[decltype(ic)::value] = load(ic); });
     auto step = [&](auto ic) INL {
       constexpr int i = decltype(ic)::value;
-      constexpr Step st = step_of(mode, i);
+      constexpr Step st = step_of(mode, i, NKK, NDB);
       const f16x8 a = fr[i % kRing];
       if constexpr (i + kRing < nsteps) fr[i % kRing] = load(std::integral_constant<int, i + kRing>{});
       if constexpr (st.pv)
@@ -485,12 +511,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(Params p) {
     if constexpr (!kSoftmax) {
       static_for<nsteps>(step);
       static_for<kRing>([&](auto ic) INL {
-        __builtin_amdgcn_sched_group_barrier(0x100, reads_of(mode, decltype(ic)::value), 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, reads_of(mode, decltype(ic)::value, NKK, NDB), 0);
       });
       static_for<nsteps>([&](auto ic) INL {
         constexpr int i = decltype(ic)::value;
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if constexpr (i + kRing < nsteps) __builtin_amdgcn_sched_group_barrier(0x100, reads_of(mode, i + kRing), 0);
+        if constexpr (i + kRing < nsteps)
+          __builtin_amdgcn_sched_group_barrier(0x100, reads_of(mode, i + kRing, NKK, NDB), 0);
       });
     } else {
       static_for<nsteps>([&](auto ic) INL {
@@ -609,7 +636,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(Params p) {
       // max parts of tile j+1 read S^T block 0 (chains 0, 1) from MFMA 10 on
       // and block 1 (chains 2, 3) from MFMA 18 on (mode 3; with QK^T alone
       // the block-1 chains, X8, X9 and D follow the block).
-      constexpr int nsteps = kQK ? steps_of(kPV ? 3 : 2) : steps_of(1);
+      constexpr int nsteps = kQK ? steps_of(kPV ? 3 : 2, NKK, NDB) : steps_of(1, NKK, NDB);
       auto part_x = [&](auto kc) INL { sm_x(kc, sn, mask_x, nx); };
       auto x_at = [&](auto ic) INL {
         constexpr int i = decltype(ic)::value;
@@ -714,7 +741,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(Params p) {
       const float inv = 1.0f / l_run;
       _Float16* dst = p.o + (int64_t)b * p.q_bstride + (int64_t)qrow * p.q_sstride + (int64_t)h * HD;
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           f16x4 hv;
@@ -737,18 +764,23 @@ hipError_t launch_attn_fwd(const Params& p, hipStream_t stream) {
   const int64_t nb = grid_blocks(p);
   if (nb <= 0) return hipErrorInvalidValue;
   const dim3 grid((unsigned)nb), block(NTHREADS);
-#define LIBATTN_LAUNCH(S, R) hipLaunchKernelGGL((attn_fwd_kernel<S, R>), grid, block, 0, stream, p)
+#define LIBATTN_LAUNCH(S, R, H) hipLaunchKernelGGL((attn_fwd_kernel<S, R, H>), grid, block, 0, stream, p)
   if (p.ring != 2 && p.ring != 4) return hipErrorInvalidValue;
   const bool r2 = p.ring == 2;
-  if (p.schedule == SCHEDULE_OVERLAP) {
-    if (r2) LIBATTN_LAUNCH(SCHEDULE_OVERLAP, 2);
-    else LIBATTN_LAUNCH(SCHEDULE_OVERLAP, 4);
+  if (p.hd == 64) {  // serial schedule only
+    if (r2) LIBATTN_LAUNCH(SCHEDULE_SERIAL, 2, 64);
+    else LIBATTN_LAUNCH(SCHEDULE_SERIAL, 4, 64);
+  } else if (p.hd != 128) {
+    return hipErrorInvalidValue;
+  } else if (p.schedule == SCHEDULE_OVERLAP) {
+    if (r2) LIBATTN_LAUNCH(SCHEDULE_OVERLAP, 2, 128);
+    else LIBATTN_LAUNCH(SCHEDULE_OVERLAP, 4, 128);
   } else if (p.schedule == SCHEDULE_PINGPONG) {
-    if (r2) LIBATTN_LAUNCH(SCHEDULE_PINGPONG, 2);
-    else LIBATTN_LAUNCH(SCHEDULE_PINGPONG, 4);
+    if (r2) LIBATTN_LAUNCH(SCHEDULE_PINGPONG, 2, 128);
+    else LIBATTN_LAUNCH(SCHEDULE_PINGPONG, 4, 128);
   } else {
-    if (r2) LIBATTN_LAUNCH(SCHEDULE_SERIAL, 2);
-    else LIBATTN_LAUNCH(SCHEDULE_SERIAL, 4);
+    if (r2) LIBATTN_LAUNCH(SCHEDULE_SERIAL, 2, 128);
+    else LIBATTN_LAUNCH(SCHEDULE_SERIAL, 4, 128);
   }
 #undef LIBATTN_LAUNCH
   return hipGetLastError();

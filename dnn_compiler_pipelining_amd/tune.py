@@ -41,12 +41,12 @@ MAX_LDS = 160 * 1024
 
 
 def kernel_resources(asm_path: str):
-    """{(schedule, ring): {vgpr, agpr, vgpr_spill, scratch, lds}} from the AMDGPU metadata of a device asm file."""
+    """{(schedule, ring, hd): {vgpr, agpr, vgpr_spill, scratch, lds}} from the AMDGPU metadata of a device asm file."""
     text = open(asm_path).read()
     meta = text[text.index("amdhsa.kernels:"):]
     out = {}
     for block in re.split(r"\n  - ", meta)[1:]:
-        m = re.search(r"\.name:\s+\S*attn_fwd_kernelILi(\d)ELi(\d)E", block)
+        m = re.search(r"\.name:\s+\S*attn_fwd_kernelILi(\d)ELi(\d)ELi(\d+)E", block)
         if not m:
             continue
 
@@ -54,7 +54,7 @@ def kernel_resources(asm_path: str):
             mm = re.search(r"\." + key + r":\s+(\d+)", block)
             return int(mm.group(1)) if mm else 0
 
-        out[(SCHEDULES[int(m.group(1))], int(m.group(2)))] = dict(
+        out[(SCHEDULES[int(m.group(1))], int(m.group(2)), int(m.group(3)))] = dict(
             vgpr=num("vgpr_count"), agpr=num("agpr_count"), vgpr_spill=num("vgpr_spill_count"),
             scratch=num("private_segment_fixed_size"), lds=num("group_segment_fixed_size"))
     return out
@@ -72,7 +72,7 @@ def check_valid(res: dict) -> tuple[bool, str]:
 
 
 def valid_variants(asm_path: str | None = None):
-    """{(schedule, ring): (valid, reason, resources)} for the current sources."""
+    """{(schedule, ring, hd): (valid, reason, resources)} for the current sources."""
     from dnn_compiler_pipelining_amd import build
 
     if asm_path is None:
@@ -142,7 +142,7 @@ def search_workload(w, valid, log=print):
                 if val == best[field]:
                     continue
                 cand = dict(best, **{field: val})
-                if not valid.get((cand["schedule"], cand["ring"]), (False,))[0]:
+                if not valid.get((cand["schedule"], cand["ring"], w.D), (False,))[0]:
                     continue
                 r = rate(cand)
                 if r > best_rate * 1.01:
@@ -161,9 +161,9 @@ def search(out_dir: str, names=None):
     from dnn_compiler_pipelining_amd import inputs
 
     valid = valid_variants()
-    for (s, r), (ok, why, _) in sorted(valid.items()):
-        print("variant %-9s ring %d: %s" % (s, r, why), flush=True)
-    rec = {"valid": {"%s/%d" % k: dict(ok=v[0], reason=v[1], **v[2]) for k, v in valid.items()},
+    for (s, r, hd), (ok, why, _) in sorted(valid.items()):
+        print("variant %-9s ring %d hd %d: %s" % (s, r, hd, why), flush=True)
+    rec = {"valid": {"%s/%d/%d" % k: dict(ok=v[0], reason=v[1], **v[2]) for k, v in valid.items()},
            "rule": "greedy coordinate search from %s; a change is kept when > 1%% faster" % json.dumps(SEED),
            "results": []}
     for w in inputs.WORKLOADS:
@@ -214,8 +214,8 @@ def main(argv=None):
     if ROOT not in sys.path:
         sys.path.insert(0, ROOT)
     if args.check:
-        for (s, r), (ok, why, res) in sorted(valid_variants().items()):
-            print("%-9s ring %d: %-5s %s  %s" % (s, r, ok, why, res))
+        for (s, r, hd), (ok, why, res) in sorted(valid_variants().items()):
+            print("%-9s ring %d hd %3d: %-5s %s  %s" % (s, r, hd, ok, why, res))
     if args.search:
         search(args.search, args.workload)
     if args.emit:

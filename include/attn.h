@@ -23,10 +23,10 @@
  * to nearest even from fp32.  Internal offsets are 64-bit, so tensors larger
  * than 4 GiB are supported.
  *
- * Scalars: B, S, Hq, Hkv >= 1; S <= 2^30; Hq % Hkv == 0; D == 128 (other
- * head sizes return ATTN_ERR_UNSUPPORTED, and so does Hkv * D * 2 * 64 >=
- * 2^32, i.e. a 64-row K/V tile spanning 4 GiB or more); causal is 0 or 1;
- * scale is any finite float.
+ * Scalars: B, S, Hq, Hkv >= 1; S <= 2^30; Hq % Hkv == 0; D is 64 or 128
+ * (other head sizes return ATTN_ERR_UNSUPPORTED, and so does
+ * Hkv * D * 2 * 64 >= 2^32, i.e. a 64-row K/V tile spanning 4 GiB or more);
+ * causal is 0 or 1; scale is any finite float.
  *
  * attn_fwd_ex takes different query and key lengths (chunked prefill): q and
  * o are [B][Sq][Hq][D], k and v [B][Sk][Hkv][D], lse [B][Hq][Sq].  With
@@ -61,7 +61,7 @@ enum {
   ATTN_OK = 0,
   ATTN_ERR_NULL = 1,        /* a required pointer is NULL */
   ATTN_ERR_SHAPE = 2,       /* a size < 1 or > 2^30, Hq % Hkv != 0, causal not 0/1, causal with Sq > Sk, scale not finite */
-  ATTN_ERR_UNSUPPORTED = 3, /* D other than 128 */
+  ATTN_ERR_UNSUPPORTED = 3, /* D other than 64 or 128, or Hkv * D * 2 * 64 >= 2^32 */
   ATTN_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
   ATTN_ERR_HIP = 5,         /* the HIP runtime reported an error at launch */
   ATTN_ERR_OVERLAP = 6      /* o overlaps q, k, v or lse */

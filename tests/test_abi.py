@@ -68,7 +68,7 @@ def test_bad_shapes(lib, kw):
     assert call(**kw) == L.ATTN_ERR_SHAPE
 
 
-@pytest.mark.parametrize("D", [64, 256, 127, 0 + 1])
+@pytest.mark.parametrize("D", [96, 256, 127, 32, 1])
 def test_unsupported_head_dim(lib, D):
     assert call(D=D) == L.ATTN_ERR_UNSUPPORTED
 
@@ -89,8 +89,8 @@ def test_overlap(lib):
 def test_validation_order(lib):
     # a null pointer is reported before a bad shape, a bad shape before an unsupported D
     assert call(q=0, B=0) == L.ATTN_ERR_NULL
-    assert call(B=0, D=64) == L.ATTN_ERR_SHAPE
-    assert call(D=64, q=QP + 8) == L.ATTN_ERR_UNSUPPORTED
+    assert call(B=0, D=96) == L.ATTN_ERR_SHAPE
+    assert call(D=96, q=QP + 8) == L.ATTN_ERR_UNSUPPORTED
 
 
 def test_stream_entry_point_validates_too(lib):
@@ -123,9 +123,9 @@ def test_ex_bad_shapes(lib, kw):
 
 
 def test_ex_limits_and_order(lib):
-    assert call_ex(D=64) == L.ATTN_ERR_UNSUPPORTED
+    assert call_ex(D=256) == L.ATTN_ERR_UNSUPPORTED
     # 64 rows of K/V must span less than 4 GiB: Hkv * 128 * 2 * 64 >= 2^32 is refused
     assert call_ex(Hq=262144, Hkv=262144) == L.ATTN_ERR_UNSUPPORTED
     assert call_ex(q=0, Sq=65) == L.ATTN_ERR_NULL
-    assert call_ex(Sq=65, D=64) == L.ATTN_ERR_SHAPE
+    assert call_ex(Sq=65, D=96) == L.ATTN_ERR_SHAPE
     assert call_ex(o=KP + 4096, Sq=16, Sk=64) == L.ATTN_ERR_OVERLAP

@@ -163,7 +163,7 @@ def test_gpu_validation_errors_launch_nothing():
     q, k, v = cpu_qkv(1, 64, 8, 2, seed=82)
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
     o = torch.full_like(qd, float("nan"))
-    st = binding.attn_fwd(qd, kd, vd, o, None, 1, 64, 8, 2, 64, 1, SC)
+    st = binding.attn_fwd(qd, kd, vd, o, None, 1, 64, 8, 2, 96, 1, SC)
     assert st == binding.ATTN_ERR_UNSUPPORTED
     torch.cuda.synchronize()
     assert bool(torch.isnan(o).all().item())

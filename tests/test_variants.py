@@ -13,7 +13,8 @@ CSRC = os.path.join(tune.PKG, "csrc")
 
 def test_every_compiled_variant_is_valid():
     vs = tune.valid_variants()
-    assert set(vs) == {(s, r) for s in tune.SCHEDULES for r in tune.RINGS}
+    assert set(vs) == ({(s, r, 128) for s in tune.SCHEDULES for r in tune.RINGS} |
+                       {("serial", r, 64) for r in tune.RINGS})
     for key, (ok, why, res) in vs.items():
         assert ok, (key, why, res)
         assert res["lds"] > 0 and res["vgpr"] > 0
