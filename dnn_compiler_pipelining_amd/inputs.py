@@ -1,8 +1,8 @@
-"""Seeded synthetic inputs for the attention forward pass.
+"""Seeded synthetic inputs for the attention forward pass and the fp16 GEMM.
 
-This module holds no attention arithmetic.  It is the only code shared by the
-GPU path's tests/bench and the oracle's callers: both sides read the exact
-fp16 values produced here.
+This module holds no attention or GEMM arithmetic.  It is the only code shared
+by the GPU path's tests/bench and the oracle's callers: both sides read the
+exact fp16 values produced here.
 
 Workloads: the FlashAttention evaluation of PipeThreader runs LLaMA3-8B and
 LLaMA3-70B head shapes at sequence lengths 512..8k and batch sizes 1 and 64
@@ -114,3 +114,78 @@ def make_batch_cpu(w: Workload, b: int):
     """(q, k, v) of batch entry b on the CPU: [S,Hq,D], [S,Hkv,D], [S,Hkv,D] fp16."""
     return (make_slice(w.S, w.Hq, w.D, w.seed, Q, b), make_slice(w.S, w.Hkv, w.D, w.seed, K, b),
             make_slice(w.S, w.Hkv, w.D, w.seed, V, b))
+
+
+# ---------------------------------------------------------------- GEMM inputs
+#
+# The fp16 GEMM runs the "8k MatMul" workload that PipeThreader compiles and
+# whose hardware-scheduled tensor-core utilisation it quotes (page "PipeThreader
+# ... (OSDI 2025)" summary, sections "问题与动机" and "实验与结果", citing the
+# paper's section 6.4 / Table 4): M = N = K = 8192.
+#
+# Recipe: matrix t in {A: 0, B: 1} is drawn by a CPU torch.Generator seeded
+# with base * 1_000_003 + t * 65_537 + 7_919.  dist "normal": torch.randn
+# float32 rounded to fp16.  dist "int": integers uniform in [-lim, lim]
+# (torch.randint), stored as fp16; with these every partial sum of a dot
+# product of length K <= 2^24 / lim^2 is an integer below 2^24, so fp32
+# accumulation is exact in any order.
+
+MAT_A, MAT_B = 0, 1
+B_KN, B_NK = 0, 1  # B stored [K, N] (C = A B) or [N, K] (C = A B^T, the linear-layer weight layout)
+
+
+@dataclass(frozen=True)
+class GemmWorkload:
+    name: str
+    M: int
+    N: int
+    K: int
+    b_layout: int
+    seed: int
+    dist: str = "normal"
+    lim: int = 0
+
+    @property
+    def flops(self) -> float:
+        """2 * M * N * K."""
+        return 2.0 * self.M * self.N * self.K
+
+    def b_shape(self):
+        return (self.K, self.N) if self.b_layout == B_KN else (self.N, self.K)
+
+    def describe(self) -> dict:
+        return {"workload": self.name, "M": self.M, "N": self.N, "K": self.K,
+                "b_layout": "B[K,N], C = A B" if self.b_layout == B_KN else "B[N,K], C = A B^T",
+                "layout": "row-major fp16 A[M,K], fp16 C[M,N], fp32 accumulation",
+                "dist": self.dist if self.dist == "normal" else "int[-%d,%d]" % (self.lim, self.lim),
+                "seed": self.seed}
+
+
+GEMM_WORKLOADS = [
+    GemmWorkload("gemm_8k_nn", 8192, 8192, 8192, B_KN, 11),
+    GemmWorkload("gemm_8k_nt", 8192, 8192, 8192, B_NK, 12),
+]
+GEMM_BY_NAME = {w.name: w for w in GEMM_WORKLOADS}
+
+
+def make_matrix(rows: int, cols: int, base: int, which: int, dist: str = "normal", lim: int = 0,
+                device="cpu") -> torch.Tensor:
+    """CPU-generated fp16 [rows, cols] matrix (see the recipe above), moved to `device`."""
+    g = torch.Generator(device="cpu").manual_seed(base * 1_000_003 + which * 65_537 + 7_919)
+    if dist == "normal":
+        x = torch.randn((rows, cols), generator=g, dtype=torch.float32).to(torch.float16)
+    elif dist == "int":
+        if lim < 1:
+            raise ValueError("dist 'int' needs lim >= 1")
+        x = torch.randint(-lim, lim + 1, (rows, cols), generator=g, dtype=torch.int32).to(torch.float16)
+    else:
+        raise ValueError("dist must be 'normal' or 'int'")
+    return x if device == "cpu" else x.to(device)
+
+
+def make_gemm_inputs(w: GemmWorkload, device="cpu"):
+    """(a, b) for a GEMM workload: a [M, K], b [K, N] or [N, K] by w.b_layout, fp16."""
+    a = make_matrix(w.M, w.K, w.seed, MAT_A, w.dist, w.lim, device)
+    br, bc = w.b_shape()
+    b = make_matrix(br, bc, w.seed, MAT_B, w.dist, w.lim, device)
+    return a, b
