@@ -1,10 +1,11 @@
 """Python binding of libattn: argument marshalling only.
 
 The functions carry the names of the C entry points in include/attn.h
-(attn_fwd, attn_fwd_stream, attn_status_string, attn_version) and forward to
-them through ctypes; every step of the computation runs in the HIP kernel.
-`forward()` is a convenience that allocates the outputs with torch and checks
-the tensors first.  There is no fallback: if libattn.so is missing or fails to
+(attn_fwd, attn_fwd_stream, attn_fwd_ex, attn_status_string, attn_version) and
+include/gemm.h (gemm_f16) and forward to them through ctypes; every step of
+the computation runs in the HIP kernels.  `forward()` and `matmul()` are
+conveniences that allocate the outputs with torch and check the tensors
+first.  There is no fallback: if libattn.so is missing or fails to
 load, every call raises.
 """
 from __future__ import annotations
@@ -25,7 +26,10 @@ ATTN_ERR_ALIGN = 4
 ATTN_ERR_HIP = 5
 ATTN_ERR_OVERLAP = 6
 
-EXPORTS = ("attn_fwd", "attn_fwd_stream", "attn_fwd_ex", "attn_status_string", "attn_version")
+EXPORTS = ("attn_fwd", "attn_fwd_stream", "attn_fwd_ex", "attn_status_string", "attn_version", "gemm_f16")
+
+GEMM_B_KN = 0  # B stored [K, N]: C = A B
+GEMM_B_NK = 1  # B stored [N, K]: C = A B^T
 
 _lock = threading.Lock()
 _lib = None
@@ -57,6 +61,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
             lib.attn_status_string.argtypes = [i]
             lib.attn_version.restype = i
             lib.attn_version.argtypes = []
+            lib.gemm_f16.restype = i
+            lib.gemm_f16.argtypes = [vp, vp, vp, i, i, i, i, vp]
             _lib = lib
         return _lib
 
@@ -89,6 +95,13 @@ def attn_fwd_ex(q, k, v, o, lse, B: int, Sq: int, Sk: int, Hq: int, Hkv: int, D:
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else (stream or 0)
     return load().attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Sq, Sk, Hq, Hkv, D, int(causal),
                               float(scale), handle)
+
+
+def gemm_f16(a, b, c, M: int, N: int, K: int, b_layout: int, stream) -> int:
+    """C gemm_f16: C[M,N] = A[M,K] B (b_layout 0, B [K,N]) or A B^T (b_layout 1, B [N,K]).  `stream` as for
+    attn_fwd_stream."""
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else (stream or 0)
+    return load().gemm_f16(_ptr(a), _ptr(b), _ptr(c), int(M), int(N), int(K), int(b_layout), handle)
 
 
 def attn_status_string(status: int) -> str:
@@ -139,3 +152,37 @@ def forward(q, k, v, causal: bool = True, scale: float | None = None, out=None, 
     if st != ATTN_OK:
         raise AttnError(st)
     return out, lse
+
+
+def matmul(a, b, b_layout: int = GEMM_B_KN, out=None, stream=None):
+    """C = A B (b_layout 0, b [K, N]) or A B^T (b_layout 1, b [N, K]) on fp16 torch tensors, fp32 accumulation.
+
+    a is [M, K]; all tensors contiguous float16 on one GPU.  Returns c [M, N] fp16.  Enqueues on `stream`
+    (default: torch's current stream) and does not synchronise.
+    """
+    import torch
+
+    for name, t in (("a", a), ("b", b)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.float16 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous float16 tensor on a GPU" % name)
+        if t.dim() != 2:
+            raise ValueError("%s must be 2-D" % name)
+    if b_layout not in (GEMM_B_KN, GEMM_B_NK):
+        raise ValueError("b_layout must be 0 ([K, N]) or 1 ([N, K])")
+    M, K = a.shape
+    Kb, N = b.shape if b_layout == GEMM_B_KN else (b.shape[1], b.shape[0])
+    if Kb != K:
+        raise ValueError("shapes do not chain: a %s, b %s (b_layout %d)" % (tuple(a.shape), tuple(b.shape), b_layout))
+    if a.device != b.device:
+        raise ValueError("a and b must be on the same device")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=a.device)
+    if out.dtype != torch.float16 or not out.is_contiguous() or tuple(out.shape) != (M, N):
+        raise ValueError("out must be a contiguous float16 [M, N] tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(a.device)
+    with torch.cuda.device(a.device):
+        st = gemm_f16(a, b, out, M, N, K, b_layout, stream)
+    if st != ATTN_OK:
+        raise AttnError(st)
+    return out

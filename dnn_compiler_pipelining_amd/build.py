@@ -11,7 +11,9 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libattn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = [os.path.join(CSRC, "attn_fwd.hip"), os.path.join(CSRC, "attn_api.cpp")]
+ATTN_SOURCES = [os.path.join(CSRC, "attn_fwd.hip"), os.path.join(CSRC, "attn_api.cpp")]
+GEMM_SOURCES = [os.path.join(CSRC, "gemm_fwd.hip"), os.path.join(CSRC, "gemm_api.cpp")]
+SOURCES = ATTN_SOURCES + GEMM_SOURCES
 
 # Packed fp32 VALU forms are switched off for all device code.
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -30,11 +32,12 @@ def build(out: str = LIB, extra_flags=()) -> str:
     return out
 
 
-def device_asm(out: str) -> str:
-    """Write the gfx950 assembly of the kernel (for register/LDS/scratch inspection)."""
+def device_asm(out: str, src: str | None = None) -> str:
+    """Write the gfx950 assembly of one kernel source (default: the attention kernel), for register, LDS and
+    scratch inspection."""
     cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-S", "--cuda-device-only",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-I" + INCLUDE, "-I" + CSRC,
-           SOURCES[0], "-o", out]
+           src or ATTN_SOURCES[0], "-o", out]
     subprocess.run(cmd, check=True, capture_output=True)
     return out
 

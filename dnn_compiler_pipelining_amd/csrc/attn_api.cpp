@@ -128,8 +128,10 @@ const char* attn_status_string(int status) {
   switch (status) {
     case ATTN_OK: return "ok";
     case ATTN_ERR_NULL: return "a required pointer is NULL";
-    case ATTN_ERR_SHAPE: return "invalid shape, causal flag or scale";
-    case ATTN_ERR_UNSUPPORTED: return "unsupported head dimension (D must be 64 or 128) or K/V heads too wide";
+    case ATTN_ERR_SHAPE: return "invalid shape, layout, causal flag or scale";
+    case ATTN_ERR_UNSUPPORTED:
+      return "unsupported size: attention needs D of 64 or 128 and K/V heads under 4 GiB per 64 rows, "
+             "the GEMM K and N multiples of 8";
     case ATTN_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case ATTN_ERR_HIP: return "HIP launch error";
     case ATTN_ERR_OVERLAP: return "output overlaps an input";

@@ -1,0 +1,269 @@
+// gemm_fwd.hip -- fp16 GEMM with fp32 accumulation for gfx950 (CDNA4):
+// C[M][N] = A[M][K] B, B stored [K][N] (C = A B) or [N][K] (C = A B^T).
+//
+// This is the load / mma pipeline of the attention kernel without its softmax
+// task: PipeThreader's MatMul workload (page "PipeThreader: Software-Defined
+// Pipelining ... (OSDI 2025)" summary, sections "问题与动机" and "实验与结果")
+// split into a load sTask (A and B tiles, global -> LDS by direct loads into a
+// two-slot ring: prologue / steady state / epilogue, page "AI编译器融合技术 --
+// 5. 并行性与分布式融合", section 5.4.2) and an mma sTask (v_mfma_f32_32x32x16_f16
+// with fragments conformed to the instruction's layout, same page, section
+// 5.2.2).
+//
+// One workgroup = 8 waves computes a 256 x 256 tile of C over 64-deep K
+// tiles.  Wave (wm, wn) = (w % 2, w / 2) owns rows 128 wm .. +128 and columns
+// 64 wn .. +64 of the tile: 4 x 2 accumulators of 32 x 32.  The MFMA computes
+// the transposed block, D[n][m] = sum_k B^T[n][k] A^T[k][m], so that each lane
+// holds one row m of C and runs of 4 consecutive columns n: the epilogue
+// writes 8-byte runs.
+//
+// LDS layouts (bytes; one slot of each ring is 32 KiB, both rings 128 KiB):
+//   A tile and B tile stored [N][K]: 256 rows of 64 k = 128 B.  Its 16-byte
+//     chunk c of row r sits at position c ^ ((r >> 1) & 7).  A 32 x 16
+//     fragment is one ds_read_b128 per lane (row l % 32, chunk 2kk + l / 32);
+//     each 16-lane pass of it touches rows r0..r0+15 at one chunk, which
+//     the swizzle spreads over all 64 banks.
+//   B tile stored [K][N]: 64 rows of 256 n = 512 B, chunk c of row r at
+//     c ^ (4 * (r & 3)).  A B^T fragment (n rows, k columns) is two
+//     ds_read_b64_tr_b16 of 4 k rows each; a half-wave of such a read covers
+//     4 rows x 64 B, which the swizzle spreads over all 64 banks.
+// The direct loads write 1 KiB per instruction in LDS order; each lane picks
+// the global 16 bytes that belong at its LDS position.  Rows and columns past
+// the end of A or B are loaded from the last valid ones (finite data that
+// only reaches discarded outputs); K positions past the end are zeroed in LDS
+// by the lane that loaded them, after its own load has landed.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gemm_kernel.h"
+#include "gfx950.h"
+
+namespace libattn {
+
+constexpr int GBM = 256, GBN = 256, GBK = 64;
+constexpr int GTHREADS = 512;
+constexpr int G_TILEB = 256 * GBK * 2;  // bytes of one A or B slot (32 KiB)
+constexpr int G_BAND = 8;               // output tile rows per raster band
+static_assert(4 * G_TILEB <= 160 * 1024, "two slots of A and B fit the LDS");
+
+template <int kBL>  // 0: B stored [K][N]; 1: B stored [N][K]
+__global__ __launch_bounds__(GTHREADS, 1) void gemm_kernel(GemmParams p) {
+  __shared__ __attribute__((aligned(1024))) char a_smem[2 * G_TILEB];
+  __shared__ __attribute__((aligned(1024))) char b_smem[2 * G_TILEB];
+  LDS char* const a_lds = (LDS char*)a_smem;
+  LDS char* const b_lds = (LDS char*)b_smem;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  const int wm = wave_s & 1, wn = wave_s >> 1;
+
+  // ---- workgroup -> output tile.  Workgroups are dealt round-robin to the 8
+  // XCDs; when the tile count allows, XCD x takes the x-th eighth of the
+  // raster, so the tiles that run together on one XCD are neighbours.  The
+  // raster walks bands of G_BAND tile rows column by column, so concurrent
+  // tiles share A row panels and B column panels in that XCD's L2.
+  const int T = p.ntm * p.ntn;
+  int t = blockIdx.x;
+  if ((T & 7) == 0) t = (t & 7) * (T >> 3) + (t >> 3);
+  const int band = t / (G_BAND * p.ntn);
+  const int tm0 = band * G_BAND;
+  const int gh = min(G_BAND, p.ntm - tm0);
+  const int local = t - tm0 * p.ntn;
+  const int tm = tm0 + local % gh, tn = local / gh;
+  const int m0 = tm * GBM, n0 = tn * GBN;
+  const int M = p.M, N = p.N, K = p.K;
+
+  // ---- per-lane direct-load maps.  Wave w issues instructions w + 8u
+  // (u = 0..3) of each 32-instruction tile.
+  //   [row][k] tiles (A, and B stored [N][K]): instruction i holds rows
+  //     8i .. 8i+7; lane l has row 8i + l/8 and LDS chunk l % 8, i.e. logical
+  //     chunk (l % 8) ^ ((row >> 1) & 7), the same for every u.
+  //   [k][n] tile (B stored [K][N]): instruction i holds k rows 2i, 2i+1;
+  //     lane l has k row 2i + l/32 and LDS chunk l % 32, i.e. logical chunk
+  //     (l % 32) ^ (4 * (row & 3)), the same for every u.
+  const uint32_t a_lds_base = (uint32_t)(uintptr_t)a_lds, b_lds_base = (uint32_t)(uintptr_t)b_lds;
+  const int rk_row0 = 8 * wave + (lane >> 3);  // + 64u
+  const int rk_chunk = (lane & 7) ^ ((4 * wave + (lane >> 4)) & 7);
+  const int kn_row0 = 2 * wave + (lane >> 5);  // + 16u
+  const int kn_chunk = (lane & 31) ^ (4 * ((2 * wave + (lane >> 5)) & 3));
+  const int kchunks = K >> 3;  // 16-byte chunks per row of A (and of B stored [N][K])
+
+  auto stage = [&](int kt) INL {  // this wave's loads of K tile kt into slot kt & 1
+    const int k0 = kt * GBK;
+    const uint32_t slot_off = (uint32_t)(kt & 1) * G_TILEB;
+    // A: rows past M read row M-1, chunks past K read the last chunk (zeroed later)
+    {
+      const char* base = (const char*)(p.a + (int64_t)m0 * K + k0);
+      const int c = min(rk_chunk, kchunks - 1 - (k0 >> 3));
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int row = min(rk_row0 + 64 * u, M - 1 - m0);
+        dma16(base, (uint32_t)row * (uint32_t)(2 * K) + 16u * c,
+              a_lds_base + slot_off + 1024u * (uint32_t)(wave_s + 8 * u));
+      }
+    }
+    if constexpr (kBL == 1) {
+      const char* base = (const char*)(p.b + (int64_t)n0 * K + k0);
+      const int c = min(rk_chunk, kchunks - 1 - (k0 >> 3));
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int row = min(rk_row0 + 64 * u, N - 1 - n0);
+        dma16(base, (uint32_t)row * (uint32_t)(2 * K) + 16u * c,
+              b_lds_base + slot_off + 1024u * (uint32_t)(wave_s + 8 * u));
+      }
+    } else {
+      const char* base = (const char*)(p.b + (int64_t)k0 * N + n0);
+      const int c = min(kn_chunk, (N >> 3) - 1 - (n0 >> 3));
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int row = min(kn_row0 + 16 * u, K - 1 - k0);
+        dma16(base, (uint32_t)row * (uint32_t)(2 * N) + 16u * c,
+              b_lds_base + slot_off + 1024u * (uint32_t)(wave_s + 8 * u));
+      }
+    }
+  };
+  // After this wave's loads of the last K tile have landed: zero the LDS
+  // positions it loaded that lie at k >= K.
+  auto zero_tail = [&](int kt) INL {
+    const int k0 = kt * GBK;
+    const uint32_t slot_off = (uint32_t)(kt & 1) * G_TILEB;
+    const u32x4 z = {0, 0, 0, 0};
+    if (rk_chunk >= kchunks - (k0 >> 3)) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        *(LDS u32x4*)(a_lds + slot_off + 1024 * (wave_s + 8 * u) + 16 * lane) = z;
+        if constexpr (kBL == 1) *(LDS u32x4*)(b_lds + slot_off + 1024 * (wave_s + 8 * u) + 16 * lane) = z;
+      }
+    }
+    if constexpr (kBL == 0) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (kn_row0 + 16 * u >= K - k0) *(LDS u32x4*)(b_lds + slot_off + 1024 * (wave_s + 8 * u) + 16 * lane) = z;
+    }
+  };
+
+  // ---- per-lane fragment offsets (bytes).  Row l % 32 of a 32-row block and
+  // logical chunk 2kk + l/32 of a [row][k] tile, for kk = 0..3:
+  int rk_frag[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+    rk_frag[kk] = (lane & 31) * 128 + 16 * ((2 * kk + (lane >> 5)) ^ ((lane >> 1) & 7));
+  // B stored [K][N]: lane (group g = l/16, s = l%16) of a transpose read
+  // addresses k row 8(g/2) + s/4 (+4 for the second read, +16kk per step) and
+  // columns n = 64wn + 32nf + 16(g%2) + 4(s%4) .. +3.
+  int kn_frag[2];
+  {
+    const int g = lane >> 4, s = lane & 15;
+    const int row = 8 * (g >> 1) + (s >> 2);
+    const int chunk = 8 * wn + 2 * (g & 1) + ((s & 3) >> 1);  // 16-byte chunk for nf = 0
+    const int f0 = row * 512 + ((chunk ^ (4 * (s >> 2))) << 4) + ((s & 1) << 3);
+    kn_frag[0] = f0;
+    kn_frag[1] = f0 ^ 64;  // nf = 1: chunk + 4, i.e. bit 2 of the chunk, which the swizzle XORs too
+  }
+
+  auto frag_a = [&](int slot, int kk, int mf) INL -> f16x8 {  // B operand: A^T[k][m], m = 128wm + 32mf + l%32
+    return *(const LDS f16x8*)(a_lds + slot * G_TILEB + (128 * wm + 32 * mf) * 128 + rk_frag[kk]);
+  };
+  auto frag_b = [&](int slot, int kk, int nf) INL -> f16x8 {  // A operand: B^T[n][k], n = 64wn + 32nf + l%32
+    if constexpr (kBL == 1) {
+      return *(const LDS f16x8*)(b_lds + slot * G_TILEB + (64 * wn + 32 * nf) * 128 + rk_frag[kk]);
+    } else {
+      const LDS char* a = b_lds + slot * G_TILEB + kn_frag[nf] + 16 * kk * 512;
+      const f16x4 h1 = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS i16x4*)a));
+      const f16x4 h2 = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS i16x4*)(a + 4 * 512)));
+      return f16x8{h1[0], h1[1], h1[2], h1[3], h2[0], h2[1], h2[2], h2[3]};
+    }
+  };
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int mf = 0; mf < 4; ++mf)
+#pragma unroll
+    for (int nf = 0; nf < 2; ++nf) acc[mf][nf] = f32x16{};
+
+  auto compute = [&](int slot) INL {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      f16x8 bf[2], af[4];
+#pragma unroll
+      for (int nf = 0; nf < 2; ++nf) bf[nf] = frag_b(slot, kk, nf);
+#pragma unroll
+      for (int mf = 0; mf < 4; ++mf) af[mf] = frag_a(slot, kk, mf);
+#pragma unroll
+      for (int mf = 0; mf < 4; ++mf)
+#pragma unroll
+        for (int nf = 0; nf < 2; ++nf)
+          acc[mf][nf] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[nf], af[mf], acc[mf][nf], 0, 0, 0);
+    }
+  };
+
+  // ---- K loop: tile kt+1 loads while tile kt computes; slot (kt+1) & 1 was
+  // last read in iteration kt-1, before that iteration's closing barrier.
+  const int nkt = p.nkt;
+  const bool tail = (K & (GBK - 1)) != 0;
+  stage(0);
+  dma_wait();
+  if (tail && nkt == 1) zero_tail(0);
+  lds_barrier();
+  for (int kt = 0; kt < nkt; ++kt) {
+    if (kt + 1 < nkt) stage(kt + 1);
+    compute(kt & 1);
+    if (kt + 1 < nkt) {
+      dma_wait();
+      if (tail && kt + 2 == nkt) zero_tail(kt + 1);
+    }
+    lds_barrier();
+  }
+
+  // ---- epilogue: lane l holds C[m][n] for m = m0 + 128wm + 32mf + l%32 and
+  // n = n0 + 64wn + 32nf + 8(r/4) + 4(l/32) + r%4; fp16, round to nearest even.
+  const int h = lane >> 5;
+#pragma unroll
+  for (int mf = 0; mf < 4; ++mf) {
+    const int m = m0 + 128 * wm + 32 * mf + (lane & 31);
+    if (m >= M) continue;
+    _Float16* crow = p.c + (int64_t)m * N;
+#pragma unroll
+    for (int nf = 0; nf < 2; ++nf)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int n = n0 + 64 * wn + 32 * nf + 8 * r4 + 4 * h;
+        if (n < N) {
+          f16x4 hv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) hv[e] = (_Float16)acc[mf][nf][4 * r4 + e];
+          *reinterpret_cast<f16x4*>(crow + n) = hv;
+        }
+      }
+  }
+}
+
+__global__ void gemm_zero_kernel(u32x4* c, int64_t n16) {
+  const u32x4 z = {0, 0, 0, 0};
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (int64_t)gridDim.x * blockDim.x)
+    c[i] = z;
+}
+
+hipError_t launch_gemm(const GemmParams& p, hipStream_t stream) {
+  const int64_t nb = (int64_t)p.ntm * p.ntn;
+  if (nb <= 0 || nb > 0x7fffffff || p.nkt < 1) return hipErrorInvalidValue;
+  if (p.b_layout == 0)
+    hipLaunchKernelGGL(gemm_kernel<0>, dim3((unsigned)nb), dim3(GTHREADS), 0, stream, p);
+  else if (p.b_layout == 1)
+    hipLaunchKernelGGL(gemm_kernel<1>, dim3((unsigned)nb), dim3(GTHREADS), 0, stream, p);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_zero(_Float16* c, int64_t elems, hipStream_t stream) {
+  const int64_t n16 = elems / 8;  // 16-byte stores; elems is a multiple of 8
+  if (n16 <= 0) return hipSuccess;
+  const int64_t blocks = n16 / 256 + 1 < 4096 ? n16 / 256 + 1 : 4096;
+  hipLaunchKernelGGL(gemm_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, reinterpret_cast<u32x4*>(c), n16);
+  return hipGetLastError();
+}
+
+}  // namespace libattn

@@ -1,4 +1,4 @@
-"""CPU tests of the C ABI: the library builds, loads, exports what include/attn.h declares,
+"""CPU tests of the C ABI: the library builds, loads, exports what include/*.h declares,
 and rejects invalid arguments before touching the GPU (fake pointers are never dereferenced)."""
 import ctypes
 import os
@@ -10,16 +10,19 @@ import pytest
 from dnn_compiler_pipelining_amd import binding as L
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "attn.h")
+HEADERS = [os.path.join(ROOT, "include", n) for n in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if n.endswith(".h")]
 
 # Aligned, distinct, never-dereferenced fake device addresses (validation fails before use).
 QP, KP, VP, OP, LP = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(attn_\w+)\s*\(", text, flags=re.M)))
+    names = set()
+    for path in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(path).read(), flags=re.S)
+        names.update(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b((?:attn|gemm)_\w+)\s*\(", text, flags=re.M))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -129,3 +132,52 @@ def test_ex_limits_and_order(lib):
     assert call_ex(q=0, Sq=65) == L.ATTN_ERR_NULL
     assert call_ex(Sq=65, D=96) == L.ATTN_ERR_SHAPE
     assert call_ex(o=KP + 4096, Sq=16, Sk=64) == L.ATTN_ERR_OVERLAP
+
+
+# ---------------------------------------------------------------- gemm_f16 (include/gemm.h)
+AP, BP, CP = 0x60000000, 0x70000000, 0x80000000
+
+
+def gcall(a=AP, b=BP, c=CP, M=300, N=264, K=136, b_layout=0):
+    return L.gemm_f16(a, b, c, M, N, K, b_layout, None)
+
+
+def test_gemm_null_pointers(lib):
+    assert gcall(a=0) == L.ATTN_ERR_NULL
+    assert gcall(b=0) == L.ATTN_ERR_NULL
+    assert gcall(c=0) == L.ATTN_ERR_NULL
+
+
+def test_gemm_empty_output_launches_nothing(lib):
+    # M = 0 or N = 0: nothing to compute, NULL pointers allowed, no GPU touched
+    assert gcall(a=0, b=0, c=0, M=0) == L.ATTN_OK
+    assert gcall(a=0, b=0, c=0, N=0) == L.ATTN_OK
+    assert gcall(M=0, N=0, K=0) == L.ATTN_OK
+
+
+@pytest.mark.parametrize("kw", [dict(M=-1), dict(N=-8), dict(K=-8), dict(M=(1 << 24) + 1), dict(N=(1 << 24) + 8),
+                                dict(K=(1 << 22) + 8), dict(b_layout=2), dict(b_layout=-1)])
+def test_gemm_bad_shapes(lib, kw):
+    assert gcall(**kw) == L.ATTN_ERR_SHAPE
+
+
+@pytest.mark.parametrize("kw", [dict(K=130), dict(N=260), dict(K=7, b_layout=1), dict(N=1)])
+def test_gemm_unsupported(lib, kw):
+    assert gcall(**kw) == L.ATTN_ERR_UNSUPPORTED
+
+
+def test_gemm_alignment_and_overlap(lib):
+    assert gcall(a=AP + 8) == L.ATTN_ERR_ALIGN
+    assert gcall(b=BP + 2) == L.ATTN_ERR_ALIGN
+    assert gcall(c=CP + 4) == L.ATTN_ERR_ALIGN
+    a_bytes = 300 * 136 * 2
+    assert gcall(c=AP + 16 * (a_bytes // 32)) == L.ATTN_ERR_OVERLAP  # c starts inside a
+    assert gcall(c=BP - 16) == L.ATTN_ERR_OVERLAP                    # c runs into b
+
+
+def test_gemm_check_order(lib):
+    # NULL before shape, shape before unsupported, unsupported before alignment, alignment before overlap
+    assert gcall(a=0, M=-1) == L.ATTN_ERR_NULL
+    assert gcall(K=130, b_layout=3) == L.ATTN_ERR_SHAPE
+    assert gcall(K=130, a=AP + 8) == L.ATTN_ERR_UNSUPPORTED
+    assert gcall(a=AP + 8, c=AP) == L.ATTN_ERR_ALIGN
