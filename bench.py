@@ -25,6 +25,11 @@ reads and writes BYTES bytes after the timed region (counter calibration for the
 `--summarize-kernel-trace TRACE_DIR COMMAND` writes the kernel-trace summary,
 and `--summarize-counters DIR [DIR ...]` the summary of rocprofv3 --pmc runs of
 SQ/GRBM counters (MFMA busy fraction, VALU/MFMA co-execution, LDS activity).
+
+`--workload gemm_8k_nn` / `gemm_8k_nt` time the fp16 GEMM instead (the 8k
+MatMul: M = N = K = 8192, B stored [K,N] or [N,K]); its line has the same
+fields, with metric FLOPs 2*M*N*K and the fp64 GEMM oracle as cpu_baseline.
+`--all` prints one line per attention workload and per GEMM workload.
 """
 from __future__ import annotations
 
@@ -45,6 +50,18 @@ METRIC = "causal attention fwd TFLOP/s (fp16) + % of MFMA peak, LLaMA3 shapes"
 PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, published
 DEFAULT_WORKLOAD = "llama3-70b_b64_s8192"
 KERNEL_NAME = "attn_fwd_kernel"
+GEMM_METRIC = "fp16 GEMM TFLOP/s (8k MatMul, fp32 accumulation) + % of MFMA peak"
+GEMM_KERNEL_NAME = "gemm_kernel"
+
+
+def is_gemm(workload: str) -> bool:
+    from dnn_compiler_pipelining_amd import inputs
+
+    return workload in inputs.GEMM_BY_NAME
+
+
+def kernel_name(workload: str) -> str:
+    return GEMM_KERNEL_NAME if is_gemm(workload) else KERNEL_NAME
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -52,13 +69,18 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_fingerprint() -> str:
-    """sha256 over the kernel sources and build flags: identifies the measured kernel build."""
+def kernel_fingerprint(workload: str = DEFAULT_WORKLOAD) -> str:
+    """sha256 over the sources and build flags of the kernel that runs `workload`: identifies the measured
+    kernel build."""
     from dnn_compiler_pipelining_amd import build as hipbuild
 
+    if is_gemm(workload):
+        files = hipbuild.GEMM_SOURCES + [os.path.join(hipbuild.CSRC, n) for n in ("gemm_kernel.h", "gfx950.h")]
+    else:
+        files = hipbuild.ATTN_SOURCES + [os.path.join(hipbuild.CSRC, n) for n in
+                                         ("attn_kernel.h", "variant.h", "tuned_table.h", "gfx950.h")]
     h = hashlib.sha256()
-    for path in hipbuild.SOURCES + [os.path.join(hipbuild.CSRC, n) for n in ("attn_kernel.h", "variant.h",
-                                                                           "tuned_table.h")]:
+    for path in files:
         with open(path, "rb") as f:
             h.update(f.read())
     h.update(" ".join(hipbuild.HIP_FLAGS[:9]).encode())
@@ -75,7 +97,7 @@ def load_traffic(workload: str):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_fingerprint") != kernel_fingerprint():
+    if t.get("kernel_fingerprint") != kernel_fingerprint(workload):
         return None
     return t
 
@@ -130,6 +152,53 @@ def time_workload(w, steps: int, warmup: int, pmc_copy: int = 0):
     return wall_ms, kernel_ms, ok
 
 
+def time_gemm(w, steps: int, warmup: int, pmc_copy: int = 0):
+    import torch
+
+    from dnn_compiler_pipelining_amd import binding, inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log("[bench] %s: generating seeded inputs" % w.name)
+    a, b = inputs.make_gemm_inputs(w, dev)
+    c = torch.empty((w.M, w.N), dtype=torch.float16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    torch.cuda.synchronize()
+
+    def step():
+        binding.matmul(a, b, w.b_layout, out=c, stream=stream)
+
+    log("[bench] %s: %d warmup steps" % (w.name, warmup))
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    log("[bench] %s: %d timed steps" % (w.name, steps))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall_ms = (t1 - t0) * 1e3 / steps
+    kernel_ms = e0.elapsed_time(e1) / steps
+    ok = bool(torch.isfinite(c[-1]).all().item())
+    if pmc_copy:
+        n = pmc_copy // 2
+        src = torch.ones(n, dtype=torch.float16, device=dev)
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        log("[bench] calibration copy of %d bytes done" % (2 * n))
+        del src, dst
+    del a, b, c
+    torch.cuda.empty_cache()
+    return wall_ms, kernel_ms, ok
+
+
 # ------------------------------------------------------------------ CPU oracle baseline
 
 def cpu_baseline(w, target_s: float = 15.0):
@@ -165,6 +234,37 @@ def cpu_baseline(w, target_s: float = 15.0):
                       "fp64, %.1f s wall; FLOPs = 4*D*(allowed keys) per row" % (256 * threads + n, w.name, secs)}
 
 
+def cpu_baseline_gemm(w, target_s: float = 15.0):
+    """Times the fp64 GEMM oracle (numpy's float64 matmul) on blocks of rows of C."""
+    import numpy as np
+
+    from dnn_compiler_pipelining_amd import inputs
+    from oracle import gemm_oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    a, b = inputs.make_gemm_inputs(w)
+    an, bn = a.numpy(), b.numpy()
+    order = np.random.default_rng(54321).permutation(w.M)
+    flops = secs = 0.0
+    done = 0
+    while secs < target_s and done < w.M:  # blocks of 512 rows of C until the target time is reached
+        rows = np.sort(order[done:done + 512])
+        t = time.perf_counter()
+        gemm_oracle.gemm_rows(an, bn, w.b_layout, rows)
+        secs += time.perf_counter() - t
+        flops += 2.0 * len(rows) * w.N * w.K
+        done += len(rows)
+    log("[bench] cpu oracle: %d BLAS threads, %d rows in %.1f s" % (threads, done, secs))
+    return {"value": round(flops / secs / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "%d rows of C (uniform without replacement, blocks of 512) of %s, binary64, %.1f s wall; "
+                      "FLOPs = 2*N*K per row" % (done, w.name, secs)}
+
+
 # ------------------------------------------------------------------ traffic summary from rocprofv3 --pmc runs
 
 def _db_files(d: str):
@@ -195,6 +295,7 @@ def summarize_kernel_trace(d: str, workload: str, command: str):
     lines = ["# rocprofv3 kernel trace: %s" % workload, "", "Command (from the repository root):", "",
              "    " + command, "", "| kernel | calls | average us | total us | share % |", "|---|---|---|---|---|"]
     info = None
+    kn = kernel_name(workload)
     for f in _db_files(d):
         con = sqlite3.connect(f)
         for name, calls, total, avg, pct in con.execute(
@@ -202,16 +303,16 @@ def summarize_kernel_trace(d: str, workload: str, command: str):
             short = name if len(name) < 70 else name[:67] + "..."
             lines.append("| `%s` | %d | %.1f | %.1f | %.3f |" % (short, calls, avg, total, pct))
         row = con.execute("select grid_x, workgroup_x, lds_size, scratch_size, vgpr_count, accum_vgpr_count, "
-                          "sgpr_count from kernels where name like ? limit 1", ("%" + KERNEL_NAME + "%",)).fetchone()
+                          "sgpr_count from kernels where name like ? limit 1", ("%" + kn + "%",)).fetchone()
         if row:
             info = row
         con.close()
     if info:
         lines += ["", "%s dispatch: grid %d work-items, workgroup %d, LDS %d B, scratch %d B, vgpr_count %d, "
-                      "accum_vgpr_count %d, sgpr_count %d (as the trace reports them)" % ((KERNEL_NAME,) + tuple(info))]
-    lines += ["", "Kernel source fingerprint: %s" % kernel_fingerprint(), ""]
+                      "accum_vgpr_count %d, sgpr_count %d (as the trace reports them)" % ((kn,) + tuple(info))]
+    lines += ["", "Kernel source fingerprint: %s" % kernel_fingerprint(workload), ""]
     os.makedirs(PROFILES, exist_ok=True)
-    out = os.path.join(PROFILES, "%s_%s_kernel_trace.md" % (KERNEL_NAME, workload))
+    out = os.path.join(PROFILES, "%s_%s_kernel_trace.md" % (kn, workload))
     with open(out, "w") as f:
         f.write("\n".join(lines))
     print("\n".join(lines))
@@ -219,12 +320,13 @@ def summarize_kernel_trace(d: str, workload: str, command: str):
 
 def summarize_traffic(fetch_dir: str, write_dir: str, workload: str, copy_bytes: int):
     res = {}
+    knm = kernel_name(workload)
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         vals = _per_dispatch(d, counter)
-        attn = [v for (kn, _), v in vals.items() if KERNEL_NAME in kn]
-        other = [(kn, v) for (kn, _), v in vals.items() if KERNEL_NAME not in kn]
+        attn = [v for (kn, _), v in vals.items() if knm in kn]
+        other = [(kn, v) for (kn, _), v in vals.items() if knm not in kn]
         if not attn:
-            raise RuntimeError("no %s dispatches in %s" % (KERNEL_NAME, d))
+            raise RuntimeError("no %s dispatches in %s" % (knm, d))
         # the calibration copy is the largest non-attention dispatch
         copy_kib = max(v for _, v in other) if other else 0.0
         factor = copy_bytes / (copy_kib * 1024.0) if copy_kib else None
@@ -237,11 +339,15 @@ def summarize_traffic(fetch_dir: str, write_dir: str, workload: str, copy_bytes:
         total = res["FETCH_SIZE"]["bytes_per_launch"] + res["WRITE_SIZE"]["bytes_per_launch"]
     from dnn_compiler_pipelining_amd import inputs
 
-    w = inputs.BY_NAME[workload]
-    algo = 2 * (2 * w.B * w.S * w.Hq * w.D + 2 * w.B * w.S * w.Hkv * w.D) + 4 * w.B * w.Hq * w.S
+    if is_gemm(workload):
+        g = inputs.GEMM_BY_NAME[workload]
+        algo = 2 * (g.M * g.K + g.K * g.N + g.M * g.N)
+    else:
+        w = inputs.BY_NAME[workload]
+        algo = 2 * (2 * w.B * w.S * w.Hq * w.D + 2 * w.B * w.S * w.Hkv * w.D) + 4 * w.B * w.Hq * w.S
     cmd = ("rocprofv3 --pmc %s -d <dir> -o <name> -- python3 bench.py --workload %s --steps 2 --warmup 1 "
            "--no-cpu-baseline --pmc-copy %d")
-    out = {"workload": workload, "kernel": KERNEL_NAME, "kernel_fingerprint": kernel_fingerprint(),
+    out = {"workload": workload, "kernel": knm, "kernel_fingerprint": kernel_fingerprint(workload),
            "hbm_bytes_per_launch": total, "algorithmic_bytes_per_launch": algo,
            "commands": [cmd % ("FETCH_SIZE", workload, copy_bytes), cmd % ("WRITE_SIZE", workload, copy_bytes),
                         "python3 bench.py --workload %s --pmc-copy %d --summarize-traffic <fetch dir> <write dir>"
@@ -272,16 +378,16 @@ def summarize_counters(dirs, workload: str):
             con = sqlite3.connect(f)
             for name, counter, val, n in con.execute(
                     "select kernel_name, counter_name, sum(value), count(distinct dispatch_id) from counters_collection "
-                    "where kernel_name like ? group by kernel_name, counter_name", ("%" + KERNEL_NAME + "%",)):
+                    "where kernel_name like ? group by kernel_name, counter_name", ("%" + kernel_name(workload) + "%",)):
                 vals[counter] = val / max(n, 1)
                 names.add(counter)
             con.close()
         cmds.append("rocprofv3 --pmc %s -d <dir> -o <name> -- python3 bench.py --workload %s --steps 2 --warmup 1 "
                     "--no-cpu-baseline" % (" ".join(sorted(names)), workload))
-    lines = ["# rocprofv3 counters: %s, %s" % (KERNEL_NAME, workload), "", "Commands (from the repository root; one "
+    lines = ["# rocprofv3 counters: %s, %s" % (kernel_name(workload), workload), "", "Commands (from the repository root; one "
              "--pmc pass per line, counters grouped within the per-block limits):", ""]
     lines += ["    " + c for c in cmds]
-    lines += ["", "Values are per dispatch of the attention kernel, summed over the device.", "",
+    lines += ["", "Values are per dispatch of %s, summed over the device." % kernel_name(workload), "",
               "| counter | per dispatch |", "|---|---|"]
     for k in sorted(vals):
         lines.append("| %s | %.4g |" % (k, vals[k]))
@@ -298,9 +404,9 @@ def summarize_counters(dirs, workload: str):
         if "SQ_LDS_IDX_ACTIVE" in vals:
             lines.append("- LDS indexed-access active: %.1f %% of active cycles per CU" %
                          (100.0 * vals["SQ_LDS_IDX_ACTIVE"] / (256 * cyc)))
-    lines += ["", "Kernel source fingerprint: %s" % kernel_fingerprint(), ""]
+    lines += ["", "Kernel source fingerprint: %s" % kernel_fingerprint(workload), ""]
     os.makedirs(PROFILES, exist_ok=True)
-    out = os.path.join(PROFILES, "%s_%s_counters.md" % (KERNEL_NAME, workload))
+    out = os.path.join(PROFILES, "%s_%s_counters.md" % (kernel_name(workload), workload))
     with open(out, "w") as f:
         f.write("\n".join(lines))
     print("\n".join(lines))
@@ -341,10 +447,16 @@ def main():
               "--gpus %d (WORLD_SIZE %d) is not supported" % (args.gpus, world), file=sys.stderr)
         return 2
 
-    names = [w.name for w in inputs.WORKLOADS] if args.all else [args.workload]
+    names = ([w.name for w in inputs.WORKLOADS] + [w.name for w in inputs.GEMM_WORKLOADS]) if args.all \
+        else [args.workload]
     for name in names:
-        w = inputs.BY_NAME[name]
-        wall_ms, kernel_ms, ok = time_workload(w, args.steps, args.warmup, args.pmc_copy)
+        gemm = is_gemm(name)
+        if gemm:
+            w = inputs.GEMM_BY_NAME[name]
+            wall_ms, kernel_ms, ok = time_gemm(w, args.steps, args.warmup, args.pmc_copy)
+        else:
+            w = inputs.BY_NAME[name]
+            wall_ms, kernel_ms, ok = time_workload(w, args.steps, args.warmup, args.pmc_copy)
         if not ok:
             log("[bench] non-finite output")
             return 1
@@ -352,7 +464,7 @@ def main():
         achieved = w.flops / (kernel_ms * 1e-3) / 1e12
         traffic = load_traffic(w.name)
         line = {
-            "metric": METRIC,
+            "metric": GEMM_METRIC if gemm else METRIC,
             "value": round(value, 2),
             "unit": "TFLOP/s",
             "n_gpus": 1,
@@ -363,18 +475,18 @@ def main():
             "scaling": "weak",
             "vs_baseline": None,
             "dtype": "f16",
-            "data": "synthetic: seeded i.i.d. N(0,1) fp16 Q/K/V",
+            "data": "synthetic: seeded i.i.d. N(0,1) fp16 %s" % ("A/B" if gemm else "Q/K/V"),
             "pct_of_mfma_peak": round(100.0 * value / PEAK_TFLOPS, 2),
             "config": w.describe(),
             "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(achieved / PEAK_TFLOPS, 4),
                          "traffic": (round(traffic["hbm_bytes_per_launch"])
                                      if traffic and traffic.get("hbm_bytes_per_launch") else None),
-                         "kernel": KERNEL_NAME, "kernel_ms": round(kernel_ms, 4),
+                         "kernel": kernel_name(name), "kernel_ms": round(kernel_ms, 4),
                          "flops_per_launch": w.flops},
         }
         if not args.no_cpu_baseline and not args.all:
-            line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+            line["cpu_baseline"] = (cpu_baseline_gemm if gemm else cpu_baseline)(w, args.cpu_seconds)
         print(json.dumps(line), flush=True)
     return 0
 

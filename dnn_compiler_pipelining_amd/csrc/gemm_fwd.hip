@@ -183,39 +183,72 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_kernel(GemmParams p) {
 #pragma unroll
     for (int nf = 0; nf < 2; ++nf) acc[mf][nf] = f32x16{};
 
-  auto compute = [&](int slot) INL {
+  // ---- mma task: a K tile is 4 substeps of 16 k, 8 MFMAs each (mf-major).
+  // Fragments are double-buffered by substep; the 6 (or 8, with transpose
+  // reads) fragment reads of the next substep are issued one after each of
+  // the first MFMAs of the current one (pinned below), so LDS latency hides
+  // behind the matrix core.
+  constexpr int kReads = kBL == 1 ? 6 : 8;
+  f16x8 bf[2][2], af[2][4];
+  auto load_frags = [&](int slot, auto kc) INL {
+    constexpr int kk = decltype(kc)::value;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      f16x8 bf[2], af[4];
+    for (int nf = 0; nf < 2; ++nf) bf[kk & 1][nf] = frag_b(slot, kk, nf);
 #pragma unroll
-      for (int nf = 0; nf < 2; ++nf) bf[nf] = frag_b(slot, kk, nf);
+    for (int mf = 0; mf < 4; ++mf) af[kk & 1][mf] = frag_a(slot, kk, mf);
+  };
+  auto mfmas = [&](auto kc) INL {
+    constexpr int kk = decltype(kc)::value;
 #pragma unroll
-      for (int mf = 0; mf < 4; ++mf) af[mf] = frag_a(slot, kk, mf);
-#pragma unroll
-      for (int mf = 0; mf < 4; ++mf)
-#pragma unroll
-        for (int nf = 0; nf < 2; ++nf)
-          acc[mf][nf] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[nf], af[mf], acc[mf][nf], 0, 0, 0);
+    for (int j = 0; j < 8; ++j) {
+      const int mf = j >> 1, nf = j & 1;
+      acc[mf][nf] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[kk & 1][nf], af[kk & 1][mf], acc[mf][nf], 0, 0, 0);
     }
   };
+  auto pin_interleaved = [&]() INL {  // MFMA j, then read j
+    static_for<8>([&](auto jc) INL {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if constexpr (decltype(jc)::value < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    });
+  };
 
-  // ---- K loop: tile kt+1 loads while tile kt computes; slot (kt+1) & 1 was
-  // last read in iteration kt-1, before that iteration's closing barrier.
+  // ---- K loop, rotated by one substep across the barrier: iteration kt runs
+  // substeps 0..2 of tile kt, waits for tile kt+1's loads and the barrier
+  // that publishes them, then runs substep 3 of tile kt (its fragments are
+  // already in registers) beside the substep-0 reads of tile kt+1, and only
+  // then issues the loads of tile kt+2 into the slot tile kt has just left.
+  // The matrix core stays busy while the waves meet at the barrier and while
+  // the first reads of a tile are in flight.
   const int nkt = p.nkt;
   const bool tail = (K & (GBK - 1)) != 0;
   stage(0);
   dma_wait();
   if (tail && nkt == 1) zero_tail(0);
   lds_barrier();
-  for (int kt = 0; kt < nkt; ++kt) {
-    if (kt + 1 < nkt) stage(kt + 1);
-    compute(kt & 1);
-    if (kt + 1 < nkt) {
-      dma_wait();
-      if (tail && kt + 2 == nkt) zero_tail(kt + 1);
-    }
+  load_frags(0, std::integral_constant<int, 0>{});
+  if (nkt > 1) stage(1);
+  auto substeps_012 = [&](int slot) INL {
+    static_for<3>([&](auto kc) INL {
+      constexpr int kk = decltype(kc)::value;
+      load_frags(slot, std::integral_constant<int, kk + 1>{});
+      mfmas(kc);
+      pin_interleaved();
+    });
+  };
+  int kt = 0;
+  for (; kt + 1 < nkt; ++kt) {
+    const int slot = kt & 1;
+    substeps_012(slot);
+    dma_wait();
+    if (tail && kt + 2 == nkt) zero_tail(kt + 1);
     lds_barrier();
+    load_frags(slot ^ 1, std::integral_constant<int, 0>{});
+    mfmas(std::integral_constant<int, 3>{});
+    pin_interleaved();
+    if (kt + 2 < nkt) stage(kt + 2);
   }
+  substeps_012(kt & 1);  // the last tile
+  mfmas(std::integral_constant<int, 3>{});
 
   // ---- epilogue: lane l holds C[m][n] for m = m0 + 128wm + 32mf + l%32 and
   // n = n0 + 64wn + 32nf + 8(r/4) + 4(l/32) + r%4; fp16, round to nearest even.
