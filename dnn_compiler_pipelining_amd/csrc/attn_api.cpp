@@ -18,7 +18,7 @@ constexpr int kVersion = 1 * 10000 + 1 * 100 + 0;
 constexpr int kMaxSeq = 1 << 30;  // sequence lengths up to 2^30 keep all tile arithmetic in int
 
 // The variant for a shape: the tuned choice (variant.h), unless the
-// environment overrides a field.  LIBATTN_SCHEDULE=serial|overlap|pingpong,
+// environment overrides a field.  LIBATTN_SCHEDULE=serial|overlap|pingpong|serial4,
 // LIBATTN_RING=2|4, LIBATTN_XCD=0|1 and LIBATTN_LPT=0|1 are read on every
 // call, so tests and the schedule search can switch them; all variants give
 // bitwise identical results.
@@ -28,6 +28,7 @@ libattn::Variant choose_variant(int B, int Sq, int Sk, int Hq, int Hkv) {
     if (std::strcmp(s, "serial") == 0) v.schedule = libattn::SCHEDULE_SERIAL;
     if (std::strcmp(s, "overlap") == 0) v.schedule = libattn::SCHEDULE_OVERLAP;
     if (std::strcmp(s, "pingpong") == 0) v.schedule = libattn::SCHEDULE_PINGPONG;
+    if (std::strcmp(s, "serial4") == 0) v.schedule = libattn::SCHEDULE_SERIAL4;
   }
   auto flag = [](const char* name, int& field, int lo, int hi) {
     if (const char* s = std::getenv(name)) {
@@ -97,14 +98,16 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
   p.Hkv = Hkv;
   p.off = causal ? Sk - Sq : 0;
   p.g = Hq / Hkv;
-  p.pairs = (p.g + 1) / 2;
   p.n_qt = (Sq + 127) / 128;
   p.causal = causal;
   p.neg = scale < 0.f ? 1 : 0;
   p.cs = std::fabs(scale) * 1.44269504088896340736f;
   const libattn::Variant var = choose_variant(B, Sq, Sk, Hq, Hkv);
   p.hd = D;
-  p.schedule = D == 128 ? var.schedule : libattn::SCHEDULE_SERIAL;  // HD 64: serial schedule only
+  // HD 64 runs the serial schedules only
+  p.schedule = D == 128 || var.schedule == libattn::SCHEDULE_SERIAL4 ? var.schedule : libattn::SCHEDULE_SERIAL;
+  // query heads per workgroup: a pair (two wave groups), or one for SERIAL4
+  p.pairs = p.schedule == libattn::SCHEDULE_SERIAL4 ? p.g : (p.g + 1) / 2;
   p.ring = var.ring;
   p.xcd = var.xcd;
   p.lpt = var.lpt;

@@ -42,7 +42,9 @@ namespace libattn {
 
 constexpr int BM = 128;          // query rows per wave group
 constexpr int BN = 64;           // keys per KV tile
-constexpr int NTHREADS = 512;    // 8 wavefronts
+// Waves per workgroup: 8 (two wave groups on two heads of a KV group), or 4
+// (one head) for the SERIAL4 schedule.
+__host__ __device__ constexpr int waves_of(int sched) { return sched == SCHEDULE_SERIAL4 ? 4 : 8; }
 constexpr float NEG_INF = -__builtin_inff();
 constexpr float M_INIT = -1e30f; // finite start for the running max
 constexpr float LN2 = 0.693147180559945309f;
@@ -72,25 +74,29 @@ struct Geo {
   static constexpr int K_ROWB = 2 * kHD + 16;
   static constexpr int K_TILEB = BN * K_ROWB;        // 17408 | 9216
   static constexpr int K_DMA = K_TILEB / 1024;       // 17 | 9
-  static constexpr int K_DMA_PER_WAVE = (K_DMA + 7) / 8;  // wave w issues K instructions w, w+8, ...
+
   static constexpr int V_ROWB = 2 * kHD;
   static constexpr int V_TILEB = BN * V_ROWB;        // 16384 | 8192
   static constexpr int V_DMA = V_TILEB / 1024;       // 16 | 8
-  static constexpr int V_DMA_PER_WAVE = V_DMA / 8;   // wave w issues V instructions w, w+8, ...
+
   static constexpr int V_ROWS_PER_DMA = 1024 / V_ROWB;
   static constexpr int NKK = kHD / 16;               // 16-wide d steps of QK^T
   static constexpr int NDB = kHD / 32;               // 32-wide d blocks of O^T
   static_assert(K_TILEB % 1024 == 0 && V_TILEB % 1024 == 0, "tile slots are whole DMA instructions");
-  static_assert(V_DMA % 8 == 0, "every wave issues the same number of V instructions");
+  static_assert(V_DMA % 8 == 0, "every wave of 4 or 8 issues the same number of V instructions");
   // physical 16-byte chunk of logical chunk c in V row r is c ^ vswz(r)
   __host__ __device__ static constexpr int vswz(int r) { return kHD == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 };
 // K tiles rotate through three slots, V tiles through two: K_t stays in LDS
 // for the whole iteration after its QK^T, so a softmax that has to be redone
-// can recompute S^T from it.
-constexpr int K_SLOTS = 3, V_SLOTS = 2;
-static_assert(K_SLOTS * Geo<128>::K_TILEB + V_SLOTS * Geo<128>::V_TILEB <= 160 * 1024,
+// can recompute S^T from it.  SERIAL4 keeps two K slots (the serial loop
+// reads K_j while K_{j+1} arrives) so that two of its workgroups fit a CU.
+__host__ __device__ constexpr int k_slots_of(int sched) { return sched == SCHEDULE_SERIAL4 ? 2 : 3; }
+constexpr int V_SLOTS = 2;
+static_assert(k_slots_of(SCHEDULE_SERIAL) * Geo<128>::K_TILEB + V_SLOTS * Geo<128>::V_TILEB <= 160 * 1024,
               "the K and V rings fit the 160 KiB LDS");
+static_assert(2 * (k_slots_of(SCHEDULE_SERIAL4) * Geo<128>::K_TILEB + V_SLOTS * Geo<128>::V_TILEB) <= 160 * 1024,
+              "two SERIAL4 workgroups fit the 160 KiB LDS");
 
 __device__ __forceinline__ float pair_max(float x) {
   // lanes l and l^32 hold the same query: combine their partial results
@@ -134,13 +140,19 @@ constexpr int reads_of(int mode, int i, int nkk, int ndb) { return step_of(mode,
 
 // kSched: tile schedule; kRing: depth of the fragment prefetch ring of the mma
 // steps (how many steps ahead the LDS reads run); kHD: head dimension.  The
-// overlap and ping-pong schedules are written for HD 128.
+// overlap and ping-pong schedules are written for HD 128.  A SERIAL4
+// workgroup asks for two waves per SIMD (two workgroups per CU).
 template <int kSched, int kRing, int kHD>
-__global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(Params p) {
+__global__ __launch_bounds__(64 * waves_of(kSched), waves_of(kSched) == 4 ? 2 : 1) void attn_fwd_kernel(Params p) {
   using G = Geo<kHD>;
-  static_assert(kHD == 128 || kSched == SCHEDULE_SERIAL, "HD 64 runs the serial schedule");
+  static_assert(kHD == 128 || kSched == SCHEDULE_SERIAL || kSched == SCHEDULE_SERIAL4,
+                "HD 64 runs the serial schedules");
+  constexpr int NW = waves_of(kSched);
+  constexpr int K_SLOTS = k_slots_of(kSched);
   constexpr int HD = G::HD, NKK = G::NKK, NDB = G::NDB;
-  constexpr int K_ROWB = G::K_ROWB, K_TILEB = G::K_TILEB, K_DMA = G::K_DMA, K_DMA_PER_WAVE = G::K_DMA_PER_WAVE;
+  constexpr int K_ROWB = G::K_ROWB, K_TILEB = G::K_TILEB, K_DMA = G::K_DMA;
+  constexpr int K_DMA_PER_WAVE = (K_DMA + NW - 1) / NW;  // wave w issues K instructions w, w+NW, ...
+  constexpr int V_DMA_PER_WAVE = G::V_DMA / NW;          // wave w issues V instructions w, w+NW, ...
   constexpr int V_ROWB = G::V_ROWB, V_TILEB = G::V_TILEB;
   __shared__ __attribute__((aligned(1024))) char k_smem[K_SLOTS * K_TILEB];
   __shared__ __attribute__((aligned(1024))) char v_smem[V_SLOTS * V_TILEB];
@@ -150,7 +162,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(Params p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int grp = wave >> 2;  // wave group: which head of the pair
+  const int grp = NW == 8 ? wave >> 2 : 0;  // wave group: which head of the pair
   const int wq = wave & 3;    // 32-row slice of the 128 query rows
   const int n = lane & 31;    // query column of this lane in S^T / O^T
   const int hh = lane >> 5;   // lane half
@@ -176,7 +188,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(Params p) {
   const int b = group / p.Hkv;
   const int c = group % p.Hkv;
   const int t = p.lpt ? p.n_qt - 1 - item / p.pairs : item / p.pairs;
-  const int hl = 2 * (item % p.pairs) + grp;  // head index inside the KV group
+  const int hl = NW == 8 ? 2 * (item % p.pairs) + grp : item % p.pairs;  // head index inside the KV group
   const bool active = hl < p.g;
   const int h = c * p.g + (active ? hl : 0);
 
@@ -220,7 +232,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(Params p) {
   uint32_t k_col[K_DMA_PER_WAVE];
 #pragma unroll
   for (int u = 0; u < K_DMA_PER_WAVE; ++u) {
-    const int o = 64 * (wave + 8 * u) + lane;  // 16-byte lane slot inside the tile
+    const int o = 64 * (wave + NW * u) + lane;  // 16-byte lane slot inside the tile
     k_row[u] = o / (K_ROWB / 16);
     const int cb = o - k_row[u] * (K_ROWB / 16);
     k_col[u] = 16u * (uint32_t)(cb < G::KC ? cb : G::KC - 1);  // padding slot: any in-bounds chunk of the row
@@ -237,7 +249,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(Params p) {
       const bool full = (tk + 1) * BN <= Sk;
 #pragma unroll
       for (int u = 0; u < K_DMA_PER_WAVE; ++u) {
-        const int i = wave_s + 8 * u;
+        const int i = wave_s + NW * u;
         if (i < K_DMA) {
           const int row = full ? k_row[u] : min(k_row[u], Sk - 1 - tk * BN);
           dma16(base, (uint32_t)row * row_bytes + k_col[u], k_lds_base + (tk % K_SLOTS) * K_TILEB + 1024 * i);
@@ -248,8 +260,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(Params p) {
       const char* base = (const char*)vb_ + (int64_t)tv * BN * row_bytes;
       const bool full = (tv + 1) * BN <= Sk;
 #pragma unroll
-      for (int u = 0; u < G::V_DMA_PER_WAVE; ++u) {
-        const int i = wave_s + 8 * u;
+      for (int u = 0; u < V_DMA_PER_WAVE; ++u) {
+        const int i = wave_s + NW * u;
         const int row0 = G::V_ROWS_PER_DMA * i + v_rowl;
         const int row = full ? row0 : min(row0, Sk - 1 - tv * BN);
         dma16(base, (uint32_t)row * row_bytes + v_col, v_lds_base + (tv & 1) * V_TILEB + 1024 * i);
@@ -487,9 +499,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(Params p) {
     rescale_o(rz);
   };
 
-  if constexpr (kSched == SCHEDULE_SERIAL) {
+  if constexpr (kSched == SCHEDULE_SERIAL || kSched == SCHEDULE_SERIAL4) {
     // ---- serial schedule: every wave runs stage-next / QK / softmax / PV per
-    // tile; slot (j+1) & 1 was last read in iteration j-1
+    // tile; K slot (j+1) % K_SLOTS and V slot (j+1) & 1 were last read in
+    // iteration j-1 or earlier
     stage(0, 0);
     dma_wait();
     lds_barrier();
@@ -712,11 +725,22 @@ int64_t grid_blocks(const Params& p) {
 hipError_t launch_attn_fwd(const Params& p, hipStream_t stream) {
   const int64_t nb = grid_blocks(p);
   if (nb <= 0) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)nb), block(NTHREADS);
+  const dim3 grid((unsigned)nb), block(64 * waves_of(p.schedule));
 #define LIBATTN_LAUNCH(S, R, H) hipLaunchKernelGGL((attn_fwd_kernel<S, R, H>), grid, block, 0, stream, p)
   if (p.ring != 2 && p.ring != 4) return hipErrorInvalidValue;
   const bool r2 = p.ring == 2;
-  if (p.hd == 64) {  // serial schedule only
+  if (p.schedule == SCHEDULE_SERIAL4) {
+    if (p.hd == 64) {
+      if (r2) LIBATTN_LAUNCH(SCHEDULE_SERIAL4, 2, 64);
+      else LIBATTN_LAUNCH(SCHEDULE_SERIAL4, 4, 64);
+    } else if (p.hd == 128) {
+      if (r2) LIBATTN_LAUNCH(SCHEDULE_SERIAL4, 2, 128);
+      else LIBATTN_LAUNCH(SCHEDULE_SERIAL4, 4, 128);
+    } else {
+      return hipErrorInvalidValue;
+    }
+  } else if (p.hd == 64) {  // serial schedules only
+    if (p.schedule != SCHEDULE_SERIAL) return hipErrorInvalidValue;
     if (r2) LIBATTN_LAUNCH(SCHEDULE_SERIAL, 2, 64);
     else LIBATTN_LAUNCH(SCHEDULE_SERIAL, 4, 64);
   } else if (p.hd != 128) {

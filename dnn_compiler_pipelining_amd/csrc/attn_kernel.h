@@ -27,7 +27,7 @@ struct Params {
   int B, Sq, Sk, Hq, Hkv;
   int off;           // causal: Sk - Sq (query row i may attend keys j <= i + off); 0 otherwise
   int g;             // Hq / Hkv
-  int pairs;         // ceil(g / 2): head pairs per KV head
+  int pairs;         // workgroups per KV head and query tile: ceil(g / 2) head pairs, or g heads (SERIAL4)
   int n_qt;          // query tiles per head (over Sq)
   int causal;
   int neg;           // scale < 0: the kernel negates Q and uses |scale|

@@ -23,7 +23,11 @@ namespace libattn {
 //   OVERLAP : every wave overlaps, inside one instruction stream, the softmax
 //             of tile j with the MFMAs of QK^T(j+1) and PV(j-1)
 //   PINGPONG: two wave groups offset by half a tile alternate MFMA and softmax
-enum Schedule { SCHEDULE_SERIAL = 0, SCHEDULE_OVERLAP = 1, SCHEDULE_PINGPONG = 2 };
+//   SERIAL4 : the serial schedule in workgroups of four waves, one query head
+//             each; two workgroups share a CU, so the two waves on a SIMD
+//             come from independently synchronised workgroups and drift out
+//             of phase (one's softmax beside the other's MFMAs)
+enum Schedule { SCHEDULE_SERIAL = 0, SCHEDULE_OVERLAP = 1, SCHEDULE_PINGPONG = 2, SCHEDULE_SERIAL4 = 3 };
 
 struct Variant {
   int schedule;  // Schedule
@@ -42,7 +46,7 @@ struct TunedEntry {
 #include "tuned_table.h"  // kTuned[], kTunedCount
 
 inline bool variant_valid(const Variant& v) {
-  return v.schedule >= SCHEDULE_SERIAL && v.schedule <= SCHEDULE_PINGPONG && (v.ring == 2 || v.ring == 4) &&
+  return v.schedule >= SCHEDULE_SERIAL && v.schedule <= SCHEDULE_SERIAL4 && (v.ring == 2 || v.ring == 4) &&
          (v.xcd == 0 || v.xcd == 1) && (v.lpt == 0 || v.lpt == 1);
 }
 

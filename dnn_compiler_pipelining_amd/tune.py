@@ -30,12 +30,13 @@ ROOT = os.path.dirname(PKG)
 TABLE = os.path.join(PKG, "csrc", "tuned_table.h")
 PROFILE = os.path.join(ROOT, "profiles", "schedule_search.json")
 
-SCHEDULES = ("serial", "overlap", "pingpong")  # Schedule enum order in csrc/variant.h
+SCHEDULES = ("serial", "overlap", "pingpong", "serial4")  # Schedule enum order in csrc/variant.h
+WORKGROUPS_PER_CU = {"serial4": 2}  # the others: one workgroup of 8 waves per CU
 RINGS = (2, 4)
 SWITCHES = (0, 1)
 SEED = {"schedule": "serial", "ring": 4, "xcd": 1, "lpt": 1}
 
-# resource budget of one variant: 8 waves per workgroup at 2 waves per SIMD
+# resource budget of one variant: 2 waves per SIMD (one 8-wave workgroup, or two 4-wave ones, per CU)
 MAX_VGPR = 256
 MAX_LDS = 160 * 1024
 
@@ -60,14 +61,16 @@ def kernel_resources(asm_path: str):
     return out
 
 
-def check_valid(res: dict) -> tuple[bool, str]:
-    """A variant is valid when it fits 2 waves per SIMD with no spills and no scratch, and its LDS fits a CU."""
+def check_valid(res: dict, schedule: str = "serial") -> tuple[bool, str]:
+    """A variant is valid when it fits 2 waves per SIMD with no spills and no scratch, and the LDS of the
+    workgroups that share a CU fits it."""
     if res["vgpr"] + res["agpr"] > MAX_VGPR:
         return False, "%d VGPRs > %d" % (res["vgpr"] + res["agpr"], MAX_VGPR)
     if res["vgpr_spill"] or res["scratch"]:
         return False, "spills %d VGPRs / %d B scratch" % (res["vgpr_spill"], res["scratch"])
-    if res["lds"] > MAX_LDS:
-        return False, "%d B LDS > %d" % (res["lds"], MAX_LDS)
+    wg = WORKGROUPS_PER_CU.get(schedule, 1)
+    if wg * res["lds"] > MAX_LDS:
+        return False, "%d x %d B LDS > %d" % (wg, res["lds"], MAX_LDS)
     return True, "ok"
 
 
@@ -80,7 +83,7 @@ def valid_variants(asm_path: str | None = None):
         os.close(fd)
         build.device_asm(asm_path)
     res = kernel_resources(asm_path)
-    return {k: check_valid(v) + (v,) for k, v in res.items()}
+    return {k: check_valid(v, k[0]) + (v,) for k, v in res.items()}
 
 
 # ------------------------------------------------------------------ search (GPU)
@@ -183,7 +186,7 @@ def search(out_dir: str, names=None):
 
 def emit(search_json: str, table: str = TABLE, profile: str | None = PROFILE):
     rec = json.load(open(search_json))
-    enum = {"serial": "SCHEDULE_SERIAL", "overlap": "SCHEDULE_OVERLAP", "pingpong": "SCHEDULE_PINGPONG"}
+    enum = {name: "SCHEDULE_" + name.upper() for name in SCHEDULES}
     lines = ["// tuned_table.h -- generated by `python -m dnn_compiler_pipelining_amd.tune --emit`",
              "// from the measured schedule search (profiles/schedule_search.json); do not edit by hand.",
              "#pragma once", "static const TunedEntry kTuned[] = {"]

@@ -42,9 +42,11 @@
  * calls, is thread-safe, and gives bitwise identical results run to run.
  *
  * The environment variable LIBATTN_SCHEDULE (read at each call) selects the
- * kernel's tile schedule: "serial" (the default), "overlap" or "pingpong";
- * unset or any other value gives the default.  All schedules give bitwise
- * identical results, so each serves as a cross-check of the others.
+ * kernel's tile schedule: "serial", "overlap", "pingpong" or "serial4" (the
+ * serial schedule in 4-wave workgroups, two per CU); unset or any other value
+ * gives the schedule tuned for the nearest measured shape.  D = 64 runs
+ * "serial" or "serial4" only.  All schedules give bitwise identical results,
+ * so each serves as a cross-check of the others.
  *
  * Errors: on invalid arguments nothing is launched and a nonzero ATTN_ERR_*
  * code is returned; a failed launch returns ATTN_ERR_HIP.  No exception

@@ -84,7 +84,7 @@ def test_rect_schedules_bitwise_identical(monkeypatch):
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
     monkeypatch.delenv("LIBATTN_SCHEDULE", raising=False)
     o1, l1 = U.run(qd, kd, vd, True, SC)
-    for sched in ("overlap", "pingpong"):
+    for sched in ("overlap", "pingpong", "serial4"):
         monkeypatch.setenv("LIBATTN_SCHEDULE", sched)
         o2, l2 = U.run(qd, kd, vd, True, SC)
         assert torch.equal(o1, o2) and torch.equal(l1, l2), sched

@@ -70,7 +70,7 @@ def test_d64_variants_bitwise_identical(monkeypatch):
     for key in ("LIBATTN_SCHEDULE", "LIBATTN_RING", "LIBATTN_XCD", "LIBATTN_LPT"):
         monkeypatch.delenv(key, raising=False)
     o1, l1 = U.run(qd, kd, vd, True, SC)
-    for sched in ("serial", "overlap", "pingpong"):
+    for sched in ("serial", "overlap", "pingpong", "serial4"):
         for ring in ("2", "4"):
             for xcd, lpt in (("0", "0"), ("1", "1")):
                 monkeypatch.setenv("LIBATTN_SCHEDULE", sched)

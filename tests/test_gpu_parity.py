@@ -172,14 +172,14 @@ def test_gpu_validation_errors_launch_nothing():
 @pytest.mark.parametrize("B,S,Hq,Hkv,causal", [(1, 1000, 8, 2, 1), (2, 333, 16, 4, 0), (1, 257, 6, 2, 1),
                                                (1, 8192, 64, 8, 1)], ids=str)
 def test_schedules_bitwise_identical(monkeypatch, B, S, Hq, Hkv, causal):
-    """The three tile schedules (default serial, overlap, ping-pong) against each other: each
+    """The tile schedules (default serial, overlap, ping-pong, serial4) against each other: each
     accumulator sees the same arithmetic in the same order, so any LDS race (a slot rewritten while
     another wave still reads it) would show up as a difference."""
     q, k, v = cpu_qkv(B, S, Hq, Hkv, seed=90 + S)
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
     monkeypatch.delenv("LIBATTN_SCHEDULE", raising=False)
     o1, l1 = U.run(qd, kd, vd, bool(causal), SC)
-    for sched in ("overlap", "pingpong"):
+    for sched in ("overlap", "pingpong", "serial4"):
         monkeypatch.setenv("LIBATTN_SCHEDULE", sched)
         o2, l2 = U.run(qd, kd, vd, bool(causal), SC)
         assert torch.equal(o1, o2) and torch.equal(l1, l2), sched
@@ -195,7 +195,7 @@ def test_all_variants_bitwise_identical(monkeypatch, B, S, Hq, Hkv, causal):
     for key in ("LIBATTN_SCHEDULE", "LIBATTN_RING", "LIBATTN_XCD", "LIBATTN_LPT"):
         monkeypatch.delenv(key, raising=False)
     o1, l1 = U.run(qd, kd, vd, bool(causal), SC)
-    for sched in ("serial", "overlap", "pingpong"):
+    for sched in ("serial", "overlap", "pingpong", "serial4"):
         for ring in ("2", "4"):
             for xcd in ("0", "1"):
                 for lpt in ("0", "1"):

@@ -14,7 +14,7 @@ CSRC = os.path.join(tune.PKG, "csrc")
 def test_every_compiled_variant_is_valid():
     vs = tune.valid_variants()
     assert set(vs) == ({(s, r, 128) for s in tune.SCHEDULES for r in tune.RINGS} |
-                       {("serial", r, 64) for r in tune.RINGS})
+                       {(s, r, 64) for s in ("serial", "serial4") for r in tune.RINGS})
     for key, (ok, why, res) in vs.items():
         assert ok, (key, why, res)
         assert res["lds"] > 0 and res["vgpr"] > 0
@@ -30,6 +30,13 @@ def test_every_compiled_variant_is_valid():
 def test_check_valid_rejects_over_budget(res, reason):
     ok, why = tune.check_valid(res)
     assert not ok and reason in why
+
+
+def test_check_valid_counts_two_workgroups_per_cu_for_serial4():
+    res = dict(vgpr=180, agpr=0, vgpr_spill=0, scratch=0, lds=84992)
+    assert tune.check_valid(res, "serial")[0]
+    ok, why = tune.check_valid(res, "serial4")
+    assert not ok and "LDS" in why
 
 
 LOOKUP_MAIN = r'''
@@ -62,7 +69,7 @@ def lookup(tmp_path, table_dir, shapes):
 def test_committed_table_picks_its_own_entries(tmp_path):
     text = open(os.path.join(CSRC, "tuned_table.h")).read()
     import re
-    enum = {"SCHEDULE_SERIAL": 0, "SCHEDULE_OVERLAP": 1, "SCHEDULE_PINGPONG": 2}
+    enum = {"SCHEDULE_SERIAL": 0, "SCHEDULE_OVERLAP": 1, "SCHEDULE_PINGPONG": 2, "SCHEDULE_SERIAL4": 3}
     rows = re.findall(r"\{(\d+), (\d+), (\d+), (\d+), (\d+), \{(SCHEDULE_\w+), (\d), (\d), (\d)\}", text)
     assert rows
     got = lookup(tmp_path, CSRC, [r[:5] for r in rows])
