@@ -80,6 +80,7 @@ SDPA_SHAPES = [
     (1, 64, 4, 1, 128),
     (1, 129, 8, 8, 64),
     (2, 33, 8, 1, 128),
+    (1, 40, 4, 2, 256),
 ]
 
 
