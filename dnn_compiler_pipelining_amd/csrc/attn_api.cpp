@@ -59,7 +59,7 @@ int validate(const void* q, const void* k, const void* v, const void* o, const f
   if (causal != 0 && causal != 1) return ATTN_ERR_SHAPE;
   if (causal && Sq > Sk) return ATTN_ERR_SHAPE;
   if (!std::isfinite(scale)) return ATTN_ERR_SHAPE;
-  if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+  if (D != 64 && D != 128 && D != 256) return ATTN_ERR_UNSUPPORTED;
   if ((int64_t)Hkv * D * 2 * 64 > 0xffffffffLL) return ATTN_ERR_UNSUPPORTED;  // 64 K/V rows must span < 4 GiB
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned16(lse)))
     return ATTN_ERR_ALIGN;
@@ -104,8 +104,10 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
   p.cs = std::fabs(scale) * 1.44269504088896340736f;
   const libattn::Variant var = choose_variant(B, Sq, Sk, Hq, Hkv);
   p.hd = D;
-  // HD 64 runs the serial schedules only
-  p.schedule = D == 128 || var.schedule == libattn::SCHEDULE_SERIAL4 ? var.schedule : libattn::SCHEDULE_SERIAL;
+  // HD 64 runs the serial schedules only, HD 256 the SERIAL4 schedule only
+  if (D == 256) p.schedule = libattn::SCHEDULE_SERIAL4;
+  else if (D == 128 || var.schedule == libattn::SCHEDULE_SERIAL4) p.schedule = var.schedule;
+  else p.schedule = libattn::SCHEDULE_SERIAL;
   // query heads per workgroup: a pair (two wave groups), or one for SERIAL4
   p.pairs = p.schedule == libattn::SCHEDULE_SERIAL4 ? p.g : (p.g + 1) / 2;
   p.ring = var.ring;
@@ -133,7 +135,7 @@ const char* attn_status_string(int status) {
     case ATTN_ERR_NULL: return "a required pointer is NULL";
     case ATTN_ERR_SHAPE: return "invalid shape, layout, causal flag or scale";
     case ATTN_ERR_UNSUPPORTED:
-      return "unsupported size: attention needs D of 64 or 128 and K/V heads under 4 GiB per 64 rows, "
+      return "unsupported size: attention needs D of 64, 128 or 256 and K/V heads under 4 GiB per 64 rows, "
              "the GEMM K and N multiples of 8";
     case ATTN_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case ATTN_ERR_HIP: return "HIP launch error";

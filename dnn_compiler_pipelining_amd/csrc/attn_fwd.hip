@@ -53,31 +53,31 @@ constexpr float LN2 = 0.693147180559945309f;
 // final O / l and LSE = m + log2(l) are exact for any m.
 constexpr float TAU = 8.0f;
 
-// LDS layouts (bytes), per head dimension HD (64 or 128).  A tile slot is a
+// LDS layouts (bytes), per head dimension HD (64, 128 or 256).  A tile slot is a
 // run of 1 KiB DMA instructions.
-//  K: 64 key rows of 2*HD + 16 B.  Consecutive keys fall 68 (HD 128) or 36
-//    (HD 64) banks apart, so the 16 keys of a ds_read_b128 pass at one
+//  K: 64 key rows of 2*HD + 16 B.  Consecutive keys fall 68 (HD 128), 36
+//    (HD 64) or 132 (HD 256) banks apart, so the 16 keys of a ds_read_b128 pass at one
 //    16-byte column cover all 64 banks once; every K fragment read is a
 //    compile-time offset from one per-lane base.  One 16-byte lane slot per
 //    row lands in the padding.
 //  V: 64 key rows of 2*HD B whose 16-byte chunks are XOR-swizzled: by
-//    4*(row & 3) for HD 128, by 4*((row >> 1) & 1) for HD 64.  A
+//    4*(row & 3) for HD 128 and 256, by 4*((row >> 1) & 1) for HD 64.  A
 //    ds_read_b64_tr_b16 group reads 4 consecutive rows x 32 B; with the
 //    swizzle the 4 rows of the two groups of a half-wave (4 rows x 64 B) hit
 //    all 64 banks once.  Across the 32-wide d blocks the per-lane address
 //    changes by an XOR with 64*db.
 template <int kHD>
 struct Geo {
-  static_assert(kHD == 64 || kHD == 128, "head dimension");
+  static_assert(kHD == 64 || kHD == 128 || kHD == 256, "head dimension");
   static constexpr int HD = kHD;
   static constexpr int KC = kHD / 8;                 // 16-byte chunks per K/V row
   static constexpr int K_ROWB = 2 * kHD + 16;
-  static constexpr int K_TILEB = BN * K_ROWB;        // 17408 | 9216
-  static constexpr int K_DMA = K_TILEB / 1024;       // 17 | 9
+  static constexpr int K_TILEB = BN * K_ROWB;        // 17408 | 9216 | 33792
+  static constexpr int K_DMA = K_TILEB / 1024;       // 17 | 9 | 33
 
   static constexpr int V_ROWB = 2 * kHD;
-  static constexpr int V_TILEB = BN * V_ROWB;        // 16384 | 8192
-  static constexpr int V_DMA = V_TILEB / 1024;       // 16 | 8
+  static constexpr int V_TILEB = BN * V_ROWB;        // 16384 | 8192 | 32768
+  static constexpr int V_DMA = V_TILEB / 1024;       // 16 | 8 | 32
 
   static constexpr int V_ROWS_PER_DMA = 1024 / V_ROWB;
   static constexpr int NKK = kHD / 16;               // 16-wide d steps of QK^T
@@ -85,7 +85,7 @@ struct Geo {
   static_assert(K_TILEB % 1024 == 0 && V_TILEB % 1024 == 0, "tile slots are whole DMA instructions");
   static_assert(V_DMA % 8 == 0, "every wave of 4 or 8 issues the same number of V instructions");
   // physical 16-byte chunk of logical chunk c in V row r is c ^ vswz(r)
-  __host__ __device__ static constexpr int vswz(int r) { return kHD == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+  __host__ __device__ static constexpr int vswz(int r) { return kHD == 64 ? 4 * ((r >> 1) & 1) : 4 * (r & 3); }
 };
 // K tiles rotate through three slots, V tiles through two: K_t stays in LDS
 // for the whole iteration after its QK^T, so a softmax that has to be redone
@@ -141,12 +141,16 @@ constexpr int reads_of(int mode, int i, int nkk, int ndb) { return step_of(mode,
 // kSched: tile schedule; kRing: depth of the fragment prefetch ring of the mma
 // steps (how many steps ahead the LDS reads run); kHD: head dimension.  The
 // overlap and ping-pong schedules are written for HD 128.  A SERIAL4
-// workgroup asks for two waves per SIMD (two workgroups per CU).
+// workgroup asks for two waves per SIMD (two workgroups per CU), except at
+// HD 256: there one workgroup fills the LDS and each wave may use the whole
+// register file of its SIMD (O^T alone is 128 registers).
 template <int kSched, int kRing, int kHD>
-__global__ __launch_bounds__(64 * waves_of(kSched), waves_of(kSched) == 4 ? 2 : 1) void attn_fwd_kernel(Params p) {
+__global__ __launch_bounds__(64 * waves_of(kSched), waves_of(kSched) == 4 && kHD <= 128 ? 2 : 1)
+void attn_fwd_kernel(Params p) {
   using G = Geo<kHD>;
   static_assert(kHD == 128 || kSched == SCHEDULE_SERIAL || kSched == SCHEDULE_SERIAL4,
                 "HD 64 runs the serial schedules");
+  static_assert(kHD <= 128 || kSched == SCHEDULE_SERIAL4, "HD 256 runs the SERIAL4 schedule");
   constexpr int NW = waves_of(kSched);
   constexpr int K_SLOTS = k_slots_of(kSched);
   constexpr int HD = G::HD, NKK = G::NKK, NDB = G::NDB;
@@ -238,9 +242,11 @@ __global__ __launch_bounds__(64 * waves_of(kSched), waves_of(kSched) == 4 ? 2 : 
     k_col[u] = 16u * (uint32_t)(cb < G::KC ? cb : G::KC - 1);  // padding slot: any in-bounds chunk of the row
   }
   const int v_rowl = lane / G::KC;  // row inside the instruction's rows (V_ROWS_PER_DMA * i + v_rowl)
-  // chunk stored at slot lane % KC; the swizzle depends on row bits the
-  // instruction base (a multiple of V_ROWS_PER_DMA >= 4) does not touch
-  const uint32_t v_col = 16u * (uint32_t)((lane % G::KC) ^ G::vswz(v_rowl));
+  // chunk stored at slot lane % KC.  The swizzle reads row bits 0..1; the
+  // rows of this wave's instructions i = wave + NW*u differ by multiples of
+  // NW * V_ROWS_PER_DMA >= 8, so the column is the same for every u.
+  static_assert(NW * G::V_ROWS_PER_DMA % 4 == 0, "one V column per lane");
+  const uint32_t v_col = 16u * (uint32_t)((lane % G::KC) ^ G::vswz(G::V_ROWS_PER_DMA * wave + v_rowl));
   auto stage = [&](int tk, int tv) INL {  // issue this wave's DMA for K tile tk and V tile tv
     tk = __builtin_amdgcn_readfirstlane(tk);
     tv = __builtin_amdgcn_readfirstlane(tv);
@@ -736,6 +742,9 @@ hipError_t launch_attn_fwd(const Params& p, hipStream_t stream) {
     } else if (p.hd == 128) {
       if (r2) LIBATTN_LAUNCH(SCHEDULE_SERIAL4, 2, 128);
       else LIBATTN_LAUNCH(SCHEDULE_SERIAL4, 4, 128);
+    } else if (p.hd == 256) {
+      if (r2) LIBATTN_LAUNCH(SCHEDULE_SERIAL4, 2, 256);
+      else LIBATTN_LAUNCH(SCHEDULE_SERIAL4, 4, 256);
     } else {
       return hipErrorInvalidValue;
     }

@@ -32,7 +32,7 @@ struct Params {
   int causal;
   int neg;           // scale < 0: the kernel negates Q and uses |scale|
   float cs;          // |scale| * log2(e)
-  int hd;            // head dimension: 64 or 128
+  int hd;            // head dimension: 64, 128 or 256
   int schedule;      // Schedule (HD 64: serial only)
   int ring;          // fragment prefetch depth of the mma steps: 2 or 4
   int xcd;           // 1: give each XCD whole (batch, kv head) groups

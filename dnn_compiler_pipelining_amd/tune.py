@@ -31,13 +31,20 @@ TABLE = os.path.join(PKG, "csrc", "tuned_table.h")
 PROFILE = os.path.join(ROOT, "profiles", "schedule_search.json")
 
 SCHEDULES = ("serial", "overlap", "pingpong", "serial4")  # Schedule enum order in csrc/variant.h
-WORKGROUPS_PER_CU = {"serial4": 2}  # the others: one workgroup of 8 waves per CU
+def workgroups_per_cu(schedule: str, hd: int) -> int:
+    """serial4 runs two 4-wave workgroups per CU, except at head dimension 256 (one); the others one of 8 waves."""
+    return 2 if schedule == "serial4" and hd <= 128 else 1
+
+
+def waves_per_simd(schedule: str, hd: int) -> int:
+    return 1 if schedule == "serial4" and hd > 128 else 2
 RINGS = (2, 4)
 SWITCHES = (0, 1)
 SEED = {"schedule": "serial", "ring": 4, "xcd": 1, "lpt": 1}
 
-# resource budget of one variant: 2 waves per SIMD (one 8-wave workgroup, or two 4-wave ones, per CU)
-MAX_VGPR = 256
+# resource budget of one variant: the SIMD's 512 VGPRs + AGPRs per lane shared by its waves, and 160 KiB of
+# LDS shared by the workgroups of a CU
+REGISTER_FILE = 512
 MAX_LDS = 160 * 1024
 
 
@@ -61,14 +68,15 @@ def kernel_resources(asm_path: str):
     return out
 
 
-def check_valid(res: dict, schedule: str = "serial") -> tuple[bool, str]:
-    """A variant is valid when it fits 2 waves per SIMD with no spills and no scratch, and the LDS of the
-    workgroups that share a CU fits it."""
-    if res["vgpr"] + res["agpr"] > MAX_VGPR:
-        return False, "%d VGPRs > %d" % (res["vgpr"] + res["agpr"], MAX_VGPR)
+def check_valid(res: dict, schedule: str = "serial", hd: int = 128) -> tuple[bool, str]:
+    """A variant is valid when its waves per SIMD fit the register file with no spills and no scratch, and the
+    LDS of the workgroups that share a CU fits it."""
+    max_regs = REGISTER_FILE // waves_per_simd(schedule, hd)
+    if res["vgpr"] + res["agpr"] > max_regs:
+        return False, "%d VGPRs > %d" % (res["vgpr"] + res["agpr"], max_regs)
     if res["vgpr_spill"] or res["scratch"]:
         return False, "spills %d VGPRs / %d B scratch" % (res["vgpr_spill"], res["scratch"])
-    wg = WORKGROUPS_PER_CU.get(schedule, 1)
+    wg = workgroups_per_cu(schedule, hd)
     if wg * res["lds"] > MAX_LDS:
         return False, "%d x %d B LDS > %d" % (wg, res["lds"], MAX_LDS)
     return True, "ok"
@@ -83,7 +91,7 @@ def valid_variants(asm_path: str | None = None):
         os.close(fd)
         build.device_asm(asm_path)
     res = kernel_resources(asm_path)
-    return {k: check_valid(v, k[0]) + (v,) for k, v in res.items()}
+    return {k: check_valid(v, k[0], k[2]) + (v,) for k, v in res.items()}
 
 
 # ------------------------------------------------------------------ search (GPU)

@@ -71,7 +71,7 @@ def test_bad_shapes(lib, kw):
     assert call(**kw) == L.ATTN_ERR_SHAPE
 
 
-@pytest.mark.parametrize("D", [96, 256, 127, 32, 1])
+@pytest.mark.parametrize("D", [96, 512, 127, 32, 1, 192])
 def test_unsupported_head_dim(lib, D):
     assert call(D=D) == L.ATTN_ERR_UNSUPPORTED
 
@@ -126,7 +126,7 @@ def test_ex_bad_shapes(lib, kw):
 
 
 def test_ex_limits_and_order(lib):
-    assert call_ex(D=256) == L.ATTN_ERR_UNSUPPORTED
+    assert call_ex(D=512) == L.ATTN_ERR_UNSUPPORTED
     # 64 rows of K/V must span less than 4 GiB: Hkv * 128 * 2 * 64 >= 2^32 is refused
     assert call_ex(Hq=262144, Hkv=262144) == L.ATTN_ERR_UNSUPPORTED
     assert call_ex(q=0, Sq=65) == L.ATTN_ERR_NULL

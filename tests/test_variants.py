@@ -14,7 +14,8 @@ CSRC = os.path.join(tune.PKG, "csrc")
 def test_every_compiled_variant_is_valid():
     vs = tune.valid_variants()
     assert set(vs) == ({(s, r, 128) for s in tune.SCHEDULES for r in tune.RINGS} |
-                       {(s, r, 64) for s in ("serial", "serial4") for r in tune.RINGS})
+                       {(s, r, 64) for s in ("serial", "serial4") for r in tune.RINGS} |
+                       {("serial4", r, 256) for r in tune.RINGS})
     for key, (ok, why, res) in vs.items():
         assert ok, (key, why, res)
         assert res["lds"] > 0 and res["vgpr"] > 0
@@ -37,6 +38,10 @@ def test_check_valid_counts_two_workgroups_per_cu_for_serial4():
     assert tune.check_valid(res, "serial")[0]
     ok, why = tune.check_valid(res, "serial4")
     assert not ok and "LDS" in why
+    # head dimension 256: one workgroup per CU, one wave per SIMD with the whole register file
+    big = dict(vgpr=256, agpr=200, vgpr_spill=0, scratch=0, lds=133120)
+    assert tune.check_valid(big, "serial4", 256)[0]
+    assert not tune.check_valid(big, "serial4", 128)[0]
 
 
 LOOKUP_MAIN = r'''
