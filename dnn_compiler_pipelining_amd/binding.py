@@ -1,11 +1,12 @@
 """Python binding of libattn: argument marshalling only.
 
 The functions carry the names of the C entry points in include/attn.h
-(attn_fwd, attn_fwd_stream, attn_fwd_ex, attn_status_string, attn_version) and
+(attn_fwd, attn_fwd_stream, attn_fwd_ex, attn_fwd_decode,
+attn_decode_workspace_size, attn_status_string, attn_version) and
 include/gemm.h (gemm_f16) and forward to them through ctypes; every step of
-the computation runs in the HIP kernels.  `forward()` and `matmul()` are
-conveniences that allocate the outputs with torch and check the tensors
-first.  There is no fallback: if libattn.so is missing or fails to
+the computation runs in the HIP kernels.  `forward()`, `decode()` and
+`matmul()` are conveniences that allocate the outputs (and the decode
+workspace) with torch and check the tensors first.  There is no fallback: if libattn.so is missing or fails to
 load, every call raises.
 """
 from __future__ import annotations
@@ -25,8 +26,10 @@ ATTN_ERR_UNSUPPORTED = 3
 ATTN_ERR_ALIGN = 4
 ATTN_ERR_HIP = 5
 ATTN_ERR_OVERLAP = 6
+ATTN_ERR_WORKSPACE = 7
 
-EXPORTS = ("attn_fwd", "attn_fwd_stream", "attn_fwd_ex", "attn_status_string", "attn_version", "gemm_f16")
+EXPORTS = ("attn_fwd", "attn_fwd_stream", "attn_fwd_ex", "attn_fwd_decode", "attn_decode_workspace_size",
+           "attn_status_string", "attn_version", "gemm_f16")
 
 GEMM_B_KN = 0  # B stored [K, N]: C = A B
 GEMM_B_NK = 1  # B stored [N, K]: C = A B^T
@@ -57,6 +60,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
             lib.attn_fwd_stream.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
             lib.attn_fwd_ex.restype = i
             lib.attn_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
+            lib.attn_fwd_decode.restype = i
+            lib.attn_fwd_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, ctypes.c_size_t, vp]
+            lib.attn_decode_workspace_size.restype = ctypes.c_size_t
+            lib.attn_decode_workspace_size.argtypes = [i, i, i, i, i, i]
             lib.attn_status_string.restype = ctypes.c_char_p
             lib.attn_status_string.argtypes = [i]
             lib.attn_version.restype = i
@@ -102,6 +109,19 @@ def gemm_f16(a, b, c, M: int, N: int, K: int, b_layout: int, stream) -> int:
     attn_fwd_stream."""
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else (stream or 0)
     return load().gemm_f16(_ptr(a), _ptr(b), _ptr(c), int(M), int(N), int(K), int(b_layout), handle)
+
+
+def attn_fwd_decode(q, k, v, o, lse, B: int, Sq: int, Sk: int, Hq: int, Hkv: int, D: int, causal: int,
+                    scale: float, workspace, workspace_bytes: int, stream) -> int:
+    """C attn_fwd_decode (split-KV path).  `workspace` is a tensor or raw device address of at least
+    attn_decode_workspace_size(...) bytes; `stream` as for attn_fwd_stream."""
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else (stream or 0)
+    return load().attn_fwd_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Sq, Sk, Hq, Hkv, D, int(causal),
+                                  float(scale), _ptr(workspace), int(workspace_bytes), handle)
+
+
+def attn_decode_workspace_size(B: int, Sq: int, Sk: int, Hq: int, Hkv: int, D: int) -> int:
+    return int(load().attn_decode_workspace_size(B, Sq, Sk, Hq, Hkv, D))
 
 
 def attn_status_string(status: int) -> str:
@@ -186,3 +206,38 @@ def matmul(a, b, b_layout: int = GEMM_B_KN, out=None, stream=None):
     if st != ATTN_OK:
         raise AttnError(st)
     return out
+
+
+def decode(q, k, v, causal: bool = True, scale: float | None = None, out=None, lse=None, want_lse: bool = True,
+           workspace=None, stream=None):
+    """The split-KV path on torch tensors (same layout and result as forward()); allocates the workspace
+    with torch unless one is given.  Returns (o, lse)."""
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.float16 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous float16 tensor on a GPU" % name)
+        if t.dim() != 4:
+            raise ValueError("%s must be [B, S, H, D]" % name)
+    B, Sq, Hq, D = q.shape
+    Sk, Hkv = k.shape[1], k.shape[2]
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != D:
+        raise ValueError("shape mismatch: q %s k %s v %s" % (tuple(q.shape), tuple(k.shape), tuple(v.shape)))
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if want_lse and lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    need = attn_decode_workspace_size(B, Sq, Sk, Hq, Hkv, D)
+    if workspace is None:
+        workspace = torch.empty((max(need, 16) + 15) // 16 * 4, dtype=torch.float32, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if hasattr(workspace, "numel") else need
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    with torch.cuda.device(q.device):
+        st = attn_fwd_decode(q, k, v, out, lse, B, Sq, Sk, Hq, Hkv, D, int(bool(causal)), float(scale), workspace,
+                             ws_bytes, stream)
+    if st != ATTN_OK:
+        raise AttnError(st)
+    return out, lse

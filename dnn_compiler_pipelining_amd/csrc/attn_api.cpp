@@ -72,16 +72,9 @@ int validate(const void* q, const void* k, const void* v, const void* o, const f
   return ATTN_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Sq, int Sk, int Hq,
-                int Hkv, int D, int causal, float scale, void* stream) {
-  const int st = validate(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, D, causal, scale);
-  if (st != ATTN_OK) return st;
-
-  libattn::Params p;
+libattn::Params base_params(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Sq, int Sk,
+                            int Hq, int Hkv, int D, int causal, float scale) {
+  libattn::Params p = {};
   p.q = static_cast<const _Float16*>(q);
   p.k = static_cast<const _Float16*>(k);
   p.v = static_cast<const _Float16*>(v);
@@ -98,12 +91,49 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
   p.Hkv = Hkv;
   p.off = causal ? Sk - Sq : 0;
   p.g = Hq / Hkv;
-  p.n_qt = (Sq + 127) / 128;
   p.causal = causal;
   p.neg = scale < 0.f ? 1 : 0;
   p.cs = std::fabs(scale) * 1.44269504088896340736f;
-  const libattn::Variant var = choose_variant(B, Sq, Sk, Hq, Hkv);
   p.hd = D;
+  return p;
+}
+
+// Split-KV plan: the packed (head, query row) rows of a KV group in 128-row
+// tiles, and the keys cut into splits of whole 64-key tiles so that the grid
+// has about kDecodeTarget workgroups (two per CU on 256 CUs, twice over).
+constexpr int64_t kDecodeTarget = 1024;
+struct DecodePlan {
+  int n_pt, n_splits, split_tiles;
+  int64_t ws_o_floats, ws_lse_floats;
+};
+DecodePlan decode_plan(int B, int Sq, int Sk, int Hq, int Hkv, int D) {
+  DecodePlan d;
+  const int64_t g = Hq / Hkv;
+  d.n_pt = (int)((g * Sq + 127) / 128);
+  const int64_t tiles = ((int64_t)Sk + 63) / 64;
+  const int64_t base = (int64_t)B * Hkv * d.n_pt;
+  int64_t want = (kDecodeTarget + base - 1) / base;
+  want = want < 1 ? 1 : (want > tiles ? tiles : want);
+  d.split_tiles = (int)((tiles + want - 1) / want);
+  d.n_splits = (int)((tiles + d.split_tiles - 1) / d.split_tiles);
+  const int64_t rows = (int64_t)B * Hq * Sq;
+  d.ws_lse_floats = rows * d.n_splits;
+  d.ws_o_floats = d.ws_lse_floats * D;
+  return d;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Sq, int Sk, int Hq,
+                int Hkv, int D, int causal, float scale, void* stream) {
+  const int st = validate(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, D, causal, scale);
+  if (st != ATTN_OK) return st;
+
+  libattn::Params p = base_params(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, D, causal, scale);
+  p.n_qt = (Sq + 127) / 128;
+  const libattn::Variant var = choose_variant(B, Sq, Sk, Hq, Hkv);
   // HD 64 runs the serial schedules only, HD 256 the SERIAL4 schedule only
   if (D == 256) p.schedule = libattn::SCHEDULE_SERIAL4;
   else if (D == 128 || var.schedule == libattn::SCHEDULE_SERIAL4) p.schedule = var.schedule;
@@ -129,6 +159,46 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   return attn_fwd_stream(q, k, v, o, lse, B, S, Hq, Hkv, D, causal, scale, nullptr);
 }
 
+size_t attn_decode_workspace_size(int B, int Sq, int Sk, int Hq, int Hkv, int D) {
+  if (B < 1 || Sq < 1 || Sk < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || Sq > kMaxSeq || Sk > kMaxSeq) return 0;
+  if (D != 64 && D != 128 && D != 256) return 0;
+  if ((int64_t)(Hq / Hkv) * Sq > kMaxSeq) return 0;
+  const DecodePlan d = decode_plan(B, Sq, Sk, Hq, Hkv, D);
+  return (size_t)(d.ws_o_floats + d.ws_lse_floats) * sizeof(float);
+}
+
+int attn_fwd_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Sq, int Sk, int Hq,
+                    int Hkv, int D, int causal, float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  const int st = validate(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, D, causal, scale);
+  if (st != ATTN_OK) return st;
+  if ((int64_t)(Hq / Hkv) * Sq > kMaxSeq) return ATTN_ERR_SHAPE;  // packed rows of a KV group stay below 2^30
+  const DecodePlan d = decode_plan(B, Sq, Sk, Hq, Hkv, D);
+  const size_t need = (size_t)(d.ws_o_floats + d.ws_lse_floats) * sizeof(float);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return ATTN_ERR_WORKSPACE;
+  const uint64_t q_bytes = (uint64_t)B * Sq * Hq * D * 2, kv_bytes = (uint64_t)B * Sk * Hkv * D * 2;
+  const uint64_t lse_bytes = (uint64_t)B * Hq * Sq * 4;
+  if (overlaps(workspace, need, q, q_bytes) || overlaps(workspace, need, k, kv_bytes) ||
+      overlaps(workspace, need, v, kv_bytes) || overlaps(workspace, need, o, q_bytes) ||
+      overlaps(workspace, need, lse, lse_bytes))
+    return ATTN_ERR_OVERLAP;
+
+  libattn::Params p = base_params(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, D, causal, scale);
+  const libattn::Variant var = choose_variant(B, Sq, Sk, Hq, Hkv);
+  p.schedule = libattn::SCHEDULE_SERIAL4;
+  p.ring = var.ring;
+  p.xcd = var.xcd;
+  p.lpt = 0;
+  p.pairs = 1;
+  p.n_qt = d.n_pt;
+  p.n_splits = d.n_splits;
+  p.split_tiles = d.split_tiles;
+  p.ws_o = static_cast<float*>(workspace);
+  p.ws_lse = p.ws_o + d.ws_o_floats;
+  if (libattn::grid_blocks_decode(p) < 0) return ATTN_ERR_SHAPE;
+  const hipError_t e = libattn::launch_attn_decode(p, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
 const char* attn_status_string(int status) {
   switch (status) {
     case ATTN_OK: return "ok";
@@ -139,7 +209,8 @@ const char* attn_status_string(int status) {
              "the GEMM K and N multiples of 8";
     case ATTN_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case ATTN_ERR_HIP: return "HIP launch error";
-    case ATTN_ERR_OVERLAP: return "output overlaps an input";
+    case ATTN_ERR_OVERLAP: return "output or workspace overlaps an input or output";
+    case ATTN_ERR_WORKSPACE: return "workspace missing, too small or not 16-byte aligned";
     default: return "unknown status";
   }
 }

@@ -144,13 +144,21 @@ constexpr int reads_of(int mode, int i, int nkk, int ndb) { return step_of(mode,
 // workgroup asks for two waves per SIMD (two workgroups per CU), except at
 // HD 256: there one workgroup fills the LDS and each wave may use the whole
 // register file of its SIMD (O^T alone is 128 registers).
-template <int kSched, int kRing, int kHD>
+//
+// kSplit (SERIAL4 only): split-KV mode for few query rows against many keys
+// (decode).  A workgroup takes one split of the keys (p.split_tiles tiles)
+// and a 128-row tile of the KV group's packed query rows: packed row r is
+// query head c*g + r / Sq, query row r % Sq, so the g heads that share K/V
+// read each K/V tile once.  It writes the split's O (normalised, fp32) and
+// LSE to the workspace; attn_combine_kernel merges the splits.
+template <int kSched, int kRing, int kHD, bool kSplit = false>
 __global__ __launch_bounds__(64 * waves_of(kSched), waves_of(kSched) == 4 && kHD <= 128 ? 2 : 1)
 void attn_fwd_kernel(Params p) {
   using G = Geo<kHD>;
   static_assert(kHD == 128 || kSched == SCHEDULE_SERIAL || kSched == SCHEDULE_SERIAL4,
                 "HD 64 runs the serial schedules");
   static_assert(kHD <= 128 || kSched == SCHEDULE_SERIAL4, "HD 256 runs the SERIAL4 schedule");
+  static_assert(!kSplit || kSched == SCHEDULE_SERIAL4, "split-KV mode runs the SERIAL4 schedule");
   constexpr int NW = waves_of(kSched);
   constexpr int K_SLOTS = k_slots_of(kSched);
   constexpr int HD = G::HD, NKK = G::NKK, NDB = G::NDB;
@@ -175,7 +183,7 @@ void attn_fwd_kernel(Params p) {
   // Workgroups are dealt round-robin to the 8 XCDs.  With p.xcd, give each XCD
   // whole (batch, kv head) groups so that co-resident workgroups share K/V in
   // that XCD's L2; with p.lpt, run the longest causal tiles of a group first.
-  const int items = p.pairs * p.n_qt;  // workgroups per (b, c) group
+  const int items = (kSplit ? p.n_splits : p.pairs) * p.n_qt;  // workgroups per (b, c) group
   const int ngroups = p.B * p.Hkv;
   int group, item;
   {
@@ -191,8 +199,9 @@ void attn_fwd_kernel(Params p) {
   }
   const int b = group / p.Hkv;
   const int c = group % p.Hkv;
-  const int t = p.lpt ? p.n_qt - 1 - item / p.pairs : item / p.pairs;
-  const int hl = NW == 8 ? 2 * (item % p.pairs) + grp : item % p.pairs;  // head index inside the KV group
+  const int t = kSplit ? item / p.n_splits : p.lpt ? p.n_qt - 1 - item / p.pairs : item / p.pairs;
+  const int split = kSplit ? item % p.n_splits : 0;  // split-KV mode: which split of the keys
+  const int hl = kSplit ? 0 : NW == 8 ? 2 * (item % p.pairs) + grp : item % p.pairs;  // head inside the KV group
   const bool active = hl < p.g;
   const int h = c * p.g + (active ? hl : 0);
 
@@ -201,7 +210,34 @@ void attn_fwd_kernel(Params p) {
   const int q0 = t * BM;
   const int qw = q0 + 32 * wq;  // first query row of this wave
   const int kv_tiles_all = (Sk + BN - 1) / BN;
-  const int n_tiles = p.causal ? min(kv_tiles_all, (q0 + off + BM + BN - 1) / BN) : kv_tiles_all;
+  int n_tiles = p.causal ? min(kv_tiles_all, (q0 + off + BM + BN - 1) / BN) : kv_tiles_all;
+  int j_lo = 0;  // first key tile
+
+  // Split-KV mode: this lane's packed row, its query head and query row, and
+  // wave-uniform bounds of the wave's query rows for the causal tests.
+  int h_lane = h, qidx = qw + n, q_lo = qw, q_hi = qw + 31;
+  bool lane_ok = active && qidx < Sq, wave_active = active;
+  if constexpr (kSplit) {
+    const int R = p.g * Sq;
+    const int pr0 = q0 + 32 * wq, pr = pr0 + n;
+    lane_ok = pr < R;
+    const int prc = min(pr, R - 1);
+    h_lane = c * p.g + prc / Sq;
+    qidx = prc % Sq;
+    wave_active = pr0 < R;
+    const int pr_end = min(pr0 + 31, R - 1);
+    q_lo = 0;
+    q_hi = Sq - 1;
+    if (pr_end - pr0 + 1 < Sq) {
+      const int i0 = pr0 % Sq, i1 = pr_end % Sq;
+      if (i1 >= i0) {
+        q_lo = i0;
+        q_hi = i1;
+      }
+    }
+    j_lo = split * p.split_tiles;
+    n_tiles = min(kv_tiles_all, j_lo + p.split_tiles);  // causal: row Sq-1 sees every key
+  }
 
   const _Float16* qb = p.q + (int64_t)b * p.q_bstride + (int64_t)h * HD;
   const _Float16* kb_ = p.k + (int64_t)b * p.kv_bstride + (int64_t)c * HD;
@@ -211,9 +247,11 @@ void attn_fwd_kernel(Params p) {
   f16x8 qf[NKK];
   {
     const int qrow = qw + n;
-    const bool ok = active && qrow < Sq;
+    const bool ok = kSplit ? lane_ok : active && qrow < Sq;
     const uint32_t flip = p.neg ? 0x80008000u : 0u;
-    const _Float16* src = qb + (int64_t)qrow * p.q_sstride + 8 * hh;
+    const _Float16* src = kSplit ? p.q + (int64_t)b * p.q_bstride + (int64_t)h_lane * HD +
+                                       (int64_t)qidx * p.q_sstride + 8 * hh
+                                 : qb + (int64_t)qrow * p.q_sstride + 8 * hh;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       u32x4 u = {0, 0, 0, 0};
@@ -298,8 +336,16 @@ void attn_fwd_kernel(Params p) {
   // tests take wave-uniform copies so that they compile to scalar branches.
   const int qw_u = __builtin_amdgcn_readfirstlane(qw);
   const bool active_u = __builtin_amdgcn_readfirstlane(active ? 1 : 0) != 0;
-  auto skip = [&](int j) INL { return !active_u || (p.causal && j * BN > qw_u + 31 + off); };
-  auto is_masked = [&](int j) INL { return (p.causal && j * BN + BN - 1 > qw_u + off) || j * BN + BN > Sk; };
+  const int qlo_u = __builtin_amdgcn_readfirstlane(q_lo), qhi_u = __builtin_amdgcn_readfirstlane(q_hi);
+  const bool wact_u = __builtin_amdgcn_readfirstlane(wave_active ? 1 : 0) != 0;
+  auto skip = [&](int j) INL {
+    if constexpr (kSplit) return !wact_u || (p.causal && j * BN > qhi_u + off);
+    else return !active_u || (p.causal && j * BN > qw_u + 31 + off);
+  };
+  auto is_masked = [&](int j) INL {
+    if constexpr (kSplit) return (p.causal && j * BN + BN - 1 > qlo_u + off) || j * BN + BN > Sk;
+    else return (p.causal && j * BN + BN - 1 > qw_u + off) || j * BN + BN > Sk;
+  };
 
   // ---- fragments of the mma sTasks
   auto frag_qk = [&](int j, int kk, int sb) INL -> f16x8 {
@@ -355,7 +401,7 @@ void attn_fwd_kernel(Params p) {
   // the compile-time part 32sb + 8(r/4) + r%4 is below lim.
   auto sm_init = [&](int j, auto masked, SmState& st) INL {
     if constexpr (decltype(masked)::value) {
-      const int query = qw + n;
+      const int query = kSplit ? qidx : qw + n;
       const int end = p.causal ? min(Sk, query + off + 1) : Sk;
       st.lim = end - j * BN - 4 * hh;
     }
@@ -509,10 +555,10 @@ void attn_fwd_kernel(Params p) {
     // ---- serial schedule: every wave runs stage-next / QK / softmax / PV per
     // tile; K slot (j+1) % K_SLOTS and V slot (j+1) & 1 were last read in
     // iteration j-1 or earlier
-    stage(0, 0);
+    stage(j_lo, j_lo);
     dma_wait();
     lds_barrier();
-    for (int j = 0; j < n_tiles; ++j) {
+    for (int j = j_lo; j < n_tiles; ++j) {
       stage(j + 1, j + 1);
       if (!skip(j)) {
         block(M_QK{}, j, s, 0, pf, NoSoftmax{});
@@ -702,6 +748,27 @@ void attn_fwd_kernel(Params p) {
     block(M_PV{}, 0, sa, n_tiles - 1, pb, NoSoftmax{});
   }
 
+  // ---- split-KV epilogue: this split's O = O^T / l (fp32) and LSE (natural
+  // log; -inf when the split holds no allowed key for the row) to the workspace
+  if constexpr (kSplit) {
+    if (lane_ok) {
+      const int64_t row = ((int64_t)b * p.Hq + h_lane) * Sq + qidx;
+      float* dst = p.ws_o + (row * p.n_splits + split) * HD;
+      const bool any = l_run > 0.f;
+      const float inv = any ? 1.0f / l_run : 0.f;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          f32x4 ov;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ov[e] = o_acc[db][4 * r4 + e] * inv;
+          *reinterpret_cast<f32x4*>(dst + 32 * db + 8 * r4 + 4 * hh) = ov;
+        }
+      if (hh == 0) p.ws_lse[row * p.n_splits + split] = any ? (m_run + log2f(l_run)) * LN2 : NEG_INF;
+    }
+    return;
+  }
   // ---- epilogue: O = O^T / l (fp16, round to nearest even), LSE in natural log
   if (active) {
     const int qrow = qw + n;
@@ -765,6 +832,80 @@ hipError_t launch_attn_fwd(const Params& p, hipStream_t stream) {
     else LIBATTN_LAUNCH(SCHEDULE_SERIAL, 4, 128);
   }
 #undef LIBATTN_LAUNCH
+  return hipGetLastError();
+}
+
+// ---- combine the splits of the split-KV kernel.  One wave per (b, h, row):
+// LSE = log sum_s exp(LSE_s) and O = sum_s exp(LSE_s - LSE) O_s, the exact
+// merge of softmax partials over disjoint key sets; O is rounded to fp16 (RNE).
+template <int kHD>
+__global__ __launch_bounds__(256) void attn_combine_kernel(Params p, int64_t rows) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int lane = threadIdx.x & 63;
+  constexpr int PER = kHD / 64;  // head-dimension elements per lane
+  const int ns = p.n_splits;
+  const float* ls = p.ws_lse + row * ns;
+  float mx = NEG_INF;
+  for (int s = 0; s < ns; ++s) mx = fmaxf(mx, ls[s]);
+  float sum = 0.f;
+  for (int s = 0; s < ns; ++s) sum += (ls[s] == NEG_INF) ? 0.f : expf(ls[s] - mx);
+  const float L = mx + logf(sum);
+  float acc[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+  for (int s = 0; s < ns; ++s) {
+    if (ls[s] == NEG_INF) continue;
+    const float w = expf(ls[s] - L);
+    const float* src = p.ws_o + (row * ns + s) * kHD + lane * PER;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) acc[e] = fmaf(w, src[e], acc[e]);
+  }
+  const int64_t hs = (int64_t)p.Hq * p.Sq;
+  const int64_t b = row / hs, rem = row % hs;
+  const int h = (int)(rem / p.Sq), i = (int)(rem % p.Sq);
+  _Float16* dst = p.o + b * p.q_bstride + (int64_t)i * p.q_sstride + (int64_t)h * kHD + lane * PER;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) dst[e] = (_Float16)acc[e];
+  if (p.lse && lane == 0) p.lse[row] = L;
+}
+
+int64_t grid_blocks_decode(const Params& p) {
+  const int64_t nb = (int64_t)p.B * p.Hkv * p.n_splits * p.n_qt;
+  return nb > 0x7fffffff ? -1 : nb;
+}
+
+hipError_t launch_attn_decode(const Params& p, hipStream_t stream) {
+  const int64_t nb = grid_blocks_decode(p);
+  if (nb <= 0 || p.schedule != SCHEDULE_SERIAL4) return hipErrorInvalidValue;
+  if (p.ring != 2 && p.ring != 4) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)nb), block(64 * waves_of(SCHEDULE_SERIAL4));
+#define LIBATTN_SPLIT(R, H) hipLaunchKernelGGL((attn_fwd_kernel<SCHEDULE_SERIAL4, R, H, true>), grid, block, 0, stream, p)
+  const bool r2 = p.ring == 2;
+  if (p.hd == 64) {
+    if (r2) LIBATTN_SPLIT(2, 64);
+    else LIBATTN_SPLIT(4, 64);
+  } else if (p.hd == 128) {
+    if (r2) LIBATTN_SPLIT(2, 128);
+    else LIBATTN_SPLIT(4, 128);
+  } else if (p.hd == 256) {
+    if (r2) LIBATTN_SPLIT(2, 256);
+    else LIBATTN_SPLIT(4, 256);
+  } else {
+    return hipErrorInvalidValue;
+  }
+#undef LIBATTN_SPLIT
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t rows = (int64_t)p.B * p.Hq * p.Sq;
+  const int64_t cb = (rows + 3) / 4;
+  if (cb > 0x7fffffff) return hipErrorInvalidValue;
+  if (p.hd == 64)
+    hipLaunchKernelGGL(attn_combine_kernel<64>, dim3((unsigned)cb), dim3(256), 0, stream, p, rows);
+  else if (p.hd == 128)
+    hipLaunchKernelGGL(attn_combine_kernel<128>, dim3((unsigned)cb), dim3(256), 0, stream, p, rows);
+  else
+    hipLaunchKernelGGL(attn_combine_kernel<256>, dim3((unsigned)cb), dim3(256), 0, stream, p, rows);
   return hipGetLastError();
 }
 

@@ -37,10 +37,25 @@ struct Params {
   int ring;          // fragment prefetch depth of the mma steps: 2 or 4
   int xcd;           // 1: give each XCD whole (batch, kv head) groups
   int lpt;           // 1: longest causal query tiles of a group first
+  // split-KV mode (attn_fwd_decode): n_qt counts 128-row tiles of the packed
+  // (head, query row) rows of a KV group; the keys are cut into n_splits
+  // splits of split_tiles 64-key tiles; partial results go to ws_o
+  // [B][Hq][Sq][n_splits][D] and ws_lse [B][Hq][Sq][n_splits] (fp32)
+  int n_splits;
+  int split_tiles;
+  float* ws_o;
+  float* ws_lse;
 };
 
 // Grid size for p (number of workgroups), or -1 if it does not fit an int.
 int64_t grid_blocks(const Params& p);
+
+// Grid size of the split-KV kernel, or -1 if it does not fit an int.
+int64_t grid_blocks_decode(const Params& p);
+
+// Enqueue the split-KV kernel and the kernel that combines its splits into o
+// and lse (SERIAL4 schedule, any ring).  Returns the hipError_t of the launches.
+hipError_t launch_attn_decode(const Params& p, hipStream_t stream);
 
 // Enqueue the forward kernel.  Returns the hipError_t of the launch.
 hipError_t launch_attn_fwd(const Params& p, hipStream_t stream);

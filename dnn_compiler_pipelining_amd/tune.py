@@ -33,11 +33,11 @@ PROFILE = os.path.join(ROOT, "profiles", "schedule_search.json")
 SCHEDULES = ("serial", "overlap", "pingpong", "serial4")  # Schedule enum order in csrc/variant.h
 def workgroups_per_cu(schedule: str, hd: int) -> int:
     """serial4 runs two 4-wave workgroups per CU, except at head dimension 256 (one); the others one of 8 waves."""
-    return 2 if schedule == "serial4" and hd <= 128 else 1
+    return 2 if schedule.startswith("serial4") and hd <= 128 else 1
 
 
 def waves_per_simd(schedule: str, hd: int) -> int:
-    return 1 if schedule == "serial4" and hd > 128 else 2
+    return 1 if schedule.startswith("serial4") and hd > 128 else 2
 RINGS = (2, 4)
 SWITCHES = (0, 1)
 SEED = {"schedule": "serial", "ring": 4, "xcd": 1, "lpt": 1}
@@ -49,12 +49,15 @@ MAX_LDS = 160 * 1024
 
 
 def kernel_resources(asm_path: str):
-    """{(schedule, ring, hd): {vgpr, agpr, vgpr_spill, scratch, lds}} from the AMDGPU metadata of a device asm file."""
+    """{(schedule, ring, hd): {vgpr, agpr, vgpr_spill, scratch, lds}} from the AMDGPU metadata of a device asm file.
+
+    The split-KV instances (attn_fwd_decode) appear under the schedule name "serial4-split".  On gfx950
+    `vgpr` (.vgpr_count) is the unified register count, AGPRs included; `agpr` is the AGPR part of it."""
     text = open(asm_path).read()
     meta = text[text.index("amdhsa.kernels:"):]
     out = {}
     for block in re.split(r"\n  - ", meta)[1:]:
-        m = re.search(r"\.name:\s+\S*attn_fwd_kernelILi(\d)ELi(\d)ELi(\d+)E", block)
+        m = re.search(r"\.name:\s+\S*attn_fwd_kernelILi(\d)ELi(\d)ELi(\d+)ELb([01])E", block)
         if not m:
             continue
 
@@ -62,7 +65,8 @@ def kernel_resources(asm_path: str):
             mm = re.search(r"\." + key + r":\s+(\d+)", block)
             return int(mm.group(1)) if mm else 0
 
-        out[(SCHEDULES[int(m.group(1))], int(m.group(2)), int(m.group(3)))] = dict(
+        sched = SCHEDULES[int(m.group(1))] + ("-split" if m.group(4) == "1" else "")
+        out[(sched, int(m.group(2)), int(m.group(3)))] = dict(
             vgpr=num("vgpr_count"), agpr=num("agpr_count"), vgpr_spill=num("vgpr_spill_count"),
             scratch=num("private_segment_fixed_size"), lds=num("group_segment_fixed_size"))
     return out
@@ -72,8 +76,8 @@ def check_valid(res: dict, schedule: str = "serial", hd: int = 128) -> tuple[boo
     """A variant is valid when its waves per SIMD fit the register file with no spills and no scratch, and the
     LDS of the workgroups that share a CU fits it."""
     max_regs = REGISTER_FILE // waves_per_simd(schedule, hd)
-    if res["vgpr"] + res["agpr"] > max_regs:
-        return False, "%d VGPRs > %d" % (res["vgpr"] + res["agpr"], max_regs)
+    if res["vgpr"] > max_regs:
+        return False, "%d VGPRs (AGPRs included) > %d" % (res["vgpr"], max_regs)
     if res["vgpr_spill"] or res["scratch"]:
         return False, "spills %d VGPRs / %d B scratch" % (res["vgpr_spill"], res["scratch"])
     wg = workgroups_per_cu(schedule, hd)

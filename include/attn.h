@@ -55,6 +55,8 @@
 #ifndef LIBATTN_ATTN_H
 #define LIBATTN_ATTN_H
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -66,7 +68,9 @@ enum {
   ATTN_ERR_UNSUPPORTED = 3, /* D other than 64 or 128, or Hkv * D * 2 * 64 >= 2^32 */
   ATTN_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
   ATTN_ERR_HIP = 5,         /* the HIP runtime reported an error at launch */
-  ATTN_ERR_OVERLAP = 6      /* o overlaps q, k, v or lse */
+  ATTN_ERR_OVERLAP = 6,     /* o overlaps q, k, v or lse; or the workspace overlaps any tensor */
+  ATTN_ERR_WORKSPACE = 7    /* attn_fwd_decode: workspace NULL, smaller than attn_decode_workspace_size(), or not
+                               16-byte aligned */
 };
 
 /* Forward pass on the null stream.  Returns ATTN_OK or an ATTN_ERR_* code. */
@@ -82,6 +86,20 @@ int attn_fwd_stream(const void* q, const void* k, const void* v, void* o, float*
 int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Sq, int Sk, int Hq,
                 int Hkv, int D, int causal, float scale, void* stream);
 
+/* Split-KV path for few query rows against many keys (decode, short chunks): the same operation and
+ * arguments as attn_fwd_ex, computed in two kernels.  The first packs the g = Hq / Hkv query heads of a KV
+ * group with their Sq query rows into 128-row tiles, so each K/V tile is read once for all of them, and
+ * cuts the keys into splits run by different workgroups, each writing its normalised partial O and LSE
+ * (fp32) to `workspace`; the second merges the splits (O = sum_s exp(LSE_s - LSE) O_s, LSE = log sum_s
+ * exp(LSE_s)) into o and lse.  Results match attn_fwd_ex within the attention tolerance, not bit for bit.
+ * `workspace` is caller-owned device memory of at least attn_decode_workspace_size(...) bytes, 16-byte
+ * aligned, not overlapping any tensor; its contents on entry do not matter and are overwritten.  Needs
+ * (Hq / Hkv) * Sq <= 2^30.  Both kernels are enqueued on `stream`; the workspace must not be reused
+ * before they complete. */
+int attn_fwd_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Sq, int Sk, int Hq,
+                    int Hkv, int D, int causal, float scale, void* workspace, size_t workspace_bytes, void* stream);
+/* Workspace bytes attn_fwd_decode needs for these sizes (0 for sizes it rejects). */
+size_t attn_decode_workspace_size(int B, int Sq, int Sk, int Hq, int Hkv, int D);
 /* Static, NUL-terminated description of a status code ("unknown status" for others). */
 const char* attn_status_string(int status);
 

@@ -48,7 +48,7 @@ def test_library_exports_every_declared_symbol(lib):
 def test_version_and_status_strings(lib):
     assert L.attn_version() >= 10000
     assert L.attn_status_string(L.ATTN_OK) == "ok"
-    for code in range(1, 7):
+    for code in range(1, 8):
         s = L.attn_status_string(code)
         assert s and s != "unknown status"
     assert L.attn_status_string(99) == "unknown status"
@@ -181,3 +181,36 @@ def test_gemm_check_order(lib):
     assert gcall(K=130, b_layout=3) == L.ATTN_ERR_SHAPE
     assert gcall(K=130, a=AP + 8) == L.ATTN_ERR_UNSUPPORTED
     assert gcall(a=AP + 8, c=AP) == L.ATTN_ERR_ALIGN
+
+
+# ---------------------------------------------------------------- attn_fwd_decode (split-KV path)
+WSP = 0x90000000
+
+
+def dcall(ws=WSP, ws_bytes=1 << 30, q=QP, k=KP, v=VP, o=OP, lse=LP, B=2, Sq=1, Sk=8192, Hq=64, Hkv=8, D=128,
+          causal=1, scale=0.088):
+    return L.attn_fwd_decode(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, D, causal, scale, ws, ws_bytes, None)
+
+
+def test_decode_workspace_size(lib):
+    # B=2, Sq=1, Sk=8192, 64/8 heads, D=128: 16 packed rows -> one tile per KV group, 16 groups, so the keys
+    # are cut into 64 splits of 2 tiles; partials are 2*64*1*64 rows x (128 + 1) floats
+    assert L.attn_decode_workspace_size(2, 1, 8192, 64, 8, 128) == 2 * 64 * 64 * 129 * 4
+    # a big grid needs no split: one partial per row
+    assert L.attn_decode_workspace_size(64, 1024, 8192, 64, 8, 128) == 64 * 64 * 1024 * 129 * 4
+    for bad in [(0, 1, 8, 8, 8, 128), (1, 1, 8, 9, 2, 128), (1, 1, 8, 8, 8, 96), (1, 0, 8, 8, 8, 128)]:
+        assert L.attn_decode_workspace_size(*bad) == 0
+
+
+def test_decode_validation(lib):
+    need = L.attn_decode_workspace_size(2, 1, 8192, 64, 8, 128)
+    assert dcall(q=0) == L.ATTN_ERR_NULL
+    assert dcall(Sq=2, Sk=1) == L.ATTN_ERR_SHAPE
+    assert dcall(D=96) == L.ATTN_ERR_UNSUPPORTED
+    assert dcall(ws=0) == L.ATTN_ERR_WORKSPACE
+    assert dcall(ws_bytes=need - 4) == L.ATTN_ERR_WORKSPACE
+    assert dcall(ws=WSP + 8) == L.ATTN_ERR_WORKSPACE
+    assert dcall(ws=QP) == L.ATTN_ERR_OVERLAP          # workspace over q
+    assert dcall(ws=LP - 64) == L.ATTN_ERR_OVERLAP     # workspace running into lse
+    assert dcall(q=0, ws=0) == L.ATTN_ERR_NULL          # argument checks come before workspace checks
+    assert L.attn_status_string(L.ATTN_ERR_WORKSPACE) != "unknown status"

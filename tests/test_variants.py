@@ -15,7 +15,8 @@ def test_every_compiled_variant_is_valid():
     vs = tune.valid_variants()
     assert set(vs) == ({(s, r, 128) for s in tune.SCHEDULES for r in tune.RINGS} |
                        {(s, r, 64) for s in ("serial", "serial4") for r in tune.RINGS} |
-                       {("serial4", r, 256) for r in tune.RINGS})
+                       {("serial4", r, 256) for r in tune.RINGS} |
+                       {("serial4-split", r, hd) for r in tune.RINGS for hd in (64, 128, 256)})
     for key, (ok, why, res) in vs.items():
         assert ok, (key, why, res)
         assert res["lds"] > 0 and res["vgpr"] > 0
@@ -23,7 +24,7 @@ def test_every_compiled_variant_is_valid():
 
 @pytest.mark.parametrize("res,reason", [
     (dict(vgpr=257, agpr=0, vgpr_spill=0, scratch=0, lds=1024), "VGPRs"),
-    (dict(vgpr=200, agpr=64, vgpr_spill=0, scratch=0, lds=1024), "VGPRs"),
+    (dict(vgpr=264, agpr=64, vgpr_spill=0, scratch=0, lds=1024), "VGPRs"),
     (dict(vgpr=200, agpr=0, vgpr_spill=3, scratch=12, lds=1024), "spills"),
     (dict(vgpr=200, agpr=0, vgpr_spill=0, scratch=16, lds=1024), "spills"),
     (dict(vgpr=200, agpr=0, vgpr_spill=0, scratch=0, lds=160 * 1024 + 16), "LDS"),
@@ -39,7 +40,7 @@ def test_check_valid_counts_two_workgroups_per_cu_for_serial4():
     ok, why = tune.check_valid(res, "serial4")
     assert not ok and "LDS" in why
     # head dimension 256: one workgroup per CU, one wave per SIMD with the whole register file
-    big = dict(vgpr=256, agpr=200, vgpr_spill=0, scratch=0, lds=133120)
+    big = dict(vgpr=456, agpr=200, vgpr_spill=0, scratch=0, lds=133120)
     assert tune.check_valid(big, "serial4", 256)[0]
     assert not tune.check_valid(big, "serial4", 128)[0]
 
