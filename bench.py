@@ -29,7 +29,10 @@ SQ/GRBM counters (MFMA busy fraction, VALU/MFMA co-execution, LDS activity).
 `--workload gemm_8k_nn` / `gemm_8k_nt` time the fp16 GEMM instead (the 8k
 MatMul: M = N = K = 8192, B stored [K,N] or [N,K]); its line has the same
 fields, with metric FLOPs 2*M*N*K and the fp64 GEMM oracle as cpu_baseline.
-`--all` prints one line per attention workload and per GEMM workload.
+`--workload llama3-70b_decode_b64_s8192` times the split-KV decode path
+(attn_fwd_decode: split kernel + combine kernel per step) and reports HBM
+GB/s (K, V, Q, O and LSE once) against the 8 TB/s HBM roofline.
+`--all` prints one line per attention, GEMM and decode workload.
 """
 from __future__ import annotations
 
@@ -52,12 +55,20 @@ DEFAULT_WORKLOAD = "llama3-70b_b64_s8192"
 KERNEL_NAME = "attn_fwd_kernel"
 GEMM_METRIC = "fp16 GEMM TFLOP/s (8k MatMul, fp32 accumulation) + % of MFMA peak"
 GEMM_KERNEL_NAME = "gemm_kernel"
+DECODE_METRIC = "split-KV decode attention, HBM GB/s (K/V/Q/O/LSE once) + % of HBM peak"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 
 
 def is_gemm(workload: str) -> bool:
     from dnn_compiler_pipelining_amd import inputs
 
     return workload in inputs.GEMM_BY_NAME
+
+
+def is_decode(workload: str) -> bool:
+    from dnn_compiler_pipelining_amd import inputs
+
+    return workload in inputs.DECODE_BY_NAME
 
 
 def kernel_name(workload: str) -> str:
@@ -197,6 +208,73 @@ def time_gemm(w, steps: int, warmup: int, pmc_copy: int = 0):
     del a, b, c
     torch.cuda.empty_cache()
     return wall_ms, kernel_ms, ok
+
+
+def time_decode(w, steps: int, warmup: int):
+    import torch
+
+    from dnn_compiler_pipelining_amd import binding, inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log("[bench] %s: generating seeded inputs" % w.name)
+    q, k, v = inputs.make_decode_inputs(w, dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device=dev)
+    need = binding.attn_decode_workspace_size(w.B, w.Sq, w.Sk, w.Hq, w.Hkv, w.D)
+    ws = torch.empty(((need + 3) // 4,), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    torch.cuda.synchronize()
+
+    def step():
+        binding.decode(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse, workspace=ws, stream=stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    log("[bench] %s: %d timed steps" % (w.name, steps))
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ok = bool(torch.isfinite(o).all().item())
+    del q, k, v, o, lse, ws
+    torch.cuda.empty_cache()
+    return (t1 - t0) * 1e3 / steps, e0.elapsed_time(e1) / steps, ok
+
+
+def cpu_baseline_decode(w, target_s: float = 15.0):
+    """Times the fp64 oracle on (head, query row) outputs of batch entries in turn, in the decode metric's
+    unit: each output row accounts for its share of the algorithmic bytes."""
+    import numpy as np
+
+    from dnn_compiler_pipelining_amd import inputs
+    from oracle import oracle as oracle_mod
+
+    threads = oracle_mod.default_threads()
+    per_row = w.bytes / (w.B * w.Hq * w.Sq)
+    rows = secs = 0.0
+    b = 0
+    while secs < target_s and b < w.B:
+        q = inputs.make_slice(w.Sq, w.Hq, w.D, w.seed, inputs.Q, b).numpy()
+        k = inputs.make_slice(w.Sk, w.Hkv, w.D, w.seed, inputs.K, b).numpy()
+        v = inputs.make_slice(w.Sk, w.Hkv, w.D, w.seed, inputs.V, b).numpy()
+        hs = np.repeat(np.arange(w.Hq, dtype=np.int32), w.Sq)
+        rs = np.tile(np.arange(w.Sq, dtype=np.int32), w.Hq)
+        t = time.perf_counter()
+        oracle_mod.attn_rows(q, k, v, hs, rs, w.causal, w.scale, nthreads=threads)
+        secs += time.perf_counter() - t
+        rows += len(hs)
+        b += 1
+    log("[bench] cpu oracle: %d threads, %d batch entries in %.1f s" % (threads, b, secs))
+    return {"value": round(rows * per_row / secs / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "all %d (head, row) outputs of %d batch entries of %s, fp64, %.1f s wall; bytes = the "
+                      "workload's algorithmic bytes per output row" % (w.Hq * w.Sq, b, w.name, secs)}
 
 
 # ------------------------------------------------------------------ CPU oracle baseline
@@ -447,9 +525,29 @@ def main():
               "--gpus %d (WORLD_SIZE %d) is not supported" % (args.gpus, world), file=sys.stderr)
         return 2
 
-    names = ([w.name for w in inputs.WORKLOADS] + [w.name for w in inputs.GEMM_WORKLOADS]) if args.all \
-        else [args.workload]
+    names = ([w.name for w in inputs.WORKLOADS] + [w.name for w in inputs.GEMM_WORKLOADS] +
+             [w.name for w in inputs.DECODE_WORKLOADS]) if args.all else [args.workload]
     for name in names:
+        if is_decode(name):
+            w = inputs.DECODE_BY_NAME[name]
+            wall_ms, kernel_ms, ok = time_decode(w, args.steps, args.warmup)
+            if not ok:
+                log("[bench] non-finite output")
+                return 1
+            value = w.bytes / (wall_ms * 1e-3) / 1e9
+            achieved = w.bytes / (kernel_ms * 1e-3) / 1e9
+            line = {"metric": DECODE_METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+                    "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall_ms, 4),
+                    "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+                    "data": "synthetic: seeded i.i.d. N(0,1) fp16 Q/K/V", "config": w.describe(),
+                    "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                                 "kernel": "attn_fwd_kernel (split-KV) + attn_combine_kernel",
+                                 "kernel_ms": round(kernel_ms, 4), "bytes_per_step": w.bytes}}
+            if not args.no_cpu_baseline and not args.all:
+                line["cpu_baseline"] = cpu_baseline_decode(w, args.cpu_seconds)
+            print(json.dumps(line), flush=True)
+            continue
         gemm = is_gemm(name)
         if gemm:
             w = inputs.GEMM_BY_NAME[name]

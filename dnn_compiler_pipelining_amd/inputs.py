@@ -189,3 +189,46 @@ def make_gemm_inputs(w: GemmWorkload, device="cpu"):
     br, bc = w.b_shape()
     b = make_matrix(br, bc, w.seed, MAT_B, w.dist, w.lim, device)
     return a, b
+
+
+# ---------------------------------------------------------------- decode inputs
+#
+# Single-token decode at LLaMA3-70B head shapes against an 8192-key cache (the
+# pages' longest FlashAttention sequence), batch 64: the split-KV path
+# (attn_fwd_decode).  Q, K and V follow the attention recipe above, with
+# per-(tensor, batch entry) seeds; Q has Sq rows and K/V have Sk rows.
+
+
+@dataclass(frozen=True)
+class DecodeWorkload:
+    name: str
+    B: int
+    Sq: int
+    Sk: int
+    Hq: int
+    Hkv: int
+    D: int
+    causal: bool
+    seed: int
+    scale: float = SCALE_D128
+
+    @property
+    def bytes(self) -> float:
+        """Algorithmic HBM bytes: K and V read once, Q read, O written (fp16), LSE written (fp32)."""
+        return 2.0 * 2 * self.B * self.Sk * self.Hkv * self.D + 2.0 * 2 * self.B * self.Sq * self.Hq * self.D + \
+            4.0 * self.B * self.Hq * self.Sq
+
+    def describe(self) -> dict:
+        return {"workload": self.name, "B": self.B, "Sq": self.Sq, "Sk": self.Sk, "Hq": self.Hq, "Hkv": self.Hkv,
+                "D": self.D, "causal": self.causal, "path": "attn_fwd_decode (split-KV + combine)",
+                "layout": "[B,S,H,D] fp16 in/out, LSE [B,Hq,Sq] fp32", "scale": self.scale, "seed": self.seed}
+
+
+DECODE_WORKLOADS = [DecodeWorkload("llama3-70b_decode_b64_s8192", 64, 1, 8192, 64, 8, 128, True, 21)]
+DECODE_BY_NAME = {w.name: w for w in DECODE_WORKLOADS}
+
+
+def make_decode_inputs(w: DecodeWorkload, device="cpu"):
+    """(q, k, v): [B,Sq,Hq,D], [B,Sk,Hkv,D], [B,Sk,Hkv,D] fp16."""
+    return (make_tensor(w.B, w.Sq, w.Hq, w.D, w.seed, Q, device), make_tensor(w.B, w.Sk, w.Hkv, w.D, w.seed, K, device),
+            make_tensor(w.B, w.Sk, w.Hkv, w.D, w.seed, V, device))
