@@ -100,8 +100,10 @@ libattn::Params base_params(const void* q, const void* k, const void* v, void* o
 
 // Split-KV plan: the packed (head, query row) rows of a KV group in 128-row
 // tiles, and the keys cut into splits of whole 64-key tiles so that the grid
-// has about kDecodeTarget workgroups (two per CU on 256 CUs, twice over).
-constexpr int64_t kDecodeTarget = 1024;
+// has about kDecodeTarget workgroups: one round of two per CU on 256 CUs.
+// Measured on MI355X, fewer and longer splits stream K/V faster than more and
+// shorter ones (each workgroup pays its Q load and first-tile latency once).
+constexpr int64_t kDecodeTarget = 512;
 struct DecodePlan {
   int n_pt, n_splits, split_tiles;
   int64_t ws_o_floats, ws_lse_floats;
@@ -115,6 +117,12 @@ DecodePlan decode_plan(int B, int Sq, int Sk, int Hq, int Hkv, int D) {
   int64_t want = (kDecodeTarget + base - 1) / base;
   want = want < 1 ? 1 : (want > tiles ? tiles : want);
   d.split_tiles = (int)((tiles + want - 1) / want);
+  // LIBATTN_DECODE_SPLIT_TILES=n (read by both attn_decode_workspace_size and
+  // attn_fwd_decode) fixes the split length instead, for tuning
+  if (const char* e = std::getenv("LIBATTN_DECODE_SPLIT_TILES")) {
+    const long n = std::atol(e);
+    if (n >= 1 && n <= (1 << 24)) d.split_tiles = (int)(n < tiles ? n : tiles);
+  }
   d.n_splits = (int)((tiles + d.split_tiles - 1) / d.split_tiles);
   const int64_t rows = (int64_t)B * Hq * Sq;
   d.ws_lse_floats = rows * d.n_splits;

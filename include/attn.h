@@ -95,7 +95,8 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
  * `workspace` is caller-owned device memory of at least attn_decode_workspace_size(...) bytes, 16-byte
  * aligned, not overlapping any tensor; its contents on entry do not matter and are overwritten.  Needs
  * (Hq / Hkv) * Sq <= 2^30.  Both kernels are enqueued on `stream`; the workspace must not be reused
- * before they complete. */
+ * before they complete.  The split length is chosen for about 512 workgroups; the environment variable
+ * LIBATTN_DECODE_SPLIT_TILES=n (64-key tiles per split, read by both functions below) overrides it. */
 int attn_fwd_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Sq, int Sk, int Hq,
                     int Hkv, int D, int causal, float scale, void* workspace, size_t workspace_bytes, void* stream);
 /* Workspace bytes attn_fwd_decode needs for these sizes (0 for sizes it rejects). */

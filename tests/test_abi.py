@@ -193,9 +193,10 @@ def dcall(ws=WSP, ws_bytes=1 << 30, q=QP, k=KP, v=VP, o=OP, lse=LP, B=2, Sq=1, S
 
 
 def test_decode_workspace_size(lib):
-    # B=2, Sq=1, Sk=8192, 64/8 heads, D=128: 16 packed rows -> one tile per KV group, 16 groups, so the keys
-    # are cut into 64 splits of 2 tiles; partials are 2*64*1*64 rows x (128 + 1) floats
-    assert L.attn_decode_workspace_size(2, 1, 8192, 64, 8, 128) == 2 * 64 * 64 * 129 * 4
+    # B=2, Sq=1, Sk=8192, 64/8 heads, D=128: 8 packed rows -> one tile per KV group, 16 groups, so the 128 key
+    # tiles are cut into 32 splits of 4 tiles (about 512 workgroups); partials are 2*64*1 rows x 32 splits x
+    # (128 + 1) floats
+    assert L.attn_decode_workspace_size(2, 1, 8192, 64, 8, 128) == 2 * 64 * 32 * 129 * 4
     # a big grid needs no split: one partial per row
     assert L.attn_decode_workspace_size(64, 1024, 8192, 64, 8, 128) == 64 * 64 * 1024 * 129 * 4
     for bad in [(0, 1, 8, 8, 8, 128), (1, 1, 8, 9, 2, 128), (1, 1, 8, 8, 8, 96), (1, 0, 8, 8, 8, 128)]:
