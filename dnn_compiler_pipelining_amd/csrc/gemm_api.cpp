@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <cstdlib>
 
 #include "gemm.h"
 #include "gemm_kernel.h"
@@ -13,6 +14,7 @@ namespace {
 
 constexpr int kMaxMN = 1 << 24;  // M, N <= 2^24 and K <= 2^22 keep every
 constexpr int kMaxK = 1 << 22;   // per-tile load offset below 2^32
+constexpr int kDefaultWaves = 8;
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
@@ -59,6 +61,12 @@ int gemm_f16(const void* a, const void* b, void* c, int M, int N, int K, int b_l
   p.ntm = (M + 255) / 256;
   p.ntn = (N + 255) / 256;
   p.nkt = (K + 63) / 64;
+  // LIBATTN_GEMM_WAVES=4|8 picks the workgroup shape (read at each call)
+  p.waves = kDefaultWaves;
+  if (const char* e = std::getenv("LIBATTN_GEMM_WAVES")) {
+    const int w = std::atoi(e);
+    if (w == 4 || w == 8) p.waves = w;
+  }
   if ((int64_t)p.ntm * p.ntn > 0x7fffffff) return ATTN_ERR_SHAPE;
   const hipError_t e = libattn::launch_gemm(p, s);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;

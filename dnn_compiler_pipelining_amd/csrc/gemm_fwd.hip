@@ -10,9 +10,12 @@
 // with fragments conformed to the instruction's layout, same page, section
 // 5.2.2).
 //
-// One workgroup = 8 waves computes a 256 x 256 tile of C over 64-deep K
-// tiles.  Wave (wm, wn) = (w % 2, w / 2) owns rows 128 wm .. +128 and columns
-// 64 wn .. +64 of the tile: 4 x 2 accumulators of 32 x 32.  The MFMA computes
+// One workgroup computes a 256 x 256 tile of C over 64-deep K tiles, with 8
+// waves (two per SIMD) or 4 (one per SIMD, kNW = 4).  Wave (wm, wn) =
+// (w % 2, w / 2) owns rows 128 wm .. +128 of the tile and columns
+// 64 wn .. +64 (8 waves: 4 x 2 accumulators of 32 x 32) or 128 wn .. +128
+// (4 waves: 4 x 4 accumulators, 256 registers that live in AGPRs; half the
+// LDS reads per MFMA).  The MFMA computes
 // the transposed block, D[n][m] = sum_k B^T[n][k] A^T[k][m], so that each lane
 // holds one row m of C and runs of 4 consecutive columns n: the epilogue
 // writes 8-byte runs.
@@ -41,13 +44,16 @@
 namespace libattn {
 
 constexpr int GBM = 256, GBN = 256, GBK = 64;
-constexpr int GTHREADS = 512;
 constexpr int G_TILEB = 256 * GBK * 2;  // bytes of one A or B slot (32 KiB)
 constexpr int G_BAND = 8;               // output tile rows per raster band
 static_assert(4 * G_TILEB <= 160 * 1024, "two slots of A and B fit the LDS");
 
-template <int kBL>  // 0: B stored [K][N]; 1: B stored [N][K]
-__global__ __launch_bounds__(GTHREADS, 1) void gemm_kernel(GemmParams p) {
+template <int kBL, int kNW>  // kBL 0: B stored [K][N]; 1: B stored [N][K].  kNW: waves per workgroup, 8 or 4
+__global__ __launch_bounds__(64 * kNW, 1) void gemm_kernel(GemmParams p) {
+  static_assert(kNW == 8 || kNW == 4, "8 or 4 waves");
+  constexpr int WNX = kNW == 8 ? 64 : 128;  // columns of C per wave
+  constexpr int NFR = WNX / 32;             // 32-column accumulator blocks per wave
+  constexpr int UPW = 32 / kNW;             // direct-load instructions per wave per tile, for A and for B
   __shared__ __attribute__((aligned(1024))) char a_smem[2 * G_TILEB];
   __shared__ __attribute__((aligned(1024))) char b_smem[2 * G_TILEB];
   LDS char* const a_lds = (LDS char*)a_smem;
@@ -75,8 +81,8 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_kernel(GemmParams p) {
   const int m0 = tm * GBM, n0 = tn * GBN;
   const int M = p.M, N = p.N, K = p.K;
 
-  // ---- per-lane direct-load maps.  Wave w issues instructions w + 8u
-  // (u = 0..3) of each 32-instruction tile.
+  // ---- per-lane direct-load maps.  Wave w issues instructions w + kNW u
+  // (u = 0..UPW-1) of each 32-instruction tile.
   //   [row][k] tiles (A, and B stored [N][K]): instruction i holds rows
   //     8i .. 8i+7; lane l has row 8i + l/8 and LDS chunk l % 8, i.e. logical
   //     chunk (l % 8) ^ ((row >> 1) & 7), the same for every u.
@@ -84,9 +90,9 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_kernel(GemmParams p) {
   //     lane l has k row 2i + l/32 and LDS chunk l % 32, i.e. logical chunk
   //     (l % 32) ^ (4 * (row & 3)), the same for every u.
   const uint32_t a_lds_base = (uint32_t)(uintptr_t)a_lds, b_lds_base = (uint32_t)(uintptr_t)b_lds;
-  const int rk_row0 = 8 * wave + (lane >> 3);  // + 64u
+  const int rk_row0 = 8 * wave + (lane >> 3);  // + 8 kNW u
   const int rk_chunk = (lane & 7) ^ ((4 * wave + (lane >> 4)) & 7);
-  const int kn_row0 = 2 * wave + (lane >> 5);  // + 16u
+  const int kn_row0 = 2 * wave + (lane >> 5);  // + 2 kNW u
   const int kn_chunk = (lane & 31) ^ (4 * ((2 * wave + (lane >> 5)) & 3));
   const int kchunks = K >> 3;  // 16-byte chunks per row of A (and of B stored [N][K])
 
@@ -98,29 +104,29 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_kernel(GemmParams p) {
       const char* base = (const char*)(p.a + (int64_t)m0 * K + k0);
       const int c = min(rk_chunk, kchunks - 1 - (k0 >> 3));
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int row = min(rk_row0 + 64 * u, M - 1 - m0);
+      for (int u = 0; u < UPW; ++u) {
+        const int row = min(rk_row0 + 8 * kNW * u, M - 1 - m0);
         dma16(base, (uint32_t)row * (uint32_t)(2 * K) + 16u * c,
-              a_lds_base + slot_off + 1024u * (uint32_t)(wave_s + 8 * u));
+              a_lds_base + slot_off + 1024u * (uint32_t)(wave_s + kNW * u));
       }
     }
     if constexpr (kBL == 1) {
       const char* base = (const char*)(p.b + (int64_t)n0 * K + k0);
       const int c = min(rk_chunk, kchunks - 1 - (k0 >> 3));
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int row = min(rk_row0 + 64 * u, N - 1 - n0);
+      for (int u = 0; u < UPW; ++u) {
+        const int row = min(rk_row0 + 8 * kNW * u, N - 1 - n0);
         dma16(base, (uint32_t)row * (uint32_t)(2 * K) + 16u * c,
-              b_lds_base + slot_off + 1024u * (uint32_t)(wave_s + 8 * u));
+              b_lds_base + slot_off + 1024u * (uint32_t)(wave_s + kNW * u));
       }
     } else {
       const char* base = (const char*)(p.b + (int64_t)k0 * N + n0);
       const int c = min(kn_chunk, (N >> 3) - 1 - (n0 >> 3));
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int row = min(kn_row0 + 16 * u, K - 1 - k0);
+      for (int u = 0; u < UPW; ++u) {
+        const int row = min(kn_row0 + 2 * kNW * u, K - 1 - k0);
         dma16(base, (uint32_t)row * (uint32_t)(2 * N) + 16u * c,
-              b_lds_base + slot_off + 1024u * (uint32_t)(wave_s + 8 * u));
+              b_lds_base + slot_off + 1024u * (uint32_t)(wave_s + kNW * u));
       }
     }
   };
@@ -132,15 +138,16 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_kernel(GemmParams p) {
     const u32x4 z = {0, 0, 0, 0};
     if (rk_chunk >= kchunks - (k0 >> 3)) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        *(LDS u32x4*)(a_lds + slot_off + 1024 * (wave_s + 8 * u) + 16 * lane) = z;
-        if constexpr (kBL == 1) *(LDS u32x4*)(b_lds + slot_off + 1024 * (wave_s + 8 * u) + 16 * lane) = z;
+      for (int u = 0; u < UPW; ++u) {
+        *(LDS u32x4*)(a_lds + slot_off + 1024 * (wave_s + kNW * u) + 16 * lane) = z;
+        if constexpr (kBL == 1) *(LDS u32x4*)(b_lds + slot_off + 1024 * (wave_s + kNW * u) + 16 * lane) = z;
       }
     }
     if constexpr (kBL == 0) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (kn_row0 + 16 * u >= K - k0) *(LDS u32x4*)(b_lds + slot_off + 1024 * (wave_s + 8 * u) + 16 * lane) = z;
+      for (int u = 0; u < UPW; ++u)
+        if (kn_row0 + 2 * kNW * u >= K - k0)
+          *(LDS u32x4*)(b_lds + slot_off + 1024 * (wave_s + kNW * u) + 16 * lane) = z;
     }
   };
 
@@ -152,23 +159,24 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_kernel(GemmParams p) {
     rk_frag[kk] = (lane & 31) * 128 + 16 * ((2 * kk + (lane >> 5)) ^ ((lane >> 1) & 7));
   // B stored [K][N]: lane (group g = l/16, s = l%16) of a transpose read
   // addresses k row 8(g/2) + s/4 (+4 for the second read, +16kk per step) and
-  // columns n = 64wn + 32nf + 16(g%2) + 4(s%4) .. +3.
-  int kn_frag[2];
+  // columns n = WNX wn + 32nf + 16(g%2) + 4(s%4) .. +3.
+  int kn_frag[NFR];
   {
     const int g = lane >> 4, s = lane & 15;
     const int row = 8 * (g >> 1) + (s >> 2);
-    const int chunk = 8 * wn + 2 * (g & 1) + ((s & 3) >> 1);  // 16-byte chunk for nf = 0
+    const int chunk = (WNX / 8) * wn + 2 * (g & 1) + ((s & 3) >> 1);  // 16-byte chunk for nf = 0
     const int f0 = row * 512 + ((chunk ^ (4 * (s >> 2))) << 4) + ((s & 1) << 3);
-    kn_frag[0] = f0;
-    kn_frag[1] = f0 ^ 64;  // nf = 1: chunk + 4, i.e. bit 2 of the chunk, which the swizzle XORs too
+    // nf adds 4nf to the chunk: bits 2..3, which are zero in the nf = 0 chunk and which the swizzle XORs too
+#pragma unroll
+    for (int nf = 0; nf < NFR; ++nf) kn_frag[nf] = f0 ^ (64 * nf);
   }
 
   auto frag_a = [&](int slot, int kk, int mf) INL -> f16x8 {  // B operand: A^T[k][m], m = 128wm + 32mf + l%32
     return *(const LDS f16x8*)(a_lds + slot * G_TILEB + (128 * wm + 32 * mf) * 128 + rk_frag[kk]);
   };
-  auto frag_b = [&](int slot, int kk, int nf) INL -> f16x8 {  // A operand: B^T[n][k], n = 64wn + 32nf + l%32
+  auto frag_b = [&](int slot, int kk, int nf) INL -> f16x8 {  // A operand: B^T[n][k], n = WNX wn + 32nf + l%32
     if constexpr (kBL == 1) {
-      return *(const LDS f16x8*)(b_lds + slot * G_TILEB + (64 * wn + 32 * nf) * 128 + rk_frag[kk]);
+      return *(const LDS f16x8*)(b_lds + slot * G_TILEB + (WNX * wn + 32 * nf) * 128 + rk_frag[kk]);
     } else {
       const LDS char* a = b_lds + slot * G_TILEB + kn_frag[nf] + 16 * kk * 512;
       const f16x4 h1 = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS i16x4*)a));
@@ -177,36 +185,38 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_kernel(GemmParams p) {
     }
   };
 
-  f32x16 acc[4][2];
+  f32x16 acc[4][NFR];
 #pragma unroll
   for (int mf = 0; mf < 4; ++mf)
 #pragma unroll
-    for (int nf = 0; nf < 2; ++nf) acc[mf][nf] = f32x16{};
+    for (int nf = 0; nf < NFR; ++nf) acc[mf][nf] = f32x16{};
 
-  // ---- mma task: a K tile is 4 substeps of 16 k, 8 MFMAs each (mf-major).
-  // Fragments are double-buffered by substep; the 6 (or 8, with transpose
-  // reads) fragment reads of the next substep are issued one after each of
-  // the first MFMAs of the current one (pinned below), so LDS latency hides
-  // behind the matrix core.
-  constexpr int kReads = kBL == 1 ? 6 : 8;
-  f16x8 bf[2][2], af[2][4];
+  // ---- mma task: a K tile is 4 substeps of 16 k, 4 NFR MFMAs each
+  // (mf-major).  Fragments are double-buffered by substep; the NFR + 4 (or
+  // 2 NFR + 4, with transpose reads) fragment reads of the next substep are
+  // issued one after each of the first MFMAs of the current one (pinned
+  // below), so LDS latency hides behind the matrix core.
+  constexpr int kSteps = 4 * NFR;
+  constexpr int kReads = kBL == 1 ? NFR + 4 : 2 * NFR + 4;
+  static_assert(kReads <= kSteps, "one read after each MFMA at most");
+  f16x8 bf[2][NFR], af[2][4];
   auto load_frags = [&](int slot, auto kc) INL {
     constexpr int kk = decltype(kc)::value;
 #pragma unroll
-    for (int nf = 0; nf < 2; ++nf) bf[kk & 1][nf] = frag_b(slot, kk, nf);
+    for (int nf = 0; nf < NFR; ++nf) bf[kk & 1][nf] = frag_b(slot, kk, nf);
 #pragma unroll
     for (int mf = 0; mf < 4; ++mf) af[kk & 1][mf] = frag_a(slot, kk, mf);
   };
   auto mfmas = [&](auto kc) INL {
     constexpr int kk = decltype(kc)::value;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int mf = j >> 1, nf = j & 1;
+    for (int j = 0; j < kSteps; ++j) {
+      const int mf = j / NFR, nf = j % NFR;
       acc[mf][nf] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[kk & 1][nf], af[kk & 1][mf], acc[mf][nf], 0, 0, 0);
     }
   };
   auto pin_interleaved = [&]() INL {  // MFMA j, then read j
-    static_for<8>([&](auto jc) INL {
+    static_for<kSteps>([&](auto jc) INL {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       if constexpr (decltype(jc)::value < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     });
@@ -259,10 +269,10 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_kernel(GemmParams p) {
     if (m >= M) continue;
     _Float16* crow = p.c + (int64_t)m * N;
 #pragma unroll
-    for (int nf = 0; nf < 2; ++nf)
+    for (int nf = 0; nf < NFR; ++nf)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        const int n = n0 + 64 * wn + 32 * nf + 8 * r4 + 4 * h;
+        const int n = n0 + WNX * wn + 32 * nf + 8 * r4 + 4 * h;
         if (n < N) {
           f16x4 hv;
 #pragma unroll
@@ -282,12 +292,17 @@ __global__ void gemm_zero_kernel(u32x4* c, int64_t n16) {
 hipError_t launch_gemm(const GemmParams& p, hipStream_t stream) {
   const int64_t nb = (int64_t)p.ntm * p.ntn;
   if (nb <= 0 || nb > 0x7fffffff || p.nkt < 1) return hipErrorInvalidValue;
-  if (p.b_layout == 0)
-    hipLaunchKernelGGL(gemm_kernel<0>, dim3((unsigned)nb), dim3(GTHREADS), 0, stream, p);
-  else if (p.b_layout == 1)
-    hipLaunchKernelGGL(gemm_kernel<1>, dim3((unsigned)nb), dim3(GTHREADS), 0, stream, p);
-  else
+  if (p.waves != 4 && p.waves != 8) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)nb), block(64 * p.waves);
+  if (p.b_layout == 0) {
+    if (p.waves == 8) hipLaunchKernelGGL((gemm_kernel<0, 8>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((gemm_kernel<0, 4>), grid, block, 0, stream, p);
+  } else if (p.b_layout == 1) {
+    if (p.waves == 8) hipLaunchKernelGGL((gemm_kernel<1, 8>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((gemm_kernel<1, 4>), grid, block, 0, stream, p);
+  } else {
     return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

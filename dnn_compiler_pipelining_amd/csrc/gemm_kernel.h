@@ -14,6 +14,7 @@ struct GemmParams {
   int b_layout;
   int ntm, ntn;       // 256 x 256 output tiles along M and N
   int nkt;            // 64-deep K tiles
+  int waves;          // waves per workgroup: 8 (two per SIMD) or 4 (one per SIMD)
 };
 
 // Enqueue C = A B (or A B^T) for K >= 1.  Returns the hipError_t of the launch.

@@ -163,3 +163,19 @@ def test_validation_launches_nothing():
     assert st == binding.ATTN_ERR_UNSUPPORTED
     torch.cuda.synchronize()
     assert bool(torch.isnan(c).all().item())
+
+
+@pytest.mark.parametrize("layout", [KN, NK], ids=["kn", "nk"])
+@pytest.mark.parametrize("M,N,K", [(300, 264, 136), (513, 520, 520), (1000, 1024, 1000), (64, 8, 4096)], ids=str)
+def test_four_wave_workgroups_give_the_same_bits(monkeypatch, M, N, K, layout):
+    """Workgroups of 4 waves (128 x 128 per wave) and of 8 (128 x 64) feed every accumulator the same MFMAs in
+    the same order, so they give the same bits; the 4-wave result also meets the oracle bar."""
+    a, b = mats(M, N, K, layout, seed=500 + M + K)
+    ad, bd = a.cuda(), b.cuda()
+    monkeypatch.setenv("LIBATTN_GEMM_WAVES", "8")
+    c8 = run(ad, bd, layout, M, N, K)
+    monkeypatch.setenv("LIBATTN_GEMM_WAVES", "4")
+    c4 = run(ad, bd, layout, M, N, K)
+    assert torch.equal(c8, c4)
+    check_normal(c4.cpu().numpy(), G.gemm(a.numpy(), b.numpy(), layout), G.abs_products(a.numpy(), b.numpy(), layout),
+                 K, "4 waves M%d N%d K%d layout %d" % (M, N, K, layout))
