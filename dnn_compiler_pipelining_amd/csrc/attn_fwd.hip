@@ -48,10 +48,14 @@ __host__ __device__ constexpr int waves_of(int sched) { return sched == SCHEDULE
 constexpr float NEG_INF = -__builtin_inff();
 constexpr float M_INIT = -1e30f; // finite start for the running max
 constexpr float LN2 = 0.693147180559945309f;
-// Lazy rescaling: the running max (log2 units) is only raised when a tile's
-// max exceeds it by more than TAU, so P = 2^(s - m) stays below 2^TAU; the
-// final O / l and LSE = m + log2(l) are exact for any m.
-constexpr float TAU = 8.0f;
+// Sum-checked lazy rescaling: a tile's exponentials are first taken against
+// the running max m (log2 units) as it stands.  If no row's sum over the tile
+// exceeds RS_MAX, every P of the tile is at most RS_MAX (fp16 P and the fp32
+// sums stay in range) and m stays; otherwise -- in practice only on a row's
+// first tile -- m is raised to the tile max and the exponentials are redone.
+// No tile max is needed in the common case, and the final O / l and
+// LSE = m + log2(l) are exact for any m.
+constexpr float RS_MAX = 256.0f;
 
 // LDS layouts (bytes), per head dimension HD (64, 128 or 256).  A tile slot is a
 // run of 1 KiB DMA instructions.
@@ -365,22 +369,22 @@ void attn_fwd_kernel(Params p) {
   //
   // The work is cut into parts with compile-time indices so that a fused mma
   // block can place each part between two MFMAs:
-  //   X0..X7  tile max: four chains of 8 scores, half a chain per part
-  //   X8, X9  lane-pair max, tile max in log2 units, ballot of the lazy
-  //           rescale test (is the tile max more than TAU above m?)
-  //   D       new running max m, alpha = 2^(m_old - m), -m for the exponents
   //   E0..E31 P = 2^(s*cs - m) for score e; every second part also packs an
   //           earlier pair to fp16 and adds it to the row sum (dot2 against
   //           (1, 1)), one pair behind to hide the exponential's latency
   //   E32     packs the last pair
   //   E33     row sum across the lane pair
+  //   C       the check: does any row's tile sum exceed RS_MAX?  (ballot,
+  //           wave-uniform)
   //   F       l = l * alpha + row sum (one fused multiply-add)
-  // In order X, D, E, F this is the textbook online softmax.  The fused
-  // blocks of the overlap schedule run the E parts speculatively with the
-  // current m alongside the X parts, and D after the block; only when the
-  // test fires (in practice on a row's first tiles) are the E parts run
-  // again with the new m.  Either way P is computed with the final m, so
-  // every schedule produces the same bits.
+  // and, only on a wave's first tile or when C fires, before F:
+  //   X0..X7  tile max: four chains of 8 scores, half a chain per part
+  //   X8, X9  lane-pair max, tile max in log2 units
+  //   D       m = max(m, tile max), alpha = 2^(m_old - m), -m for the exponents
+  //   E0..E33 again, with the new m
+  // On the first tile this is the textbook online softmax step in order X,
+  // D, E, F.  Every schedule runs the same parts on the same values in the
+  // same order per tile, so they all produce the same bits.
   struct Rescale {
     bool any;
     float alpha;
@@ -399,15 +403,19 @@ void attn_fwd_kernel(Params p) {
   // Key (sb, r) of this lane is j*BN + 32sb + 8(r/4) + 4hh + r%4; it is
   // allowed iff it is below end = min(Sk, query + off + 1) (causal) or Sk, i.e. iff
   // the compile-time part 32sb + 8(r/4) + r%4 is below lim.
-  auto sm_init = [&](int j, auto masked, SmState& st) INL {
+  auto sm_lim = [&](int j, auto masked, SmState& st) INL {
     if constexpr (decltype(masked)::value) {
       const int query = kSplit ? qidx : qw + n;
       const int end = p.causal ? min(Sk, query + off + 1) : Sk;
       st.lim = end - j * BN - 4 * hh;
     }
+  };
+  auto sm_start = [&](SmState& st) INL {  // before the E parts
     st.negm = -m_run;
     st.rq[0] = 0.f;
     st.rq[1] = 0.f;
+    st.rz.any = false;
+    st.rz.alpha = 1.0f;
   };
   auto sm_x = [&](auto kc, f32x16 (&sc)[2], auto masked, SmState& st) INL {  // parts X0..X9
     constexpr int k = decltype(kc)::value;
@@ -431,14 +439,16 @@ void attn_fwd_kernel(Params p) {
       static_assert(k == 9, "max part index");
       const float mt = fmaxf(st.sw[0], st.sw[1]);
       st.mts = (mt == NEG_INF) ? NEG_INF : mt * cs;
-      st.rz.any = __builtin_amdgcn_ballot_w64(st.mts > m_run + TAU) != 0;  // wave-uniform
     }
   };
-  auto sm_d = [&](SmState& st) INL {  // part D
-    const float m_new = st.rz.any ? fmaxf(m_run, st.mts) : m_run;
+  auto sm_d = [&](SmState& st) INL {  // part D (rows without an allowed key keep m)
+    const float m_new = fmaxf(m_run, st.mts);
+    st.negm = -m_new;
+    st.rq[0] = 0.f;
+    st.rq[1] = 0.f;
+    st.rz.any = true;
     st.rz.alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
-    st.negm = -m_run;
   };
   auto sm_e = [&](auto kc, f32x16 (&sc)[2], f16x8 (&pd)[4], auto masked, SmState& st) INL {  // E0..E33
     constexpr int e = decltype(kc)::value;
@@ -465,21 +475,27 @@ void attn_fwd_kernel(Params p) {
       st.rs = pair_sum(st.rq[0] + st.rq[1]);
     }
   };
+  // part C; !(rs <= RS_MAX) also catches an infinite sum (m not yet set)
+  auto sm_c = [&](SmState& st) INL { return __builtin_amdgcn_ballot_w64(!(st.rs <= RS_MAX)) != 0; };
   auto sm_f = [&](SmState& st) INL { l_run = __builtin_fmaf(l_run, st.rz.alpha, st.rs); };  // part F
   constexpr int SM_X = 10, SM_E = 34;
-  constexpr int SM_ORDERED = SM_X + 1 + SM_E + 1;  // X, D, E, F
-  // part k of the ordered sequence
-  auto sm_ordered = [&](auto kc, f32x16 (&sc)[2], f16x8 (&pd)[4], auto masked, SmState& st) INL {
-    constexpr int k = decltype(kc)::value;
-    if constexpr (k < SM_X) sm_x(kc, sc, masked, st);
-    else if constexpr (k == SM_X) sm_d(st);
-    else if constexpr (k < SM_X + 1 + SM_E) sm_e(std::integral_constant<int, k - SM_X - 1>{}, sc, pd, masked, st);
-    else sm_f(st);
+  // X, D, E: the tile with its max (first tile, or C fired)
+  auto sm_full = [&](f32x16 (&sc)[2], f16x8 (&pd)[4], auto masked, SmState& st) INL {
+    static_for<SM_X>([&](auto kc) INL { sm_x(kc, sc, masked, st); });
+    sm_d(st);
+    static_for<SM_E>([&](auto ec) INL { sm_e(ec, sc, pd, masked, st); });
   };
-  auto softmax = [&](int j, f32x16 (&sc)[2], f16x8 (&pd)[4], auto masked) INL -> Rescale {
+  auto softmax = [&](int j, f32x16 (&sc)[2], f16x8 (&pd)[4], auto masked, bool first) INL -> Rescale {
     SmState st;
-    sm_init(j, masked, st);
-    static_for<SM_ORDERED>([&](auto kc) INL { sm_ordered(kc, sc, pd, masked, st); });
+    sm_lim(j, masked, st);
+    sm_start(st);
+    bool redo = first;
+    if (!first) {
+      static_for<SM_E>([&](auto ec) INL { sm_e(ec, sc, pd, masked, st); });
+      redo = sm_c(st);
+    }
+    if (__builtin_expect(redo, 0)) sm_full(sc, pd, masked, st);
+    sm_f(st);
     return st.rz;
   };
   auto rescale_o = [&](const Rescale& rz) INL {
@@ -546,8 +562,9 @@ void attn_fwd_kernel(Params p) {
   using M_FUSED = std::integral_constant<int, 3>;
   f16x8 pf[4];  // P^T of the tile whose softmax ran last
   f32x16 s[2];  // S^T of the tile whose QK^T ran last
-  auto softmax_tile = [&](int j) INL {
-    const Rescale rz = is_masked(j) ? softmax(j, s, pf, std::true_type{}) : softmax(j, s, pf, std::false_type{});
+  auto softmax_tile = [&](int j, bool first) INL {  // first: the wave's first tile
+    const Rescale rz = is_masked(j) ? softmax(j, s, pf, std::true_type{}, first)
+                                    : softmax(j, s, pf, std::false_type{}, first);
     rescale_o(rz);
   };
 
@@ -562,7 +579,7 @@ void attn_fwd_kernel(Params p) {
       stage(j + 1, j + 1);
       if (!skip(j)) {
         block(M_QK{}, j, s, 0, pf, NoSoftmax{});
-        softmax_tile(j);
+        softmax_tile(j, j == j_lo);
         block(M_PV{}, 0, s, j, pf, NoSoftmax{});
       }
       dma_wait();
@@ -594,7 +611,7 @@ void attn_fwd_kernel(Params p) {
           else if (do_qk) block(M_QK{}, j, s, j - 1, pf, NoSoftmax{});
           __builtin_amdgcn_s_setprio(0);
         } else if (!skip(j)) {
-          softmax_tile(j);
+          softmax_tile(j, j == 0);
         }
       }
       if (hs & 1) dma_wait();
@@ -605,9 +622,9 @@ void attn_fwd_kernel(Params p) {
     // overlap of MFMA and VALU work happens inside each wave.  The softmax is
     // pipelined across iterations.  Iteration j is one block of 32 MFMAs --
     // QK^T of tile j+1, then PV of tile j-1 -- with, between them, the
-    // exponentials and row sum of tile j (whose running max was fixed in
-    // iteration j-1) and, once S^T of tile j+1 is complete, the max of tile
-    // j+1 and the new running max; then O *= alpha_j and a barrier.
+    // exponentials and row sum of tile j; then the sum check of tile j (and
+    // in the rare case it fires, its max and the exponentials again),
+    // O *= alpha_j and a barrier.
     // Iteration j reads K_{j+1} and V_{j-1} and loads K_{j+2} and V_j into
     // the slots that K_{j-1} and V_{j-2} left.  Per tile the softmax runs the
     // same parts in the same order as the serial schedule, and per
@@ -616,8 +633,8 @@ void attn_fwd_kernel(Params p) {
     // No wave skips a tile here: the steady-state loop has one code path per
     // mask case, so O, S and P each keep a single set of registers.  A tile
     // wholly above a wave's diagonal (only ever the last one) is computed with
-    // every key masked, which is an exact no-op: the tile max is -inf, so
-    // alpha = 1 and the running max stays, every P is 0, l gains 0 and PV adds
+    // every key masked, which is an exact no-op: every P is 0, the sum check
+    // passes so alpha = 1 and the running max stays, l gains 0 and PV adds
     // zeros.  Waves of a missing odd head (hl == g) compute head h of the pair
     // and store nothing.
     //
@@ -628,13 +645,6 @@ void attn_fwd_kernel(Params p) {
     f32x16 sa[2], sb[2];
     f16x8 pa[4], pb[4];
     SmState cur;
-    auto set_lim = [&](int j, auto masked, SmState& st) INL {
-      if constexpr (decltype(masked)::value) {
-        const int query = qw + n;
-        const int end = p.causal ? min(Sk, query + off + 1) : Sk;
-        st.lim = end - j * BN - 4 * hh;
-      }
-    };
     // One iteration.  with_pv / with_qk: whether PV(j-1) / QK(j+1) exist;
     // mask_e / mask_x: whether tile j / tile j+1 need the key mask.
     auto iter = [&](int j, auto with_pv, auto with_qk, auto mask_e, auto mask_x, f32x16 (&sc)[2],
@@ -642,51 +652,28 @@ void attn_fwd_kernel(Params p) {
       constexpr bool kPV = decltype(with_pv)::value, kQK = decltype(with_qk)::value;
       stage(j + 2, j);
       SmState nx;  // tile j+1
-      if constexpr (kQK) set_lim(j + 1, mask_x, nx);
-      cur.rq[0] = 0.f;
-      cur.rq[1] = 0.f;
-      // Placement of the softmax parts before the MFMAs of the block:
-      // E part e before MFMA floor(e * (nsteps - 1) / 33), F after E33; the
-      // max parts of tile j+1 read S^T block 0 (chains 0, 1) from MFMA 10 on
-      // and block 1 (chains 2, 3) from MFMA 18 on (mode 3; with QK^T alone
-      // the block-1 chains, X8, X9 and D follow the block).
+      if constexpr (kQK) sm_lim(j + 1, mask_x, nx);
+      sm_start(cur);
+      // E part e runs before MFMA floor(e * (nsteps - 1) / 33) of the block;
+      // C, the rare X / D / E redo and F follow the block.
       constexpr int nsteps = kQK ? steps_of(kPV ? 3 : 2, NKK, NDB) : steps_of(1, NKK, NDB);
-      auto part_x = [&](auto kc) INL { sm_x(kc, sn, mask_x, nx); };
-      auto x_at = [&](auto ic) INL {
-        constexpr int i = decltype(ic)::value;
-        if constexpr (i == 10) part_x(std::integral_constant<int, 0>{});
-        if constexpr (i == 11) part_x(std::integral_constant<int, 1>{});
-        if constexpr (i == 12) part_x(std::integral_constant<int, 4>{});
-        if constexpr (i == 13) part_x(std::integral_constant<int, 5>{});
-        if constexpr (i == 18) part_x(std::integral_constant<int, 2>{});
-        if constexpr (i == 19) part_x(std::integral_constant<int, 3>{});
-        if constexpr (i == 20) part_x(std::integral_constant<int, 6>{});
-        if constexpr (i == 21) part_x(std::integral_constant<int, 7>{});
-        if constexpr (i == 23) part_x(std::integral_constant<int, 8>{});
-        if constexpr (i == 25) part_x(std::integral_constant<int, 9>{});
-        if constexpr (i == 27) sm_d(nx);
-      };
       auto sm = [&](auto ic) INL {
         constexpr int i = decltype(ic)::value;
         static_for<SM_E>([&](auto ec) INL {
           if constexpr (decltype(ec)::value * (nsteps - 1) / (SM_E - 1) == i) sm_e(ec, sc, pc, mask_e, cur);
         });
-        if constexpr (i == nsteps - 1) sm_f(cur);
-        if constexpr (kQK) x_at(ic);
       };
       if constexpr (kPV && kQK) {
         block(M_FUSED{}, j + 1, sn, j - 1, pp, sm);
       } else if constexpr (kQK) {
         block(M_QK{}, j + 1, sn, j - 1, pp, sm);
-        static_for<32>([&](auto ic) INL {  // the max parts placed beyond MFMA 15
-          if constexpr (decltype(ic)::value >= 16) x_at(ic);
-        });
       } else if constexpr (kPV) {
         block(M_PV{}, j + 1, sn, j - 1, pp, sm);
       } else {
         static_for<SM_E>([&](auto ec) INL { sm_e(ec, sc, pc, mask_e, cur); });
-        sm_f(cur);
       }
+      if (__builtin_expect(sm_c(cur), 0)) sm_full(sc, pc, mask_e, cur);
+      sm_f(cur);
       rescale_o(cur.rz);
       if constexpr (kQK) cur = nx;
       dma_wait();
@@ -710,9 +697,11 @@ void attn_fwd_kernel(Params p) {
     dma_wait();
     lds_barrier();
     // prologue: S^T of tile 0, its max and the first running max (K_0 keeps
-    // its slot while iteration 0 loads K_2, so no barrier is needed here)
+    // its slot while iteration 0 loads K_2, so no barrier is needed here);
+    // iteration 0 then runs the E parts of tile 0 against that max, as the
+    // first tile of the serial schedule does
     block(M_QK{}, 0, sa, 0, pa, NoSoftmax{});
-    set_lim(0, T{}, cur);
+    sm_lim(0, T{}, cur);
     static_for<SM_X>([&](auto kc) INL { sm_x(kc, sa, T{}, cur); });
     sm_d(cur);
     int j = 0;
