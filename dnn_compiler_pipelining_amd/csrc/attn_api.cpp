@@ -22,14 +22,20 @@ constexpr int kMaxSeq = 1 << 30;  // sequence lengths up to 2^30 keep all tile a
 // LIBATTN_RING=2|4, LIBATTN_XCD=0|1 and LIBATTN_LPT=0|1 are read on every
 // call, so tests and the schedule search can switch them; all variants give
 // bitwise identical results.
+// The schedule named by LIBATTN_SCHEDULE, or -1.
+int env_schedule() {
+  if (const char* s = std::getenv("LIBATTN_SCHEDULE")) {
+    if (std::strcmp(s, "serial") == 0) return libattn::SCHEDULE_SERIAL;
+    if (std::strcmp(s, "overlap") == 0) return libattn::SCHEDULE_OVERLAP;
+    if (std::strcmp(s, "pingpong") == 0) return libattn::SCHEDULE_PINGPONG;
+    if (std::strcmp(s, "serial4") == 0) return libattn::SCHEDULE_SERIAL4;
+  }
+  return -1;
+}
+
 libattn::Variant choose_variant(int B, int Sq, int Sk, int Hq, int Hkv) {
   libattn::Variant v = libattn::tuned_variant(B, Sq, Sk, Hq, Hkv);
-  if (const char* s = std::getenv("LIBATTN_SCHEDULE")) {
-    if (std::strcmp(s, "serial") == 0) v.schedule = libattn::SCHEDULE_SERIAL;
-    if (std::strcmp(s, "overlap") == 0) v.schedule = libattn::SCHEDULE_OVERLAP;
-    if (std::strcmp(s, "pingpong") == 0) v.schedule = libattn::SCHEDULE_PINGPONG;
-    if (std::strcmp(s, "serial4") == 0) v.schedule = libattn::SCHEDULE_SERIAL4;
-  }
+  if (env_schedule() >= 0) v.schedule = env_schedule();
   auto flag = [](const char* name, int& field, int lo, int hi) {
     if (const char* s = std::getenv(name)) {
       const int x = std::atoi(s);
@@ -142,10 +148,14 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
   libattn::Params p = base_params(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, D, causal, scale);
   p.n_qt = (Sq + 127) / 128;
   const libattn::Variant var = choose_variant(B, Sq, Sk, Hq, Hkv);
-  // HD 64 runs the serial schedules only, HD 256 the SERIAL4 schedule only
+  // HD 256 runs the SERIAL4 schedule only.  HD 64 runs the serial
+  // schedules only, SERIAL4 unless SERIAL is named in LIBATTN_SCHEDULE: its
+  // one-head workgroups (142 VGPRs, 34 KiB of LDS) fit three to a CU, where
+  // SERIAL's 8-wave workgroups fit one (measured on MI355X at B=16 S=8192
+  // Hq=32 Hkv=8: 878 against 822 TFLOP/s)
   if (D == 256) p.schedule = libattn::SCHEDULE_SERIAL4;
-  else if (D == 128 || var.schedule == libattn::SCHEDULE_SERIAL4) p.schedule = var.schedule;
-  else p.schedule = libattn::SCHEDULE_SERIAL;
+  else if (D == 128) p.schedule = var.schedule;
+  else p.schedule = env_schedule() == libattn::SCHEDULE_SERIAL ? libattn::SCHEDULE_SERIAL : libattn::SCHEDULE_SERIAL4;
   // query heads per workgroup: a pair (two wave groups), or one for SERIAL4
   p.pairs = p.schedule == libattn::SCHEDULE_SERIAL4 ? p.g : (p.g + 1) / 2;
   p.ring = var.ring;
