@@ -205,3 +205,45 @@ def test_all_variants_bitwise_identical(monkeypatch, B, S, Hq, Hkv, causal):
                     monkeypatch.setenv("LIBATTN_LPT", lpt)
                     o2, l2 = U.run(qd, kd, vd, bool(causal), SC)
                     assert torch.equal(o1, o2) and torch.equal(l1, l2), (sched, ring, xcd, lpt)
+
+
+def spiked_qkv(S, Hq, Hkv, hd, seed, spikes):
+    """Q shifted by +1 per element, and at each (position j, c) every K head's row j set to the constant
+    c * 128 / hd: key j then scores about 16 c log2 units above the N(0,1) keys for every query, so the
+    tile sum check fires part-way through each row that sees it (the running max is raised after the
+    first tile, the rare path of the online softmax), and before the redo the largest P overflow fp16."""
+    q = inputs.make_tensor(1, S, Hq, hd, seed, inputs.Q)
+    k = inputs.make_tensor(1, S, Hkv, hd, seed, inputs.K)
+    v = inputs.make_tensor(1, S, Hkv, hd, seed, inputs.V)
+    q = (q.float() + 1.0).half()
+    for j, c in spikes:
+        k[:, j] = c * 128.0 / hd
+    return q, k, v
+
+
+@pytest.mark.parametrize("hd", [128, 64, 256], ids=lambda x: "D%d" % x)
+@pytest.mark.parametrize("causal", [1, 0], ids=lambda x: "causal%d" % x)
+def test_running_max_raised_mid_row(monkeypatch, hd, causal):
+    """Keys 400 and 800 (tiles 6 and 12) score far above everything before them: parity with the oracle,
+    the same bits from every schedule the head dimension runs, and the split-KV path on the last rows."""
+    q, k, v = spiked_qkv(1000, 8, 2, hd, seed=77, spikes=[(400, 1.0), (800, 2.0)])
+    monkeypatch.delenv("LIBATTN_SCHEDULE", raising=False)
+    tag = "spiked D%d causal%d" % (hd, causal)
+    U.say(tag)
+    U.full_parity(q, k, v, bool(causal), SC, tag)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    o1, l1 = U.run(qd, kd, vd, bool(causal), SC)
+    scheds = ("serial", "overlap", "pingpong", "serial4") if hd == 128 else ("serial", "serial4")
+    for sched in scheds:
+        monkeypatch.setenv("LIBATTN_SCHEDULE", sched)
+        o2, l2 = U.run(qd, kd, vd, bool(causal), SC)
+        assert torch.equal(o1, o2) and torch.equal(l1, l2), sched
+    monkeypatch.delenv("LIBATTN_SCHEDULE")
+    # the last 4 query rows through the split-KV path against the same rows of the regular path
+    qt = qd[:, -4:].contiguous()
+    od, ld = binding.decode(qt, kd, vd, causal=bool(causal), scale=SC)
+    ot, lt = torch.empty_like(qt), torch.empty((1, 8, 4), dtype=torch.float32, device=qt.device)
+    binding.forward(qt, kd, vd, causal=bool(causal), scale=SC, out=ot, lse=lt)
+    torch.cuda.synchronize()
+    assert float((od.float() - ot.float()).abs().max()) <= U.MAX_ABS_O
+    assert float((ld - lt).abs().max()) <= U.MAX_ABS_LSE
