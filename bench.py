@@ -32,7 +32,10 @@ fields, with metric FLOPs 2*M*N*K and the fp64 GEMM oracle as cpu_baseline.
 `--workload llama3-70b_decode_b64_s8192` times the split-KV decode path
 (attn_fwd_decode: split kernel + combine kernel per step) and reports HBM
 GB/s (K, V, Q, O and LSE once) against the 8 TB/s HBM roofline.
-`--all` prints one line per attention, GEMM and decode workload.
+`--all` prints one line per attention, GEMM and decode workload; there each workload gets at
+least about 0.25 s of warmup and 0.25 s of timed launches (more steps than --warmup / --steps
+for the short ones, reported in the line), so that its launches are timed at the clock a
+sustained run settles to rather than while the clock is still rising after input generation.
 """
 from __future__ import annotations
 
@@ -527,17 +530,26 @@ def main():
 
     names = ([w.name for w in inputs.WORKLOADS] + [w.name for w in inputs.GEMM_WORKLOADS] +
              [w.name for w in inputs.DECODE_WORKLOADS]) if args.all else [args.workload]
+
+    def counts(est_ms: float):
+        # --all: at least ~0.25 s of warmup and of timed launches per workload
+        if not args.all:
+            return args.steps, args.warmup
+        n = min(5000, max(1, int(250.0 / max(est_ms, 1e-3)) + 1))  # launch-bound shapes: at most 5000
+        return max(args.steps, n), max(args.warmup, n)
+
     for name in names:
         if is_decode(name):
             w = inputs.DECODE_BY_NAME[name]
-            wall_ms, kernel_ms, ok = time_decode(w, args.steps, args.warmup)
+            steps, warmup = counts(w.bytes / 5e9)
+            wall_ms, kernel_ms, ok = time_decode(w, steps, warmup)
             if not ok:
                 log("[bench] non-finite output")
                 return 1
             value = w.bytes / (wall_ms * 1e-3) / 1e9
             achieved = w.bytes / (kernel_ms * 1e-3) / 1e9
             line = {"metric": DECODE_METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
-                    "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall_ms, 4),
+                    "steps": steps, "warmup": warmup, "ms_per_step": round(wall_ms, 4),
                     "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
                     "data": "synthetic: seeded i.i.d. N(0,1) fp16 Q/K/V", "config": w.describe(),
                     "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -551,10 +563,12 @@ def main():
         gemm = is_gemm(name)
         if gemm:
             w = inputs.GEMM_BY_NAME[name]
-            wall_ms, kernel_ms, ok = time_gemm(w, args.steps, args.warmup, args.pmc_copy)
+            steps, warmup = counts(w.flops / 8e11)
+            wall_ms, kernel_ms, ok = time_gemm(w, steps, warmup, args.pmc_copy)
         else:
             w = inputs.BY_NAME[name]
-            wall_ms, kernel_ms, ok = time_workload(w, args.steps, args.warmup, args.pmc_copy)
+            steps, warmup = counts(w.flops / 8e11)
+            wall_ms, kernel_ms, ok = time_workload(w, steps, warmup, args.pmc_copy)
         if not ok:
             log("[bench] non-finite output")
             return 1
@@ -566,8 +580,8 @@ def main():
             "value": round(value, 2),
             "unit": "TFLOP/s",
             "n_gpus": 1,
-            "steps": args.steps,
-            "warmup": args.warmup,
+            "steps": steps,
+            "warmup": warmup,
             "ms_per_step": round(wall_ms, 4),
             "higher_is_better": True,
             "scaling": "weak",
