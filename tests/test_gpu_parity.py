@@ -239,11 +239,16 @@ def test_running_max_raised_mid_row(monkeypatch, hd, causal):
         o2, l2 = U.run(qd, kd, vd, bool(causal), SC)
         assert torch.equal(o1, o2) and torch.equal(l1, l2), sched
     monkeypatch.delenv("LIBATTN_SCHEDULE")
-    # the last 4 query rows through the split-KV path against the same rows of the regular path
+    # the last 4 query rows through the split-KV path against the same rows of the regular path, with
+    # the planned splits and with splits of 8 tiles (512 keys), which put both spikes inside a split
     qt = qd[:, -4:].contiguous()
-    od, ld = binding.decode(qt, kd, vd, causal=bool(causal), scale=SC)
     ot, lt = torch.empty_like(qt), torch.empty((1, 8, 4), dtype=torch.float32, device=qt.device)
     binding.forward(qt, kd, vd, causal=bool(causal), scale=SC, out=ot, lse=lt)
-    torch.cuda.synchronize()
-    assert float((od.float() - ot.float()).abs().max()) <= U.MAX_ABS_O
-    assert float((ld - lt).abs().max()) <= U.MAX_ABS_LSE
+    for split_tiles in (None, "8"):
+        if split_tiles:
+            monkeypatch.setenv("LIBATTN_DECODE_SPLIT_TILES", split_tiles)
+        od, ld = binding.decode(qt, kd, vd, causal=bool(causal), scale=SC)
+        torch.cuda.synchronize()
+        assert float((od.float() - ot.float()).abs().max()) <= U.MAX_ABS_O, split_tiles
+        assert float((ld - lt).abs().max()) <= U.MAX_ABS_LSE, split_tiles
+    monkeypatch.delenv("LIBATTN_DECODE_SPLIT_TILES", raising=False)
