@@ -47,11 +47,14 @@ def test_edge_shapes(B, S, Hq, Hkv, causal, scale):
 
 
 def test_workload_small_full():
-    """The 8B-shaped B=1 S=512 workload, whole output against the oracle."""
+    """The 8B-shaped B=1 S=512 workload, whole output against the oracle; and the errors are at the level
+    of the kernel's own arithmetic (tests/test_tolerance_model.py: round-to-nearest P and O give
+    max |dLSE| about 1.5e-4 on such inputs, truncation over 3e-4), not merely inside the bar."""
     w = inputs.WORKLOADS[0]
     U.say("workload " + w.name)
     q, k, v = inputs.make_inputs(w, "cpu")
-    U.full_parity(q, k, v, w.causal, w.scale, w.name)
+    st = U.full_parity(q, k, v, w.causal, w.scale, w.name)
+    assert st["max_lse"] <= 3e-4 and st["max_o"] <= 2e-3, st
 
 
 @pytest.mark.parametrize("idx", [1, 2, 3, 4], ids=lambda i: inputs.WORKLOADS[i].name)
