@@ -21,10 +21,11 @@
 //             need one cross-lane step (v_permlane32_swap) because the S^T
 //             layout keeps each query in one lane pair (same page, section
 //             5.2.1: subgroup reductions by lane exchange instead of LDS)
-// Three tile schedules (see Schedule in attn_kernel.h) order these tasks and
-// give the same bits: serial (the default), an overlap schedule that fuses the
-// softmax of tile j with the MFMAs of QK^T(j+1) and PV(j-1) in every wave,
-// and a ping-pong schedule of two wave groups offset by half a tile.
+// Four tile schedules (see Schedule in variant.h) order these tasks and give
+// the same bits: serial, an overlap schedule that fuses the softmax of tile j
+// with the MFMAs of QK^T(j+1) and PV(j-1) in every wave, a ping-pong schedule
+// of two wave groups offset by half a tile, and serial4 (the serial schedule
+// in four-wave, one-head workgroups).
 //
 // Besides the MFMA, transpose-read and direct-load layouts listed in gfx950.h,
 // this file relies on v_permlane32_swap(x, y): x's upper 32 lanes trade places

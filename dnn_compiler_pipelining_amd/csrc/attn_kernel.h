@@ -9,9 +9,10 @@
 
 namespace libattn {
 
-// Tile schedules and the variant choice: variant.h.  Measured on MI355X all
-// three schedules land within a few percent of each other: the kernel runs at
-// the chip's power limit, where the clock, not the issue order, sets the rate.
+// Tile schedules and the variant choice: variant.h.  Measured on MI355X the
+// serial, overlap and serial4 schedules land within a few percent of each
+// other: the softmax's VALU instructions take issue from the MFMAs of every
+// wave on a SIMD whatever the order, and the chip runs at its power limit.
 
 // Launch parameters.  Pointers are device pointers; strides are in elements.
 struct Params {

@@ -23,7 +23,7 @@
  * to nearest even from fp32.  Internal offsets are 64-bit, so tensors larger
  * than 4 GiB are supported.
  *
- * Scalars: B, S, Hq, Hkv >= 1; S <= 2^30; Hq % Hkv == 0; D is 64 or 128
+ * Scalars: B, S, Hq, Hkv >= 1; S <= 2^30; Hq % Hkv == 0; D is 64, 128 or 256
  * (other head sizes return ATTN_ERR_UNSUPPORTED, and so does
  * Hkv * D * 2 * 64 >= 2^32, i.e. a 64-row K/V tile spanning 4 GiB or more);
  * causal is 0 or 1; scale is any finite float.
@@ -45,8 +45,9 @@
  * kernel's tile schedule: "serial", "overlap", "pingpong" or "serial4" (the
  * serial schedule in 4-wave workgroups, two per CU); unset or any other value
  * gives the schedule tuned for the nearest measured shape.  D = 64 runs
- * "serial" or "serial4" only.  All schedules give bitwise identical results,
- * so each serves as a cross-check of the others.
+ * "serial" when that is named and "serial4" otherwise; D = 256 runs "serial4"
+ * only.  All schedules give bitwise identical results, so each serves as a
+ * cross-check of the others.
  *
  * Errors: on invalid arguments nothing is launched and a nonzero ATTN_ERR_*
  * code is returned; a failed launch returns ATTN_ERR_HIP.  No exception
@@ -65,7 +66,7 @@ enum {
   ATTN_OK = 0,
   ATTN_ERR_NULL = 1,        /* a required pointer is NULL */
   ATTN_ERR_SHAPE = 2,       /* a size < 1 or > 2^30, Hq % Hkv != 0, causal not 0/1, causal with Sq > Sk, scale not finite */
-  ATTN_ERR_UNSUPPORTED = 3, /* D other than 64 or 128, or Hkv * D * 2 * 64 >= 2^32 */
+  ATTN_ERR_UNSUPPORTED = 3, /* D other than 64, 128 or 256, or Hkv * D * 2 * 64 >= 2^32 */
   ATTN_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
   ATTN_ERR_HIP = 5,         /* the HIP runtime reported an error at launch */
   ATTN_ERR_OVERLAP = 6,     /* o overlaps q, k, v or lse; or the workspace overlaps any tensor */
