@@ -118,6 +118,15 @@ def load_traffic(workload: str):
 
 # ------------------------------------------------------------------ GPU timing
 
+def device_info() -> dict:
+    """The GPU the line was measured on (torch's view of the HIP device properties)."""
+    import torch
+
+    pr = torch.cuda.get_device_properties(0)
+    return {"name": pr.name, "arch": getattr(pr, "gcnArchName", None), "compute_units": pr.multi_processor_count,
+            "memory_gib": round(pr.total_memory / 2**30, 1)}
+
+
 def time_workload(w, steps: int, warmup: int, pmc_copy: int = 0):
     import torch
 
@@ -555,7 +564,8 @@ def main():
                     "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                  "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                                  "kernel": "attn_fwd_kernel (split-KV) + attn_combine_kernel",
-                                 "kernel_ms": round(kernel_ms, 4), "bytes_per_step": w.bytes}}
+                                 "kernel_ms": round(kernel_ms, 4), "bytes_per_step": w.bytes},
+                    "device": device_info()}
             if not args.no_cpu_baseline and not args.all:
                 line["cpu_baseline"] = cpu_baseline_decode(w, args.cpu_seconds)
             print(json.dumps(line), flush=True)
@@ -596,6 +606,7 @@ def main():
                                      if traffic and traffic.get("hbm_bytes_per_launch") else None),
                          "kernel": kernel_name(name), "kernel_ms": round(kernel_ms, 4),
                          "flops_per_launch": w.flops},
+            "device": device_info(),
         }
         if not args.no_cpu_baseline and not args.all:
             line["cpu_baseline"] = (cpu_baseline_gemm if gemm else cpu_baseline)(w, args.cpu_seconds)

@@ -43,13 +43,15 @@ def stats(o_gpu: np.ndarray, lse_gpu: np.ndarray, o_ref: np.ndarray, lse_ref: np
     finite = bool(np.isfinite(o_gpu).all() and np.isfinite(lse_gpu).all())
     e = np.abs(o_gpu - o_ref)
     el = np.abs(lse_gpu - lse_ref)
+    where = tuple(int(x) for x in np.unravel_index(int(np.argmax(e)), e.shape)) if e.size else ()
     return dict(finite=finite, max_o=float(e.max()) if e.size else 0.0, mean_o=float(e.mean()) if e.size else 0.0,
-                max_lse=float(el.max()) if el.size else 0.0, n=int(e.size))
+                max_lse=float(el.max()) if el.size else 0.0, n=int(e.size),
+                p9999_o=float(np.quantile(e, 0.9999)) if e.size else 0.0, argmax_o=where)
 
 
 def check(st, tag=""):
-    say("  %s: max|dO| %.3e mean|dO| %.3e max|dLSE| %.3e over %d O elements" %
-        (tag, st["max_o"], st["mean_o"], st["max_lse"], st["n"]))
+    say("  %s: max|dO| %.3e at %s, 99.99th pct %.3e, mean|dO| %.3e, max|dLSE| %.3e over %d O elements" %
+        (tag, st["max_o"], st.get("argmax_o", ()), st.get("p9999_o", 0.0), st["mean_o"], st["max_lse"], st["n"]))
     assert st["finite"], "%s: NaN/Inf in output" % tag
     assert st["max_o"] <= MAX_ABS_O, "%s: max |dO| %.3e > %.1e" % (tag, st["max_o"], MAX_ABS_O)
     assert st["mean_o"] <= MEAN_ABS_O, "%s: mean |dO| %.3e > %.1e" % (tag, st["mean_o"], MEAN_ABS_O)
@@ -97,8 +99,12 @@ def sampled_parity(w: inputs.Workload, q, k, v, o, lse, batches, heads=None, n_r
         lg = lse[b][heads_t, rows_t].cpu().numpy()
         allst.append(stats(og, lg, O, L))
     n = sum(s["n"] for s in allst)
+    worst = max(range(len(allst)), key=lambda x: allst[x]["max_o"])
+    si, d = allst[worst]["argmax_o"] if allst[worst]["argmax_o"] else (0, 0)
     st = dict(finite=all(s["finite"] for s in allst), max_o=max(s["max_o"] for s in allst),
-              mean_o=sum(s["mean_o"] * s["n"] for s in allst) / n, max_lse=max(s["max_lse"] for s in allst), n=n)
+              mean_o=sum(s["mean_o"] * s["n"] for s in allst) / n, max_lse=max(s["max_lse"] for s in allst), n=n,
+              p9999_o=max(s["p9999_o"] for s in allst),  # the largest per-batch 99.99th percentile
+              argmax_o=(batches[worst], int(rs[si]), int(hs[si]), int(d)))  # (b, row, head, d)
     check(st, tag)
     return st
 
