@@ -41,6 +41,10 @@ def waves_per_simd(schedule: str, hd: int) -> int:
 RINGS = (2, 4)
 SWITCHES = (0, 1)
 SEED = {"schedule": "serial", "ring": 4, "xcd": 1, "lpt": 1}
+# A change is kept when it is this much faster.  The median of five timed batches repeats to about
+# 0.2% on one box (repeated same-box pairs of the serial and overlap schedules on the 70B-shaped
+# B = 16 S = 8192 problem differed by 0.3-1.1%, always in the same direction).
+KEEP_GAIN = 0.005
 
 # resource budget of one variant: the SIMD's 512 VGPRs + AGPRs per lane shared by its waves, and 160 KiB of
 # LDS shared by the workgroups of a CU
@@ -115,7 +119,7 @@ def _time(fn, reps: int) -> float:
 
 
 def measure(w, point: dict, q, k, v, o, lse) -> float:
-    """TFLOP/s of one variant on one workload (median of three timed batches)."""
+    """TFLOP/s of one variant on one workload (median of five timed batches)."""
     from dnn_compiler_pipelining_amd import binding
 
     os.environ["LIBATTN_SCHEDULE"] = point["schedule"]
@@ -123,13 +127,13 @@ def measure(w, point: dict, q, k, v, o, lse) -> float:
     os.environ["LIBATTN_XCD"] = str(point["xcd"])
     os.environ["LIBATTN_LPT"] = str(point["lpt"])
     reps = max(2, min(50, int(0.15 / max(w.flops / 1e15, 1e-6))))  # about 0.15 s per batch at 1 PFLOP/s
-    ms = sorted(_time(lambda: binding.forward(q, k, v, w.causal, w.scale, o, lse), reps) for _ in range(3))[1]
+    ms = sorted(_time(lambda: binding.forward(q, k, v, w.causal, w.scale, o, lse), reps) for _ in range(5))[2]
     return w.flops / ms / 1e9
 
 
 def search_workload(w, valid, log=print):
     """Greedy coordinate search from the seed variant: change one field at a time, keep a change only when it
-    is more than 1% faster (measurement noise on one box is about that), repeat until nothing improves."""
+    is more than KEEP_GAIN faster, repeat until nothing improves."""
     from dnn_compiler_pipelining_amd import inputs
 
     q, k, v = inputs.make_inputs(w, "cuda")
@@ -160,7 +164,7 @@ def search_workload(w, valid, log=print):
                 if not valid.get((cand["schedule"], cand["ring"], w.D), (False,))[0]:
                     continue
                 r = rate(cand)
-                if r > best_rate * 1.01:
+                if r > best_rate * (1.0 + KEEP_GAIN):
                     best, best_rate, improved = cand, r, True
     del q, k, v, o, lse
     torch.cuda.empty_cache()
@@ -179,7 +183,8 @@ def search(out_dir: str, names=None):
     for (s, r, hd), (ok, why, _) in sorted(valid.items()):
         print("variant %-9s ring %d hd %d: %s" % (s, r, hd, why), flush=True)
     rec = {"valid": {"%s/%d/%d" % k: dict(ok=v[0], reason=v[1], **v[2]) for k, v in valid.items()},
-           "rule": "greedy coordinate search from %s; a change is kept when > 1%% faster" % json.dumps(SEED),
+           "rule": "greedy coordinate search from %s; a change is kept when > %.1f%% faster (median of five "
+                   "timed batches)" % (json.dumps(SEED), 100 * KEEP_GAIN),
            "results": []}
     for w in inputs.WORKLOADS:
         if names and w.name not in names:
