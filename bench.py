@@ -127,6 +127,20 @@ def device_info() -> dict:
             "memory_gib": round(pr.total_memory / 2**30, 1)}
 
 
+def calibration_copy(nbytes: int):
+    """One elementwise kernel that reads and writes `nbytes` bytes each: the reference reading for the
+    FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+
+    n = nbytes // 2
+    src = torch.ones(n, dtype=torch.float16, device="cuda")
+    dst = torch.empty_like(src)
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    log("[bench] calibration copy of %d bytes done" % (2 * n))
+    del src, dst
+
+
 def time_workload(w, steps: int, warmup: int, pmc_copy: int = 0):
     import torch
 
@@ -163,13 +177,7 @@ def time_workload(w, steps: int, warmup: int, pmc_copy: int = 0):
     kernel_ms = e0.elapsed_time(e1) / steps
     ok = bool(torch.isfinite(o[-1, -1]).all().item()) and bool(torch.isfinite(lse[-1, -1]).all().item())
     if pmc_copy:
-        n = pmc_copy // 2
-        src = torch.ones(n, dtype=torch.float16, device=dev)
-        dst = torch.empty_like(src)
-        torch.neg(src, out=dst)  # one elementwise kernel: reads and writes `pmc_copy` bytes each
-        torch.cuda.synchronize()
-        log("[bench] calibration copy of %d bytes done" % (2 * n))
-        del src, dst
+        calibration_copy(pmc_copy)
     del q, k, v, o, lse
     torch.cuda.empty_cache()
     return wall_ms, kernel_ms, ok
@@ -210,19 +218,13 @@ def time_gemm(w, steps: int, warmup: int, pmc_copy: int = 0):
     kernel_ms = e0.elapsed_time(e1) / steps
     ok = bool(torch.isfinite(c[-1]).all().item())
     if pmc_copy:
-        n = pmc_copy // 2
-        src = torch.ones(n, dtype=torch.float16, device=dev)
-        dst = torch.empty_like(src)
-        torch.neg(src, out=dst)
-        torch.cuda.synchronize()
-        log("[bench] calibration copy of %d bytes done" % (2 * n))
-        del src, dst
+        calibration_copy(pmc_copy)
     del a, b, c
     torch.cuda.empty_cache()
     return wall_ms, kernel_ms, ok
 
 
-def time_decode(w, steps: int, warmup: int):
+def time_decode(w, steps: int, warmup: int, pmc_copy: int = 0):
     import torch
 
     from dnn_compiler_pipelining_amd import binding, inputs
@@ -255,6 +257,8 @@ def time_decode(w, steps: int, warmup: int):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ok = bool(torch.isfinite(o).all().item())
+    if pmc_copy:
+        calibration_copy(pmc_copy)
     del q, k, v, o, lse, ws
     torch.cuda.empty_cache()
     return (t1 - t0) * 1e3 / steps, e0.elapsed_time(e1) / steps, ok
@@ -410,18 +414,22 @@ def summarize_kernel_trace(d: str, workload: str, command: str):
 
 def summarize_traffic(fetch_dir: str, write_dir: str, workload: str, copy_bytes: int):
     res = {}
-    knm = kernel_name(workload)
+    # a step of the decode workload is two kernels (the split kernel and the combine kernel): its bytes are the
+    # sum of their per-dispatch means
+    knames = ("attn_fwd_kernel", "attn_combine_kernel") if is_decode(workload) else (kernel_name(workload),)
+    knm = " + ".join(knames)
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         vals = _per_dispatch(d, counter)
-        attn = [v for (kn, _), v in vals.items() if knm in kn]
-        other = [(kn, v) for (kn, _), v in vals.items() if knm not in kn]
-        if not attn:
+        per_kernel = {n: [v for (kn, _), v in vals.items() if n in kn] for n in knames}
+        other = [(kn, v) for (kn, _), v in vals.items() if not any(n in kn for n in knames)]
+        if not all(per_kernel.values()):
             raise RuntimeError("no %s dispatches in %s" % (knm, d))
-        # the calibration copy is the largest non-attention dispatch
+        # the calibration copy is the largest dispatch of another kernel
         copy_kib = max(v for _, v in other) if other else 0.0
         factor = copy_bytes / (copy_kib * 1024.0) if copy_kib else None
-        raw = sum(attn) / len(attn) * 1024.0
-        res[counter] = {"kib_per_launch": raw / 1024.0, "launches": len(attn), "copy_kib": copy_kib,
+        raw = sum(sum(v) / len(v) for v in per_kernel.values()) * 1024.0
+        launches = min(len(v) for v in per_kernel.values())
+        res[counter] = {"kib_per_launch": raw / 1024.0, "launches": launches, "copy_kib": copy_kib,
                         "copy_bytes": copy_bytes, "factor": factor,
                         "bytes_per_launch": raw * factor if factor else None}
     total = None
@@ -432,6 +440,8 @@ def summarize_traffic(fetch_dir: str, write_dir: str, workload: str, copy_bytes:
     if is_gemm(workload):
         g = inputs.GEMM_BY_NAME[workload]
         algo = 2 * (g.M * g.K + g.K * g.N + g.M * g.N)
+    elif is_decode(workload):
+        algo = inputs.DECODE_BY_NAME[workload].bytes
     else:
         w = inputs.BY_NAME[workload]
         algo = 2 * (2 * w.B * w.S * w.Hq * w.D + 2 * w.B * w.S * w.Hkv * w.D) + 4 * w.B * w.Hq * w.S
@@ -551,7 +561,8 @@ def main():
         if is_decode(name):
             w = inputs.DECODE_BY_NAME[name]
             steps, warmup = counts(w.bytes / 5e9)
-            wall_ms, kernel_ms, ok = time_decode(w, steps, warmup)
+            wall_ms, kernel_ms, ok = time_decode(w, steps, warmup, args.pmc_copy)
+            traffic = load_traffic(w.name)
             if not ok:
                 log("[bench] non-finite output")
                 return 1
@@ -562,7 +573,9 @@ def main():
                     "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
                     "data": "synthetic: seeded i.i.d. N(0,1) fp16 Q/K/V", "config": w.describe(),
                     "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                                 "frac": round(achieved / HBM_PEAK_GBS, 4),
+                                 "traffic": (round(traffic["hbm_bytes_per_launch"])
+                                             if traffic and traffic.get("hbm_bytes_per_launch") else None),
                                  "kernel": "attn_fwd_kernel (split-KV) + attn_combine_kernel",
                                  "kernel_ms": round(kernel_ms, 4), "bytes_per_step": w.bytes},
                     "device": device_info()}
