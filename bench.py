@@ -92,7 +92,7 @@ def kernel_fingerprint(workload: str = DEFAULT_WORKLOAD) -> str:
         files = hipbuild.GEMM_SOURCES + [os.path.join(hipbuild.CSRC, n) for n in ("gemm_kernel.h", "gfx950.h")]
     else:
         files = hipbuild.ATTN_SOURCES + [os.path.join(hipbuild.CSRC, n) for n in
-                                         ("attn_kernel.h", "variant.h", "tuned_table.h", "gfx950.h")]
+                                         ("attn_kernel.h", "attn_tile.h", "variant.h", "tuned_table.h", "gfx950.h")]
     h = hashlib.sha256()
     for path in files:
         with open(path, "rb") as f:
@@ -141,7 +141,7 @@ def calibration_copy(nbytes: int):
     del src, dst
 
 
-def time_workload(w, steps: int, warmup: int, pmc_copy: int = 0):
+def time_workload(w, steps: int, warmup: int, pmc_copy: int = 0, variant=None):
     import torch
 
     from dnn_compiler_pipelining_amd import binding, inputs
@@ -156,7 +156,7 @@ def time_workload(w, steps: int, warmup: int, pmc_copy: int = 0):
     torch.cuda.synchronize()
 
     def step():
-        binding.forward(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream)
+        binding.forward(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream, variant=variant)
 
     log("[bench] %s: %d warmup steps" % (w.name, warmup))
     for _ in range(warmup):
@@ -524,6 +524,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--pmc-copy", type=int, default=0)
+    ap.add_argument("--schedule", default=None, help="attention tile schedule to time instead of the tuned one "
+                    "(serial, overlap, pingpong, serial4, wide), for same-box comparisons")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-kernel-trace", nargs=2, metavar=("TRACE_DIR", "COMMAND"))
     ap.add_argument("--summarize-counters", nargs="+", metavar="DIR")
@@ -591,7 +593,7 @@ def main():
         else:
             w = inputs.BY_NAME[name]
             steps, warmup = counts(w.flops / 8e11)
-            wall_ms, kernel_ms, ok = time_workload(w, steps, warmup, args.pmc_copy)
+            wall_ms, kernel_ms, ok = time_workload(w, steps, warmup, args.pmc_copy, args.schedule)
         if not ok:
             log("[bench] non-finite output")
             return 1
@@ -621,6 +623,8 @@ def main():
                          "flops_per_launch": w.flops},
             "device": device_info(),
         }
+        if args.schedule and not gemm:
+            line["schedule"] = args.schedule
         if not args.no_cpu_baseline and not args.all:
             line["cpu_baseline"] = (cpu_baseline_gemm if gemm else cpu_baseline)(w, args.cpu_seconds)
         print(json.dumps(line), flush=True)

@@ -1,10 +1,11 @@
 """Python binding of libattn: argument marshalling only.
 
 The functions carry the names of the C entry points in include/attn.h
-(attn_fwd, attn_fwd_stream, attn_fwd_ex, attn_fwd_decode,
-attn_decode_workspace_size, attn_status_string, attn_version) and
-include/gemm.h (gemm_f16) and forward to them through ctypes; every step of
-the computation runs in the HIP kernels.  `forward()`, `decode()` and
+(attn_fwd, attn_fwd_stream, attn_fwd_ex, attn_fwd_variant, attn_fwd_decode,
+attn_fwd_decode_split, attn_decode_workspace_size,
+attn_decode_workspace_size_split, attn_status_string, attn_version) and
+include/gemm.h (gemm_f16, gemm_f16_waves) and forward to them through ctypes;
+every step of the computation runs in the HIP kernels.  `forward()`, `decode()` and
 `matmul()` are conveniences that allocate the outputs (and the decode
 workspace) with torch and check the tensors first.  There is no fallback: if libattn.so is missing or fails to
 load, every call raises.
@@ -28,8 +29,12 @@ ATTN_ERR_HIP = 5
 ATTN_ERR_OVERLAP = 6
 ATTN_ERR_WORKSPACE = 7
 
-EXPORTS = ("attn_fwd", "attn_fwd_stream", "attn_fwd_ex", "attn_fwd_decode", "attn_decode_workspace_size",
-           "attn_status_string", "attn_version", "gemm_f16")
+EXPORTS = ("attn_fwd", "attn_fwd_stream", "attn_fwd_ex", "attn_fwd_variant", "attn_fwd_decode",
+           "attn_fwd_decode_split", "attn_decode_workspace_size", "attn_decode_workspace_size_split",
+           "attn_status_string", "attn_version", "gemm_f16", "gemm_f16_waves")
+
+# Tile schedules (ATTN_SCHEDULE_* in include/attn.h), by name
+SCHEDULES = {"serial": 0, "overlap": 1, "pingpong": 2, "serial4": 3, "wide": 4}
 
 GEMM_B_KN = 0  # B stored [K, N]: C = A B
 GEMM_B_NK = 1  # B stored [N, K]: C = A B^T
@@ -60,6 +65,15 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
             lib.attn_fwd_stream.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
             lib.attn_fwd_ex.restype = i
             lib.attn_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
+            lib.attn_fwd_variant.restype = i
+            lib.attn_fwd_variant.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i, i, i, vp]
+            lib.attn_fwd_decode_split.restype = i
+            lib.attn_fwd_decode_split.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp, ctypes.c_size_t,
+                                                  vp]
+            lib.attn_decode_workspace_size_split.restype = ctypes.c_size_t
+            lib.attn_decode_workspace_size_split.argtypes = [i, i, i, i, i, i, i]
+            lib.gemm_f16_waves.restype = i
+            lib.gemm_f16_waves.argtypes = [vp, vp, vp, i, i, i, i, i, vp]
             lib.attn_fwd_decode.restype = i
             lib.attn_fwd_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, ctypes.c_size_t, vp]
             lib.attn_decode_workspace_size.restype = ctypes.c_size_t
@@ -104,6 +118,21 @@ def attn_fwd_ex(q, k, v, o, lse, B: int, Sq: int, Sk: int, Hq: int, Hkv: int, D:
                               float(scale), handle)
 
 
+def attn_fwd_variant(q, k, v, o, lse, B: int, Sq: int, Sk: int, Hq: int, Hkv: int, D: int, causal: int,
+                     scale: float, schedule: int, ring: int, xcd: int, lpt: int, stream) -> int:
+    """C attn_fwd_variant: attn_fwd_ex with an explicit kernel variant (-1 in a field: the tuned value)."""
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else (stream or 0)
+    return load().attn_fwd_variant(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Sq, Sk, Hq, Hkv, D,
+                                   int(causal), float(scale), int(schedule), int(ring), int(xcd), int(lpt), handle)
+
+
+def gemm_f16_waves(a, b, c, M: int, N: int, K: int, b_layout: int, waves: int, stream) -> int:
+    """C gemm_f16_waves: gemm_f16 with an explicit workgroup shape (waves 4 or 8; 0 the default)."""
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else (stream or 0)
+    return load().gemm_f16_waves(_ptr(a), _ptr(b), _ptr(c), int(M), int(N), int(K), int(b_layout), int(waves),
+                                 handle)
+
+
 def gemm_f16(a, b, c, M: int, N: int, K: int, b_layout: int, stream) -> int:
     """C gemm_f16: C[M,N] = A[M,K] B (b_layout 0, B [K,N]) or A B^T (b_layout 1, B [N,K]).  `stream` as for
     attn_fwd_stream."""
@@ -120,8 +149,34 @@ def attn_fwd_decode(q, k, v, o, lse, B: int, Sq: int, Sk: int, Hq: int, Hkv: int
                                   float(scale), _ptr(workspace), int(workspace_bytes), handle)
 
 
+def attn_fwd_decode_split(q, k, v, o, lse, B: int, Sq: int, Sk: int, Hq: int, Hkv: int, D: int, causal: int,
+                          scale: float, split_tiles: int, workspace, workspace_bytes: int, stream) -> int:
+    """C attn_fwd_decode_split: attn_fwd_decode with an explicit split length (64-key tiles per split)."""
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else (stream or 0)
+    return load().attn_fwd_decode_split(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Sq, Sk, Hq, Hkv, D,
+                                        int(causal), float(scale), int(split_tiles), _ptr(workspace),
+                                        int(workspace_bytes), handle)
+
+
 def attn_decode_workspace_size(B: int, Sq: int, Sk: int, Hq: int, Hkv: int, D: int) -> int:
     return int(load().attn_decode_workspace_size(B, Sq, Sk, Hq, Hkv, D))
+
+
+def attn_decode_workspace_size_split(B: int, Sq: int, Sk: int, Hq: int, Hkv: int, D: int, split_tiles: int) -> int:
+    return int(load().attn_decode_workspace_size_split(B, Sq, Sk, Hq, Hkv, D, int(split_tiles)))
+
+
+def variant_fields(variant) -> tuple:
+    """(schedule, ring, xcd, lpt) for attn_fwd_variant from None (all tuned), a schedule name, or a dict with
+    any of the keys schedule (name or number), ring, xcd, lpt; missing fields are -1 (tuned)."""
+    if variant is None:
+        return (-1, -1, -1, -1)
+    if isinstance(variant, str):
+        variant = {"schedule": variant}
+    sched = variant.get("schedule", -1)
+    if isinstance(sched, str):
+        sched = SCHEDULES[sched]
+    return (int(sched), int(variant.get("ring", -1)), int(variant.get("xcd", -1)), int(variant.get("lpt", -1)))
 
 
 def attn_status_string(status: int) -> str:
@@ -133,12 +188,13 @@ def attn_version() -> int:
 
 
 def forward(q, k, v, causal: bool = True, scale: float | None = None, out=None, lse=None, want_lse: bool = True,
-            stream=None):
+            stream=None, variant=None):
     """Run the kernel on torch tensors q [B,Sq,Hq,D], k/v [B,Sk,Hkv,D] (fp16, contiguous, same GPU).
 
     Sk may differ from Sq (causal then aligns the last query row with the last key; see attn_fwd_ex).
     Returns (o, lse) with o [B,Sq,Hq,D] fp16 and lse [B,Hq,Sq] fp32 (None if not wanted).  Enqueues on
-    `stream` (default: torch's current stream) and does not synchronise.
+    `stream` (default: torch's current stream) and does not synchronise.  `variant` (see variant_fields)
+    names a kernel variant through attn_fwd_variant; None runs the tuned one.
     """
     import torch
 
@@ -165,7 +221,10 @@ def forward(q, k, v, causal: bool = True, scale: float | None = None, out=None, 
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     with torch.cuda.device(q.device):
-        if Sk == S:
+        if variant is not None:
+            st = attn_fwd_variant(q, k, v, out, lse, B, S, Sk, Hq, Hkv, D, int(bool(causal)), float(scale),
+                                  *variant_fields(variant), stream)
+        elif Sk == S:
             st = attn_fwd_stream(q, k, v, out, lse, B, S, Hq, Hkv, D, int(bool(causal)), float(scale), stream)
         else:
             st = attn_fwd_ex(q, k, v, out, lse, B, S, Sk, Hq, Hkv, D, int(bool(causal)), float(scale), stream)
@@ -174,11 +233,12 @@ def forward(q, k, v, causal: bool = True, scale: float | None = None, out=None, 
     return out, lse
 
 
-def matmul(a, b, b_layout: int = GEMM_B_KN, out=None, stream=None):
+def matmul(a, b, b_layout: int = GEMM_B_KN, out=None, stream=None, waves: int = 0):
     """C = A B (b_layout 0, b [K, N]) or A B^T (b_layout 1, b [N, K]) on fp16 torch tensors, fp32 accumulation.
 
     a is [M, K]; all tensors contiguous float16 on one GPU.  Returns c [M, N] fp16.  Enqueues on `stream`
-    (default: torch's current stream) and does not synchronise.
+    (default: torch's current stream) and does not synchronise.  `waves` 4 or 8 picks the workgroup shape
+    through gemm_f16_waves (0: the default).
     """
     import torch
 
@@ -202,16 +262,21 @@ def matmul(a, b, b_layout: int = GEMM_B_KN, out=None, stream=None):
     if stream is None:
         stream = torch.cuda.current_stream(a.device)
     with torch.cuda.device(a.device):
-        st = gemm_f16(a, b, out, M, N, K, b_layout, stream)
+        if waves:
+            st = gemm_f16_waves(a, b, out, M, N, K, b_layout, waves, stream)
+        else:
+            st = gemm_f16(a, b, out, M, N, K, b_layout, stream)
     if st != ATTN_OK:
         raise AttnError(st)
     return out
 
 
 def decode(q, k, v, causal: bool = True, scale: float | None = None, out=None, lse=None, want_lse: bool = True,
-           workspace=None, stream=None):
+           workspace=None, stream=None, split_tiles: int = 0):
     """The split-KV path on torch tensors (same layout and result as forward()); allocates the workspace
-    with torch unless one is given.  Returns (o, lse)."""
+    with torch unless one is given (then on `stream`, so torch's allocator does not hand the memory to other
+    work before the kernels are done).  `split_tiles` > 0 fixes the split length (attn_fwd_decode_split).
+    Returns (o, lse)."""
     import torch
 
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -225,19 +290,24 @@ def decode(q, k, v, causal: bool = True, scale: float | None = None, out=None, l
         raise ValueError("shape mismatch: q %s k %s v %s" % (tuple(q.shape), tuple(k.shape), tuple(v.shape)))
     if scale is None:
         scale = 1.0 / math.sqrt(D)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    torch_stream = stream if isinstance(stream, torch.cuda.Stream) else None
     if out is None:
         out = torch.empty_like(q)
     if want_lse and lse is None:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
-    need = attn_decode_workspace_size(B, Sq, Sk, Hq, Hkv, D)
-    if workspace is None:
+    need = attn_decode_workspace_size_split(B, Sq, Sk, Hq, Hkv, D, split_tiles)
+    own_ws = workspace is None
+    if own_ws:
         workspace = torch.empty((max(need, 16) + 15) // 16 * 4, dtype=torch.float32, device=q.device)
     ws_bytes = workspace.numel() * workspace.element_size() if hasattr(workspace, "numel") else need
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device)
     with torch.cuda.device(q.device):
-        st = attn_fwd_decode(q, k, v, out, lse, B, Sq, Sk, Hq, Hkv, D, int(bool(causal)), float(scale), workspace,
-                             ws_bytes, stream)
+        st = attn_fwd_decode_split(q, k, v, out, lse, B, Sq, Sk, Hq, Hkv, D, int(bool(causal)), float(scale),
+                                   split_tiles, workspace, ws_bytes, stream)
     if st != ATTN_OK:
         raise AttnError(st)
+    if own_ws and torch_stream is not None and torch_stream != torch.cuda.current_stream(q.device):
+        # the workspace was allocated on the current stream but is used on another one
+        workspace.record_stream(torch_stream)
     return out, lse

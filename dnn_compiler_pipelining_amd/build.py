@@ -2,7 +2,9 @@
 from __future__ import annotations
 
 import os
+import shutil
 import subprocess
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -11,7 +13,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libattn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-ATTN_SOURCES = [os.path.join(CSRC, "attn_fwd.hip"), os.path.join(CSRC, "attn_api.cpp")]
+ATTN_SOURCES = [os.path.join(CSRC, "attn_fwd.hip"), os.path.join(CSRC, "attn_wide.hip"), os.path.join(CSRC, "attn_api.cpp")]
 GEMM_SOURCES = [os.path.join(CSRC, "gemm_fwd.hip"), os.path.join(CSRC, "gemm_api.cpp")]
 SOURCES = ATTN_SOURCES + GEMM_SOURCES
 
@@ -22,13 +24,27 @@ HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
 
 
 def build(out: str = LIB, extra_flags=()) -> str:
-    """Compile libattn.so (always recompiles).  Returns the library path."""
-    tmp = out + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, *HIP_FLAGS, *extra_flags, *SOURCES, "-o", tmp]
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        raise RuntimeError("hipcc failed (%d):\n%s\n%s" % (res.returncode, " ".join(cmd), res.stderr))
-    os.replace(tmp, out)
+    """Compile libattn.so (always recompiles): each source to an object in parallel, then one link.  Returns
+    the library path."""
+    tmpdir = tempfile.mkdtemp(prefix="libattn_build_")
+    try:
+        procs = []
+        for src in SOURCES:
+            obj = os.path.join(tmpdir, os.path.basename(src) + ".o")
+            cmd = [HIPCC, *[f for f in HIP_FLAGS if f != "-shared"], *extra_flags, "-c", src, "-o", obj]
+            procs.append((cmd, obj, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
+        for cmd, _, proc in procs:
+            _, err = proc.communicate()
+            if proc.returncode != 0:
+                raise RuntimeError("hipcc failed (%d):\n%s\n%s" % (proc.returncode, " ".join(cmd), err))
+        tmp = out + ".tmp%d" % os.getpid()
+        cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *[obj for _, obj, _ in procs], "-o", tmp]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError("hipcc link failed (%d):\n%s\n%s" % (res.returncode, " ".join(cmd), res.stderr))
+        os.replace(tmp, out)
+    finally:
+        shutil.rmtree(tmpdir, ignore_errors=True)
     return out
 
 

@@ -1,52 +1,47 @@
 // attn_api.cpp -- the extern "C" boundary of libattn (declared in include/attn.h).
 //
 // Validation runs before any HIP call, so every error path is reachable
-// without a GPU.  Valid calls enqueue exactly one kernel and return.
+// without a GPU.  Valid calls enqueue their kernels and return.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
 #include <cstdint>
-#include <cstdlib>
-#include <cstring>
 
 #include "attn.h"
 #include "attn_kernel.h"
 
 namespace {
 
-constexpr int kVersion = 1 * 10000 + 1 * 100 + 0;
+constexpr int kVersion = 1 * 10000 + 2 * 100 + 0;
 constexpr int kMaxSeq = 1 << 30;  // sequence lengths up to 2^30 keep all tile arithmetic in int
 
-// The variant for a shape: the tuned choice (variant.h), unless the
-// environment overrides a field.  LIBATTN_SCHEDULE=serial|overlap|pingpong|serial4,
-// LIBATTN_RING=2|4, LIBATTN_XCD=0|1 and LIBATTN_LPT=0|1 are read on every
-// call, so tests and the schedule search can switch them; all variants give
-// bitwise identical results.
-// The schedule named by LIBATTN_SCHEDULE, or -1.
-int env_schedule() {
-  if (const char* s = std::getenv("LIBATTN_SCHEDULE")) {
-    if (std::strcmp(s, "serial") == 0) return libattn::SCHEDULE_SERIAL;
-    if (std::strcmp(s, "overlap") == 0) return libattn::SCHEDULE_OVERLAP;
-    if (std::strcmp(s, "pingpong") == 0) return libattn::SCHEDULE_PINGPONG;
-    if (std::strcmp(s, "serial4") == 0) return libattn::SCHEDULE_SERIAL4;
-  }
-  return -1;
-}
+// Fields of a requested variant: -1 takes the tuned value (variant.h) for the
+// nearest measured shape.  The library reads no environment and keeps no
+// state: attn_fwd_variant passes a request explicitly (the schedule search
+// and the tests use it), every other entry point asks for the tuned variant.
+struct Request {
+  int schedule, ring, xcd, lpt;
+};
+constexpr Request kTunedRequest = {-1, -1, -1, -1};
 
-libattn::Variant choose_variant(int B, int Sq, int Sk, int Hq, int Hkv) {
-  libattn::Variant v = libattn::tuned_variant(B, Sq, Sk, Hq, Hkv);
-  if (env_schedule() >= 0) v.schedule = env_schedule();
-  auto flag = [](const char* name, int& field, int lo, int hi) {
-    if (const char* s = std::getenv(name)) {
-      const int x = std::atoi(s);
-      if (x == lo || x == hi) field = x;
-    }
-  };
-  flag("LIBATTN_RING", v.ring, 2, 4);
-  flag("LIBATTN_XCD", v.xcd, 0, 1);
-  flag("LIBATTN_LPT", v.lpt, 0, 1);
-  if (!libattn::variant_valid(v)) v = libattn::Variant{libattn::SCHEDULE_SERIAL, 4, 1, 1};
-  return v;
+// The variant a call runs, or false if the request names a value that does
+// not exist or a schedule the head dimension does not run.  D = 128 runs
+// every schedule; D = 64 the serial ones (SERIAL4 unless SERIAL is asked for:
+// its one-head workgroups, 142 VGPRs and 34 KiB of LDS, fit three to a CU,
+// where SERIAL's eight-wave workgroups fit one; measured on MI355X at B=16
+// S=8192 Hq=32 Hkv=8: 878 against 822 TFLOP/s); D = 256 SERIAL4 only.
+bool choose_variant(const Request& r, int B, int Sq, int Sk, int Hq, int Hkv, int D, libattn::Variant& v) {
+  v = libattn::tuned_variant(B, Sq, Sk, Hq, Hkv);
+  if (D == 64) v.schedule = libattn::SCHEDULE_SERIAL4;
+  if (D == 256) v.schedule = libattn::SCHEDULE_SERIAL4;
+  if (r.schedule >= 0) v.schedule = r.schedule;
+  if (r.ring >= 0) v.ring = r.ring;
+  if (r.xcd >= 0) v.xcd = r.xcd;
+  if (r.lpt >= 0) v.lpt = r.lpt;
+  if (!libattn::variant_valid(v)) return false;
+  if (D == 64) return v.schedule == libattn::SCHEDULE_SERIAL || v.schedule == libattn::SCHEDULE_SERIAL4;
+  if (D == 256) return v.schedule == libattn::SCHEDULE_SERIAL4;
+  return true;
 }
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
@@ -73,7 +68,8 @@ int validate(const void* q, const void* k, const void* v, const void* o, const f
   const uint64_t kv_bytes = (uint64_t)B * Sk * Hkv * D * 2;
   const uint64_t lse_bytes = (uint64_t)B * Hq * Sq * 4;
   if (overlaps(o, q_bytes, q, q_bytes) || overlaps(o, q_bytes, k, kv_bytes) || overlaps(o, q_bytes, v, kv_bytes) ||
-      overlaps(o, q_bytes, lse, lse_bytes))
+      overlaps(o, q_bytes, lse, lse_bytes) || overlaps(lse, lse_bytes, q, q_bytes) ||
+      overlaps(lse, lse_bytes, k, kv_bytes) || overlaps(lse, lse_bytes, v, kv_bytes))
     return ATTN_ERR_OVERLAP;
   return ATTN_OK;
 }
@@ -114,7 +110,7 @@ struct DecodePlan {
   int n_pt, n_splits, split_tiles;
   int64_t ws_o_floats, ws_lse_floats;
 };
-DecodePlan decode_plan(int B, int Sq, int Sk, int Hq, int Hkv, int D) {
+DecodePlan decode_plan(int B, int Sq, int Sk, int Hq, int Hkv, int D, int split_tiles) {
   DecodePlan d;
   const int64_t g = Hq / Hkv;
   d.n_pt = (int)((g * Sq + 127) / 128);
@@ -123,17 +119,46 @@ DecodePlan decode_plan(int B, int Sq, int Sk, int Hq, int Hkv, int D) {
   int64_t want = (kDecodeTarget + base - 1) / base;
   want = want < 1 ? 1 : (want > tiles ? tiles : want);
   d.split_tiles = (int)((tiles + want - 1) / want);
-  // LIBATTN_DECODE_SPLIT_TILES=n (read by both attn_decode_workspace_size and
-  // attn_fwd_decode) fixes the split length instead, for tuning
-  if (const char* e = std::getenv("LIBATTN_DECODE_SPLIT_TILES")) {
-    const long n = std::atol(e);
-    if (n >= 1 && n <= (1 << 24)) d.split_tiles = (int)(n < tiles ? n : tiles);
-  }
+  // an explicit split length (attn_fwd_decode_split), for tuning and tests
+  if (split_tiles > 0) d.split_tiles = (int)(split_tiles < tiles ? split_tiles : tiles);
   d.n_splits = (int)((tiles + d.split_tiles - 1) / d.split_tiles);
   const int64_t rows = (int64_t)B * Hq * Sq;
   d.ws_lse_floats = rows * d.n_splits;
   d.ws_o_floats = d.ws_lse_floats * D;
   return d;
+}
+
+// The forward pass with a variant request (attn_fwd_ex and attn_fwd_variant).
+int forward(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Sq, int Sk, int Hq, int Hkv,
+            int D, int causal, float scale, const Request& req, void* stream) {
+  const int st = validate(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, D, causal, scale);
+  if (st != ATTN_OK) return st;
+  libattn::Variant var;
+  if (!choose_variant(req, B, Sq, Sk, Hq, Hkv, D, var)) return ATTN_ERR_UNSUPPORTED;
+
+  libattn::Params p = base_params(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, D, causal, scale);
+  p.schedule = var.schedule;
+  p.ring = var.ring;
+  p.xcd = var.xcd;
+  p.lpt = var.lpt;
+  hipError_t e;
+  if (p.schedule == libattn::SCHEDULE_WIDE) {
+    // four heads of a KV group per workgroup at 64 query rows, or two at 128,
+    // or one at 256, whichever divides the GQA ratio
+    p.hpw = p.g % 4 == 0 ? 4 : p.g % 2 == 0 ? 2 : 1;
+    p.pairs = (p.g + p.hpw - 1) / p.hpw;
+    const int rows = 256 / p.hpw;
+    p.n_qt = (Sq + rows - 1) / rows;
+    if (libattn::grid_blocks_wide(p) < 0) return ATTN_ERR_SHAPE;
+    e = libattn::launch_attn_wide(p, static_cast<hipStream_t>(stream));
+  } else {
+    p.n_qt = (Sq + 127) / 128;
+    // query heads per workgroup: a pair (two wave groups), or one for SERIAL4
+    p.pairs = p.schedule == libattn::SCHEDULE_SERIAL4 ? p.g : (p.g + 1) / 2;
+    if (libattn::grid_blocks(p) < 0) return ATTN_ERR_SHAPE;
+    e = libattn::launch_attn_fwd(p, static_cast<hipStream_t>(stream));
+  }
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
 }  // namespace
@@ -142,29 +167,12 @@ extern "C" {
 
 int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Sq, int Sk, int Hq,
                 int Hkv, int D, int causal, float scale, void* stream) {
-  const int st = validate(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, D, causal, scale);
-  if (st != ATTN_OK) return st;
+  return forward(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, D, causal, scale, kTunedRequest, stream);
+}
 
-  libattn::Params p = base_params(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, D, causal, scale);
-  p.n_qt = (Sq + 127) / 128;
-  const libattn::Variant var = choose_variant(B, Sq, Sk, Hq, Hkv);
-  // HD 256 runs the SERIAL4 schedule only.  HD 64 runs the serial
-  // schedules only, SERIAL4 unless SERIAL is named in LIBATTN_SCHEDULE: its
-  // one-head workgroups (142 VGPRs, 34 KiB of LDS) fit three to a CU, where
-  // SERIAL's 8-wave workgroups fit one (measured on MI355X at B=16 S=8192
-  // Hq=32 Hkv=8: 878 against 822 TFLOP/s)
-  if (D == 256) p.schedule = libattn::SCHEDULE_SERIAL4;
-  else if (D == 128) p.schedule = var.schedule;
-  else p.schedule = env_schedule() == libattn::SCHEDULE_SERIAL ? libattn::SCHEDULE_SERIAL : libattn::SCHEDULE_SERIAL4;
-  // query heads per workgroup: a pair (two wave groups), or one for SERIAL4
-  p.pairs = p.schedule == libattn::SCHEDULE_SERIAL4 ? p.g : (p.g + 1) / 2;
-  p.ring = var.ring;
-  p.xcd = var.xcd;
-  p.lpt = var.lpt;
-  if (libattn::grid_blocks(p) < 0) return ATTN_ERR_SHAPE;
-
-  const hipError_t e = libattn::launch_attn_fwd(p, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+int attn_fwd_variant(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Sq, int Sk, int Hq,
+                     int Hkv, int D, int causal, float scale, int schedule, int ring, int xcd, int lpt, void* stream) {
+  return forward(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, D, causal, scale, Request{schedule, ring, xcd, lpt}, stream);
 }
 
 int attn_fwd_stream(const void* q, const void* k, const void* v, void* o, float* lse, int B, int S, int Hq, int Hkv,
@@ -177,20 +185,25 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   return attn_fwd_stream(q, k, v, o, lse, B, S, Hq, Hkv, D, causal, scale, nullptr);
 }
 
-size_t attn_decode_workspace_size(int B, int Sq, int Sk, int Hq, int Hkv, int D) {
+size_t attn_decode_workspace_size_split(int B, int Sq, int Sk, int Hq, int Hkv, int D, int split_tiles) {
   if (B < 1 || Sq < 1 || Sk < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || Sq > kMaxSeq || Sk > kMaxSeq) return 0;
   if (D != 64 && D != 128 && D != 256) return 0;
   if ((int64_t)(Hq / Hkv) * Sq > kMaxSeq) return 0;
-  const DecodePlan d = decode_plan(B, Sq, Sk, Hq, Hkv, D);
+  const DecodePlan d = decode_plan(B, Sq, Sk, Hq, Hkv, D, split_tiles);
   return (size_t)(d.ws_o_floats + d.ws_lse_floats) * sizeof(float);
 }
 
-int attn_fwd_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Sq, int Sk, int Hq,
-                    int Hkv, int D, int causal, float scale, void* workspace, size_t workspace_bytes, void* stream) {
+size_t attn_decode_workspace_size(int B, int Sq, int Sk, int Hq, int Hkv, int D) {
+  return attn_decode_workspace_size_split(B, Sq, Sk, Hq, Hkv, D, 0);
+}
+
+int attn_fwd_decode_split(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Sq, int Sk,
+                          int Hq, int Hkv, int D, int causal, float scale, int split_tiles, void* workspace,
+                          size_t workspace_bytes, void* stream) {
   const int st = validate(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, D, causal, scale);
   if (st != ATTN_OK) return st;
   if ((int64_t)(Hq / Hkv) * Sq > kMaxSeq) return ATTN_ERR_SHAPE;  // packed rows of a KV group stay below 2^30
-  const DecodePlan d = decode_plan(B, Sq, Sk, Hq, Hkv, D);
+  const DecodePlan d = decode_plan(B, Sq, Sk, Hq, Hkv, D, split_tiles);
   const size_t need = (size_t)(d.ws_o_floats + d.ws_lse_floats) * sizeof(float);
   if (!workspace || workspace_bytes < need || !aligned16(workspace)) return ATTN_ERR_WORKSPACE;
   const uint64_t q_bytes = (uint64_t)B * Sq * Hq * D * 2, kv_bytes = (uint64_t)B * Sk * Hkv * D * 2;
@@ -201,7 +214,7 @@ int attn_fwd_decode(const void* q, const void* k, const void* v, void* o, float*
     return ATTN_ERR_OVERLAP;
 
   libattn::Params p = base_params(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, D, causal, scale);
-  const libattn::Variant var = choose_variant(B, Sq, Sk, Hq, Hkv);
+  const libattn::Variant var = libattn::tuned_variant(B, Sq, Sk, Hq, Hkv);
   p.schedule = libattn::SCHEDULE_SERIAL4;
   p.ring = var.ring;
   p.xcd = var.xcd;
@@ -217,6 +230,12 @@ int attn_fwd_decode(const void* q, const void* k, const void* v, void* o, float*
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
+int attn_fwd_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Sq, int Sk, int Hq,
+                    int Hkv, int D, int causal, float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  return attn_fwd_decode_split(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, D, causal, scale, 0, workspace, workspace_bytes,
+                               stream);
+}
+
 const char* attn_status_string(int status) {
   switch (status) {
     case ATTN_OK: return "ok";
@@ -227,7 +246,7 @@ const char* attn_status_string(int status) {
              "the GEMM K and N multiples of 8";
     case ATTN_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case ATTN_ERR_HIP: return "HIP launch error";
-    case ATTN_ERR_OVERLAP: return "output or workspace overlaps an input or output";
+    case ATTN_ERR_OVERLAP: return "an output or the workspace overlaps an input or another output";
     case ATTN_ERR_WORKSPACE: return "workspace missing, too small or not 16-byte aligned";
     default: return "unknown status";
   }

@@ -37,61 +37,15 @@
 #include <utility>
 
 #include "attn_kernel.h"
+#include "attn_tile.h"
 #include "gfx950.h"
 
 namespace libattn {
 
 constexpr int BM = 128;          // query rows per wave group
-constexpr int BN = 64;           // keys per KV tile
 // Waves per workgroup: 8 (two wave groups on two heads of a KV group), or 4
 // (one head) for the SERIAL4 schedule.
 __host__ __device__ constexpr int waves_of(int sched) { return sched == SCHEDULE_SERIAL4 ? 4 : 8; }
-constexpr float NEG_INF = -__builtin_inff();
-constexpr float M_INIT = -1e30f; // finite start for the running max
-constexpr float LN2 = 0.693147180559945309f;
-// Sum-checked lazy rescaling: a tile's exponentials are first taken against
-// the running max m (log2 units) as it stands.  If no row's sum over the tile
-// exceeds RS_MAX, every P of the tile is at most RS_MAX (fp16 P and the fp32
-// sums stay in range) and m stays; otherwise -- in practice only on a row's
-// first tile -- m is raised to the tile max and the exponentials are redone.
-// No tile max is needed in the common case, and the final O / l and
-// LSE = m + log2(l) are exact for any m.
-constexpr float RS_MAX = 256.0f;
-
-// LDS layouts (bytes), per head dimension HD (64, 128 or 256).  A tile slot is a
-// run of 1 KiB DMA instructions.
-//  K: 64 key rows of 2*HD + 16 B.  Consecutive keys fall 68 (HD 128), 36
-//    (HD 64) or 132 (HD 256) banks apart, so the 16 keys of a ds_read_b128 pass at one
-//    16-byte column cover all 64 banks once; every K fragment read is a
-//    compile-time offset from one per-lane base.  One 16-byte lane slot per
-//    row lands in the padding.
-//  V: 64 key rows of 2*HD B whose 16-byte chunks are XOR-swizzled: by
-//    4*(row & 3) for HD 128 and 256, by 4*((row >> 1) & 1) for HD 64.  A
-//    ds_read_b64_tr_b16 group reads 4 consecutive rows x 32 B; with the
-//    swizzle the 4 rows of the two groups of a half-wave (4 rows x 64 B) hit
-//    all 64 banks once.  Across the 32-wide d blocks the per-lane address
-//    changes by an XOR with 64*db.
-template <int kHD>
-struct Geo {
-  static_assert(kHD == 64 || kHD == 128 || kHD == 256, "head dimension");
-  static constexpr int HD = kHD;
-  static constexpr int KC = kHD / 8;                 // 16-byte chunks per K/V row
-  static constexpr int K_ROWB = 2 * kHD + 16;
-  static constexpr int K_TILEB = BN * K_ROWB;        // 17408 | 9216 | 33792
-  static constexpr int K_DMA = K_TILEB / 1024;       // 17 | 9 | 33
-
-  static constexpr int V_ROWB = 2 * kHD;
-  static constexpr int V_TILEB = BN * V_ROWB;        // 16384 | 8192 | 32768
-  static constexpr int V_DMA = V_TILEB / 1024;       // 16 | 8 | 32
-
-  static constexpr int V_ROWS_PER_DMA = 1024 / V_ROWB;
-  static constexpr int NKK = kHD / 16;               // 16-wide d steps of QK^T
-  static constexpr int NDB = kHD / 32;               // 32-wide d blocks of O^T
-  static_assert(K_TILEB % 1024 == 0 && V_TILEB % 1024 == 0, "tile slots are whole DMA instructions");
-  static_assert(V_DMA % 8 == 0, "every wave of 4 or 8 issues the same number of V instructions");
-  // physical 16-byte chunk of logical chunk c in V row r is c ^ vswz(r)
-  __host__ __device__ static constexpr int vswz(int r) { return kHD == 64 ? 4 * ((r >> 1) & 1) : 4 * (r & 3); }
-};
 // K tiles rotate through three slots, V tiles through two: K_t stays in LDS
 // for the whole iteration after its QK^T, so a softmax that has to be redone
 // can recompute S^T from it.  SERIAL4 keeps two K slots (the serial loop
@@ -102,17 +56,6 @@ static_assert(k_slots_of(SCHEDULE_SERIAL) * Geo<128>::K_TILEB + V_SLOTS * Geo<12
               "the K and V rings fit the 160 KiB LDS");
 static_assert(2 * (k_slots_of(SCHEDULE_SERIAL4) * Geo<128>::K_TILEB + V_SLOTS * Geo<128>::V_TILEB) <= 160 * 1024,
               "two SERIAL4 workgroups fit the 160 KiB LDS");
-
-__device__ __forceinline__ float pair_max(float x) {
-  // lanes l and l^32 hold the same query: combine their partial results
-  auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
-}
-__device__ __forceinline__ float pair_sum(float x) {
-  auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
-}
-
 
 // Steps of an mma block, for NKK = HD/16 k steps of QK^T and NDB = HD/32
 // blocks of O^T.  A QK step (kk, x = sb) adds K[32sb.., 16kk..] x
@@ -371,8 +314,8 @@ void attn_fwd_kernel(Params p) {
   // The work is cut into parts with compile-time indices so that a fused mma
   // block can place each part between two MFMAs:
   //   E0..E31 P = 2^(s*cs - m) for score e; every second part also packs an
-  //           earlier pair to fp16 and adds it to the row sum (dot2 against
-  //           (1, 1)), one pair behind to hide the exponential's latency
+  //           earlier pair to fp16 and adds it to the row sum (add_pair_f16),
+  //           one pair behind to hide the exponential's latency
   //   E32     packs the last pair
   //   E33     row sum across the lane pair
   //   C       the check: does any row's tile sum exceed RS_MAX?  (ballot,
@@ -459,9 +402,7 @@ void attn_fwd_kernel(Params p) {
       constexpr int pp = decltype(pc)::value, kk = pp >> 2, c = 2 * (pp & 3);
       pd[kk][c] = (_Float16)st.t[pp & 1][0];
       pd[kk][c + 1] = (_Float16)st.t[pp & 1][1];
-      const f16x2 pr = {pd[kk][c], pd[kk][c + 1]};
-      const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
-      st.rq[kk & 1] = __builtin_amdgcn_fdot2(pr, ones, st.rq[kk & 1], false);
+      add_pair_f16(st.rq[kk & 1], f16x2{pd[kk][c], pd[kk][c + 1]});
     };
     if constexpr (e < 32) {  // score e = pair e/2, element e%2: (sb, r)
       constexpr int pair = e >> 1, u = e & 1, sb = pair >> 3, r = 2 * (pair & 7) + u;

@@ -5,7 +5,6 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
-#include <cstdlib>
 
 #include "gemm.h"
 #include "gemm_kernel.h"
@@ -41,9 +40,11 @@ int validate(const void* a, const void* b, const void* c, int M, int N, int K, i
 
 extern "C" {
 
-int gemm_f16(const void* a, const void* b, void* c, int M, int N, int K, int b_layout, void* stream) {
+int gemm_f16_waves(const void* a, const void* b, void* c, int M, int N, int K, int b_layout, int waves,
+                   void* stream) {
   const int st = validate(a, b, c, M, N, K, b_layout);
   if (st != ATTN_OK) return st;
+  if (waves != 0 && waves != 4 && waves != 8) return ATTN_ERR_UNSUPPORTED;
   if (M == 0 || N == 0) return ATTN_OK;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (K == 0) {  // the empty sum: C = 0
@@ -61,15 +62,14 @@ int gemm_f16(const void* a, const void* b, void* c, int M, int N, int K, int b_l
   p.ntm = (M + 255) / 256;
   p.ntn = (N + 255) / 256;
   p.nkt = (K + 63) / 64;
-  // LIBATTN_GEMM_WAVES=4|8 picks the workgroup shape (read at each call)
-  p.waves = kDefaultWaves;
-  if (const char* e = std::getenv("LIBATTN_GEMM_WAVES")) {
-    const int w = std::atoi(e);
-    if (w == 4 || w == 8) p.waves = w;
-  }
+  p.waves = waves == 0 ? kDefaultWaves : waves;
   if ((int64_t)p.ntm * p.ntn > 0x7fffffff) return ATTN_ERR_SHAPE;
   const hipError_t e = libattn::launch_gemm(p, s);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+int gemm_f16(const void* a, const void* b, void* c, int M, int N, int K, int b_layout, void* stream) {
+  return gemm_f16_waves(a, b, c, M, N, K, b_layout, 0, stream);
 }
 
 }  // extern "C"

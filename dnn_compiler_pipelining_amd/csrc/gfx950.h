@@ -42,17 +42,49 @@ __device__ __forceinline__ void lds_barrier() {
 // address lds_base + 16*l with the 16 bytes at base + off.  Issued as inline
 // assembly so the compiler does not add conservative waits before unrelated
 // LDS reads; the caller waits with dma_wait() before the barrier that
-// publishes the tile.  M0 is restored afterwards.
+// publishes the tile.  M0 is restored afterwards.  An LDS DMA that reads M0
+// needs one wait state after the scalar write of M0 (the compiler's hazard
+// pass does not look inside inline assembly), hence the s_nop.
 __device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds_base) {
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
       "global_load_lds_dwordx4 %1, %2\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
       : "v"(off), "s"(base), "s"(lds_base)
       : "memory");
+}
+// dma16 without saving M0: the assembly declares M0 clobbered, so the
+// compiler keeps nothing of its own there across it.  Two instructions fewer
+// per load, for kernels that issue loads back to back.
+__device__ __forceinline__ void dma16_m0(const void* base, uint32_t off, uint32_t lds_base) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(off), "s"(base), "s"(lds_base)
+      : "memory", "m0");
+}
+// dma16_m0 for the lanes in `lanes` only (EXEC is set for the one load and
+// restored): lane l of them still writes LDS byte lds_base + 16*l, so waves
+// that pass disjoint lane sets with the same lds_base fill one 1 KiB run
+// together, each with one instruction.
+__device__ __forceinline__ void dma16_m0_lanes(const void* base, uint32_t off, uint32_t lds_base, uint64_t lanes) {
+  uint64_t saved;
+  asm volatile(
+      "s_mov_b64 %0, exec\n\t"
+      "s_mov_b64 exec, %4\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b64 exec, %0"
+      : "=&s"(saved)
+      : "v"(off), "s"(base), "s"(lds_base), "s"(lanes)
+      : "memory", "m0");
 }
 __device__ __forceinline__ void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 

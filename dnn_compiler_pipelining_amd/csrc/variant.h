@@ -27,7 +27,17 @@ namespace libattn {
 //             each; two workgroups share a CU, so the two waves on a SIMD
 //             come from independently synchronised workgroups and drift out
 //             of phase (one's softmax beside the other's MFMAs)
-enum Schedule { SCHEDULE_SERIAL = 0, SCHEDULE_OVERLAP = 1, SCHEDULE_PINGPONG = 2, SCHEDULE_SERIAL4 = 3 };
+//   WIDE    : 64 query rows per wave (attn_wide.hip): one wave per SIMD, each
+//             K/V fragment read from LDS feeds two MFMAs, the overlap
+//             schedule inside each wave, K/V loaded two tiles ahead
+//             (head dimension 128)
+enum Schedule {
+  SCHEDULE_SERIAL = 0,
+  SCHEDULE_OVERLAP = 1,
+  SCHEDULE_PINGPONG = 2,
+  SCHEDULE_SERIAL4 = 3,
+  SCHEDULE_WIDE = 4
+};
 
 struct Variant {
   int schedule;  // Schedule
@@ -46,7 +56,7 @@ struct TunedEntry {
 #include "tuned_table.h"  // kTuned[], kTunedCount
 
 inline bool variant_valid(const Variant& v) {
-  return v.schedule >= SCHEDULE_SERIAL && v.schedule <= SCHEDULE_SERIAL4 && (v.ring == 2 || v.ring == 4) &&
+  return v.schedule >= SCHEDULE_SERIAL && v.schedule <= SCHEDULE_WIDE && (v.ring == 2 || v.ring == 4) &&
          (v.xcd == 0 || v.xcd == 1) && (v.lpt == 0 || v.lpt == 1);
 }
 

@@ -30,14 +30,18 @@ ROOT = os.path.dirname(PKG)
 TABLE = os.path.join(PKG, "csrc", "tuned_table.h")
 PROFILE = os.path.join(ROOT, "profiles", "schedule_search.json")
 
-SCHEDULES = ("serial", "overlap", "pingpong", "serial4")  # Schedule enum order in csrc/variant.h
+SCHEDULES = ("serial", "overlap", "pingpong", "serial4", "wide")  # Schedule enum order in csrc/variant.h
+
+
 def workgroups_per_cu(schedule: str, hd: int) -> int:
-    """serial4 runs two 4-wave workgroups per CU, except at head dimension 256 (one); the others one of 8 waves."""
+    """serial4 runs two 4-wave workgroups per CU, except at head dimension 256 (one); wide one of 4 waves; the
+    others one of 8 waves."""
     return 2 if schedule.startswith("serial4") and hd <= 128 else 1
 
 
 def waves_per_simd(schedule: str, hd: int) -> int:
-    return 1 if schedule.startswith("serial4") and hd > 128 else 2
+    """wide (64 query rows per wave) and serial4 at head dimension 256 run one wave per SIMD; the others two."""
+    return 1 if schedule == "wide" or (schedule.startswith("serial4") and hd > 128) else 2
 RINGS = (2, 4)
 SWITCHES = (0, 1)
 SEED = {"schedule": "serial", "ring": 4, "xcd": 1, "lpt": 1}
@@ -52,8 +56,25 @@ REGISTER_FILE = 512
 MAX_LDS = 160 * 1024
 
 
+def loop_scratch(text: str, symbol: str) -> int:
+    """Scratch (spill) instructions inside the loops of one kernel of a device asm file: the instructions of
+    every basic block the compiler annotates as a loop header or as inside a loop."""
+    start = text.index("\n" + symbol + ":")
+    end = text.index(".Lfunc_end", start)
+    n, in_loop = 0, False
+    for line in text[start:end].split("\n"):
+        s = line.strip()
+        if re.match(r"^\.LBB\d+_\d+:", s):
+            in_loop = "Loop Header" in s or "in Loop:" in s
+            continue
+        if in_loop and s.startswith("scratch_"):
+            n += 1
+    return n
+
+
 def kernel_resources(asm_path: str):
-    """{(schedule, ring, hd): {vgpr, agpr, vgpr_spill, scratch, lds}} from the AMDGPU metadata of a device asm file.
+    """{(schedule, ring, hd): {vgpr, agpr, vgpr_spill, scratch, lds, loop_scratch}} from the AMDGPU metadata
+    of a device asm file and the annotated loop structure of its code.
 
     The split-KV instances (attn_fwd_decode) appear under the schedule name "serial4-split".  On gfx950
     `vgpr` (.vgpr_count) is the unified register count, AGPRs included; `agpr` is the AGPR part of it."""
@@ -62,43 +83,65 @@ def kernel_resources(asm_path: str):
     out = {}
     for block in re.split(r"\n  - ", meta)[1:]:
         m = re.search(r"\.name:\s+\S*attn_fwd_kernelILi(\d)ELi(\d)ELi(\d+)ELb([01])E", block)
-        if not m:
+        mw = re.search(r"\.name:\s+\S*attn_wide_kernelILi(\d)E", block)
+        if not m and not mw:
             continue
 
         def num(key):
             mm = re.search(r"\." + key + r":\s+(\d+)", block)
             return int(mm.group(1)) if mm else 0
 
-        sched = SCHEDULES[int(m.group(1))] + ("-split" if m.group(4) == "1" else "")
-        out[(sched, int(m.group(2)), int(m.group(3)))] = dict(
+        if mw:  # the wide kernel: head dimension 128, template argument = fragment prefetch depth
+            key = ("wide", int(mw.group(1)), 128)
+        else:
+            key = (SCHEDULES[int(m.group(1))] + ("-split" if m.group(4) == "1" else ""), int(m.group(2)),
+                   int(m.group(3)))
+        sym = re.search(r"\.name:\s+(\S+)", block).group(1)
+        out[key] = dict(
             vgpr=num("vgpr_count"), agpr=num("agpr_count"), vgpr_spill=num("vgpr_spill_count"),
-            scratch=num("private_segment_fixed_size"), lds=num("group_segment_fixed_size"))
+            scratch=num("private_segment_fixed_size"), lds=num("group_segment_fixed_size"),
+            loop_scratch=loop_scratch(text, sym))
     return out
 
 
 def check_valid(res: dict, schedule: str = "serial", hd: int = 128) -> tuple[bool, str]:
-    """A variant is valid when its waves per SIMD fit the register file with no spills and no scratch, and the
-    LDS of the workgroups that share a CU fits it."""
+    """A variant is valid when its waves per SIMD fit the register file, no spill traffic runs inside its tile
+    loop (spill code executed once per workgroup, in the prologue, the epilogue or the last tile's rare
+    redo, is allowed: `wide` at 64 query rows per wave has a little), and the LDS of the workgroups that share
+    a CU fits it.  Without the loop structure (res without loop_scratch) any spill is invalid."""
     max_regs = REGISTER_FILE // waves_per_simd(schedule, hd)
     if res["vgpr"] > max_regs:
         return False, "%d VGPRs (AGPRs included) > %d" % (res["vgpr"], max_regs)
-    if res["vgpr_spill"] or res["scratch"]:
-        return False, "spills %d VGPRs / %d B scratch" % (res["vgpr_spill"], res["scratch"])
+    if res.get("loop_scratch", res["vgpr_spill"] or res["scratch"]):
+        return False, "spills %d VGPRs / %d B scratch, %s scratch instructions in the tile loop" % (
+            res["vgpr_spill"], res["scratch"], res.get("loop_scratch", "?"))
     wg = workgroups_per_cu(schedule, hd)
     if wg * res["lds"] > MAX_LDS:
         return False, "%d x %d B LDS > %d" % (wg, res["lds"], MAX_LDS)
+    if res["vgpr_spill"]:
+        return True, "ok (%d VGPRs spilled outside the tile loop)" % res["vgpr_spill"]
     return True, "ok"
 
 
-def valid_variants(asm_path: str | None = None):
-    """{(schedule, ring, hd): (valid, reason, resources)} for the current sources."""
+def valid_variants(asm_paths=None):
+    """{(schedule, ring, hd): (valid, reason, resources)} for the current sources (device assembly of every
+    attention kernel source, or the given files)."""
     from dnn_compiler_pipelining_amd import build
 
-    if asm_path is None:
-        fd, asm_path = tempfile.mkstemp(suffix=".s")
-        os.close(fd)
-        build.device_asm(asm_path)
-    res = kernel_resources(asm_path)
+    if asm_paths is None:
+        asm_paths = []
+        for src in build.ATTN_SOURCES:
+            if not src.endswith(".hip"):
+                continue
+            fd, path = tempfile.mkstemp(suffix=".s")
+            os.close(fd)
+            build.device_asm(path, src)
+            asm_paths.append(path)
+    elif isinstance(asm_paths, str):
+        asm_paths = [asm_paths]
+    res = {}
+    for path in asm_paths:
+        res.update(kernel_resources(path))
     return {k: check_valid(v, k[0], k[2]) + (v,) for k, v in res.items()}
 
 
@@ -122,12 +165,9 @@ def measure(w, point: dict, q, k, v, o, lse) -> float:
     """TFLOP/s of one variant on one workload (median of five timed batches)."""
     from dnn_compiler_pipelining_amd import binding
 
-    os.environ["LIBATTN_SCHEDULE"] = point["schedule"]
-    os.environ["LIBATTN_RING"] = str(point["ring"])
-    os.environ["LIBATTN_XCD"] = str(point["xcd"])
-    os.environ["LIBATTN_LPT"] = str(point["lpt"])
     reps = max(2, min(50, int(0.15 / max(w.flops / 1e15, 1e-6))))  # about 0.15 s per batch at 1 PFLOP/s
-    ms = sorted(_time(lambda: binding.forward(q, k, v, w.causal, w.scale, o, lse), reps) for _ in range(5))[2]
+    ms = sorted(_time(lambda: binding.forward(q, k, v, w.causal, w.scale, o, lse, variant=point), reps)
+                for _ in range(5))[2]
     return w.flops / ms / 1e9
 
 
@@ -168,8 +208,6 @@ def search_workload(w, valid, log=print):
                     best, best_rate, improved = cand, r, True
     del q, k, v, o, lse
     torch.cuda.empty_cache()
-    for key in ("LIBATTN_SCHEDULE", "LIBATTN_RING", "LIBATTN_XCD", "LIBATTN_LPT"):
-        os.environ.pop(key, None)
     return {"workload": w.name, "B": w.B, "Sq": w.S, "Sk": w.S, "Hq": w.Hq, "Hkv": w.Hkv, "best": best,
             "best_tflops": round(best_rate, 1),
             "measured": [{"schedule": s, "ring": r, "xcd": x, "lpt": l, "tflops": round(t, 1)}

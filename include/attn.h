@@ -18,7 +18,8 @@
  * Tensors (all device memory, owned and allocated by the caller, contiguous):
  *   q   fp16 [B][S][Hq][D]     k, v  fp16 [B][S][Hkv][D]
  *   o   fp16 [B][S][Hq][D]     (written; must not overlap q, k, v or lse)
- *   lse fp32 [B][Hq][S]        (written; may be NULL when not wanted)
+ *   lse fp32 [B][Hq][S]        (written; must not overlap q, k, v or o; may be
+ *                              NULL when not wanted)
  * Every pointer must be 16-byte aligned.  fp16 is IEEE binary16; o is rounded
  * to nearest even from fp32.  Internal offsets are 64-bit, so tensors larger
  * than 4 GiB are supported.
@@ -41,13 +42,10 @@
  * synchronisation.  The library allocates no memory, keeps no state between
  * calls, is thread-safe, and gives bitwise identical results run to run.
  *
- * The environment variable LIBATTN_SCHEDULE (read at each call) selects the
- * kernel's tile schedule: "serial", "overlap", "pingpong" or "serial4" (the
- * serial schedule in 4-wave workgroups, two per CU); unset or any other value
- * gives the schedule tuned for the nearest measured shape.  D = 64 runs
- * "serial" when that is named and "serial4" otherwise; D = 256 runs "serial4"
- * only.  All schedules give bitwise identical results, so each serves as a
- * cross-check of the others.
+ * Kernel variants.  Every entry point runs the variant tuned for the nearest
+ * measured shape (a table compiled into the library); attn_fwd_variant names
+ * one explicitly.  All variants give bitwise identical results, so each
+ * serves as a cross-check of the others.  The library reads no environment.
  *
  * Errors: on invalid arguments nothing is launched and a nonzero ATTN_ERR_*
  * code is returned; a failed launch returns ATTN_ERR_HIP.  No exception
@@ -66,10 +64,11 @@ enum {
   ATTN_OK = 0,
   ATTN_ERR_NULL = 1,        /* a required pointer is NULL */
   ATTN_ERR_SHAPE = 2,       /* a size < 1 or > 2^30, Hq % Hkv != 0, causal not 0/1, causal with Sq > Sk, scale not finite */
-  ATTN_ERR_UNSUPPORTED = 3, /* D other than 64, 128 or 256, or Hkv * D * 2 * 64 >= 2^32 */
+  ATTN_ERR_UNSUPPORTED = 3, /* D other than 64, 128 or 256, or Hkv * D * 2 * 64 >= 2^32; attn_fwd_variant: a
+                               variant that does not exist or that the head dimension does not run */
   ATTN_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
   ATTN_ERR_HIP = 5,         /* the HIP runtime reported an error at launch */
-  ATTN_ERR_OVERLAP = 6,     /* o overlaps q, k, v or lse; or the workspace overlaps any tensor */
+  ATTN_ERR_OVERLAP = 6,     /* o or lse overlaps another tensor; or the workspace overlaps any tensor */
   ATTN_ERR_WORKSPACE = 7    /* attn_fwd_decode: workspace NULL, smaller than attn_decode_workspace_size(), or not
                                16-byte aligned */
 };
@@ -87,6 +86,32 @@ int attn_fwd_stream(const void* q, const void* k, const void* v, void* o, float*
 int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Sq, int Sk, int Hq,
                 int Hkv, int D, int causal, float scale, void* stream);
 
+/* Tile schedules of the forward kernel (attn_fwd_variant):
+ *   SERIAL    8-wave workgroups, 32 query rows per wave; per tile QK^T, softmax, PV back to back
+ *   OVERLAP   the same workgroups; each wave runs the softmax of tile j between the MFMAs of QK^T(j+1)
+ *             and PV(j-1)
+ *   PINGPONG  the same workgroups; two wave groups offset by half a tile alternate MFMA and softmax
+ *   SERIAL4   the serial schedule in 4-wave, one-head workgroups, two per CU
+ *   WIDE      4-wave workgroups, one wave per SIMD, 64 query rows per wave, the overlap schedule inside
+ *             each wave, K/V loaded two tiles ahead (D = 128 only)
+ * D = 64 runs SERIAL and SERIAL4, D = 256 SERIAL4, D = 128 all five. */
+enum {
+  ATTN_SCHEDULE_SERIAL = 0,
+  ATTN_SCHEDULE_OVERLAP = 1,
+  ATTN_SCHEDULE_PINGPONG = 2,
+  ATTN_SCHEDULE_SERIAL4 = 3,
+  ATTN_SCHEDULE_WIDE = 4
+};
+
+/* attn_fwd_ex with an explicit kernel variant, for schedule search and cross-checks: `schedule` is an
+ * ATTN_SCHEDULE_* value, `ring` the fragment prefetch depth (2 or 4), `xcd` 1 to give each XCD whole
+ * (batch, KV head) groups, `lpt` 1 to run the longest causal query tiles first; -1 in any of them takes
+ * the tuned value.  A value that does not exist, or a schedule the head dimension does not run, returns
+ * ATTN_ERR_UNSUPPORTED and launches nothing.  Results are bitwise identical for every variant. */
+int attn_fwd_variant(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Sq, int Sk, int Hq,
+                     int Hkv, int D, int causal, float scale, int schedule, int ring, int xcd, int lpt,
+                     void* stream);
+
 /* Split-KV path for few query rows against many keys (decode, short chunks): the same operation and
  * arguments as attn_fwd_ex, computed in two kernels.  The first packs the g = Hq / Hkv query heads of a KV
  * group with their Sq query rows into 128-row tiles, so each K/V tile is read once for all of them, and
@@ -96,12 +121,19 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
  * `workspace` is caller-owned device memory of at least attn_decode_workspace_size(...) bytes, 16-byte
  * aligned, not overlapping any tensor; its contents on entry do not matter and are overwritten.  Needs
  * (Hq / Hkv) * Sq <= 2^30.  Both kernels are enqueued on `stream`; the workspace must not be reused
- * before they complete.  The split length is chosen for about 512 workgroups; the environment variable
- * LIBATTN_DECODE_SPLIT_TILES=n (64-key tiles per split, read by both functions below) overrides it. */
+ * before they complete.  The split length is chosen for about 512 workgroups. */
 int attn_fwd_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Sq, int Sk, int Hq,
                     int Hkv, int D, int causal, float scale, void* workspace, size_t workspace_bytes, void* stream);
 /* Workspace bytes attn_fwd_decode needs for these sizes (0 for sizes it rejects). */
 size_t attn_decode_workspace_size(int B, int Sq, int Sk, int Hq, int Hkv, int D);
+
+/* attn_fwd_decode with an explicit split length: `split_tiles` 64-key tiles per split (capped at the
+ * number of key tiles; 0 or less takes the planned length).  The workspace must hold
+ * attn_decode_workspace_size_split(..., split_tiles) bytes. */
+int attn_fwd_decode_split(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Sq, int Sk,
+                          int Hq, int Hkv, int D, int causal, float scale, int split_tiles, void* workspace,
+                          size_t workspace_bytes, void* stream);
+size_t attn_decode_workspace_size_split(int B, int Sq, int Sk, int Hq, int Hkv, int D, int split_tiles);
 /* Static, NUL-terminated description of a status code ("unknown status" for others). */
 const char* attn_status_string(int status);
 

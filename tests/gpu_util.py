@@ -10,6 +10,9 @@ import torch
 from dnn_compiler_pipelining_amd import binding, inputs
 from oracle import oracle as oracle_mod
 
+# Every tile schedule at head dimension 128 (binding.SCHEDULES); all give bitwise identical results.
+SCHEDULES_D128 = ("serial", "overlap", "pingpong", "serial4", "wide")
+
 # Parity bar for fp16 outputs against the fp64 oracle.
 MAX_ABS_O = 4e-3
 MEAN_ABS_O = 5e-4
@@ -27,12 +30,13 @@ def require_gpu():
     binding.load()  # raises if libattn.so is missing: no fallback
 
 
-def run(q, k, v, causal, scale):
-    """q/k/v on the GPU.  Outputs are pre-filled with NaN so unwritten elements fail."""
+def run(q, k, v, causal, scale, variant=None):
+    """q/k/v on the GPU.  Outputs are pre-filled with NaN so unwritten elements fail.  `variant` names a
+    kernel variant (binding.variant_fields); None runs the tuned one."""
     o = torch.full_like(q, float("nan"))
     B, S, Hq, _ = q.shape
     lse = torch.full((B, Hq, S), float("nan"), dtype=torch.float32, device=q.device)
-    binding.forward(q, k, v, causal=causal, scale=scale, out=o, lse=lse)
+    binding.forward(q, k, v, causal=causal, scale=scale, out=o, lse=lse, variant=variant)
     torch.cuda.synchronize()
     return o, lse
 
@@ -58,9 +62,9 @@ def check(st, tag=""):
     assert st["max_lse"] <= MAX_ABS_LSE, "%s: max |dLSE| %.3e > %.1e" % (tag, st["max_lse"], MAX_ABS_LSE)
 
 
-def full_parity(q, k, v, causal, scale, tag):
+def full_parity(q, k, v, causal, scale, tag, variant=None):
     """Whole-tensor comparison (small shapes).  q/k/v are CPU fp16 tensors."""
-    o, lse = run(q.cuda(), k.cuda(), v.cuda(), causal, scale)
+    o, lse = run(q.cuda(), k.cuda(), v.cuda(), causal, scale, variant)
     O, L = oracle_mod.attn_full(q.numpy(), k.numpy(), v.numpy(), causal, scale)
     st = stats(o.cpu().numpy(), lse.cpu().numpy(), O, L)
     check(st, tag)

@@ -79,16 +79,24 @@ def test_chunk_equals_suffix_of_square_bitwise(Sq, Sk):
     assert torch.equal(o1, o2[:, Sk - Sq:]) and torch.equal(l1, l2[:, :, Sk - Sq:])
 
 
-def test_rect_schedules_bitwise_identical(monkeypatch):
-    q, k, v = cpu_qkv(1, 333, 1100, 16, 4, seed=51)
+# (B, Sq, Sk, Hq, Hkv, causal): bottom-right offsets that are and are not multiples of the tiles, and
+# Sk <= 64 (a single key tile) where the overlap and ping-pong schedules take their n_tiles == 1 paths
+RECT = [(1, 333, 1100, 16, 4, 1), (1, 333, 1100, 16, 4, 0), (2, 1, 64, 8, 2, 1), (1, 17, 40, 8, 8, 1),
+        (1, 64, 64, 4, 1, 0), (1, 100, 63, 8, 2, 0), (1, 129, 700, 12, 3, 1)]
+
+
+@pytest.mark.parametrize("B,Sq,Sk,Hq,Hkv,causal", RECT, ids=str)
+def test_rect_schedules_bitwise_identical(B, Sq, Sk, Hq, Hkv, causal):
+    q, k, v = cpu_qkv(B, Sq, Sk, Hq, Hkv, seed=51 + Sq + Sk)
+    tag = "rect B%d Sq%d Sk%d Hq%d Hkv%d causal%d" % (B, Sq, Sk, Hq, Hkv, causal)
+    U.say(tag)
+    st = U.full_parity(q, k, v, bool(causal), SC, tag)
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
-    monkeypatch.delenv("LIBATTN_SCHEDULE", raising=False)
-    o1, l1 = U.run(qd, kd, vd, True, SC)
-    for sched in ("overlap", "pingpong", "serial4"):
-        monkeypatch.setenv("LIBATTN_SCHEDULE", sched)
-        o2, l2 = U.run(qd, kd, vd, True, SC)
+    o1, l1 = U.run(qd, kd, vd, bool(causal), SC)
+    for sched in U.SCHEDULES_D128:
+        o2, l2 = U.run(qd, kd, vd, bool(causal), SC, sched)
         assert torch.equal(o1, o2) and torch.equal(l1, l2), sched
-    monkeypatch.delenv("LIBATTN_SCHEDULE")
+    assert st["finite"]
 
 
 def test_ex_validation_launches_nothing():

@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 import torch
 
-from dnn_compiler_pipelining_amd import inputs
+from dnn_compiler_pipelining_amd import binding, inputs
 from oracle import oracle as oracle_mod
 from tests import gpu_util as U
 
@@ -63,19 +63,22 @@ def test_d64_larger_sampled():
         U.check(st, "D64 B%d S%d batch %d" % (B, S, b))
 
 
-def test_d64_variants_bitwise_identical(monkeypatch):
-    """Ring depth and workgroup order give the same bits; at D=64 only serial runs as named, the others run serial4."""
+def test_d64_variants_bitwise_identical():
+    """Ring depth and workgroup order give the same bits, for each schedule D=64 runs (serial, serial4);
+    the schedules written for D=128 only are refused with ATTN_ERR_UNSUPPORTED and launch nothing."""
     q, k, v = cpu_qkv(1, 700, 700, 8, 2, seed=62)
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
-    for key in ("LIBATTN_SCHEDULE", "LIBATTN_RING", "LIBATTN_XCD", "LIBATTN_LPT"):
-        monkeypatch.delenv(key, raising=False)
     o1, l1 = U.run(qd, kd, vd, True, SC)
-    for sched in ("serial", "overlap", "pingpong", "serial4"):
-        for ring in ("2", "4"):
-            for xcd, lpt in (("0", "0"), ("1", "1")):
-                monkeypatch.setenv("LIBATTN_SCHEDULE", sched)
-                monkeypatch.setenv("LIBATTN_RING", ring)
-                monkeypatch.setenv("LIBATTN_XCD", xcd)
-                monkeypatch.setenv("LIBATTN_LPT", lpt)
-                o2, l2 = U.run(qd, kd, vd, True, SC)
-                assert torch.equal(o1, o2) and torch.equal(l1, l2), (sched, ring, xcd, lpt)
+    for sched in ("serial", "serial4"):
+        for ring in (2, 4):
+            for xcd, lpt in ((0, 0), (1, 1)):
+                var = {"schedule": sched, "ring": ring, "xcd": xcd, "lpt": lpt}
+                o2, l2 = U.run(qd, kd, vd, True, SC, var)
+                assert torch.equal(o1, o2) and torch.equal(l1, l2), var
+    for sched in sorted(set(binding.SCHEDULES) - set(("serial", "serial4"))):
+        o = torch.full_like(qd, float("nan"))
+        st = binding.attn_fwd_variant(qd, kd, vd, o, None, 1, 700, 700, 8, 2, 64, 1, SC, binding.SCHEDULES[sched],
+                                      -1, -1, -1, None)
+        assert st == binding.ATTN_ERR_UNSUPPORTED, sched
+        torch.cuda.synchronize()
+        assert bool(torch.isnan(o).all().item()), sched

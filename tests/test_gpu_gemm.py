@@ -35,10 +35,14 @@ def mats(M, N, K, layout, seed, dist="normal", lim=0):
     return a, b
 
 
-def run(a, b, layout, M, N, K, guard=4096):
-    """C on the GPU, from a NaN-filled buffer with a guard region after it that must stay NaN."""
+def run(a, b, layout, M, N, K, guard=4096, waves=0):
+    """C on the GPU, from a NaN-filled buffer with a guard region after it that must stay NaN.  `waves` 4 or 8
+    picks the workgroup shape (gemm_f16_waves); 0 runs gemm_f16."""
     buf = torch.full((M * N + guard,), float("nan"), dtype=torch.float16, device="cuda")
-    st = binding.gemm_f16(a, b, buf, M, N, K, layout, None)
+    if waves:
+        st = binding.gemm_f16_waves(a, b, buf, M, N, K, layout, waves, None)
+    else:
+        st = binding.gemm_f16(a, b, buf, M, N, K, layout, None)
     assert st == binding.ATTN_OK, binding.attn_status_string(st)
     torch.cuda.synchronize()
     assert bool(torch.isnan(buf[M * N:]).all().item()), "write past the end of C"
@@ -167,15 +171,13 @@ def test_validation_launches_nothing():
 
 @pytest.mark.parametrize("layout", [KN, NK], ids=["kn", "nk"])
 @pytest.mark.parametrize("M,N,K", [(300, 264, 136), (513, 520, 520), (1000, 1024, 1000), (64, 8, 4096)], ids=str)
-def test_four_wave_workgroups_give_the_same_bits(monkeypatch, M, N, K, layout):
+def test_four_wave_workgroups_give_the_same_bits(M, N, K, layout):
     """Workgroups of 4 waves (128 x 128 per wave) and of 8 (128 x 64) feed every accumulator the same MFMAs in
     the same order, so they give the same bits; the 4-wave result also meets the oracle bar."""
     a, b = mats(M, N, K, layout, seed=500 + M + K)
     ad, bd = a.cuda(), b.cuda()
-    monkeypatch.setenv("LIBATTN_GEMM_WAVES", "8")
-    c8 = run(ad, bd, layout, M, N, K)
-    monkeypatch.setenv("LIBATTN_GEMM_WAVES", "4")
-    c4 = run(ad, bd, layout, M, N, K)
+    c8 = run(ad, bd, layout, M, N, K, waves=8)
+    c4 = run(ad, bd, layout, M, N, K, waves=4)
     assert torch.equal(c8, c4)
     check_normal(c4.cpu().numpy(), G.gemm(a.numpy(), b.numpy(), layout), G.abs_products(a.numpy(), b.numpy(), layout),
                  K, "4 waves M%d N%d K%d layout %d" % (M, N, K, layout))

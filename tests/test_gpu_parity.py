@@ -172,42 +172,37 @@ def test_gpu_validation_errors_launch_nothing():
     assert bool(torch.isnan(o).all().item())
 
 
+# S = 1, 33 and 64 give a single key tile: the overlap and ping-pong schedules take their n_tiles == 1
+# paths there; 8192 is the bench workload's sequence length
 @pytest.mark.parametrize("B,S,Hq,Hkv,causal", [(1, 1000, 8, 2, 1), (2, 333, 16, 4, 0), (1, 257, 6, 2, 1),
-                                               (1, 8192, 64, 8, 1)], ids=str)
-def test_schedules_bitwise_identical(monkeypatch, B, S, Hq, Hkv, causal):
-    """The tile schedules (default serial, overlap, ping-pong, serial4) against each other: each
-    accumulator sees the same arithmetic in the same order, so any LDS race (a slot rewritten while
-    another wave still reads it) would show up as a difference."""
+                                               (1, 1, 8, 2, 1), (2, 33, 8, 2, 1), (1, 64, 16, 4, 0),
+                                               (1, 64, 8, 1, 1), (1, 130, 12, 3, 1), (1, 8192, 64, 8, 1)], ids=str)
+def test_schedules_bitwise_identical(B, S, Hq, Hkv, causal):
+    """The tile schedules against each other: each accumulator sees the same arithmetic in the same order,
+    so any LDS race (a slot rewritten while another wave still reads it) would show up as a difference."""
     q, k, v = cpu_qkv(B, S, Hq, Hkv, seed=90 + S)
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
-    monkeypatch.delenv("LIBATTN_SCHEDULE", raising=False)
+    U.say("schedules B%d S%d Hq%d Hkv%d causal%d" % (B, S, Hq, Hkv, causal))
     o1, l1 = U.run(qd, kd, vd, bool(causal), SC)
-    for sched in ("overlap", "pingpong", "serial4"):
-        monkeypatch.setenv("LIBATTN_SCHEDULE", sched)
-        o2, l2 = U.run(qd, kd, vd, bool(causal), SC)
+    for sched in U.SCHEDULES_D128:
+        o2, l2 = U.run(qd, kd, vd, bool(causal), SC, sched)
         assert torch.equal(o1, o2) and torch.equal(l1, l2), sched
-    monkeypatch.delenv("LIBATTN_SCHEDULE")
 
 
 @pytest.mark.parametrize("B,S,Hq,Hkv,causal", [(1, 700, 8, 2, 1), (2, 257, 12, 3, 0)], ids=str)
-def test_all_variants_bitwise_identical(monkeypatch, B, S, Hq, Hkv, causal):
+def test_all_variants_bitwise_identical(B, S, Hq, Hkv, causal):
     """Every point of the searched variant space (schedule x prefetch depth x workgroup order) gives the
     same bits as the default."""
     q, k, v = cpu_qkv(B, S, Hq, Hkv, seed=95 + S)
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
-    for key in ("LIBATTN_SCHEDULE", "LIBATTN_RING", "LIBATTN_XCD", "LIBATTN_LPT"):
-        monkeypatch.delenv(key, raising=False)
     o1, l1 = U.run(qd, kd, vd, bool(causal), SC)
-    for sched in ("serial", "overlap", "pingpong", "serial4"):
-        for ring in ("2", "4"):
-            for xcd in ("0", "1"):
-                for lpt in ("0", "1"):
-                    monkeypatch.setenv("LIBATTN_SCHEDULE", sched)
-                    monkeypatch.setenv("LIBATTN_RING", ring)
-                    monkeypatch.setenv("LIBATTN_XCD", xcd)
-                    monkeypatch.setenv("LIBATTN_LPT", lpt)
-                    o2, l2 = U.run(qd, kd, vd, bool(causal), SC)
-                    assert torch.equal(o1, o2) and torch.equal(l1, l2), (sched, ring, xcd, lpt)
+    for sched in U.SCHEDULES_D128:
+        for ring in (2, 4):
+            for xcd in (0, 1):
+                for lpt in (0, 1):
+                    var = {"schedule": sched, "ring": ring, "xcd": xcd, "lpt": lpt}
+                    o2, l2 = U.run(qd, kd, vd, bool(causal), SC, var)
+                    assert torch.equal(o1, o2) and torch.equal(l1, l2), var
 
 
 def spiked_qkv(S, Hq, Hkv, hd, seed, spikes):
@@ -226,32 +221,26 @@ def spiked_qkv(S, Hq, Hkv, hd, seed, spikes):
 
 @pytest.mark.parametrize("hd", [128, 64, 256], ids=lambda x: "D%d" % x)
 @pytest.mark.parametrize("causal", [1, 0], ids=lambda x: "causal%d" % x)
-def test_running_max_raised_mid_row(monkeypatch, hd, causal):
+def test_running_max_raised_mid_row(hd, causal):
     """Keys 400 and 800 (tiles 6 and 12) score far above everything before them: parity with the oracle,
     the same bits from every schedule the head dimension runs, and the split-KV path on the last rows."""
     q, k, v = spiked_qkv(1000, 8, 2, hd, seed=77, spikes=[(400, 1.0), (800, 2.0)])
-    monkeypatch.delenv("LIBATTN_SCHEDULE", raising=False)
     tag = "spiked D%d causal%d" % (hd, causal)
     U.say(tag)
     U.full_parity(q, k, v, bool(causal), SC, tag)
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
     o1, l1 = U.run(qd, kd, vd, bool(causal), SC)
-    scheds = ("serial", "overlap", "pingpong", "serial4") if hd == 128 else ("serial", "serial4")
+    scheds = U.SCHEDULES_D128 if hd == 128 else ("serial", "serial4") if hd == 64 else ("serial4",)
     for sched in scheds:
-        monkeypatch.setenv("LIBATTN_SCHEDULE", sched)
-        o2, l2 = U.run(qd, kd, vd, bool(causal), SC)
+        o2, l2 = U.run(qd, kd, vd, bool(causal), SC, sched)
         assert torch.equal(o1, o2) and torch.equal(l1, l2), sched
-    monkeypatch.delenv("LIBATTN_SCHEDULE")
     # the last 4 query rows through the split-KV path against the same rows of the regular path, with
     # the planned splits and with splits of 8 tiles (512 keys), which put both spikes inside a split
     qt = qd[:, -4:].contiguous()
     ot, lt = torch.empty_like(qt), torch.empty((1, 8, 4), dtype=torch.float32, device=qt.device)
     binding.forward(qt, kd, vd, causal=bool(causal), scale=SC, out=ot, lse=lt)
-    for split_tiles in (None, "8"):
-        if split_tiles:
-            monkeypatch.setenv("LIBATTN_DECODE_SPLIT_TILES", split_tiles)
-        od, ld = binding.decode(qt, kd, vd, causal=bool(causal), scale=SC)
+    for split_tiles in (0, 8):
+        od, ld = binding.decode(qt, kd, vd, causal=bool(causal), scale=SC, split_tiles=split_tiles)
         torch.cuda.synchronize()
         assert float((od.float() - ot.float()).abs().max()) <= U.MAX_ABS_O, split_tiles
         assert float((ld - lt).abs().max()) <= U.MAX_ABS_LSE, split_tiles
-    monkeypatch.delenv("LIBATTN_DECODE_SPLIT_TILES", raising=False)

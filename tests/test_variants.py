@@ -27,11 +27,27 @@ def test_every_compiled_variant_is_valid():
     (dict(vgpr=264, agpr=64, vgpr_spill=0, scratch=0, lds=1024), "VGPRs"),
     (dict(vgpr=200, agpr=0, vgpr_spill=3, scratch=12, lds=1024), "spills"),
     (dict(vgpr=200, agpr=0, vgpr_spill=0, scratch=16, lds=1024), "spills"),
+    (dict(vgpr=200, agpr=0, vgpr_spill=3, scratch=12, lds=1024, loop_scratch=2), "tile loop"),
     (dict(vgpr=200, agpr=0, vgpr_spill=0, scratch=0, lds=160 * 1024 + 16), "LDS"),
 ])
 def test_check_valid_rejects_over_budget(res, reason):
     ok, why = tune.check_valid(res)
     assert not ok and reason in why
+
+
+def test_check_valid_allows_spills_outside_the_tile_loop():
+    res = dict(vgpr=512, agpr=256, vgpr_spill=28, scratch=112, lds=135168, loop_scratch=0)
+    ok, why = tune.check_valid(res, "wide")
+    assert ok and "outside the tile loop" in why
+    assert not tune.check_valid(dict(res, loop_scratch=1), "wide")[0]
+    assert not tune.check_valid(res, "serial")[0]  # 512 registers are one wave per SIMD
+
+
+def test_loop_scratch_reads_the_loop_annotations():
+    asm = "\n".join(["", "k:", "  scratch_load_dword v0, off, off", ".LBB0_1:  ; =>This Inner Loop Header: Depth=1",
+                      "  v_add_f32 v1, v1, v1", "  scratch_store_dword off, v1, off", ".LBB0_2:  ;   in Loop: Header=BB0_1 Depth=1",
+                      "  scratch_load_dword v2, off, off", ".LBB0_3:", "  scratch_load_dword v3, off, off", ".Lfunc_end0:"])
+    assert tune.loop_scratch(asm, "k") == 2
 
 
 def test_check_valid_counts_two_workgroups_per_cu_for_serial4():
