@@ -28,9 +28,11 @@ ATTN_ERR_ALIGN = 4
 ATTN_ERR_HIP = 5
 ATTN_ERR_OVERLAP = 6
 ATTN_ERR_WORKSPACE = 7
+ATTN_ERR_TOO_LARGE = 8
+ATTN_STATIC_WORKSPACE_BYTES = 64 << 20  # the library's own split-KV workspace per GPU (attn_fwd_decode_static)
 
 EXPORTS = ("attn_fwd", "attn_fwd_stream", "attn_fwd_ex", "attn_fwd_variant", "attn_fwd_decode",
-           "attn_fwd_decode_split", "attn_decode_workspace_size", "attn_decode_workspace_size_split",
+           "attn_fwd_decode_split", "attn_fwd_decode_static", "attn_decode_workspace_size", "attn_decode_workspace_size_split",
            "attn_status_string", "attn_version", "gemm_f16", "gemm_f16_waves")
 
 # Tile schedules (ATTN_SCHEDULE_* in include/attn.h), by name
@@ -76,6 +78,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
             lib.gemm_f16_waves.argtypes = [vp, vp, vp, i, i, i, i, i, vp]
             lib.attn_fwd_decode.restype = i
             lib.attn_fwd_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, ctypes.c_size_t, vp]
+            lib.attn_fwd_decode_static.restype = i
+            lib.attn_fwd_decode_static.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
             lib.attn_decode_workspace_size.restype = ctypes.c_size_t
             lib.attn_decode_workspace_size.argtypes = [i, i, i, i, i, i]
             lib.attn_status_string.restype = ctypes.c_char_p
@@ -124,6 +128,15 @@ def attn_fwd_variant(q, k, v, o, lse, B: int, Sq: int, Sk: int, Hq: int, Hkv: in
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else (stream or 0)
     return load().attn_fwd_variant(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Sq, Sk, Hq, Hkv, D,
                                    int(causal), float(scale), int(schedule), int(ring), int(xcd), int(lpt), handle)
+
+
+def attn_fwd_decode_static(q, k, v, o, lse, B: int, Sq: int, Sk: int, Hq: int, Hkv: int, D: int, causal: int,
+                           scale: float, stream) -> int:
+    """C attn_fwd_decode_static: the split-KV path on the library's own per-GPU workspace (no allocation).
+    `stream` as for attn_fwd_stream; the current device must be the stream's."""
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else (stream or 0)
+    return load().attn_fwd_decode_static(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Sq, Sk, Hq, Hkv, D,
+                                         int(causal), float(scale), handle)
 
 
 def gemm_f16_waves(a, b, c, M: int, N: int, K: int, b_layout: int, waves: int, stream) -> int:

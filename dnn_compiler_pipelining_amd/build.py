@@ -13,7 +13,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libattn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-ATTN_SOURCES = [os.path.join(CSRC, "attn_fwd.hip"), os.path.join(CSRC, "attn_wide.hip"), os.path.join(CSRC, "attn_api.cpp")]
+ATTN_SOURCES = [os.path.join(CSRC, "attn_fwd.hip"), os.path.join(CSRC, "attn_wide.hip"), os.path.join(CSRC, "attn_api.cpp"),
+                os.path.join(CSRC, "attn_static_ws.hip")]
 GEMM_SOURCES = [os.path.join(CSRC, "gemm_fwd.hip"), os.path.join(CSRC, "gemm_api.cpp")]
 SOURCES = ATTN_SOURCES + GEMM_SOURCES
 

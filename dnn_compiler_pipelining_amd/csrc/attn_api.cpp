@@ -248,6 +248,7 @@ const char* attn_status_string(int status) {
     case ATTN_ERR_HIP: return "HIP launch error";
     case ATTN_ERR_OVERLAP: return "an output or the workspace overlaps an input or another output";
     case ATTN_ERR_WORKSPACE: return "workspace missing, too small or not 16-byte aligned";
+    case ATTN_ERR_TOO_LARGE: return "the sizes need more workspace than the library's static array holds";
     default: return "unknown status";
   }
 }

@@ -69,8 +69,10 @@ enum {
   ATTN_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
   ATTN_ERR_HIP = 5,         /* the HIP runtime reported an error at launch */
   ATTN_ERR_OVERLAP = 6,     /* o or lse overlaps another tensor; or the workspace overlaps any tensor */
-  ATTN_ERR_WORKSPACE = 7    /* attn_fwd_decode: workspace NULL, smaller than attn_decode_workspace_size(), or not
+  ATTN_ERR_WORKSPACE = 7,   /* attn_fwd_decode: workspace NULL, smaller than attn_decode_workspace_size(), or not
                                16-byte aligned */
+  ATTN_ERR_TOO_LARGE = 8    /* attn_fwd_decode_static: the sizes need more workspace than
+                               ATTN_STATIC_WORKSPACE_BYTES */
 };
 
 /* Forward pass on the null stream.  Returns ATTN_OK or an ATTN_ERR_* code. */
@@ -134,6 +136,23 @@ int attn_fwd_decode_split(const void* q, const void* k, const void* v, void* o, 
                           int Hq, int Hkv, int D, int causal, float scale, int split_tiles, void* workspace,
                           size_t workspace_bytes, void* stream);
 size_t attn_decode_workspace_size_split(int B, int Sq, int Sk, int Hq, int Hkv, int D, int split_tiles);
+
+/* Size of the library's own split-KV workspace, per GPU (64 MiB). */
+#define ATTN_STATIC_WORKSPACE_BYTES ((size_t)64 << 20)
+
+/* attn_fwd_decode without a caller workspace, for callers that cannot allocate device memory: code under
+ * HIP graph capture, serving loops and harnesses that forbid hipMalloc.  It calls no allocating routine;
+ * the partial results go to a device array of ATTN_STATIC_WORKSPACE_BYTES that the library holds on every
+ * GPU it runs on until the process ends (looked up on the first call on each device, which is the current
+ * device: make it the one `stream` belongs to).  Same operation, arguments, split plan and results as
+ * attn_fwd_decode (bit for bit).  Sizes whose attn_decode_workspace_size() exceeds
+ * ATTN_STATIC_WORKSPACE_BYTES return ATTN_ERR_TOO_LARGE and launch nothing; other invalid arguments
+ * return attn_fwd_decode's codes.  Every call on a GPU shares that GPU's array: calls on one stream are
+ * ordered, but calls that overlap in time on one GPU (different streams, or threads without ordering)
+ * race on it and give wrong results.  Nothing in the array has to start at zero. */
+int attn_fwd_decode_static(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Sq, int Sk,
+                           int Hq, int Hkv, int D, int causal, float scale, void* stream);
+
 /* Static, NUL-terminated description of a status code ("unknown status" for others). */
 const char* attn_status_string(int status);
 
