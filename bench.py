@@ -15,8 +15,16 @@ Rank 0 prints one JSON line per workload:
              against MI355X's published dense fp16 MFMA peak (2.5 PFLOP/s);
              traffic = HBM bytes per launch from the committed rocprofv3
              counter summary (null if that summary is for another kernel build)
+  peak_derived  the same peak from the runtime's compute-unit count and peak
+             clock (CUs x clock x 4096 FLOP/clk), with the derivation;
+             pct_of_mfma_peak is taken against it
+  variant    the kernel variant that ran (schedule, ring, xcd, lpt)
+  per_config (default workload only) the other four attention configurations,
+             each timed in the same run under the --all warmup rule below:
+             TFLOP/s, % of peak, kernel ms per launch and variant
   cpu_baseline  the fp64 CPU oracle timed on the host on a bounded sample of
-             rows of the same workload (a baseline, not a target)
+             rows of the same workload (a baseline, not a target), with the
+             host CPU model
 
 `--pmc-copy BYTES` also launches a plain elementwise copy (negation) kernel that
 reads and writes BYTES bytes after the timed region (counter calibration for the HBM traffic figure), and
@@ -56,6 +64,8 @@ METRIC = "causal attention fwd TFLOP/s (fp16) + % of MFMA peak, LLaMA3 shapes"
 PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, published
 DEFAULT_WORKLOAD = "llama3-70b_b64_s8192"
 KERNEL_NAME = "attn_fwd_kernel"
+WIDE_KERNEL_NAME = "attn_wide_kernel"
+MFMA_FP16_FLOP_PER_CU_CLK = 4 * 1024  # gfx950: 4 SIMDs, each 1024 dense fp16 MFMA FLOP per clock
 GEMM_METRIC = "fp16 GEMM TFLOP/s (8k MatMul, fp32 accumulation) + % of MFMA peak"
 GEMM_KERNEL_NAME = "gemm_kernel"
 DECODE_METRIC = "split-KV decode attention, HBM GB/s (K/V/Q/O/LSE once) + % of HBM peak"
@@ -74,8 +84,26 @@ def is_decode(workload: str) -> bool:
     return workload in inputs.DECODE_BY_NAME
 
 
-def kernel_name(workload: str) -> str:
-    return GEMM_KERNEL_NAME if is_gemm(workload) else KERNEL_NAME
+def tuned_variant(workload: str, schedule: str | None = None) -> dict | None:
+    """The attention variant that runs `workload` (the library's tuned choice, or `schedule` forced)."""
+    from dnn_compiler_pipelining_amd import binding, inputs
+
+    if is_gemm(workload) or is_decode(workload):
+        return None
+    w = inputs.BY_NAME[workload]
+    v = binding.attn_tuned_variant(w.B, w.S, w.S, w.Hq, w.Hkv, w.D)
+    if schedule:
+        v["schedule"] = schedule
+    return v
+
+
+def kernel_name(workload: str, schedule: str | None = None) -> str:
+    """Symbol (substring) of the kernel that runs `workload`."""
+    if is_gemm(workload):
+        return GEMM_KERNEL_NAME
+    if is_decode(workload):
+        return KERNEL_NAME
+    return WIDE_KERNEL_NAME if tuned_variant(workload, schedule)["schedule"] == "wide" else KERNEL_NAME
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -125,6 +153,28 @@ def device_info() -> dict:
     pr = torch.cuda.get_device_properties(0)
     return {"name": pr.name, "arch": getattr(pr, "gcnArchName", None), "compute_units": pr.multi_processor_count,
             "memory_gib": round(pr.total_memory / 2**30, 1)}
+
+
+def mfma_peak() -> dict:
+    """Dense fp16 MFMA peak of device 0 from the runtime's compute-unit count and peak clock, with the
+    derivation, beside the published figure."""
+    from dnn_compiler_pipelining_amd import binding
+
+    cu, khz = binding.attn_device_clock(0)
+    tf = cu * khz * 1e3 * MFMA_FP16_FLOP_PER_CU_CLK / 1e12
+    return {"tflops": round(tf, 1), "derivation": "%d CUs x %.3f GHz x %d FLOP/clk/CU (dense fp16 MFMA)" %
+            (cu, khz / 1e6, MFMA_FP16_FLOP_PER_CU_CLK), "published_tflops": PEAK_TFLOPS}
+
+
+def cpu_model() -> str | None:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def calibration_copy(nbytes: int):
@@ -293,6 +343,29 @@ def cpu_baseline_decode(w, target_s: float = 15.0):
                       "workload's algorithmic bytes per output row" % (w.Hq * w.Sq, b, w.name, secs)}
 
 
+def per_config(skip: str, schedule: str | None, peak: dict) -> dict:
+    """{workload: rates} for every attention workload but `skip`: at least about 0.25 s of warmup and 0.25 s
+    of timed launches each (as --all), so each is timed at the clock a sustained run settles to."""
+    from dnn_compiler_pipelining_amd import inputs
+
+    out = {}
+    for w in inputs.WORKLOADS:
+        if w.name == skip:
+            continue
+        n = min(5000, max(1, int(250.0 / max(w.flops / 8e11, 1e-3)) + 1))
+        wall_ms, kernel_ms, ok = time_workload(w, n, n, 0, schedule)
+        if not ok:
+            raise RuntimeError("non-finite output in %s" % w.name)
+        value = w.flops / (wall_ms * 1e-3) / 1e12
+        achieved = w.flops / (kernel_ms * 1e-3) / 1e12
+        out[w.name] = {"tflops": round(value, 2), "pct_of_mfma_peak": round(100.0 * value / peak["tflops"], 2),
+                       "kernel_tflops": round(achieved, 2), "kernel_ms": round(kernel_ms, 4),
+                       "ms_per_step": round(wall_ms, 4), "steps": n, "warmup": n,
+                       "variant": tuned_variant(w.name, schedule), "config": w.describe()}
+        log("[bench] %s: %.1f TFLOP/s (%.4f ms per launch)" % (w.name, value, kernel_ms))
+    return out
+
+
 # ------------------------------------------------------------------ CPU oracle baseline
 
 def cpu_baseline(w, target_s: float = 15.0):
@@ -382,14 +455,14 @@ def _per_dispatch(d: str, counter: str):
     return out
 
 
-def summarize_kernel_trace(d: str, workload: str, command: str):
+def summarize_kernel_trace(d: str, workload: str, command: str, schedule: str | None = None):
     """Markdown summary of a rocprofv3 --kernel-trace --stats run, written under profiles/."""
     import sqlite3
 
     lines = ["# rocprofv3 kernel trace: %s" % workload, "", "Command (from the repository root):", "",
              "    " + command, "", "| kernel | calls | average us | total us | share % |", "|---|---|---|---|---|"]
     info = None
-    kn = kernel_name(workload)
+    kn = kernel_name(workload, schedule)
     for f in _db_files(d):
         con = sqlite3.connect(f)
         for name, calls, total, avg, pct in con.execute(
@@ -412,11 +485,11 @@ def summarize_kernel_trace(d: str, workload: str, command: str):
     print("\n".join(lines))
 
 
-def summarize_traffic(fetch_dir: str, write_dir: str, workload: str, copy_bytes: int):
+def summarize_traffic(fetch_dir: str, write_dir: str, workload: str, copy_bytes: int, schedule: str | None = None):
     res = {}
     # a step of the decode workload is two kernels (the split kernel and the combine kernel): its bytes are the
     # sum of their per-dispatch means
-    knames = ("attn_fwd_kernel", "attn_combine_kernel") if is_decode(workload) else (kernel_name(workload),)
+    knames = ("attn_fwd_kernel", "attn_combine_kernel") if is_decode(workload) else (kernel_name(workload, schedule),)
     knm = " + ".join(knames)
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         vals = _per_dispatch(d, counter)
@@ -446,7 +519,7 @@ def summarize_traffic(fetch_dir: str, write_dir: str, workload: str, copy_bytes:
         w = inputs.BY_NAME[workload]
         algo = 2 * (2 * w.B * w.S * w.Hq * w.D + 2 * w.B * w.S * w.Hkv * w.D) + 4 * w.B * w.Hq * w.S
     cmd = ("rocprofv3 --pmc %s -d <dir> -o <name> -- python3 bench.py --workload %s --steps 2 --warmup 1 "
-           "--no-cpu-baseline --pmc-copy %d")
+           "--no-cpu-baseline --no-per-config --pmc-copy %d")
     out = {"workload": workload, "kernel": knm, "kernel_fingerprint": kernel_fingerprint(workload),
            "hbm_bytes_per_launch": total, "algorithmic_bytes_per_launch": algo,
            "commands": [cmd % ("FETCH_SIZE", workload, copy_bytes), cmd % ("WRITE_SIZE", workload, copy_bytes),
@@ -461,7 +534,7 @@ def summarize_traffic(fetch_dir: str, write_dir: str, workload: str, copy_bytes:
     print(json.dumps(out, indent=1))
 
 
-def summarize_counters(dirs, workload: str):
+def summarize_counters(dirs, workload: str, schedule: str | None = None):
     """Markdown summary of rocprofv3 --pmc runs of SQ/GRBM counters for the attention kernel.
 
     Per-dispatch averages of each counter (summed over the device), plus derived figures:
@@ -478,16 +551,16 @@ def summarize_counters(dirs, workload: str):
             con = sqlite3.connect(f)
             for name, counter, val, n in con.execute(
                     "select kernel_name, counter_name, sum(value), count(distinct dispatch_id) from counters_collection "
-                    "where kernel_name like ? group by kernel_name, counter_name", ("%" + kernel_name(workload) + "%",)):
+                    "where kernel_name like ? group by kernel_name, counter_name", ("%" + kernel_name(workload, schedule) + "%",)):
                 vals[counter] = val / max(n, 1)
                 names.add(counter)
             con.close()
         cmds.append("rocprofv3 --pmc %s -d <dir> -o <name> -- python3 bench.py --workload %s --steps 2 --warmup 1 "
-                    "--no-cpu-baseline" % (" ".join(sorted(names)), workload))
-    lines = ["# rocprofv3 counters: %s, %s" % (kernel_name(workload), workload), "", "Commands (from the repository root; one "
+                    "--no-cpu-baseline --no-per-config" % (" ".join(sorted(names)), workload))
+    lines = ["# rocprofv3 counters: %s, %s" % (kernel_name(workload, schedule), workload), "", "Commands (from the repository root; one "
              "--pmc pass per line, counters grouped within the per-block limits):", ""]
     lines += ["    " + c for c in cmds]
-    lines += ["", "Values are per dispatch of %s, summed over the device." % kernel_name(workload), "",
+    lines += ["", "Values are per dispatch of %s, summed over the device." % kernel_name(workload, schedule), "",
               "| counter | per dispatch |", "|---|---|"]
     for k in sorted(vals):
         lines.append("| %s | %.4g |" % (k, vals[k]))
@@ -506,7 +579,7 @@ def summarize_counters(dirs, workload: str):
                          (100.0 * vals["SQ_LDS_IDX_ACTIVE"] / (256 * cyc)))
     lines += ["", "Kernel source fingerprint: %s" % kernel_fingerprint(workload), ""]
     os.makedirs(PROFILES, exist_ok=True)
-    out = os.path.join(PROFILES, "%s_%s_counters.md" % (kernel_name(workload), workload))
+    out = os.path.join(PROFILES, "%s_%s_counters.md" % (kernel_name(workload, schedule), workload))
     with open(out, "w") as f:
         f.write("\n".join(lines))
     print("\n".join(lines))
@@ -522,6 +595,8 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--all", action="store_true", help="one line per workload (parity-test configurations too)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="time only the named workload (profiling runs: no other configuration's launches)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--pmc-copy", type=int, default=0)
     ap.add_argument("--schedule", default=None, help="attention tile schedule to time instead of the tuned one "
@@ -534,13 +609,13 @@ def main():
     from dnn_compiler_pipelining_amd import inputs
 
     if args.summarize_counters:
-        summarize_counters(args.summarize_counters, args.workload)
+        summarize_counters(args.summarize_counters, args.workload, args.schedule)
         return
     if args.summarize_kernel_trace:
-        summarize_kernel_trace(args.summarize_kernel_trace[0], args.workload, args.summarize_kernel_trace[1])
+        summarize_kernel_trace(args.summarize_kernel_trace[0], args.workload, args.summarize_kernel_trace[1], args.schedule)
         return 0
     if args.summarize_traffic:
-        summarize_traffic(args.summarize_traffic[0], args.summarize_traffic[1], args.workload, args.pmc_copy)
+        summarize_traffic(args.summarize_traffic[0], args.summarize_traffic[1], args.workload, args.pmc_copy, args.schedule)
         return 0
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -559,6 +634,9 @@ def main():
         n = min(5000, max(1, int(250.0 / max(est_ms, 1e-3)) + 1))  # launch-bound shapes: at most 5000
         return max(args.steps, n), max(args.warmup, n)
 
+    peak = mfma_peak()
+    log("[bench] dense fp16 MFMA peak: %.1f TFLOP/s = %s (published %.0f)" %
+        (peak["tflops"], peak["derivation"], PEAK_TFLOPS))
     for name in names:
         if is_decode(name):
             w = inputs.DECODE_BY_NAME[name]
@@ -613,20 +691,25 @@ def main():
             "vs_baseline": None,
             "dtype": "f16",
             "data": "synthetic: seeded i.i.d. N(0,1) fp16 %s" % ("A/B" if gemm else "Q/K/V"),
-            "pct_of_mfma_peak": round(100.0 * value / PEAK_TFLOPS, 2),
+            "pct_of_mfma_peak": round(100.0 * value / peak["tflops"], 2),
             "config": w.describe(),
             "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(achieved / PEAK_TFLOPS, 4),
                          "traffic": (round(traffic["hbm_bytes_per_launch"])
                                      if traffic and traffic.get("hbm_bytes_per_launch") else None),
-                         "kernel": kernel_name(name), "kernel_ms": round(kernel_ms, 4),
+                         "kernel": kernel_name(name, args.schedule), "kernel_ms": round(kernel_ms, 4),
                          "flops_per_launch": w.flops},
+            "peak_derived": dict(peak, frac=round(achieved / peak["tflops"], 4)),
             "device": device_info(),
         }
-        if args.schedule and not gemm:
-            line["schedule"] = args.schedule
+        if not gemm:
+            line["variant"] = tuned_variant(name, args.schedule)
+        if not args.all and not args.no_per_config and not gemm and name == DEFAULT_WORKLOAD:
+            # the other attention configurations, each timed under the --all warmup rule, in the same run
+            line["per_config"] = per_config(w.name, args.schedule, peak)
         if not args.no_cpu_baseline and not args.all:
             line["cpu_baseline"] = (cpu_baseline_gemm if gemm else cpu_baseline)(w, args.cpu_seconds)
+            line["cpu_baseline"]["cpu_model"] = cpu_model()
         print(json.dumps(line), flush=True)
     return 0
 

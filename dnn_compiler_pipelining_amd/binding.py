@@ -33,7 +33,7 @@ ATTN_STATIC_WORKSPACE_BYTES = 64 << 20  # the library's own split-KV workspace p
 
 EXPORTS = ("attn_fwd", "attn_fwd_stream", "attn_fwd_ex", "attn_fwd_variant", "attn_fwd_decode",
            "attn_fwd_decode_split", "attn_fwd_decode_static", "attn_decode_workspace_size", "attn_decode_workspace_size_split",
-           "attn_status_string", "attn_version", "gemm_f16", "gemm_f16_waves")
+           "attn_status_string", "attn_version", "attn_tuned_variant", "attn_device_clock", "gemm_f16", "gemm_f16_waves")
 
 # Tile schedules (ATTN_SCHEDULE_* in include/attn.h), by name
 SCHEDULES = {"serial": 0, "overlap": 1, "pingpong": 2, "serial4": 3, "wide": 4}
@@ -82,6 +82,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
             lib.attn_fwd_decode_static.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
             lib.attn_decode_workspace_size.restype = ctypes.c_size_t
             lib.attn_decode_workspace_size.argtypes = [i, i, i, i, i, i]
+            ip = ctypes.POINTER(ctypes.c_int)
+            lib.attn_tuned_variant.restype = i
+            lib.attn_tuned_variant.argtypes = [i, i, i, i, i, i, ip, ip, ip, ip]
+            lib.attn_device_clock.restype = i
+            lib.attn_device_clock.argtypes = [i, ip, ip]
             lib.attn_status_string.restype = ctypes.c_char_p
             lib.attn_status_string.argtypes = [i]
             lib.attn_version.restype = i
@@ -137,6 +142,25 @@ def attn_fwd_decode_static(q, k, v, o, lse, B: int, Sq: int, Sk: int, Hq: int, H
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else (stream or 0)
     return load().attn_fwd_decode_static(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Sq, Sk, Hq, Hkv, D,
                                          int(causal), float(scale), handle)
+
+
+def attn_tuned_variant(B: int, Sq: int, Sk: int, Hq: int, Hkv: int, D: int) -> dict:
+    """C attn_tuned_variant: the variant attn_fwd_ex runs for these sizes, as variant_fields() names it."""
+    out = [ctypes.c_int(-1) for _ in range(4)]
+    st = load().attn_tuned_variant(B, Sq, Sk, Hq, Hkv, D, *[ctypes.byref(x) for x in out])
+    if st != ATTN_OK:
+        raise AttnError(st)
+    names = {v: n for n, v in SCHEDULES.items()}
+    return {"schedule": names[out[0].value], "ring": out[1].value, "xcd": out[2].value, "lpt": out[3].value}
+
+
+def attn_device_clock(device: int = 0) -> tuple[int, int]:
+    """C attn_device_clock: (compute units, peak shader clock in kHz) of a HIP device."""
+    cu, khz = ctypes.c_int(0), ctypes.c_int(0)
+    st = load().attn_device_clock(int(device), ctypes.byref(cu), ctypes.byref(khz))
+    if st != ATTN_OK:
+        raise AttnError(st)
+    return cu.value, khz.value
 
 
 def gemm_f16_waves(a, b, c, M: int, N: int, K: int, b_layout: int, waves: int, stream) -> int:

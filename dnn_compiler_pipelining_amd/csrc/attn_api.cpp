@@ -12,7 +12,7 @@
 
 namespace {
 
-constexpr int kVersion = 1 * 10000 + 2 * 100 + 0;
+constexpr int kVersion = 1 * 10000 + 3 * 100 + 0;
 constexpr int kMaxSeq = 1 << 30;  // sequence lengths up to 2^30 keep all tile arithmetic in int
 
 // Fields of a requested variant: -1 takes the tuned value (variant.h) for the
@@ -183,6 +183,28 @@ int attn_fwd_stream(const void* q, const void* k, const void* v, void* o, float*
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int S, int Hq, int Hkv, int D,
              int causal, float scale) {
   return attn_fwd_stream(q, k, v, o, lse, B, S, Hq, Hkv, D, causal, scale, nullptr);
+}
+
+int attn_tuned_variant(int B, int Sq, int Sk, int Hq, int Hkv, int D, int* schedule, int* ring, int* xcd, int* lpt) {
+  if (!schedule || !ring || !xcd || !lpt) return ATTN_ERR_NULL;
+  if (B < 1 || Sq < 1 || Sk < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || Sq > kMaxSeq || Sk > kMaxSeq)
+    return ATTN_ERR_SHAPE;
+  if (D != 64 && D != 128 && D != 256) return ATTN_ERR_UNSUPPORTED;
+  libattn::Variant var;
+  if (!choose_variant(kTunedRequest, B, Sq, Sk, Hq, Hkv, D, var)) return ATTN_ERR_UNSUPPORTED;
+  *schedule = var.schedule;
+  *ring = var.ring;
+  *xcd = var.xcd;
+  *lpt = var.lpt;
+  return ATTN_OK;
+}
+
+int attn_device_clock(int device, int* compute_units, int* peak_clock_khz) {
+  if (!compute_units || !peak_clock_khz) return ATTN_ERR_NULL;
+  if (hipDeviceGetAttribute(compute_units, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
+      hipDeviceGetAttribute(peak_clock_khz, hipDeviceAttributeClockRate, device) != hipSuccess)
+    return ATTN_ERR_HIP;
+  return ATTN_OK;
 }
 
 size_t attn_decode_workspace_size_split(int B, int Sq, int Sk, int Hq, int Hkv, int D, int split_tiles) {

@@ -46,11 +46,11 @@ int device_scratch(void** out) {
 
 extern "C" int attn_fwd_decode_static(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                                       int Sq, int Sk, int Hq, int Hkv, int D, int causal, float scale, void* stream) {
-  const size_t need = attn_decode_workspace_size(B, Sq, Sk, Hq, Hkv, D);
-  // sizes the split-KV path rejects: its own checks give the status
-  if (need == 0)
-    return attn_fwd_decode(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, D, causal, scale, nullptr, 0, stream);
-  if (need > kStaticWsBytes) return ATTN_ERR_TOO_LARGE;
+  // The split-KV path's own argument checks, without a workspace: any status
+  // but ATTN_ERR_WORKSPACE is an invalid argument (nothing is launched).
+  const int checked = attn_fwd_decode(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, D, causal, scale, nullptr, 0, stream);
+  if (checked != ATTN_ERR_WORKSPACE) return checked;
+  if (attn_decode_workspace_size(B, Sq, Sk, Hq, Hkv, D) > kStaticWsBytes) return ATTN_ERR_TOO_LARGE;
   void* ws = nullptr;
   const int st = device_scratch(&ws);
   if (st != ATTN_OK) return st;

@@ -114,6 +114,16 @@ int attn_fwd_variant(const void* q, const void* k, const void* v, void* o, float
                      int Hkv, int D, int causal, float scale, int schedule, int ring, int xcd, int lpt,
                      void* stream);
 
+/* The variant attn_fwd_ex runs for these sizes (ATTN_SCHEDULE_* value, ring depth, xcd and lpt switches),
+ * for reports and cross-checks.  Returns ATTN_OK, ATTN_ERR_NULL for a NULL output pointer, ATTN_ERR_SHAPE
+ * for sizes attn_fwd_ex rejects, ATTN_ERR_UNSUPPORTED for a head dimension it does not run.  No HIP call. */
+int attn_tuned_variant(int B, int Sq, int Sk, int Hq, int Hkv, int D, int* schedule, int* ring, int* xcd, int* lpt);
+
+/* Compute-unit count and peak shader clock (kHz) of HIP device `device`, as the runtime reports them: the
+ * inputs of a peak-throughput figure (dense fp16 MFMA on gfx950: 4 SIMDs x 1024 FLOP per clock per compute
+ * unit).  Returns ATTN_OK, ATTN_ERR_NULL or ATTN_ERR_HIP. */
+int attn_device_clock(int device, int* compute_units, int* peak_clock_khz);
+
 /* Split-KV path for few query rows against many keys (decode, short chunks): the same operation and
  * arguments as attn_fwd_ex, computed in two kernels.  The first packs the g = Hq / Hkv query heads of a KV
  * group with their Sq query rows into 128-row tiles, so each K/V tile is read once for all of them, and
@@ -145,9 +155,9 @@ size_t attn_decode_workspace_size_split(int B, int Sq, int Sk, int Hq, int Hkv, 
  * the partial results go to a device array of ATTN_STATIC_WORKSPACE_BYTES that the library holds on every
  * GPU it runs on until the process ends (looked up on the first call on each device, which is the current
  * device: make it the one `stream` belongs to).  Same operation, arguments, split plan and results as
- * attn_fwd_decode (bit for bit).  Sizes whose attn_decode_workspace_size() exceeds
- * ATTN_STATIC_WORKSPACE_BYTES return ATTN_ERR_TOO_LARGE and launch nothing; other invalid arguments
- * return attn_fwd_decode's codes.  Every call on a GPU shares that GPU's array: calls on one stream are
+ * attn_fwd_decode (bit for bit).  Invalid arguments return attn_fwd_decode's codes (checked first); valid
+ * sizes whose attn_decode_workspace_size() exceeds ATTN_STATIC_WORKSPACE_BYTES return ATTN_ERR_TOO_LARGE;
+ * either way nothing is launched.  Every call on a GPU shares that GPU's array: calls on one stream are
  * ordered, but calls that overlap in time on one GPU (different streams, or threads without ordering)
  * race on it and give wrong results.  Nothing in the array has to start at zero. */
 int attn_fwd_decode_static(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Sq, int Sk,

@@ -48,7 +48,7 @@ def test_library_exports_every_declared_symbol(lib):
 def test_version_and_status_strings(lib):
     assert L.attn_version() >= 10000
     assert L.attn_status_string(L.ATTN_OK) == "ok"
-    for code in range(1, 8):
+    for code in range(1, 9):
         s = L.attn_status_string(code)
         assert s and s != "unknown status"
     assert L.attn_status_string(99) == "unknown status"
@@ -215,3 +215,32 @@ def test_decode_validation(lib):
     assert dcall(ws=LP - 64) == L.ATTN_ERR_OVERLAP     # workspace running into lse
     assert dcall(q=0, ws=0) == L.ATTN_ERR_NULL          # argument checks come before workspace checks
     assert L.attn_status_string(L.ATTN_ERR_WORKSPACE) != "unknown status"
+
+
+def test_tuned_variant_reports_a_runnable_variant(lib):
+    for B, S, Hq, Hkv, D in ((1, 512, 32, 8, 128), (64, 8192, 64, 8, 128), (2, 100, 8, 2, 64), (1, 33, 4, 4, 256)):
+        v = L.attn_tuned_variant(B, S, S, Hq, Hkv, D)
+        assert set(v) == {"schedule", "ring", "xcd", "lpt"}
+        assert v["schedule"] in L.SCHEDULES and v["ring"] in (2, 4) and v["xcd"] in (0, 1) and v["lpt"] in (0, 1)
+        if D != 128:
+            assert v["schedule"] in ("serial", "serial4")  # the only schedules D = 64 and 256 run
+    out = [ctypes.c_int(0) for _ in range(4)]
+    refs = [ctypes.byref(x) for x in out]
+    assert lib.attn_tuned_variant(1, 64, 64, 8, 2, 96, *refs) == L.ATTN_ERR_UNSUPPORTED
+    assert lib.attn_tuned_variant(1, 64, 64, 6, 4, 128, *refs) == L.ATTN_ERR_SHAPE
+    assert lib.attn_tuned_variant(0, 64, 64, 8, 2, 128, *refs) == L.ATTN_ERR_SHAPE
+    assert lib.attn_tuned_variant(1, 64, 64, 8, 2, 128, None, *refs[1:]) == L.ATTN_ERR_NULL
+    assert lib.attn_device_clock(0, None, refs[0]) == L.ATTN_ERR_NULL
+
+
+def test_static_decode_validates_before_any_hip_call(lib):
+    # invalid arguments keep the split-KV path's codes; sizes past the static workspace are rejected; all
+    # before the device is touched
+    assert L.attn_fwd_decode_static(QP, KP, VP, OP, LP, 1, 1, 64, 6, 4, 128, 1, 0.06, None) == L.ATTN_ERR_SHAPE
+    assert L.attn_fwd_decode_static(0, KP, VP, OP, LP, 1, 1, 64, 8, 4, 128, 1, 0.06, None) == L.ATTN_ERR_NULL
+    assert L.attn_fwd_decode_static(QP, KP, VP, OP, LP, 1, 1, 64, 8, 4, 96, 1, 0.06, None) == L.ATTN_ERR_UNSUPPORTED
+    assert L.attn_fwd_decode_static(QP + 8, KP, VP, OP, LP, 1, 1, 64, 8, 4, 128, 1, 0.06, None) == L.ATTN_ERR_ALIGN
+    assert L.attn_decode_workspace_size(1, 128, 8192, 64, 8, 256) > L.ATTN_STATIC_WORKSPACE_BYTES
+    assert L.attn_fwd_decode_static(QP, KP, VP, OP, LP, 1, 128, 8192, 64, 8, 256, 1, 0.06, None) == \
+        L.ATTN_ERR_TOO_LARGE
+    assert L.attn_fwd_decode_static(0, KP, VP, OP, LP, 1, 128, 8192, 64, 8, 256, 1, 0.06, None) == L.ATTN_ERR_NULL

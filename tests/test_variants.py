@@ -91,7 +91,9 @@ def lookup(tmp_path, table_dir, shapes):
 def test_committed_table_picks_its_own_entries(tmp_path):
     text = open(os.path.join(CSRC, "tuned_table.h")).read()
     import re
-    enum = {"SCHEDULE_SERIAL": 0, "SCHEDULE_OVERLAP": 1, "SCHEDULE_PINGPONG": 2, "SCHEDULE_SERIAL4": 3}
+    from dnn_compiler_pipelining_amd import binding
+
+    enum = {"SCHEDULE_" + name.upper(): value for name, value in binding.SCHEDULES.items()}
     rows = re.findall(r"\{(\d+), (\d+), (\d+), (\d+), (\d+), \{(SCHEDULE_\w+), (\d), (\d), (\d)\}", text)
     assert rows
     got = lookup(tmp_path, CSRC, [r[:5] for r in rows])
