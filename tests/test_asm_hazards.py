@@ -7,7 +7,8 @@ assembly, is invisible to it.  This test compiles the kernel to gfx950 assembly 
     the 4 wait states before it, and no VALU instruction may read or write its destination within the 18
     wait states after it;
   - for a VALU instruction inside an assembly region (the accumulator rescale): no MFMA may have written a
-    register it touches within the 18 wait states before it.
+    register it touches within the 18 wait states before it, unless a VALU instruction wrote that register
+    again in between (the compiler makes its own writes wait for the MFMA).
 A wait state is one instruction, or N+1 for s_nop N (an intervening MFMA counts as one, as in the hazard
 rules).  18 covers the longest result latency of a 32x32 MFMA; 4 covers a VALU write read by an MFMA.
 """
@@ -94,6 +95,8 @@ def scan(ins) -> list[str]:
                 if ws >= AFTER_MFMA:
                     break
         elif in_asm and op.startswith("v_") and not op.startswith("v_mfma"):
+            # registers whose latest writer could still be an MFMA: a later VALU write of a register hides an
+            # earlier MFMA write of it (the later writer is the one that has to wait for the MFMA)
             touched = set().union(*[_regs(x) for x in ops]) if ops else set()
             ws = 0
             for j in range(i - 1, -1, -1):
@@ -101,7 +104,9 @@ def scan(ins) -> list[str]:
                 ws += _wait_states(op2, ops2) if j < i - 1 else 0
                 if op2.startswith("v_mfma") and ops2 and _regs(ops2[0]) & touched:
                     bad.append("assembly VALU access %d wait states after an MFMA: %s || %s" % (ws, ins[j][1], line))
-                if ws >= AFTER_MFMA:
+                elif op2.startswith("v_") and ops2:
+                    touched -= _regs(ops2[0])
+                if ws >= AFTER_MFMA or not touched:
                     break
     return bad
 
@@ -116,6 +121,14 @@ def test_scanner_finds_planted_hazards():
     # an assembly accumulator read right after a builtin MFMA that wrote it
     assert scan([(False, "v_mfma_f32_32x32x16_f16 a[0:15], v[0:3], v[4:7], a[0:15]"),
                  (True, "v_accvgpr_read_b32 v40, a5")])
+    # an assembly accumulator read of a register the VALU rewrote after the MFMA wrote it: clean
+    assert not scan([(False, "v_mfma_f32_32x32x16_f16 a[0:15], v[0:3], v[4:7], a[0:15]"),
+                     (False, "v_accvgpr_mov_b32 a5, a40"),
+                     (True, "v_accvgpr_read_b32 v40, a5")])
+    # ... but a register the rewrite does not cover still counts
+    assert scan([(False, "v_mfma_f32_32x32x16_f16 a[0:15], v[0:3], v[4:7], a[0:15]"),
+                 (False, "v_accvgpr_mov_b32 a5, a40"),
+                 (True, "v_accvgpr_read_b32 v40, a6")])
     # the same with enough wait states between, and with unrelated registers: clean
     assert not scan([mfma_asm, (True, "s_nop 7"), (True, "s_nop 7"), (True, "s_nop 2"),
                      (False, "v_add_f32_e32 v30, v3, v3")])
