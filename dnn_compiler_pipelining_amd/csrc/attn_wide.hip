@@ -703,25 +703,42 @@ __global__ __launch_bounds__(64 * W_NW, 1) void attn_wide_kernel(Params p) {
   // PV of the last tile, whose P^T the last iteration left in pb
   block(M_PV{}, 0u, sa, vslot_of(n_tiles - 1), pb, no_sm);
 
-  // ---- epilogue: O = O^T / l (fp16, round to nearest even), LSE in natural log
+  // ---- epilogue: O = O^T / l (fp16, round to nearest even), LSE in natural
+  // log.  O^T holds 4 consecutive columns of a row per lane and store, 32 rows
+  // per instruction; it goes through LDS so that the stores write whole rows
+  // instead (16 lanes per 256-byte row, 4 rows per instruction).  The K ring
+  // is not read after the last iteration's barrier, and no load targets it
+  // any more, so each wave takes one K slot: 64 rows at the padded K row
+  // stride, which spreads the 32 rows a column write touches over the banks.
+  // The reads are the wave's own writes, which LDS performs in order.
   if (active) {
+    LDS char* const ob = k_lds + (uint32_t)K_TILEB * (uint32_t)wave;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const float inv = 1.0f / l_run[qb];
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          f16x4 hv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) hv[e] = (_Float16)(o_acc[db][qb][4 * r4 + e] * inv);
+          *(LDS f16x4*)(ob + (32 * qb + n) * K_ROWB + 2 * (32 * db + 8 * r4 + 4 * hh)) = hv;
+        }
+    }
+    _Float16* const ob_g = p.o + (int64_t)b * p.q_bstride + (int64_t)h * 128 + 8 * (lane & 15);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      const int row = 4 * i + (lane >> 4);
+      const f16x8 x = *(const LDS f16x8*)(ob + row * K_ROWB + 16 * (lane & 15));
+      if (qw + row < Sq) *reinterpret_cast<f16x8*>(ob_g + (int64_t)(qw + row) * p.q_sstride) = x;
+    }
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const int qrow = qw + 32 * qb + n;
-      if (qrow < Sq) {
-        const float inv = 1.0f / l_run[qb];
-        _Float16* dst = p.o + (int64_t)b * p.q_bstride + (int64_t)qrow * p.q_sstride + (int64_t)h * 128;
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            f16x4 hv;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) hv[e] = (_Float16)(o_acc[db][qb][4 * r4 + e] * inv);
-            *reinterpret_cast<f16x4*>(dst + 32 * db + 8 * r4 + 4 * hh) = hv;
-          }
-        if (p.lse && hh == 0) p.lse[((int64_t)b * p.Hq + h) * Sq + qrow] = (m_run[qb] + log2f(l_run[qb])) * LN2;
-      }
+      if (p.lse && hh == 0 && qrow < Sq)
+        p.lse[((int64_t)b * p.Hq + h) * Sq + qrow] = (m_run[qb] + log2f(l_run[qb])) * LN2;
     }
   }
 }

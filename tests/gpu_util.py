@@ -113,6 +113,19 @@ def sampled_parity(w: inputs.Workload, q, k, v, o, lse, batches, heads=None, n_r
     return st
 
 
+def slice_parity(w: inputs.Workload, q, k, v, o, lse, b: int, h: int, tag=""):
+    """Every query row of head h of batch entry b of a full-size run against the oracle (the oracle
+    regenerates the batch entry on the CPU from its seed and checks that it is what the GPU read)."""
+    qb, kb, vb = inputs.make_batch_cpu(w, b)
+    assert torch.equal(qb, q[b].cpu()) and torch.equal(kb, k[b].cpu()) and torch.equal(vb, v[b].cpu())
+    rs = np.arange(w.S, dtype=np.int32)
+    hs = np.full(w.S, h, dtype=np.int32)
+    O, L = oracle_mod.attn_rows(qb.numpy(), kb.numpy(), vb.numpy(), hs, rs, w.causal, w.scale)
+    st = stats(o[b, :, h].cpu().numpy(), lse[b, h].cpu().numpy(), O, L)
+    check(st, tag)
+    return st
+
+
 def whole_output_sane(o, lse):
     """Properties that hold at any size: everything finite, |O| bounded by max |V|."""
     assert bool(torch.isfinite(o).all().item()), "non-finite O"

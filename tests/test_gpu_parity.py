@@ -57,16 +57,30 @@ def test_workload_small_full():
     assert st["max_lse"] <= 3e-4 and st["max_o"] <= 2e-3, st
 
 
-@pytest.mark.parametrize("idx", [1, 2, 3, 4], ids=lambda i: inputs.WORKLOADS[i].name)
-def test_workload_full_size_sampled(idx):
+@pytest.mark.parametrize("idx", [1, 2], ids=lambda i: inputs.WORKLOADS[i].name)
+def test_workload_full_output(idx):
+    """The B = 1, S = 8192 workloads (LLaMA3-8B and -70B heads): every output row of every head against
+    the oracle."""
     w = inputs.WORKLOADS[idx]
-    U.say("workload %s (full size, sampled check)" % w.name)
+    U.say("workload %s (full size, whole output)" % w.name)
+    q, k, v = inputs.make_inputs(w, "cpu")
+    U.full_parity(q, k, v, w.causal, w.scale, w.name + " whole output")
+
+
+@pytest.mark.parametrize("idx", [3, 4], ids=lambda i: inputs.WORKLOADS[i].name)
+def test_workload_full_size_sampled(idx):
+    """The B = 64 workloads at full size: sampled rows of every third head of three batch entries, and
+    three whole (batch, head) slices (every query row of that head)."""
+    w = inputs.WORKLOADS[idx]
+    U.say("workload %s (full size, sampled rows and whole slices)" % w.name)
     q, k, v = inputs.make_inputs(w, "cuda")
     o, lse = U.run(q, k, v, w.causal, w.scale)
     U.whole_output_sane(o, lse)
     batches = sorted({0, w.B // 2, w.B - 1})
-    heads = None if w.B == 1 else list(range(0, w.Hq, 3)) + [w.Hq - 1]
-    U.sampled_parity(w, q, k, v, o, lse, batches, heads=heads, n_random=64 if w.B > 1 else 128, tag=w.name)
+    heads = list(range(0, w.Hq, 3)) + [w.Hq - 1]
+    U.sampled_parity(w, q, k, v, o, lse, batches, heads=heads, n_random=64, tag=w.name)
+    for b, h in ((0, 0), (w.B // 2, w.Hq // 2 + 1), (w.B - 1, w.Hq - 1)):
+        U.slice_parity(w, q, k, v, o, lse, b, h, tag="%s slice b%d h%d" % (w.name, b, h))
     del q, k, v, o, lse
     torch.cuda.empty_cache()
 
