@@ -60,12 +60,18 @@ struct WStep {
   int kk, x, qb;
 };
 __host__ __device__ constexpr WStep wstep_of(int mode, int i) {
-  return mode == 1   ? WStep{true, (i >> 1) >> 2, (i >> 1) & 3, i & 1}
+  return mode == 1 || mode == 3 ? WStep{true, (i >> 1) >> 2, (i >> 1) & 3, i & 1}
          : mode == 2 ? WStep{false, (i >> 1) >> 1, (i >> 1) & 1, i & 1}
          : i < 32    ? wstep_of(1, i)
                      : wstep_of(2, i - 32);
 }
 constexpr int wsteps_of(int mode) { return mode == 0 ? 64 : 32; }
+// mode 3 is mode 1 for a last tile that is the causal diagonal at 64-row
+// query blocks: P^T of query half 0 is zero for keys 32..63 of the tile, so
+// those 8 PV steps issue no MFMA.
+__host__ __device__ constexpr bool wstep_dropped(int mode, int i) {
+  return mode == 3 && wstep_of(mode, i).kk >= 2 && wstep_of(mode, i).qb == 0;
+}
 
 }  // namespace
 
@@ -502,12 +508,14 @@ __global__ __launch_bounds__(64 * W_NW, 1) void attn_wide_kernel(Params p) {
       constexpr WStep st = wstep_of(mode, i);
       sm(ic);
       const f16x8 a = fr[f % kRing];
-      if constexpr (st.pv)
-        o_acc[st.x][st.qb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, ps[st.qb][st.kk], o_acc[st.x][st.qb], 0, 0, 0);
-      else if constexpr (st.kk == 0)
+      if constexpr (st.pv) {
+        if constexpr (!wstep_dropped(mode, i))
+          o_acc[st.x][st.qb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, ps[st.qb][st.kk], o_acc[st.x][st.qb], 0, 0, 0);
+      } else if constexpr (st.kk == 0) {
         qk_first(sd[st.x][st.qb], a, qf[st.qb][0]);
-      else
+      } else {
         qk_next(sd[st.x][st.qb], a, qf[st.qb][st.kk]);
+      }
       if constexpr ((i & 1) && f + kRing < nfr) fr[f % kRing] = load(std::integral_constant<int, f + kRing>{});
       __builtin_amdgcn_sched_barrier(0);
     });
@@ -654,6 +662,10 @@ __global__ __launch_bounds__(64 * W_NW, 1) void attn_wide_kernel(Params p) {
   // Tiles below j_ms need no mask for any wave of the workgroup.  The first
   // and the last iteration always take the masked path.
   const int j_ms = min(n_tiles, p.causal ? min(q0 + off, Sk) / BN : Sk / BN);
+  // The last tile is the causal diagonal at 64-row query blocks when its
+  // keys 32..63 all lie past the last key query half 0 of this wave may see:
+  // the final PV block then drops those steps for that half (mode 3).
+  const bool diag_tail = p.causal && (n_tiles - 1) * BN + 32 >= qw + 31 + off + 1;
 
   // prologue: K_0, V_0 and K_1 landed, K_2 in flight; S^T of tile 0 and its
   // max (the first tile of a row: the textbook online-softmax step, max
@@ -701,7 +713,8 @@ __global__ __launch_bounds__(64 * W_NW, 1) void attn_wide_kernel(Params p) {
   if (j > 0) iter(j, T{}, F{}, T{}, F{}, sa, sb, pa, pb);
   else iter(j, F{}, F{}, T{}, F{}, sa, sb, pa, pb);
   // PV of the last tile, whose P^T the last iteration left in pb
-  block(M_PV{}, 0u, sa, vslot_of(n_tiles - 1), pb, no_sm);
+  if (diag_tail) block(std::integral_constant<int, 3>{}, 0u, sa, vslot_of(n_tiles - 1), pb, no_sm);
+  else block(M_PV{}, 0u, sa, vslot_of(n_tiles - 1), pb, no_sm);
 
   // ---- epilogue: O = O^T / l (fp16, round to nearest even), LSE in natural
   // log.  O^T holds 4 consecutive columns of a row per lane and store, 32 rows
