@@ -120,7 +120,8 @@ def kernel_fingerprint(workload: str = DEFAULT_WORKLOAD) -> str:
         files = hipbuild.GEMM_SOURCES + [os.path.join(hipbuild.CSRC, n) for n in ("gemm_kernel.h", "gfx950.h")]
     else:
         files = hipbuild.ATTN_SOURCES + [os.path.join(hipbuild.CSRC, n) for n in
-                                         ("attn_kernel.h", "attn_tile.h", "variant.h", "tuned_table.h", "gfx950.h")]
+                                         ("attn_kernel.h", "attn_tile.h", "attn_wide.h", "variant.h", "tuned_table.h",
+                                          "gfx950.h")]
     h = hashlib.sha256()
     for path in files:
         with open(path, "rb") as f:

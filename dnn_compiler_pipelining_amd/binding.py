@@ -37,6 +37,8 @@ EXPORTS = ("attn_fwd", "attn_fwd_stream", "attn_fwd_ex", "attn_fwd_variant", "at
 
 # Tile schedules (ATTN_SCHEDULE_* in include/attn.h), by name
 SCHEDULES = {"serial": 0, "overlap": 1, "pingpong": 2, "serial4": 3, "wide": 4}
+# Placements of the softmax work in the 64-row schedule (ATTN_PLACE_* in include/attn.h), by name
+PLACES = {"even": 0, "front": 1, "early": 2}
 
 GEMM_B_KN = 0  # B stored [K, N]: C = A B
 GEMM_B_NK = 1  # B stored [N, K]: C = A B^T
@@ -68,7 +70,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
             lib.attn_fwd_ex.restype = i
             lib.attn_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
             lib.attn_fwd_variant.restype = i
-            lib.attn_fwd_variant.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i, i, i, vp]
+            lib.attn_fwd_variant.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i, i, i, i, vp]
             lib.attn_fwd_decode_split.restype = i
             lib.attn_fwd_decode_split.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp, ctypes.c_size_t,
                                                   vp]
@@ -84,7 +86,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
             lib.attn_decode_workspace_size.argtypes = [i, i, i, i, i, i]
             ip = ctypes.POINTER(ctypes.c_int)
             lib.attn_tuned_variant.restype = i
-            lib.attn_tuned_variant.argtypes = [i, i, i, i, i, i, ip, ip, ip, ip]
+            lib.attn_tuned_variant.argtypes = [i, i, i, i, i, i, ip, ip, ip, ip, ip]
             lib.attn_device_clock.restype = i
             lib.attn_device_clock.argtypes = [i, ip, ip]
             lib.attn_status_string.restype = ctypes.c_char_p
@@ -128,11 +130,12 @@ def attn_fwd_ex(q, k, v, o, lse, B: int, Sq: int, Sk: int, Hq: int, Hkv: int, D:
 
 
 def attn_fwd_variant(q, k, v, o, lse, B: int, Sq: int, Sk: int, Hq: int, Hkv: int, D: int, causal: int,
-                     scale: float, schedule: int, ring: int, xcd: int, lpt: int, stream) -> int:
+                     scale: float, schedule: int, ring: int, xcd: int, lpt: int, place: int, stream) -> int:
     """C attn_fwd_variant: attn_fwd_ex with an explicit kernel variant (-1 in a field: the tuned value)."""
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else (stream or 0)
     return load().attn_fwd_variant(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Sq, Sk, Hq, Hkv, D,
-                                   int(causal), float(scale), int(schedule), int(ring), int(xcd), int(lpt), handle)
+                                   int(causal), float(scale), int(schedule), int(ring), int(xcd), int(lpt),
+                                   int(place), handle)
 
 
 def attn_fwd_decode_static(q, k, v, o, lse, B: int, Sq: int, Sk: int, Hq: int, Hkv: int, D: int, causal: int,
@@ -146,12 +149,14 @@ def attn_fwd_decode_static(q, k, v, o, lse, B: int, Sq: int, Sk: int, Hq: int, H
 
 def attn_tuned_variant(B: int, Sq: int, Sk: int, Hq: int, Hkv: int, D: int) -> dict:
     """C attn_tuned_variant: the variant attn_fwd_ex runs for these sizes, as variant_fields() names it."""
-    out = [ctypes.c_int(-1) for _ in range(4)]
+    out = [ctypes.c_int(-1) for _ in range(5)]
     st = load().attn_tuned_variant(B, Sq, Sk, Hq, Hkv, D, *[ctypes.byref(x) for x in out])
     if st != ATTN_OK:
         raise AttnError(st)
     names = {v: n for n, v in SCHEDULES.items()}
-    return {"schedule": names[out[0].value], "ring": out[1].value, "xcd": out[2].value, "lpt": out[3].value}
+    places = {v: n for n, v in PLACES.items()}
+    return {"schedule": names[out[0].value], "ring": out[1].value, "xcd": out[2].value, "lpt": out[3].value,
+            "place": places[out[4].value]}
 
 
 def attn_device_clock(device: int = 0) -> tuple[int, int]:
@@ -204,16 +209,21 @@ def attn_decode_workspace_size_split(B: int, Sq: int, Sk: int, Hq: int, Hkv: int
 
 
 def variant_fields(variant) -> tuple:
-    """(schedule, ring, xcd, lpt) for attn_fwd_variant from None (all tuned), a schedule name, or a dict with
-    any of the keys schedule (name or number), ring, xcd, lpt; missing fields are -1 (tuned)."""
+    """(schedule, ring, xcd, lpt, place) for attn_fwd_variant from None (all tuned), a schedule name, or a
+    dict with any of the keys schedule (name or number), ring, xcd, lpt, place (name or number); missing
+    fields are -1 (tuned)."""
     if variant is None:
-        return (-1, -1, -1, -1)
+        return (-1, -1, -1, -1, -1)
     if isinstance(variant, str):
         variant = {"schedule": variant}
     sched = variant.get("schedule", -1)
     if isinstance(sched, str):
         sched = SCHEDULES[sched]
-    return (int(sched), int(variant.get("ring", -1)), int(variant.get("xcd", -1)), int(variant.get("lpt", -1)))
+    place = variant.get("place", -1)
+    if isinstance(place, str):
+        place = PLACES[place]
+    return (int(sched), int(variant.get("ring", -1)), int(variant.get("xcd", -1)), int(variant.get("lpt", -1)),
+            int(place))
 
 
 def attn_status_string(status: int) -> str:

@@ -13,7 +13,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libattn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-ATTN_SOURCES = [os.path.join(CSRC, "attn_fwd.hip"), os.path.join(CSRC, "attn_wide.hip"), os.path.join(CSRC, "attn_api.cpp"),
+WIDE_SOURCES = [os.path.join(CSRC, "attn_wide_%s.hip" % p) for p in ("even", "front", "early")]
+ATTN_SOURCES = [os.path.join(CSRC, "attn_fwd.hip"), *WIDE_SOURCES, os.path.join(CSRC, "attn_api.cpp"),
                 os.path.join(CSRC, "attn_static_ws.hip")]
 GEMM_SOURCES = [os.path.join(CSRC, "gemm_fwd.hip"), os.path.join(CSRC, "gemm_api.cpp")]
 SOURCES = ATTN_SOURCES + GEMM_SOURCES
@@ -49,14 +50,26 @@ def build(out: str = LIB, extra_flags=()) -> str:
     return out
 
 
+def _asm_cmd(out: str, src: str):
+    return [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-S", "--cuda-device-only",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-I" + INCLUDE, "-I" + CSRC, src, "-o", out]
+
+
 def device_asm(out: str, src: str | None = None) -> str:
     """Write the gfx950 assembly of one kernel source (default: the attention kernel), for register, LDS and
     scratch inspection."""
-    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-S", "--cuda-device-only",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-I" + INCLUDE, "-I" + CSRC,
-           src or ATTN_SOURCES[0], "-o", out]
-    subprocess.run(cmd, check=True, capture_output=True)
+    subprocess.run(_asm_cmd(out, src or ATTN_SOURCES[0]), check=True, capture_output=True)
     return out
+
+
+def device_asm_many(pairs) -> None:
+    """device_asm() for several (out, src) pairs, compiled in parallel."""
+    procs = [(src, subprocess.Popen(_asm_cmd(out, src), stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True))
+             for out, src in pairs]
+    for src, proc in procs:
+        _, err = proc.communicate()
+        if proc.returncode != 0:
+            raise RuntimeError("hipcc -S failed for %s:\n%s" % (src, err))
 
 
 if __name__ == "__main__":

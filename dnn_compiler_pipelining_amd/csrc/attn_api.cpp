@@ -20,9 +20,9 @@ constexpr int kMaxSeq = 1 << 30;  // sequence lengths up to 2^30 keep all tile a
 // state: attn_fwd_variant passes a request explicitly (the schedule search
 // and the tests use it), every other entry point asks for the tuned variant.
 struct Request {
-  int schedule, ring, xcd, lpt;
+  int schedule, ring, xcd, lpt, place;
 };
-constexpr Request kTunedRequest = {-1, -1, -1, -1};
+constexpr Request kTunedRequest = {-1, -1, -1, -1, -1};
 
 // The variant a call runs, or false if the request names a value that does
 // not exist or a schedule the head dimension does not run.  D = 128 runs
@@ -38,6 +38,8 @@ bool choose_variant(const Request& r, int B, int Sq, int Sk, int Hq, int Hkv, in
   if (r.ring >= 0) v.ring = r.ring;
   if (r.xcd >= 0) v.xcd = r.xcd;
   if (r.lpt >= 0) v.lpt = r.lpt;
+  if (v.schedule != libattn::SCHEDULE_WIDE) v.place = libattn::PLACE_EVEN;  // the only placement they have
+  if (r.place >= 0) v.place = r.place;
   if (!libattn::variant_valid(v)) return false;
   if (D == 64) return v.schedule == libattn::SCHEDULE_SERIAL || v.schedule == libattn::SCHEDULE_SERIAL4;
   if (D == 256) return v.schedule == libattn::SCHEDULE_SERIAL4;
@@ -141,6 +143,7 @@ int forward(const void* q, const void* k, const void* v, void* o, float* lse, in
   p.ring = var.ring;
   p.xcd = var.xcd;
   p.lpt = var.lpt;
+  p.place = var.place;
   hipError_t e;
   if (p.schedule == libattn::SCHEDULE_WIDE) {
     // four heads of a KV group per workgroup at 64 query rows, or two at 128,
@@ -171,8 +174,10 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
 }
 
 int attn_fwd_variant(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Sq, int Sk, int Hq,
-                     int Hkv, int D, int causal, float scale, int schedule, int ring, int xcd, int lpt, void* stream) {
-  return forward(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, D, causal, scale, Request{schedule, ring, xcd, lpt}, stream);
+                     int Hkv, int D, int causal, float scale, int schedule, int ring, int xcd, int lpt, int place,
+                     void* stream) {
+  return forward(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, D, causal, scale, Request{schedule, ring, xcd, lpt, place},
+                 stream);
 }
 
 int attn_fwd_stream(const void* q, const void* k, const void* v, void* o, float* lse, int B, int S, int Hq, int Hkv,
@@ -185,8 +190,9 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   return attn_fwd_stream(q, k, v, o, lse, B, S, Hq, Hkv, D, causal, scale, nullptr);
 }
 
-int attn_tuned_variant(int B, int Sq, int Sk, int Hq, int Hkv, int D, int* schedule, int* ring, int* xcd, int* lpt) {
-  if (!schedule || !ring || !xcd || !lpt) return ATTN_ERR_NULL;
+int attn_tuned_variant(int B, int Sq, int Sk, int Hq, int Hkv, int D, int* schedule, int* ring, int* xcd, int* lpt,
+                       int* place) {
+  if (!schedule || !ring || !xcd || !lpt || !place) return ATTN_ERR_NULL;
   if (B < 1 || Sq < 1 || Sk < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || Sq > kMaxSeq || Sk > kMaxSeq)
     return ATTN_ERR_SHAPE;
   if (D != 64 && D != 128 && D != 256) return ATTN_ERR_UNSUPPORTED;
@@ -196,6 +202,7 @@ int attn_tuned_variant(int B, int Sq, int Sk, int Hq, int Hkv, int D, int* sched
   *ring = var.ring;
   *xcd = var.xcd;
   *lpt = var.lpt;
+  *place = var.place;
   return ATTN_OK;
 }
 

@@ -39,6 +39,7 @@ struct Params {
   int xcd;           // 1: give each XCD whole (batch, kv head) groups
   int lpt;           // 1: longest causal query tiles of a group first
   int hpw;           // WIDE: query heads per workgroup (4, 2 or 1; 256 / hpw query rows each)
+  int place;         // WIDE: Place of the softmax parts (variant.h)
   // split-KV mode (attn_fwd_decode): n_qt counts 128-row tiles of the packed
   // (head, query row) rows of a KV group; the keys are cut into n_splits
   // splits of split_tiles 64-key tiles; partial results go to ws_o
@@ -62,9 +63,9 @@ hipError_t launch_attn_decode(const Params& p, hipStream_t stream);
 // Enqueue the forward kernel.  Returns the hipError_t of the launch.
 hipError_t launch_attn_fwd(const Params& p, hipStream_t stream);
 
-// Grid size and launch of the WIDE schedule's kernel (attn_wide.hip; head
+// Grid size and launch of the WIDE schedule's kernel (attn_wide.h; head
 // dimension 128): p.pairs head groups of p.hpw heads per KV head, p.n_qt query
-// tiles of 256 / p.hpw rows.
+// tiles of 256 / p.hpw rows, placement p.place.
 int64_t grid_blocks_wide(const Params& p);
 hipError_t launch_attn_wide(const Params& p, hipStream_t stream);
 

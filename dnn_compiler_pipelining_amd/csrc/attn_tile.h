@@ -1,5 +1,5 @@
 // attn_tile.h -- tile geometry, constants and lane-pair reductions shared by
-// the gfx950 attention kernels (attn_fwd.hip, attn_wide.hip).
+// the gfx950 attention kernels (attn_fwd.hip, attn_wide.h).
 #pragma once
 
 #include "gfx950.h"

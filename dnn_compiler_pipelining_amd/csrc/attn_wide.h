@@ -1,5 +1,7 @@
-// attn_wide.hip -- the attention forward kernel with 64 query rows per wave
-// (gfx950, CDNA4).
+// attn_wide.h -- the attention forward kernel with 64 query rows per wave
+// (gfx950, CDNA4), as a template over the fragment prefetch depth and the
+// placement of the softmax parts; attn_wide_even.hip, attn_wide_front.hip
+// and attn_wide_early.hip compile one placement each (in parallel).
 //
 // One workgroup = 4 wavefronts, one per SIMD, one workgroup per CU.  A wave
 // owns 64 query rows of one query head, as two 32-row halves (qb = 0, 1), so
@@ -25,6 +27,8 @@
 // order, the same softmax parts in the same order, the sum check decided per
 // 32-row half (one ballot per half, as one 32-row wave there decides) -- so
 // the results are bitwise identical to its schedules.
+#pragma once
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -156,7 +160,9 @@ __device__ __forceinline__ void scale_acc(f32x16& o, float alpha) {
 }
 
 // kRing: fragments (of two MFMAs each) read ahead of the MFMA that uses them.
-template <int kRing>
+// kPlace: where the softmax parts sit among the MFMAs of the fused block
+// (Place in variant.h).
+template <int kRing, int kPlace>
 __global__ __launch_bounds__(64 * W_NW, 1) void attn_wide_kernel(Params p) {
   using G = Geo<128>;
   constexpr int NW = W_NW, NS = W_SLOTS;
@@ -442,6 +448,9 @@ __global__ __launch_bounds__(64 * W_NW, 1) void attn_wide_kernel(Params p) {
     pd[qb][kk][c2] = (_Float16)st.t[qb][pp & 1][0];
     pd[qb][kk][c2 + 1] = (_Float16)st.t[qb][pp & 1][1];
     add_pair_f16(st.rq[qb][kk & 1], f16x2{pd[qb][kk][c2], pd[qb][kk][c2 + 1]});
+    // PLACE_EARLY: the conversions stay at this step; otherwise the compiler
+    // is free to sink them to the first use of the fragment
+    if constexpr (kPlace == PLACE_EARLY) asm volatile("" : "+v"(pd[qb][kk]));
   };
   // E part e of half qb (e = 0..31: score e; 32: the last pack; 33: row sum)
   auto sm_eh = [&](auto qbc, auto ec, f32x16 (&sc)[2][2], f16x8 (&pd)[2][4], auto masked, WSm& st) INL {
@@ -614,13 +623,19 @@ __global__ __launch_bounds__(64 * W_NW, 1) void attn_wide_kernel(Params p) {
     if constexpr (kPV && kQK) {
       // half 0's parts over the 32 PV steps, half 1's over the 32 QK steps:
       // part e of a half before step floor(e * 31 / 33) of its half
+      // (PLACE_EVEN); PLACE_FRONT puts half 0's first five parts before the
+      // first MFMA and spreads the rest over steps 1..31; PLACE_EARLY spreads
+      // half 1's parts over its first 28 steps
       auto sm = [&](auto ic) INL {
         constexpr int i = decltype(ic)::value;
         dma_at(ic);
         static_for<SM_EH>([&](auto ec) INL {
           constexpr int e = decltype(ec)::value, at = e * 31 / (SM_EH - 1);
-          if constexpr (i < 32 && at == i) sm_eh(Q0{}, ec, sc, pc, mask_e, st);
-          if constexpr (i >= 32 && at == i - 32) sm_eh(Q1{}, ec, sc, pc, mask_e, st);
+          constexpr int FR = 5;
+          constexpr int at0 = kPlace == PLACE_FRONT ? (e < FR ? 0 : 1 + (e - FR) * 30 / (SM_EH - 1 - FR)) : at;
+          constexpr int at1 = kPlace == PLACE_EARLY ? e * 27 / (SM_EH - 1) : at;
+          if constexpr (i < 32 && at0 == i) sm_eh(Q0{}, ec, sc, pc, mask_e, st);
+          if constexpr (i >= 32 && at1 == i - 32) sm_eh(Q1{}, ec, sc, pc, mask_e, st);
         });
       };
       block(M_FUSED{}, kslot, sn, vslot, pp, sm);
@@ -756,17 +771,15 @@ __global__ __launch_bounds__(64 * W_NW, 1) void attn_wide_kernel(Params p) {
   }
 }
 
-int64_t grid_blocks_wide(const Params& p) {
-  const int64_t nb = (int64_t)p.B * p.Hkv * p.pairs * p.n_qt;
-  return nb > 0x7fffffff ? -1 : nb;
-}
-
-hipError_t launch_attn_wide(const Params& p, hipStream_t stream) {
+// Launch of the kernel with placement kPlace, either prefetch depth
+// (grid_blocks_wide() workgroups).
+template <int kPlace>
+hipError_t launch_attn_wide_placed(const Params& p, hipStream_t stream) {
   const int64_t nb = grid_blocks_wide(p);
   if (nb <= 0 || p.hd != 128 || (p.hpw != 1 && p.hpw != 2 && p.hpw != 4)) return hipErrorInvalidValue;
   const dim3 grid((unsigned)nb), block(64 * W_NW);
-  if (p.ring == 2) hipLaunchKernelGGL(attn_wide_kernel<2>, grid, block, 0, stream, p);
-  else if (p.ring == 4) hipLaunchKernelGGL(attn_wide_kernel<4>, grid, block, 0, stream, p);
+  if (p.ring == 2) hipLaunchKernelGGL((attn_wide_kernel<2, kPlace>), grid, block, 0, stream, p);
+  else if (p.ring == 4) hipLaunchKernelGGL((attn_wide_kernel<4, kPlace>), grid, block, 0, stream, p);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

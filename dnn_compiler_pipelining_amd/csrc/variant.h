@@ -4,8 +4,9 @@
 //
 // A variant is a point of the schedule space that the search in
 // dnn_compiler_pipelining_amd/tune.py explores: the tile schedule, the depth
-// of the fragment prefetch ring, and two workgroup-order switches.  Every
-// variant computes bitwise identical results; they differ only in speed.
+// of the fragment prefetch ring, where the softmax parts sit among the MFMAs
+// (64-row schedule), and two workgroup-order switches.  Every variant
+// computes bitwise identical results; they differ only in speed.
 // PipeThreader searches such a space of task orders with a validity check
 // and profile feedback (page "PipeThreader: Software-Defined Pipelining ...
 // (OSDI 2025)" summary, section "核心方法"); tuned_table.h is the outcome of
@@ -27,7 +28,7 @@ namespace libattn {
 //             each; two workgroups share a CU, so the two waves on a SIMD
 //             come from independently synchronised workgroups and drift out
 //             of phase (one's softmax beside the other's MFMAs)
-//   WIDE    : 64 query rows per wave (attn_wide.hip): one wave per SIMD, each
+//   WIDE    : 64 query rows per wave (attn_wide.h): one wave per SIMD, each
 //             K/V fragment read from LDS feeds two MFMAs, the overlap
 //             schedule inside each wave, K/V loaded two tiles ahead
 //             (head dimension 128)
@@ -39,11 +40,22 @@ enum Schedule {
   SCHEDULE_WIDE = 4
 };
 
+// Placements of the softmax parts among the MFMAs of the 64-row schedule's
+// fused block (the other schedules have one placement, PLACE_EVEN):
+//   PLACE_EVEN : each half's parts spread evenly over its 32 steps
+//   PLACE_FRONT: query half 0's first five parts before the first MFMA, where
+//                the block waits for its first fragment, the rest spread
+//   PLACE_EARLY: half 1's parts end four steps before the block, so that its
+//                sum check is settled when the block ends; each fp16 pack is
+//                held at its step (not sunk to its first use)
+enum Place { PLACE_EVEN = 0, PLACE_FRONT = 1, PLACE_EARLY = 2 };
+
 struct Variant {
   int schedule;  // Schedule
   int ring;      // fragment prefetch depth of the mma steps: 2 or 4
   int xcd;       // 1: each XCD gets whole (batch, kv head) groups
   int lpt;       // 1: longest causal query tiles of a group first
+  int place;     // Place (SCHEDULE_WIDE only; PLACE_EVEN for the others)
 };
 
 // One measured shape and the fastest variant found for it.
@@ -57,7 +69,8 @@ struct TunedEntry {
 
 inline bool variant_valid(const Variant& v) {
   return v.schedule >= SCHEDULE_SERIAL && v.schedule <= SCHEDULE_WIDE && (v.ring == 2 || v.ring == 4) &&
-         (v.xcd == 0 || v.xcd == 1) && (v.lpt == 0 || v.lpt == 1);
+         (v.xcd == 0 || v.xcd == 1) && (v.lpt == 0 || v.lpt == 1) && v.place >= PLACE_EVEN &&
+         v.place <= PLACE_EARLY && (v.schedule == SCHEDULE_WIDE || v.place == PLACE_EVEN);
 }
 
 // The variant tuned for the measured shape nearest to (B, Sq, Sk, Hq, Hkv):

@@ -4,9 +4,10 @@ PipeThreader schedules an operator by searching the space of task orders on
 the hardware's units under a resource check, with measured feedback (page
 "PipeThreader: Software-Defined Pipelining ... (OSDI 2025)" summary, section
 "核心方法").  This module does that for libattn's space of kernel variants
-(csrc/variant.h): tile schedule x fragment-prefetch depth (compile time) x
-two workgroup-order switches (run time).  Every variant computes the same bits,
-so the search only trades speed.
+(csrc/variant.h): tile schedule x fragment-prefetch depth x placement of the
+softmax parts among the MFMAs (64-row schedule) (compile time) x two
+workgroup-order switches (run time).  Every variant computes the same bits, so
+the search only trades speed.
 
     python -m dnn_compiler_pipelining_amd.tune --check
         validity of every compiled variant from the code-object metadata (CPU)
@@ -31,6 +32,7 @@ TABLE = os.path.join(PKG, "csrc", "tuned_table.h")
 PROFILE = os.path.join(ROOT, "profiles", "schedule_search.json")
 
 SCHEDULES = ("serial", "overlap", "pingpong", "serial4", "wide")  # Schedule enum order in csrc/variant.h
+PLACES = ("even", "front", "early")  # Place enum order in csrc/variant.h; schedules other than wide: even only
 
 
 def workgroups_per_cu(schedule: str, hd: int) -> int:
@@ -44,7 +46,7 @@ def waves_per_simd(schedule: str, hd: int) -> int:
     return 1 if schedule == "wide" or (schedule.startswith("serial4") and hd > 128) else 2
 RINGS = (2, 4)
 SWITCHES = (0, 1)
-SEED = {"schedule": "serial", "ring": 4, "xcd": 1, "lpt": 1}
+SEED = {"schedule": "serial", "ring": 4, "xcd": 1, "lpt": 1, "place": "even"}
 # A change is kept when it is this much faster.  The median of five timed batches repeats to about
 # 0.2% on one box (repeated same-box pairs of the serial and overlap schedules on the 70B-shaped
 # B = 16 S = 8192 problem differed by 0.3-1.1%, always in the same direction).
@@ -73,8 +75,8 @@ def loop_scratch(text: str, symbol: str) -> int:
 
 
 def kernel_resources(asm_path: str):
-    """{(schedule, ring, hd): {vgpr, agpr, vgpr_spill, scratch, lds, loop_scratch}} from the AMDGPU metadata
-    of a device asm file and the annotated loop structure of its code.
+    """{(schedule, ring, hd, place): {vgpr, agpr, vgpr_spill, scratch, lds, loop_scratch}} from the AMDGPU
+    metadata of a device asm file and the annotated loop structure of its code.
 
     The split-KV instances (attn_fwd_decode) appear under the schedule name "serial4-split".  On gfx950
     `vgpr` (.vgpr_count) is the unified register count, AGPRs included; `agpr` is the AGPR part of it."""
@@ -83,7 +85,7 @@ def kernel_resources(asm_path: str):
     out = {}
     for block in re.split(r"\n  - ", meta)[1:]:
         m = re.search(r"\.name:\s+\S*attn_fwd_kernelILi(\d)ELi(\d)ELi(\d+)ELb([01])E", block)
-        mw = re.search(r"\.name:\s+\S*attn_wide_kernelILi(\d)E", block)
+        mw = re.search(r"\.name:\s+\S*attn_wide_kernelILi(\d)ELi(\d)E", block)
         if not m and not mw:
             continue
 
@@ -91,11 +93,11 @@ def kernel_resources(asm_path: str):
             mm = re.search(r"\." + key + r":\s+(\d+)", block)
             return int(mm.group(1)) if mm else 0
 
-        if mw:  # the wide kernel: head dimension 128, template argument = fragment prefetch depth
-            key = ("wide", int(mw.group(1)), 128)
+        if mw:  # the wide kernel: head dimension 128, template arguments = prefetch depth, placement
+            key = ("wide", int(mw.group(1)), 128, PLACES[int(mw.group(2))])
         else:
             key = (SCHEDULES[int(m.group(1))] + ("-split" if m.group(4) == "1" else ""), int(m.group(2)),
-                   int(m.group(3)))
+                   int(m.group(3)), "even")
         sym = re.search(r"\.name:\s+(\S+)", block).group(1)
         out[key] = dict(
             vgpr=num("vgpr_count"), agpr=num("agpr_count"), vgpr_spill=num("vgpr_spill_count"),
@@ -129,20 +131,26 @@ def valid_variants(asm_paths=None):
     from dnn_compiler_pipelining_amd import build
 
     if asm_paths is None:
-        asm_paths = []
+        pairs = []
         for src in build.ATTN_SOURCES:
             if not src.endswith(".hip"):
                 continue
             fd, path = tempfile.mkstemp(suffix=".s")
             os.close(fd)
-            build.device_asm(path, src)
-            asm_paths.append(path)
+            pairs.append((path, src))
+        build.device_asm_many(pairs)
+        asm_paths = [path for path, _ in pairs]
     elif isinstance(asm_paths, str):
         asm_paths = [asm_paths]
     res = {}
     for path in asm_paths:
         res.update(kernel_resources(path))
     return {k: check_valid(v, k[0], k[2]) + (v,) for k, v in res.items()}
+
+
+def variant_key(pt: dict, hd: int) -> tuple:
+    """The valid_variants() key of a search point."""
+    return (pt["schedule"], pt["ring"], hd, pt.get("place", "even"))
 
 
 # ------------------------------------------------------------------ search (GPU)
@@ -184,13 +192,13 @@ def search_workload(w, valid, log=print):
     seen = {}
 
     def rate(pt):
-        key = (pt["schedule"], pt["ring"], pt["xcd"], pt["lpt"])
+        key = (pt["schedule"], pt["ring"], pt["xcd"], pt["lpt"], pt["place"])
         if key not in seen:
             seen[key] = measure(w, pt, q, k, v, o, lse)
-            log("  %-26s %-9s ring %d xcd %d lpt %d: %7.1f TFLOP/s" % (w.name, *key, seen[key]))
+            log("  %-26s %-9s ring %d xcd %d lpt %d place %-5s: %7.1f TFLOP/s" % (w.name, *key, seen[key]))
         return seen[key]
 
-    axes = [("schedule", SCHEDULES), ("ring", RINGS), ("xcd", SWITCHES), ("lpt", SWITCHES)]
+    axes = [("schedule", SCHEDULES), ("ring", RINGS), ("xcd", SWITCHES), ("lpt", SWITCHES), ("place", PLACES)]
     best = dict(SEED)
     best_rate = rate(best)
     improved = True
@@ -201,7 +209,7 @@ def search_workload(w, valid, log=print):
                 if val == best[field]:
                     continue
                 cand = dict(best, **{field: val})
-                if not valid.get((cand["schedule"], cand["ring"], w.D), (False,))[0]:
+                if not valid.get(variant_key(cand, w.D), (False,))[0]:
                     continue
                 r = rate(cand)
                 if r > best_rate * (1.0 + KEEP_GAIN):
@@ -210,17 +218,17 @@ def search_workload(w, valid, log=print):
     torch.cuda.empty_cache()
     return {"workload": w.name, "B": w.B, "Sq": w.S, "Sk": w.S, "Hq": w.Hq, "Hkv": w.Hkv, "best": best,
             "best_tflops": round(best_rate, 1),
-            "measured": [{"schedule": s, "ring": r, "xcd": x, "lpt": l, "tflops": round(t, 1)}
-                         for (s, r, x, l), t in seen.items()]}
+            "measured": [{"schedule": s, "ring": r, "xcd": x, "lpt": l, "place": pl, "tflops": round(t, 1)}
+                         for (s, r, x, l, pl), t in seen.items()]}
 
 
 def search(out_dir: str, names=None):
     from dnn_compiler_pipelining_amd import inputs
 
     valid = valid_variants()
-    for (s, r, hd), (ok, why, _) in sorted(valid.items()):
-        print("variant %-9s ring %d hd %d: %s" % (s, r, hd, why), flush=True)
-    rec = {"valid": {"%s/%d/%d" % k: dict(ok=v[0], reason=v[1], **v[2]) for k, v in valid.items()},
+    for (s, r, hd, pl), (ok, why, _) in sorted(valid.items()):
+        print("variant %-13s ring %d hd %3d place %-5s: %s" % (s, r, hd, pl, why), flush=True)
+    rec = {"valid": {"%s/%d/%d/%s" % k: dict(ok=v[0], reason=v[1], **v[2]) for k, v in valid.items()},
            "rule": "greedy coordinate search from %s; a change is kept when > %.1f%% faster (median of five "
                    "timed batches)" % (json.dumps(SEED), 100 * KEEP_GAIN),
            "results": []}
@@ -242,14 +250,15 @@ def search(out_dir: str, names=None):
 def emit(search_json: str, table: str = TABLE, profile: str | None = PROFILE):
     rec = json.load(open(search_json))
     enum = {name: "SCHEDULE_" + name.upper() for name in SCHEDULES}
+    penum = {name: "PLACE_" + name.upper() for name in PLACES}
     lines = ["// tuned_table.h -- generated by `python -m dnn_compiler_pipelining_amd.tune --emit`",
              "// from the measured schedule search (profiles/schedule_search.json); do not edit by hand.",
              "#pragma once", "static const TunedEntry kTuned[] = {"]
     for r in rec["results"]:
         b = r["best"]
-        lines.append("    {%d, %d, %d, %d, %d, {%s, %d, %d, %d}, %.1f},  // %s" % (
+        lines.append("    {%d, %d, %d, %d, %d, {%s, %d, %d, %d, %s}, %.1f},  // %s" % (
             r["B"], r["Sq"], r["Sk"], r["Hq"], r["Hkv"], enum[b["schedule"]], b["ring"], b["xcd"], b["lpt"],
-            r["best_tflops"], r["workload"]))
+            penum[b.get("place", "even")], r["best_tflops"], r["workload"]))
     lines += ["};", "static const int kTunedCount = sizeof(kTuned) / sizeof(kTuned[0]);", ""]
     with open(table, "w") as f:
         f.write("\n".join(lines))
@@ -272,8 +281,8 @@ def main(argv=None):
     if ROOT not in sys.path:
         sys.path.insert(0, ROOT)
     if args.check:
-        for (s, r, hd), (ok, why, res) in sorted(valid_variants().items()):
-            print("%-9s ring %d hd %3d: %-5s %s  %s" % (s, r, hd, ok, why, res))
+        for (s, r, hd, pl), (ok, why, res) in sorted(valid_variants().items()):
+            print("%-13s ring %d hd %3d place %-5s: %-5s %s  %s" % (s, r, hd, pl, ok, why, res))
     if args.search:
         search(args.search, args.workload)
     if args.emit:

@@ -105,19 +105,28 @@ enum {
   ATTN_SCHEDULE_WIDE = 4
 };
 
+/* Placement of the softmax work among the MFMAs of ATTN_SCHEDULE_WIDE's main loop: spread evenly,
+ * partly before the first MFMA (where the loop waits for its first operands), or ending early (the
+ * sum check settled before the loop's next iteration).  The other schedules have ATTN_PLACE_EVEN only. */
+enum { ATTN_PLACE_EVEN = 0, ATTN_PLACE_FRONT = 1, ATTN_PLACE_EARLY = 2 };
+
 /* attn_fwd_ex with an explicit kernel variant, for schedule search and cross-checks: `schedule` is an
  * ATTN_SCHEDULE_* value, `ring` the fragment prefetch depth (2 or 4), `xcd` 1 to give each XCD whole
- * (batch, KV head) groups, `lpt` 1 to run the longest causal query tiles first; -1 in any of them takes
- * the tuned value.  A value that does not exist, or a schedule the head dimension does not run, returns
- * ATTN_ERR_UNSUPPORTED and launches nothing.  Results are bitwise identical for every variant. */
+ * (batch, KV head) groups, `lpt` 1 to run the longest causal query tiles first, `place` an ATTN_PLACE_*
+ * value; -1 in any of them takes the tuned value (place: ATTN_PLACE_EVEN for schedules other than
+ * ATTN_SCHEDULE_WIDE).  A value that does not exist, a placement the schedule does not have, or a
+ * schedule the head dimension does not run, returns ATTN_ERR_UNSUPPORTED and launches nothing.  Results
+ * are bitwise identical for every variant. */
 int attn_fwd_variant(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Sq, int Sk, int Hq,
-                     int Hkv, int D, int causal, float scale, int schedule, int ring, int xcd, int lpt,
+                     int Hkv, int D, int causal, float scale, int schedule, int ring, int xcd, int lpt, int place,
                      void* stream);
 
-/* The variant attn_fwd_ex runs for these sizes (ATTN_SCHEDULE_* value, ring depth, xcd and lpt switches),
- * for reports and cross-checks.  Returns ATTN_OK, ATTN_ERR_NULL for a NULL output pointer, ATTN_ERR_SHAPE
- * for sizes attn_fwd_ex rejects, ATTN_ERR_UNSUPPORTED for a head dimension it does not run.  No HIP call. */
-int attn_tuned_variant(int B, int Sq, int Sk, int Hq, int Hkv, int D, int* schedule, int* ring, int* xcd, int* lpt);
+/* The variant attn_fwd_ex runs for these sizes (ATTN_SCHEDULE_* value, ring depth, xcd and lpt switches,
+ * ATTN_PLACE_* value), for reports and cross-checks.  Returns ATTN_OK, ATTN_ERR_NULL for a NULL output
+ * pointer, ATTN_ERR_SHAPE for sizes attn_fwd_ex rejects, ATTN_ERR_UNSUPPORTED for a head dimension it does
+ * not run.  No HIP call. */
+int attn_tuned_variant(int B, int Sq, int Sk, int Hq, int Hkv, int D, int* schedule, int* ring, int* xcd, int* lpt,
+                       int* place);
 
 /* Compute-unit count and peak shader clock (kHz) of HIP device `device`, as the runtime reports them: the
  * inputs of a peak-throughput figure (dense fp16 MFMA on gfx950: 4 SIMDs x 1024 FLOP per clock per compute

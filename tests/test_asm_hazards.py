@@ -1,4 +1,4 @@
-"""MFMA dependency rules around inline assembly in the 64-rows-per-wave kernel (csrc/attn_wide.hip).
+"""MFMA dependency rules around inline assembly in the 64-rows-per-wave kernel (csrc/attn_wide.h).
 
 The compiler's hazard pass inserts the wait states between an MFMA and the instructions that depend on it,
 but only for instructions it understands: an MFMA written as inline assembly, or an accumulator access inside
@@ -23,7 +23,7 @@ import pytest
 
 from dnn_compiler_pipelining_amd import build
 
-KERNEL_SRC = os.path.join(build.CSRC, "attn_wide.hip")
+KERNEL_SRCS = build.WIDE_SOURCES  # attn_wide.h, one placement per source
 AFTER_MFMA = 18
 BEFORE_MFMA = 4
 
@@ -139,21 +139,32 @@ def test_scanner_finds_planted_hazards():
 
 @pytest.fixture(scope="module")
 def wide_asm():
-    fd, path = tempfile.mkstemp(suffix=".s")
-    os.close(fd)
+    paths = []
+    for _ in KERNEL_SRCS:
+        fd, path = tempfile.mkstemp(suffix=".s")
+        os.close(fd)
+        paths.append(path)
     try:
-        build.device_asm(path, KERNEL_SRC)
-        with open(path) as f:
-            yield f.read()
+        build.device_asm_many(zip(paths, KERNEL_SRCS))
+        texts = []
+        for path in paths:
+            with open(path) as f:
+                texts.append(f.read())
+        yield texts
     finally:
-        os.remove(path)
+        for path in paths:
+            os.remove(path)
 
 
 def test_wide_kernel_keeps_the_mfma_dependency_rules(wide_asm):
-    symbols = re.findall(r"^(_ZN7libattn16attn_wide_kernel\S*):", wide_asm, re.M)
-    assert symbols, "no wide kernel in the assembly"
-    for sym in symbols:
-        ins = instructions(wide_asm, sym)
-        assert sum(1 for a, l in ins if a and l.startswith("v_mfma")) >= 32, sym
-        bad = scan(ins)
-        assert not bad, "%s:\n%s" % (sym, "\n".join(bad[:20]))
+    n = 0
+    for text in wide_asm:
+        symbols = re.findall(r"^(_ZN7libattn16attn_wide_kernel\S*):", text, re.M)
+        assert symbols, "no wide kernel in the assembly"
+        for sym in symbols:
+            ins = instructions(text, sym)
+            assert sum(1 for a, l in ins if a and l.startswith("v_mfma")) >= 32, sym
+            bad = scan(ins)
+            assert not bad, "%s:\n%s" % (sym, "\n".join(bad[:20]))
+            n += 1
+    assert n == 6  # two prefetch depths x three placements

@@ -214,9 +214,10 @@ def test_all_variants_bitwise_identical(B, S, Hq, Hkv, causal):
         for ring in (2, 4):
             for xcd in (0, 1):
                 for lpt in (0, 1):
-                    var = {"schedule": sched, "ring": ring, "xcd": xcd, "lpt": lpt}
-                    o2, l2 = U.run(qd, kd, vd, bool(causal), SC, var)
-                    assert torch.equal(o1, o2) and torch.equal(l1, l2), var
+                    for place in (binding.PLACES if sched == "wide" else ("even",)):
+                        var = {"schedule": sched, "ring": ring, "xcd": xcd, "lpt": lpt, "place": place}
+                        o2, l2 = U.run(qd, kd, vd, bool(causal), SC, var)
+                        assert torch.equal(o1, o2) and torch.equal(l1, l2), var
 
 
 def spiked_qkv(S, Hq, Hkv, hd, seed, spikes):

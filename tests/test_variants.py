@@ -13,10 +13,11 @@ CSRC = os.path.join(tune.PKG, "csrc")
 
 def test_every_compiled_variant_is_valid():
     vs = tune.valid_variants()
-    assert set(vs) == ({(s, r, 128) for s in tune.SCHEDULES for r in tune.RINGS} |
-                       {(s, r, 64) for s in ("serial", "serial4") for r in tune.RINGS} |
-                       {("serial4", r, 256) for r in tune.RINGS} |
-                       {("serial4-split", r, hd) for r in tune.RINGS for hd in (64, 128, 256)})
+    assert set(vs) == ({(s, r, 128, "even") for s in tune.SCHEDULES if s != "wide" for r in tune.RINGS} |
+                       {("wide", r, 128, pl) for r in tune.RINGS for pl in tune.PLACES} |
+                       {(s, r, 64, "even") for s in ("serial", "serial4") for r in tune.RINGS} |
+                       {("serial4", r, 256, "even") for r in tune.RINGS} |
+                       {("serial4-split", r, hd, "even") for r in tune.RINGS for hd in (64, 128, 256)})
     for key, (ok, why, res) in vs.items():
         assert ok, (key, why, res)
         assert res["lds"] > 0 and res["vgpr"] > 0
@@ -68,7 +69,7 @@ int main(int argc, char** argv) {
   int B, Sq, Sk, Hq, Hkv;
   while (std::scanf("%d %d %d %d %d", &B, &Sq, &Sk, &Hq, &Hkv) == 5) {
     libattn::Variant v = libattn::tuned_variant(B, Sq, Sk, Hq, Hkv);
-    std::printf("%d %d %d %d %d\n", v.schedule, v.ring, v.xcd, v.lpt, libattn::variant_valid(v) ? 1 : 0);
+    std::printf("%d %d %d %d %d %d\n", v.schedule, v.ring, v.xcd, v.lpt, v.place, libattn::variant_valid(v) ? 1 : 0);
   }
   return 0;
 }
@@ -94,11 +95,13 @@ def test_committed_table_picks_its_own_entries(tmp_path):
     from dnn_compiler_pipelining_amd import binding
 
     enum = {"SCHEDULE_" + name.upper(): value for name, value in binding.SCHEDULES.items()}
-    rows = re.findall(r"\{(\d+), (\d+), (\d+), (\d+), (\d+), \{(SCHEDULE_\w+), (\d), (\d), (\d)\}", text)
+    penum = {"PLACE_" + name.upper(): value for name, value in binding.PLACES.items()}
+    rows = re.findall(r"\{(\d+), (\d+), (\d+), (\d+), (\d+), \{(SCHEDULE_\w+), (\d), (\d), (\d), (PLACE_\w+)\}",
+                      text)
     assert rows
     got = lookup(tmp_path, CSRC, [r[:5] for r in rows])
     for r, g in zip(rows, got):
-        assert g == (enum[r[5]], int(r[6]), int(r[7]), int(r[8]), 1), (r, g)
+        assert g == (enum[r[5]], int(r[6]), int(r[7]), int(r[8]), penum[r[9]], 1), (r, g)
 
 
 def test_emit_and_nearest_shape(tmp_path):
@@ -108,13 +111,17 @@ def test_emit_and_nearest_shape(tmp_path):
          "best": {"schedule": "overlap", "ring": 2, "xcd": 0, "lpt": 1}},
         {"workload": "big", "B": 64, "Sq": 8192, "Sk": 8192, "Hq": 64, "Hkv": 8, "best_tflops": 990.0,
          "best": {"schedule": "pingpong", "ring": 4, "xcd": 1, "lpt": 0}},
+        {"workload": "mid", "B": 64, "Sq": 2048, "Sk": 2048, "Hq": 32, "Hkv": 8, "best_tflops": 850.0,
+         "best": {"schedule": "wide", "ring": 4, "xcd": 1, "lpt": 1, "place": "early"}},
     ]}
     js = tmp_path / "search.json"
     js.write_text(json.dumps(rec))
     tdir = tmp_path / "tbl"
     tdir.mkdir()
     tune.emit(str(js), table=str(tdir / "tuned_table.h"), profile=None)
-    got = lookup(tmp_path, tdir, [(1, 600, 600, 32, 8), (48, 8192, 8192, 64, 8), (1, 2048, 8192, 64, 8)])
-    assert got[0] == (1, 2, 0, 1, 1)
-    assert got[1] == (2, 4, 1, 0, 1)
-    assert got[2] in ((1, 2, 0, 1, 1), (2, 4, 1, 0, 1))
+    got = lookup(tmp_path, tdir, [(1, 600, 600, 32, 8), (48, 8192, 8192, 64, 8), (1, 2048, 8192, 64, 8),
+                                  (64, 2000, 2000, 32, 8)])
+    assert got[0] == (1, 2, 0, 1, 0, 1)
+    assert got[1] == (2, 4, 1, 0, 0, 1)
+    assert got[2] in ((1, 2, 0, 1, 0, 1), (2, 4, 1, 0, 0, 1))
+    assert got[3] == (4, 4, 1, 1, 2, 1)
