@@ -555,12 +555,22 @@ __global__ __launch_bounds__(64 * W_NW, 1) void attn_wide_kernel(Params p) {
   };
   // the sum check of half qb of tile j; on failure the tile max (S^T of the
   // half recomputed), the running-max update and the exponentials again, and
-  // O^T of that half rescaled; then l
-  auto sm_finish = [&](auto qbc, int j, f32x16 (&sc)[2][2], f16x8 (&pd)[2][4], auto masked, WSm& st) INL {
+  // O^T of that half rescaled; then l.  In the last iteration (no QK^T, so no
+  // second S^T set to make room for) S^T is kept instead of recomputed: Q^T
+  // is then dead after the last QK^T block (kept alive for a recompute there,
+  // it was spilled to scratch at every work item's end).  Same bits either
+  // way: a recomputed S^T equals the first one.
+  auto sm_finish = [&](auto qbc, int j, f32x16 (&sc)[2][2], f16x8 (&pd)[2][4], auto masked, WSm& st,
+                       auto recompute) INL {
     constexpr int qb = decltype(qbc)::value;
     float alpha = 1.0f;
     if (__builtin_expect(st.redo[qb], 0)) {
-      recompute_half(qbc, j, sc);  // 16 guarded MFMAs: O^T's last PV MFMA is far behind too
+      if constexpr (decltype(recompute)::value) {
+        recompute_half(qbc, j, sc);  // 16 guarded MFMAs: O^T's last PV MFMA is far behind too
+      } else {
+        // O^T's last PV MFMA may be just before: keep the rescale below apart from it
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 2" ::: "memory");
+      }
       alpha = sm_max(qbc, sc, masked, st);
       static_for<SM_EH>([&](auto ec) INL { sm_eh(qbc, ec, sc, pd, masked, st); });
       static_for<4>([&](auto dc) INL { scale_acc(o_acc[decltype(dc)::value][qb], alpha); });
@@ -657,8 +667,8 @@ __global__ __launch_bounds__(64 * W_NW, 1) void attn_wide_kernel(Params p) {
       static_for<SM_EH>([&](auto ec) INL { sm_eh(Q0{}, ec, sc, pc, mask_e, st); });
       static_for<SM_EH>([&](auto ec) INL { sm_eh(Q1{}, ec, sc, pc, mask_e, st); });
     }
-    sm_finish(Q0{}, j, sc, pc, mask_e, st);
-    sm_finish(Q1{}, j, sc, pc, mask_e, st);
+    sm_finish(Q0{}, j, sc, pc, mask_e, st, with_qk);
+    sm_finish(Q1{}, j, sc, pc, mask_e, st, with_qk);
     wait_older(issued);
     lds_barrier();
   };

@@ -87,6 +87,10 @@ def test_overlap(lib):
     assert call(o=KP + 4096) == L.ATTN_ERR_OVERLAP  # o starts inside k
     assert call(o=LP - 4096) == L.ATTN_ERR_OVERLAP  # o runs into lse
     assert call(o=VP, lse=0) == L.ATTN_ERR_OVERLAP
+    # lse is written while other workgroups still read q, k and v
+    assert call(lse=QP + 256) == L.ATTN_ERR_OVERLAP
+    assert call(lse=KP) == L.ATTN_ERR_OVERLAP
+    assert call(lse=VP + 1024) == L.ATTN_ERR_OVERLAP
 
 
 def test_validation_order(lib):

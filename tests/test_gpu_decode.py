@@ -90,3 +90,19 @@ def test_decode_workspace_too_small_launches_nothing():
     assert st == binding.ATTN_ERR_WORKSPACE
     torch.cuda.synchronize()
     assert bool(torch.isnan(o).all().item())
+
+
+def test_decode_on_a_non_default_stream_with_its_own_workspace():
+    """binding.decode() allocating the workspace itself while launching on another stream (the workspace
+    is then tied to that stream): the same bits as on the current stream."""
+    B, Sq, Sk, Hq, Hkv, D = 2, 3, 2000, 32, 8, 128
+    scale = 1.0 / math.sqrt(D)
+    q, k, v = cpu_qkv(B, Sq, Sk, Hq, Hkv, D, seed=7101)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    o1, l1 = binding.decode(qd, kd, vd, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    o2, l2 = binding.decode(qd, kd, vd, causal=True, scale=scale, stream=s)
+    s.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
