@@ -220,6 +220,48 @@ def test_all_variants_bitwise_identical(B, S, Hq, Hkv, causal):
                         assert torch.equal(o1, o2) and torch.equal(l1, l2), var
 
 
+# Every compiled D = 128 kernel instance (schedule x ring depth x softmax placement) on its own against the
+# oracle, causal with a ragged tail and non-causal with g = 3, so a fault confined to one instance is named.
+INSTANCES = [(sched, ring, place) for sched in U.SCHEDULES_D128 for ring in (2, 4)
+             for place in (binding.PLACES if sched == "wide" else ("even",))]
+
+
+@pytest.mark.parametrize("sched,ring,place", INSTANCES, ids=lambda x: str(x))
+@pytest.mark.parametrize("B,S,Hq,Hkv,causal", [(1, 650, 8, 2, 1), (2, 201, 12, 4, 0)], ids=str)
+def test_every_instance_against_oracle(B, S, Hq, Hkv, causal, sched, ring, place):
+    tag = "instance %s ring%d %s B%d S%d Hq%d Hkv%d causal%d" % (sched, ring, place, B, S, Hq, Hkv, causal)
+    U.say(tag)
+    q, k, v = cpu_qkv(B, S, Hq, Hkv, seed=300 + S + Hq)
+    U.full_parity(q, k, v, bool(causal), SC, tag,
+                  {"schedule": sched, "ring": ring, "xcd": 1, "lpt": 1, "place": place})
+
+
+def tuned_entries():
+    """(B, Sq, Sk, Hq, Hkv, variant) rows of the compiled-in tuned table."""
+    import os
+    import re
+
+    from dnn_compiler_pipelining_amd import build
+    text = open(os.path.join(build.CSRC, "tuned_table.h")).read()
+    rows = re.findall(r"\{(\d+), (\d+), (\d+), (\d+), (\d+), \{SCHEDULE_(\w+), (\d), (\d), (\d), PLACE_(\w+)\}",
+                      text)
+    assert rows
+    return [tuple(int(x) for x in r[:5]) + ({"schedule": r[5].lower(), "ring": int(r[6]), "xcd": int(r[7]),
+                                             "lpt": int(r[8]), "place": r[9].lower()},) for r in rows]
+
+
+@pytest.mark.parametrize("entry", tuned_entries(), ids=lambda e: "B%d_S%d_Hq%d" % (e[0], e[1], e[3]))
+def test_tuned_entries(entry):
+    """Each tuned-table entry: the library reports that variant for the entry's own shape, and the variant
+    matches the oracle on a shortened problem with the entry's heads (B = 1, a ragged S)."""
+    B, Sq, Sk, Hq, Hkv, var = entry
+    assert binding.attn_tuned_variant(B, Sq, Sk, Hq, Hkv, D) == var
+    S = min(Sq, 777)
+    U.say("tuned entry %s at S%d" % (var, S))
+    q, k, v = cpu_qkv(1, S, Hq, Hkv, seed=400 + Hq)
+    U.full_parity(q, k, v, True, SC, "tuned %s" % var, var)
+
+
 def spiked_qkv(S, Hq, Hkv, hd, seed, spikes):
     """Q shifted by +1 per element, and at each (position j, c) every K head's row j set to the constant
     c * 128 / hd: key j then scores about 16 c log2 units above the N(0,1) keys for every query, so the
