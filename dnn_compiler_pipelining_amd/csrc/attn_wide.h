@@ -595,6 +595,10 @@ __global__ __launch_bounds__(64 * W_NW, 1) void attn_wide_kernel(Params p) {
   // store nothing.
   f32x16 sa[2][2], sb[2][2];
   f16x8 pa[2][4], pb[2][4];
+  const uint64_t tile_bytes = (uint64_t)BN * row_bytes;
+  const uint64_t dv_wave = (uint64_t)(G::V_ROWS_PER_DMA * wave_s) * row_bytes;
+  const char* dk_run = (const char*)kb_ + 4 * tile_bytes;
+  const char* dv_run = (const char*)vb_ + 2 * tile_bytes + dv_wave;
   // dma_in: the loads of K_{j+3} and V_{j+1} are issued one by one between the
   // MFMAs of the fused block (steps 3, 10, ..., 59), both tiles full (j + 3 <
   // n_full); otherwise stage() issues them before the block
@@ -613,18 +617,22 @@ __global__ __launch_bounds__(64 * W_NW, 1) void attn_wide_kernel(Params p) {
     // the loads of the in-block case: d = 0..3 K instructions u = d, d = 4..7
     // V instructions u = d - 4, d = 8 this wave's quarter of the 17th K KiB
     const int tk = __builtin_amdgcn_readfirstlane(j + 3), tv = __builtin_amdgcn_readfirstlane(j + 1);
-    const char* dk_base = (const char*)kb_ + (int64_t)tk * BN * row_bytes;
-    const uint32_t dk_slot = k_lds_base + (uint32_t)(tk % NS) * K_TILEB + 1024u * (uint32_t)wave_s;
-    const char* dv_base = (const char*)vb_ + ((int64_t)tv * BN + G::V_ROWS_PER_DMA * wave_s) * row_bytes;
-    const uint32_t dv_slot = v_lds_base + (uint32_t)(tv % NS) * V_TILEB + 1024u * (uint32_t)wave_s;
+    const char* dk_base = dk_run;
+    const uint32_t dk_slot = k_lds_base + ((uint32_t)tk & (NS - 1)) * K_TILEB + 1024u * (uint32_t)wave_s;
+    const char* dv_base = dv_run;
+    if constexpr (kDmaIn) {
+      dk_run += tile_bytes;
+      dv_run += tile_bytes;
+    }
+    const uint32_t dv_slot = v_lds_base + ((uint32_t)tv & (NS - 1)) * V_TILEB + 1024u * (uint32_t)wave_s;
     auto dma_at = [&](auto ic) INL {
       constexpr int i = decltype(ic)::value, d = (i - 3) / 7;
       if constexpr (kDmaIn && i >= 3 && (i - 3) % 7 == 0 && d < 9) {
         if constexpr (d < 4) {
-          dma16_m0(dk_base, k_off[d], dk_slot + 1024u * NW * d);
+          dma16_m0_plus<1024u * NW * d>(dk_base, k_off[d], dk_slot);
         } else if constexpr (d < 8) {
           constexpr int u = d - 4;
-          dma16_m0(dv_base + (int64_t)(G::V_ROWS_PER_DMA * NW * u) * row_bytes, v_off, dv_slot + 1024u * NW * u);
+          dma16_m0_plus<1024u * NW * u>(dv_base + (int64_t)(G::V_ROWS_PER_DMA * NW * u) * row_bytes, v_off, dv_slot);
         } else {
           dma16_m0_lanes(dk_base, k16_off, dk_slot - 1024u * (uint32_t)wave_s + 1024u * 16, k16_lanes);
         }

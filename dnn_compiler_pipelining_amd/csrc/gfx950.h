@@ -69,6 +69,19 @@ __device__ __forceinline__ void dma16_m0(const void* base, uint32_t off, uint32_
       : "v"(off), "s"(base), "s"(lds_base)
       : "memory", "m0");
 }
+// dma16_m0 with the LDS address given as a wave-uniform base plus a
+// compile-time byte offset, added straight into M0 (one scalar instruction
+// per load instead of two).
+template <uint32_t kOff>
+__device__ __forceinline__ void dma16_m0_plus(const void* base, uint32_t off, uint32_t lds_base) {
+  asm volatile(
+      "s_add_u32 m0, %2, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(off), "s"(base), "s"(lds_base), "n"(kOff)
+      : "memory", "m0", "scc");
+}
 // dma16_m0 for the lanes in `lanes` only (EXEC is set for the one load and
 // restored): lane l of them still writes LDS byte lds_base + 16*l, so waves
 // that pass disjoint lane sets with the same lds_base fill one 1 KiB run
