@@ -772,19 +772,22 @@ __global__ __launch_bounds__(64 * W_NW, 1) void attn_wide_kernel(Params p) {
           *(LDS f16x4*)(ob + (32 * qb + n) * K_ROWB + 2 * (32 * db + 8 * r4 + 4 * hh)) = hv;
         }
     }
+    // O and LSE are written once and never read here again: non-temporal
+    // stores keep them from displacing the K/V tiles that the other work
+    // items of this KV group, running on the same XCD, still stream from L2.
     _Float16* const ob_g = p.o + (int64_t)b * p.q_bstride + (int64_t)h * 128 + 8 * (lane & 15);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       __builtin_amdgcn_sched_barrier(0);
       const int row = 4 * i + (lane >> 4);
       const f16x8 x = *(const LDS f16x8*)(ob + row * K_ROWB + 16 * (lane & 15));
-      if (qw + row < Sq) *reinterpret_cast<f16x8*>(ob_g + (int64_t)(qw + row) * p.q_sstride) = x;
+      if (qw + row < Sq) __builtin_nontemporal_store(x, reinterpret_cast<f16x8*>(ob_g + (int64_t)(qw + row) * p.q_sstride));
     }
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const int qrow = qw + 32 * qb + n;
       if (p.lse && hh == 0 && qrow < Sq)
-        p.lse[((int64_t)b * p.Hq + h) * Sq + qrow] = (m_run[qb] + log2f(l_run[qb])) * LN2;
+        __builtin_nontemporal_store((m_run[qb] + log2f(l_run[qb])) * LN2, &p.lse[((int64_t)b * p.Hq + h) * Sq + qrow]);
     }
   }
 }
