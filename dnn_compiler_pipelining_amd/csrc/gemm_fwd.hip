@@ -225,10 +225,10 @@ __global__ __launch_bounds__(64 * kNW, 1) void gemm_kernel(GemmParams p) {
   // ---- K loop, rotated by one substep across the barrier: iteration kt runs
   // substeps 0..2 of tile kt, waits for tile kt+1's loads and the barrier
   // that publishes them, then runs substep 3 of tile kt (its fragments are
-  // already in registers) beside the substep-0 reads of tile kt+1, and only
-  // then issues the loads of tile kt+2 into the slot tile kt has just left.
-  // The matrix core stays busy while the waves meet at the barrier and while
-  // the first reads of a tile are in flight.
+  // already in registers) beside the substep-0 reads of tile kt+1, and issues
+  // the loads of tile kt+2 into the slot tile kt has just left.  The matrix
+  // core stays busy while the waves meet at the barrier and while the first
+  // reads of a tile are in flight.
   const int nkt = p.nkt;
   const bool tail = (K & (GBK - 1)) != 0;
   stage(0);
@@ -252,10 +252,21 @@ __global__ __launch_bounds__(64 * kNW, 1) void gemm_kernel(GemmParams p) {
     dma_wait();
     if (tail && kt + 2 == nkt) zero_tail(kt + 1);
     lds_barrier();
+    // The slot tile kt leaves is free once every wave has passed the barrier
+    // (substep 3 of tile kt reads registers only).  B stored [N][K] issues the
+    // loads of tile kt+2 into it at once, which gives them a quarter tile more
+    // time to land (measured: +1% at 8192^3); B stored [K][N] issues them after
+    // substep 3, where the load instructions do not delay its first MFMAs
+    // (issued at once there: -2%).
+    if constexpr (kBL == 1) {
+      if (kt + 2 < nkt) stage(kt + 2);
+    }
     load_frags(slot ^ 1, std::integral_constant<int, 0>{});
     mfmas(std::integral_constant<int, 3>{});
     pin_interleaved();
-    if (kt + 2 < nkt) stage(kt + 2);
+    if constexpr (kBL == 0) {
+      if (kt + 2 < nkt) stage(kt + 2);
+    }
   }
   substeps_012(kt & 1);  // the last tile
   mfmas(std::integral_constant<int, 3>{});
