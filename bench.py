@@ -6,7 +6,8 @@
 A step is one forward pass (one kernel launch) over the whole workload: the
 LLaMA3-70B-shaped B=64 S=8192 Hq=64 Hkv=8 D=128 causal configuration by
 default, inputs seeded N(0,1) fp16 and resident in HBM before timing.  W
-untimed steps, then exactly K steps between two device synchronisations.
+untimed steps, then exactly K steps between two device synchronisations
+(defaults: W = 3, K = 20 for the bench workload; see below for short ones).
 Rank 0 prints one JSON line per workload:
 
   value      whole-job TFLOP/s = metric FLOPs (2*B*Hq*S^2*D) * K / wall time
@@ -40,10 +41,11 @@ fields, with metric FLOPs 2*M*N*K and the fp64 GEMM oracle as cpu_baseline.
 `--workload llama3-70b_decode_b64_s8192` times the split-KV decode path
 (attn_fwd_decode: split kernel + combine kernel per step) and reports HBM
 GB/s (K, V, Q, O and LSE once) against the 8 TB/s HBM roofline.
-`--all` prints one line per attention, GEMM and decode workload; there each workload gets at
-least about 0.25 s of warmup and 0.25 s of timed launches (more steps than --warmup / --steps
-for the short ones, reported in the line), so that its launches are timed at the clock a
-sustained run settles to rather than while the clock is still rising after input generation.
+`--all` prints one line per attention, GEMM and decode workload.  Without --steps / --warmup, and
+under --all, each workload gets at least about 0.25 s of warmup and 0.25 s of timed launches (20
+and 3 for the long ones, more launches for the short ones, reported in the line), so that its
+launches are timed at the clock a sustained run settles to rather than while the clock is still
+rising after input generation; --steps / --warmup given alone are used exactly.
 """
 from __future__ import annotations
 
@@ -104,6 +106,8 @@ def kernel_name(workload: str, schedule: str | None = None) -> str:
     if is_decode(workload):
         return KERNEL_NAME
     return WIDE_KERNEL_NAME if tuned_variant(workload, schedule)["schedule"] == "wide" else KERNEL_NAME
+
+
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -591,8 +595,10 @@ def summarize_counters(dirs, workload: str, schedule: str | None = None):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed launches (default: 20, or more for short workloads, about 0.25 s in all)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed launches before them (default: 3, or more for short workloads, about 0.25 s)")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--all", action="store_true", help="one line per workload (parity-test configurations too)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -629,11 +635,13 @@ def main():
              [w.name for w in inputs.DECODE_WORKLOADS]) if args.all else [args.workload]
 
     def counts(est_ms: float):
-        # --all: at least ~0.25 s of warmup and of timed launches per workload
-        if not args.all:
-            return args.steps, args.warmup
+        # A count given on the command line is used as given (--all: at least that many).  Otherwise, and
+        # under --all, each workload gets at least ~0.25 s of warmup and of timed launches, so that short
+        # launches are timed at the clock a sustained run settles to, not while it is still rising.
         n = min(5000, max(1, int(250.0 / max(est_ms, 1e-3)) + 1))  # launch-bound shapes: at most 5000
-        return max(args.steps, n), max(args.warmup, n)
+        steps = args.steps if args.steps is not None and not args.all else max(args.steps or 20, n)
+        warmup = args.warmup if args.warmup is not None and not args.all else max(args.warmup or 3, n)
+        return steps, warmup
 
     peak = mfma_peak()
     log("[bench] dense fp16 MFMA peak: %.1f TFLOP/s = %s (published %.0f)" %
