@@ -245,28 +245,64 @@ __global__ __launch_bounds__(64 * kNW, 1) void gemm_kernel(GemmParams p) {
       pin_interleaved();
     });
   };
-  int kt = 0;
-  for (; kt + 1 < nkt; ++kt) {
+  // Loads of a full K tile (every K position inside K): per-lane offsets
+  // that do not change from tile to tile (rows past M or N already clamped),
+  // running base addresses, and M0 = slot base + a compile-time offset.
+  // Issued one beside each MFMA of substep 3 rather than as one block of
+  // instructions, which would leave the matrix core without work while a
+  // wave issues them (with one wave per SIMD nothing else fills the gap).
+  uint32_t off_a[UPW], off_b[UPW];
+#pragma unroll
+  for (int u = 0; u < UPW; ++u) {
+    off_a[u] = (uint32_t)min(rk_row0 + 8 * kNW * u, M - 1 - m0) * (uint32_t)(2 * K) + 16u * (uint32_t)rk_chunk;
+    if constexpr (kBL == 1)
+      off_b[u] = (uint32_t)min(rk_row0 + 8 * kNW * u, N - 1 - n0) * (uint32_t)(2 * K) + 16u * (uint32_t)rk_chunk;
+    else
+      off_b[u] = (uint32_t)(kn_row0 + 2 * kNW * u) * (uint32_t)(2 * N) +
+                 16u * (uint32_t)min(kn_chunk, (N >> 3) - 1 - (n0 >> 3));
+  }
+  const int nfull = K / GBK;  // K tiles [0, nfull) lie wholly inside K
+  const char* a_run = (const char*)(p.a + (int64_t)m0 * K) + 2 * 2 * GBK;  // tile 2
+  const char* b_run = kBL == 1 ? (const char*)(p.b + (int64_t)n0 * K) + 2 * 2 * GBK
+                               : (const char*)(p.b + (int64_t)2 * GBK * N + n0);
+  const int64_t b_step = kBL == 1 ? 2 * GBK : (int64_t)2 * GBK * N;  // bytes from one K tile to the next
+  // Substep 3 of tile kt beside the substep-0 reads of tile kt+1 (slot
+  // slot ^ 1), with (kDmaIn) this wave's loads of tile kt+2 into `slot`.
+  auto substep3 = [&](int slot, auto dma_in) INL {
+    constexpr bool kDmaIn = decltype(dma_in)::value;
+    const uint32_t a_m0 = a_lds_base + (uint32_t)slot * G_TILEB + 1024u * (uint32_t)wave_s;
+    const uint32_t b_m0 = b_lds_base + (uint32_t)slot * G_TILEB + 1024u * (uint32_t)wave_s;
+    static_for<kSteps>([&](auto jc) INL {
+      constexpr int j = decltype(jc)::value, mf = j / NFR, nf = j % NFR;
+      acc[mf][nf] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[1][nf], af[1][mf], acc[mf][nf], 0, 0, 0);
+      if constexpr (j < NFR) bf[0][j] = frag_b(slot ^ 1, 0, j);
+      else if constexpr (j < NFR + 4) af[0][j - NFR] = frag_a(slot ^ 1, 0, j - NFR);
+      if constexpr (kDmaIn && j < UPW) dma16_m0_plus<1024u * kNW * j>(a_run, off_a[j], a_m0);
+      if constexpr (kDmaIn && j >= UPW && j < 2 * UPW) dma16_m0_plus<1024u * kNW * (j - UPW)>(b_run, off_b[j - UPW], b_m0);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    if constexpr (kDmaIn) {
+      a_run += 2 * GBK;
+      b_run += b_step;
+    }
+  };
+  static_assert(2 * UPW <= kSteps && NFR + 4 <= kSteps, "one load and one fragment read beside each MFMA at most");
+  // iteration kt: substeps 0..2, the barrier that publishes tile kt+1, substep 3
+  auto iteration = [&](int kt, auto dma_in) INL {
     const int slot = kt & 1;
     substeps_012(slot);
     dma_wait();
     if (tail && kt + 2 == nkt) zero_tail(kt + 1);
     lds_barrier();
-    // The slot tile kt leaves is free once every wave has passed the barrier
-    // (substep 3 of tile kt reads registers only).  B stored [N][K] issues the
-    // loads of tile kt+2 into it at once, which gives them a quarter tile more
-    // time to land (measured: +1% at 8192^3); B stored [K][N] issues them after
-    // substep 3, where the load instructions do not delay its first MFMAs
-    // (issued at once there: -2%).
-    if constexpr (kBL == 1) {
-      if (kt + 2 < nkt) stage(kt + 2);
-    }
-    load_frags(slot ^ 1, std::integral_constant<int, 0>{});
-    mfmas(std::integral_constant<int, 3>{});
-    pin_interleaved();
-    if constexpr (kBL == 0) {
-      if (kt + 2 < nkt) stage(kt + 2);
-    }
+    substep3(slot, dma_in);
+  };
+  int kt = 0;
+  // tile kt+2 full: its loads beside the MFMAs of substep 3
+  for (; kt + 2 < nfull; ++kt) iteration(kt, std::true_type{});
+  for (; kt + 1 < nkt; ++kt) {
+    // the last iterations: tile kt+2 is the tail tile, or there is none
+    iteration(kt, std::false_type{});
+    if (kt + 2 < nkt) stage(kt + 2);
   }
   substeps_012(kt & 1);  // the last tile
   mfmas(std::integral_constant<int, 3>{});

@@ -71,7 +71,8 @@ __device__ __forceinline__ void dma16_m0(const void* base, uint32_t off, uint32_
 }
 // dma16_m0 with the LDS address given as a wave-uniform base plus a
 // compile-time byte offset, added straight into M0 (one scalar instruction
-// per load instead of two).
+// per load instead of two).  The base is read from the first lane, so that
+// it is a scalar operand even where the compiler cannot prove it uniform.
 template <uint32_t kOff>
 __device__ __forceinline__ void dma16_m0_plus(const void* base, uint32_t off, uint32_t lds_base) {
   asm volatile(
@@ -79,7 +80,7 @@ __device__ __forceinline__ void dma16_m0_plus(const void* base, uint32_t off, ui
       "s_nop 0\n\t"
       "global_load_lds_dwordx4 %0, %1"
       :
-      : "v"(off), "s"(base), "s"(lds_base), "n"(kOff)
+      : "v"(off), "s"(base), "s"(__builtin_amdgcn_readfirstlane(lds_base)), "n"(kOff)
       : "memory", "m0", "scc");
 }
 // dma16_m0 for the lanes in `lanes` only (EXEC is set for the one load and
