@@ -67,9 +67,11 @@ def check_normal(c_gpu, ref, absprod, K, tag):
     assert mean_ratio <= 0.35, tag
 
 
-# (M, N, K): one element, exact tiles, ragged M/N/K tails over several tiles, K of one 8-wide chunk
+# (M, N, K): one element, exact tiles, ragged M/N/K tails over several tiles, K of one 8-wide chunk; K = 192
+# and 128: three and two whole K tiles, where the loads of tile 2 are the only ones issued beside the MFMAs
+# (full-tile path) or none are
 SHAPES = [(1, 8, 8), (7, 16, 8), (256, 256, 64), (300, 264, 136), (513, 520, 520), (1000, 1024, 1000),
-          (64, 8, 4096), (130, 776, 72), (255, 257 - 1, 200)]
+          (64, 8, 4096), (130, 776, 72), (255, 257 - 1, 200), (333, 200, 192), (100, 96, 128)]
 
 
 @pytest.mark.parametrize("layout", [KN, NK], ids=["kn", "nk"])
