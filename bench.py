@@ -19,6 +19,10 @@ Rank 0 prints one JSON line per workload:
   peak_derived  the same peak from the runtime's compute-unit count and peak
              clock (CUs x clock x 4096 FLOP/clk), with the derivation;
              pct_of_mfma_peak is taken against it
+  mfma_ceiling  context: the rate this box's matrix cores sustain on random
+             operands with nothing else to do (attn_mfma_ceiling, measured after
+             the timed region; not with --no-per-config), and the kernel's
+             rate as a fraction of it
   variant    the kernel variant that ran (schedule, ring, xcd, lpt)
   per_config (default workload only) the other four attention configurations,
              each timed in the same run under the --all warmup rule below:
@@ -169,6 +173,17 @@ def mfma_peak() -> dict:
     tf = cu * khz * 1e3 * MFMA_FP16_FLOP_PER_CU_CLK / 1e12
     return {"tflops": round(tf, 1), "derivation": "%d CUs x %.3f GHz x %d FLOP/clk/CU (dense fp16 MFMA)" %
             (cu, khz / 1e6, MFMA_FP16_FLOP_PER_CU_CLK), "published_tflops": PEAK_TFLOPS}
+
+
+def mfma_ceiling(achieved: float) -> dict:
+    """The box's sustained MFMA-only rate on random operands, measured after the timed region (context for
+    `achieved`: under the power limit it varies from box to box and sits well below the published peak)."""
+    from dnn_compiler_pipelining_amd import binding
+
+    tf = binding.attn_mfma_ceiling(200000)
+    return {"tflops": round(tf, 1), "frac": round(achieved / tf, 4),
+            "method": "attn_mfma_ceiling: back-to-back v_mfma_f32_32x32x16_f16 on random fp16 operands, one wave per "
+                      "SIMD on every CU, timed with HIP events in this run after the timed region"}
 
 
 def cpu_model() -> str | None:
@@ -716,6 +731,8 @@ def main():
         if not args.all and not args.no_per_config and not gemm and name == DEFAULT_WORKLOAD:
             # the other attention configurations, each timed under the --all warmup rule, in the same run
             line["per_config"] = per_config(w.name, args.schedule, peak)
+        if not args.all and not args.no_per_config:
+            line["mfma_ceiling"] = mfma_ceiling(achieved)
         if not args.no_cpu_baseline and not args.all:
             line["cpu_baseline"] = (cpu_baseline_gemm if gemm else cpu_baseline)(w, args.cpu_seconds)
             line["cpu_baseline"]["cpu_model"] = cpu_model()

@@ -33,7 +33,8 @@ ATTN_STATIC_WORKSPACE_BYTES = 64 << 20  # the library's own split-KV workspace p
 
 EXPORTS = ("attn_fwd", "attn_fwd_stream", "attn_fwd_ex", "attn_fwd_variant", "attn_fwd_decode",
            "attn_fwd_decode_split", "attn_fwd_decode_static", "attn_decode_workspace_size", "attn_decode_workspace_size_split",
-           "attn_status_string", "attn_version", "attn_tuned_variant", "attn_device_clock", "gemm_f16", "gemm_f16_waves")
+           "attn_status_string", "attn_version", "attn_tuned_variant", "attn_device_clock", "attn_mfma_ceiling", "gemm_f16",
+           "gemm_f16_waves")
 
 # Tile schedules (ATTN_SCHEDULE_* in include/attn.h), by name
 SCHEDULES = {"serial": 0, "overlap": 1, "pingpong": 2, "serial4": 3, "wide": 4}
@@ -89,6 +90,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
             lib.attn_tuned_variant.argtypes = [i, i, i, i, i, i, ip, ip, ip, ip, ip]
             lib.attn_device_clock.restype = i
             lib.attn_device_clock.argtypes = [i, ip, ip]
+            lib.attn_mfma_ceiling.restype = i
+            lib.attn_mfma_ceiling.argtypes = [i, vp, ctypes.POINTER(ctypes.c_double)]
             lib.attn_status_string.restype = ctypes.c_char_p
             lib.attn_status_string.argtypes = [i]
             lib.attn_version.restype = i
@@ -166,6 +169,17 @@ def attn_device_clock(device: int = 0) -> tuple[int, int]:
     if st != ATTN_OK:
         raise AttnError(st)
     return cu.value, khz.value
+
+
+def attn_mfma_ceiling(iters: int = 200000, stream=None) -> float:
+    """C attn_mfma_ceiling: the sustained dense fp16 MFMA rate of the current device on random operands
+    (TFLOP/s), a measurement aid.  `stream` as for attn_fwd_stream; the call waits for its timed launch."""
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else (stream or 0)
+    out = ctypes.c_double(0.0)
+    st = load().attn_mfma_ceiling(int(iters), handle, ctypes.byref(out))
+    if st != ATTN_OK:
+        raise AttnError(st)
+    return out.value
 
 
 def gemm_f16_waves(a, b, c, M: int, N: int, K: int, b_layout: int, waves: int, stream) -> int:

@@ -17,7 +17,9 @@ WIDE_SOURCES = [os.path.join(CSRC, "attn_wide_%s.hip" % p) for p in ("even", "fr
 ATTN_SOURCES = [os.path.join(CSRC, "attn_fwd.hip"), *WIDE_SOURCES, os.path.join(CSRC, "attn_api.cpp"),
                 os.path.join(CSRC, "attn_static_ws.hip")]
 GEMM_SOURCES = [os.path.join(CSRC, "gemm_fwd.hip"), os.path.join(CSRC, "gemm_api.cpp")]
-SOURCES = ATTN_SOURCES + GEMM_SOURCES
+# measurement aid (attn_mfma_ceiling), outside the attention and GEMM paths
+PROBE_SOURCES = [os.path.join(CSRC, "mfma_ceiling.hip")]
+SOURCES = ATTN_SOURCES + GEMM_SOURCES + PROBE_SOURCES
 
 # Packed fp32 VALU forms are switched off for all device code.
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

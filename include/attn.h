@@ -172,6 +172,17 @@ size_t attn_decode_workspace_size_split(int B, int Sq, int Sk, int Hq, int Hkv, 
 int attn_fwd_decode_static(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Sq, int Sk,
                            int Hq, int Hkv, int D, int causal, float scale, void* stream);
 
+/* Measurement aid, not part of the attention path: the sustained dense fp16 MFMA rate of the current
+ * device on random operands, in TFLOP/s, written to *tflops.  One workgroup of four waves per compute unit
+ * (one wave per SIMD) issues `iters` x 16 back-to-back v_mfma_f32_32x32x16_f16 per wave on four independent
+ * accumulators; one untimed launch, then one launch timed with HIP events on `stream` (NULL: the null
+ * stream), whose completion the call waits for.  Under the chip's power limit this rate depends on the data
+ * and on the box, and sits well below the published peak; kernel rates read against it say how much of the
+ * box's matrix-core rate a kernel gets.  1 <= iters <= 10^7 (ATTN_ERR_SHAPE otherwise, nothing launched);
+ * ATTN_ERR_NULL for a NULL tflops; ATTN_ERR_HIP if a HIP call fails.  Allocates no device memory (events
+ * only); about 0.07 s per launch at iters = 200000 on MI355X. */
+int attn_mfma_ceiling(int iters, void* stream, double* tflops);
+
 /* Static, NUL-terminated description of a status code ("unknown status" for others). */
 const char* attn_status_string(int status);
 

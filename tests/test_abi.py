@@ -261,3 +261,13 @@ def test_variant_placements_outside_the_wide_schedule_are_rejected(lib):
     assert var(L.SCHEDULES["wide"], 3) == L.ATTN_ERR_UNSUPPORTED
     assert var(L.SCHEDULES["wide"], L.PLACES["front"], ring=3) == L.ATTN_ERR_UNSUPPORTED
     assert var(L.SCHEDULES["wide"], L.PLACES["early"], D=64) == L.ATTN_ERR_UNSUPPORTED
+
+
+def test_mfma_ceiling_validates_before_any_hip_call(lib):
+    import ctypes
+    out = ctypes.c_double(-1.0)
+    assert lib.attn_mfma_ceiling(0, None, ctypes.byref(out)) == L.ATTN_ERR_SHAPE
+    assert lib.attn_mfma_ceiling(-5, None, ctypes.byref(out)) == L.ATTN_ERR_SHAPE
+    assert lib.attn_mfma_ceiling(10000001, None, ctypes.byref(out)) == L.ATTN_ERR_SHAPE
+    assert lib.attn_mfma_ceiling(100, None, None) == L.ATTN_ERR_NULL
+    assert out.value == -1.0
