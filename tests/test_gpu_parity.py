@@ -221,13 +221,16 @@ def test_all_variants_bitwise_identical(B, S, Hq, Hkv, causal):
 
 
 # Every compiled D = 128 kernel instance (schedule x ring depth x softmax placement) on its own against the
-# oracle, causal with a ragged tail and non-causal with g = 3, so a fault confined to one instance is named.
+# oracle, causal with ragged tails and non-causal, so a fault confined to one instance is named.
 INSTANCES = [(sched, ring, place) for sched in U.SCHEDULES_D128 for ring in (2, 4)
              for place in (binding.PLACES if sched == "wide" else ("even",))]
 
 
 @pytest.mark.parametrize("sched,ring,place", INSTANCES, ids=lambda x: str(x))
-@pytest.mark.parametrize("B,S,Hq,Hkv,causal", [(1, 650, 8, 2, 1), (2, 201, 12, 4, 0)], ids=str)
+# GQA ratios 4, 3, 2 and 8: the 64-row kernel's workgroups then take 4 heads, 1 head x 256 rows, 2 heads x 128
+# rows, and 4 of 8 heads (two workgroups per KV head)
+@pytest.mark.parametrize("B,S,Hq,Hkv,causal", [(1, 650, 8, 2, 1), (2, 201, 12, 4, 0), (1, 300, 4, 2, 1),
+                                               (1, 333, 16, 2, 1)], ids=str)
 def test_every_instance_against_oracle(B, S, Hq, Hkv, causal, sched, ring, place):
     tag = "instance %s ring%d %s B%d S%d Hq%d Hkv%d causal%d" % (sched, ring, place, B, S, Hq, Hkv, causal)
     U.say(tag)
