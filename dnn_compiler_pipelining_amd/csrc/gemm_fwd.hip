@@ -14,8 +14,9 @@
 // waves (two per SIMD) or 4 (one per SIMD, kNW = 4).  Wave (wm, wn) =
 // (w % 2, w / 2) owns rows 128 wm .. +128 of the tile and columns
 // 64 wn .. +64 (8 waves: 4 x 2 accumulators of 32 x 32) or 128 wn .. +128
-// (4 waves: 4 x 4 accumulators, 256 registers that live in AGPRs; half the
-// LDS reads per MFMA).  The MFMA computes
+// (4 waves: 4 x 4 accumulators, 256 registers that live in AGPRs; a third
+// fewer LDS reads per MFMA, 0.5 against 0.75 with B stored [N][K]).  The MFMA
+// computes
 // the transposed block, D[n][m] = sum_k B^T[n][k] A^T[k][m], so that each lane
 // holds one row m of C and runs of 4 consecutive columns n: the epilogue
 // writes 8-byte runs.
