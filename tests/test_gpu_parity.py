@@ -85,6 +85,22 @@ def test_workload_full_size_sampled(idx):
     torch.cuda.empty_cache()
 
 
+def test_noncausal_full_length_sampled():
+    """Non-causal attention at the bench workload's head shape and sequence length (B = 2): every row sees
+    all 128 key tiles, the path the causal workloads take only for their last rows.  Sampled rows of every
+    fourth head of both batch entries, and one whole (batch, head) slice."""
+    w = inputs.Workload("noncausal_b2_s8192", 2, 8192, 64, 8, 128, False, 31)
+    U.say("non-causal B2 S8192 Hq64 Hkv8 (sampled rows and one slice)")
+    q, k, v = inputs.make_inputs(w, "cuda")
+    o, lse = U.run(q, k, v, w.causal, w.scale)
+    U.whole_output_sane(o, lse)
+    U.sampled_parity(w, q, k, v, o, lse, [0, 1], heads=list(range(0, w.Hq, 4)) + [w.Hq - 1], n_random=32,
+                     tag=w.name)
+    U.slice_parity(w, q, k, v, o, lse, 1, 37, tag="%s slice b1 h37" % w.name)
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
+
+
 def test_first_causal_row_is_v0_bitwise():
     q, k, v = cpu_qkv(2, 333, 16, 4, seed=77)
     o, _ = U.run(q.cuda(), k.cuda(), v.cuda(), True, SC)
