@@ -35,6 +35,9 @@ EDGE = [
     (2, 200, 16, 4, 1, SC), (1, 257, 2, 1, 1, SC), (1, 384, 32, 8, 1, SC), (1, 1000, 8, 2, 1, SC),
     (1, 1000, 8, 2, 0, SC), (1, 300, 8, 2, 1, -SC), (1, 300, 8, 2, 1, 0.0), (1, 300, 8, 2, 0, 0.25),
     (3, 77, 12, 3, 1, SC),
+    # scale 1 and 0.7: scores of standard deviation 11 and 8, sharply peaked rows whose running max rises
+    # often, so the sum-checked rescale takes its rare path many times per row
+    (1, 2048, 8, 2, 1, 1.0), (1, 1500, 16, 2, 0, 0.7),
 ]
 
 
