@@ -605,6 +605,17 @@ def summarize_counters(dirs, workload: str, schedule: str | None = None):
     print("\n".join(lines))
 
 
+def launch_counts(est_ms: float, steps: int | None, warmup: int | None, all_workloads: bool) -> tuple[int, int]:
+    """(timed launches, warmup launches) for a workload whose launch takes about `est_ms`.  A count given on
+    the command line is used as given (under --all: at least that many).  Otherwise, and under --all, each
+    workload gets at least ~0.25 s of warmup and of timed launches (20 and 3 at least), so that short launches
+    are timed at the clock a sustained run settles to, not while it is still rising."""
+    n = min(5000, max(1, int(250.0 / max(est_ms, 1e-3)) + 1))  # launch-bound shapes: at most 5000
+    k = steps if steps is not None and not all_workloads else max(steps or 20, n)
+    w = warmup if warmup is not None and not all_workloads else max(warmup or 3, n)
+    return k, w
+
+
 # ------------------------------------------------------------------ main
 
 def main():
@@ -650,13 +661,7 @@ def main():
              [w.name for w in inputs.DECODE_WORKLOADS]) if args.all else [args.workload]
 
     def counts(est_ms: float):
-        # A count given on the command line is used as given (--all: at least that many).  Otherwise, and
-        # under --all, each workload gets at least ~0.25 s of warmup and of timed launches, so that short
-        # launches are timed at the clock a sustained run settles to, not while it is still rising.
-        n = min(5000, max(1, int(250.0 / max(est_ms, 1e-3)) + 1))  # launch-bound shapes: at most 5000
-        steps = args.steps if args.steps is not None and not args.all else max(args.steps or 20, n)
-        warmup = args.warmup if args.warmup is not None and not args.all else max(args.warmup or 3, n)
-        return steps, warmup
+        return launch_counts(est_ms, args.steps, args.warmup, args.all)
 
     peak = mfma_peak()
     log("[bench] dense fp16 MFMA peak: %.1f TFLOP/s = %s (published %.0f)" %
