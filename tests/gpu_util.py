@@ -126,6 +126,27 @@ def slice_parity(w: inputs.Workload, q, k, v, o, lse, b: int, h: int, tag=""):
     return st
 
 
+def batch_entries_parity(w: inputs.Workload, q, k, v, o, lse, batches, tag=""):
+    """Every output (all rows, heads and d) of the given batch entries of a full-size run against the
+    oracle, the bar applied to all of them together.  The oracle regenerates each batch entry on the CPU
+    from its seed and checks that it is what the GPU read."""
+    allst = []
+    for b in batches:
+        qb, kb, vb = inputs.make_batch_cpu(w, b)
+        assert torch.equal(qb, q[b].cpu()) and torch.equal(kb, k[b].cpu()) and torch.equal(vb, v[b].cpu())
+        O, L = oracle_mod.attn_full(qb.numpy()[None], kb.numpy()[None], vb.numpy()[None], w.causal, w.scale)
+        allst.append(stats(o[b:b + 1].cpu().numpy(), lse[b:b + 1].cpu().numpy(), O, L))
+        say("  batch entry %d: max |dO| %.3e, max |dLSE| %.3e" % (b, allst[-1]["max_o"], allst[-1]["max_lse"]))
+    n = sum(s["n"] for s in allst)
+    worst = max(range(len(allst)), key=lambda x: allst[x]["max_o"])
+    st = dict(finite=all(s["finite"] for s in allst), max_o=max(s["max_o"] for s in allst),
+              mean_o=sum(s["mean_o"] * s["n"] for s in allst) / n, max_lse=max(s["max_lse"] for s in allst), n=n,
+              p9999_o=max(s["p9999_o"] for s in allst),  # the largest per-batch 99.99th percentile
+              argmax_o=(batches[worst],) + allst[worst]["argmax_o"][1:])  # (b, row, head, d)
+    check(st, tag)
+    return st
+
+
 def whole_output_sane(o, lse):
     """Properties that hold at any size: everything finite, |O| bounded by max |V|."""
     assert bool(torch.isfinite(o).all().item()), "non-finite O"

@@ -88,6 +88,35 @@ def test_workload_full_size_sampled(idx):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("half", [0, 1])
+def test_b64_s2048_whole_output(half):
+    """llama3-8b_b64_s2048 at full size, in the launch the bench times: every one of its 537M outputs (all
+    64 batch entries, every row, head and d) against the oracle, half of the batch entries per case."""
+    w = inputs.WORKLOADS[3]
+    U.say("workload %s (full size, whole output of batch entries %d..%d)" % (w.name, half * 32, half * 32 + 31))
+    q, k, v = inputs.make_inputs(w, "cuda")
+    o, lse = U.run(q, k, v, w.causal, w.scale)
+    batches = list(range(half * w.B // 2, (half + 1) * w.B // 2))
+    st = U.batch_entries_parity(w, q, k, v, o, lse, batches, tag="%s batch entries %d..%d" %
+                                (w.name, batches[0], batches[-1]))
+    assert st["n"] == w.B // 2 * w.S * w.Hq * w.D
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("b", [0, 21, 42, 63])
+def test_b64_s8192_whole_batch_entry(b):
+    """llama3-70b_b64_s8192 at full size, in the launch the bench times: every output of one batch entry
+    (67M outputs) against the oracle; the four cases take the first, the last and two between."""
+    w = inputs.WORKLOADS[4]
+    U.say("workload %s (full size, whole batch entry %d)" % (w.name, b))
+    q, k, v = inputs.make_inputs(w, "cuda")
+    o, lse = U.run(q, k, v, w.causal, w.scale)
+    U.batch_entries_parity(w, q, k, v, o, lse, [b], tag="%s batch entry %d" % (w.name, b))
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
+
+
 def test_noncausal_full_length_sampled():
     """Non-causal attention at the bench workload's head shape and sequence length (B = 2): every row sees
     all 128 key tiles, the path the causal workloads take only for their last rows.  Sampled rows of every
