@@ -12,7 +12,7 @@
 
 namespace {
 
-constexpr int kVersion = 1 * 10000 + 3 * 100 + 0;
+constexpr int kVersion = 2 * 10000 + 0 * 100 + 0;
 constexpr int kMaxSeq = 1 << 30;  // sequence lengths up to 2^30 keep all tile arithmetic in int
 
 // Fields of a requested variant: -1 takes the tuned value (variant.h) for the
@@ -20,16 +20,18 @@ constexpr int kMaxSeq = 1 << 30;  // sequence lengths up to 2^30 keep all tile a
 // state: attn_fwd_variant passes a request explicitly (the schedule search
 // and the tests use it), every other entry point asks for the tuned variant.
 struct Request {
-  int schedule, ring, xcd, lpt, place;
+  int schedule, ring, xcd, lpt, place, bn;
 };
-constexpr Request kTunedRequest = {-1, -1, -1, -1, -1};
+constexpr Request kTunedRequest = {-1, -1, -1, -1, -1, -1};
 
 // The variant a call runs, or false if the request names a value that does
 // not exist or a schedule the head dimension does not run.  D = 128 runs
 // every schedule; D = 64 the serial ones (SERIAL4 unless SERIAL is asked for:
 // its one-head workgroups, 142 VGPRs and 34 KiB of LDS, fit three to a CU,
 // where SERIAL's eight-wave workgroups fit one; measured on MI355X at B=16
-// S=8192 Hq=32 Hkv=8: 878 against 822 TFLOP/s); D = 256 SERIAL4 only.
+// S=8192 Hq=32 Hkv=8: 878 against 822 TFLOP/s); D = 256 SERIAL4 only.  Tiles
+// of 32 or 128 keys: SERIAL and SERIAL4 at D = 128 (a tuned tile size other
+// than 64 is dropped when the schedule or D does not have it).
 bool choose_variant(const Request& r, int B, int Sq, int Sk, int Hq, int Hkv, int D, libattn::Variant& v) {
   v = libattn::tuned_variant(B, Sq, Sk, Hq, Hkv);
   if (D == 64) v.schedule = libattn::SCHEDULE_SERIAL4;
@@ -40,7 +42,11 @@ bool choose_variant(const Request& r, int B, int Sq, int Sk, int Hq, int Hkv, in
   if (r.lpt >= 0) v.lpt = r.lpt;
   if (v.schedule != libattn::SCHEDULE_WIDE) v.place = libattn::PLACE_EVEN;  // the only placement they have
   if (r.place >= 0) v.place = r.place;
+  if (D != 128 || (v.schedule != libattn::SCHEDULE_SERIAL && v.schedule != libattn::SCHEDULE_SERIAL4))
+    v.bn = libattn::BN_STD;
+  if (r.bn >= 0) v.bn = r.bn;
   if (!libattn::variant_valid(v)) return false;
+  if (v.bn != libattn::BN_STD && D != 128) return false;
   if (D == 64) return v.schedule == libattn::SCHEDULE_SERIAL || v.schedule == libattn::SCHEDULE_SERIAL4;
   if (D == 256) return v.schedule == libattn::SCHEDULE_SERIAL4;
   return true;
@@ -99,6 +105,7 @@ libattn::Params base_params(const void* q, const void* k, const void* v, void* o
   p.neg = scale < 0.f ? 1 : 0;
   p.cs = std::fabs(scale) * 1.44269504088896340736f;
   p.hd = D;
+  p.bn = libattn::BN_STD;
   return p;
 }
 
@@ -144,6 +151,7 @@ int forward(const void* q, const void* k, const void* v, void* o, float* lse, in
   p.xcd = var.xcd;
   p.lpt = var.lpt;
   p.place = var.place;
+  p.bn = var.bn;
   hipError_t e;
   if (p.schedule == libattn::SCHEDULE_WIDE) {
     // four heads of a KV group per workgroup at 64 query rows, or two at 128,
@@ -175,9 +183,9 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
 
 int attn_fwd_variant(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Sq, int Sk, int Hq,
                      int Hkv, int D, int causal, float scale, int schedule, int ring, int xcd, int lpt, int place,
-                     void* stream) {
-  return forward(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, D, causal, scale, Request{schedule, ring, xcd, lpt, place},
-                 stream);
+                     int bn, void* stream) {
+  return forward(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, D, causal, scale,
+                 Request{schedule, ring, xcd, lpt, place, bn}, stream);
 }
 
 int attn_fwd_stream(const void* q, const void* k, const void* v, void* o, float* lse, int B, int S, int Hq, int Hkv,
@@ -191,8 +199,8 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
 }
 
 int attn_tuned_variant(int B, int Sq, int Sk, int Hq, int Hkv, int D, int* schedule, int* ring, int* xcd, int* lpt,
-                       int* place) {
-  if (!schedule || !ring || !xcd || !lpt || !place) return ATTN_ERR_NULL;
+                       int* place, int* bn) {
+  if (!schedule || !ring || !xcd || !lpt || !place || !bn) return ATTN_ERR_NULL;
   if (B < 1 || Sq < 1 || Sk < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || Sq > kMaxSeq || Sk > kMaxSeq)
     return ATTN_ERR_SHAPE;
   if (D != 64 && D != 128 && D != 256) return ATTN_ERR_UNSUPPORTED;
@@ -203,6 +211,7 @@ int attn_tuned_variant(int B, int Sq, int Sk, int Hq, int Hkv, int D, int* sched
   *xcd = var.xcd;
   *lpt = var.lpt;
   *place = var.place;
+  *bn = var.bn;
   return ATTN_OK;
 }
 

@@ -43,28 +43,35 @@
 namespace libattn {
 
 constexpr int BM = 128;          // query rows per wave group
+static_assert(BN == BN_STD, "the kernels' default tile is the variant table's");
 // Waves per workgroup: 8 (two wave groups on two heads of a KV group), or 4
 // (one head) for the SERIAL4 schedule.
 __host__ __device__ constexpr int waves_of(int sched) { return sched == SCHEDULE_SERIAL4 ? 4 : 8; }
 // K tiles rotate through three slots, V tiles through two: K_t stays in LDS
 // for the whole iteration after its QK^T, so a softmax that has to be redone
-// can recompute S^T from it.  SERIAL4 keeps two K slots (the serial loop
-// reads K_j while K_{j+1} arrives) so that two of its workgroups fit a CU.
-__host__ __device__ constexpr int k_slots_of(int sched) { return sched == SCHEDULE_SERIAL4 ? 2 : 3; }
+// can recompute S^T from it.  The serial loop reads K_j while K_{j+1} arrives,
+// so two K slots serve it: SERIAL4 keeps two so that two of its workgroups fit
+// a CU, and so does SERIAL with 128-key tiles (three would take 166 KiB).
+__host__ __device__ constexpr int k_slots_of(int sched, int bn = BN) {
+  return sched == SCHEDULE_SERIAL4 || bn == 128 ? 2 : 3;
+}
 constexpr int V_SLOTS = 2;
-static_assert(k_slots_of(SCHEDULE_SERIAL) * Geo<128>::K_TILEB + V_SLOTS * Geo<128>::V_TILEB <= 160 * 1024,
-              "the K and V rings fit the 160 KiB LDS");
-static_assert(2 * (k_slots_of(SCHEDULE_SERIAL4) * Geo<128>::K_TILEB + V_SLOTS * Geo<128>::V_TILEB) <= 160 * 1024,
-              "two SERIAL4 workgroups fit the 160 KiB LDS");
+// Workgroups per CU: SERIAL4 asks for two (one wave per SIMD each) while its
+// rings fit half the LDS, i.e. for head dimensions up to 128 and tiles of up
+// to 64 keys; every other instance for one.
+__host__ __device__ constexpr int wgs_per_cu(int sched, int hd, int bn) {
+  return sched == SCHEDULE_SERIAL4 && hd <= 128 && bn <= 64 ? 2 : 1;
+}
 
-// Steps of an mma block, for NKK = HD/16 k steps of QK^T and NDB = HD/32
-// blocks of O^T.  A QK step (kk, x = sb) adds K[32sb.., 16kk..] x
+// Steps of an mma block, for NKK = HD/16 k steps of QK^T, NDB = HD/32
+// blocks of O^T and NSB = BN/32 blocks of S^T (32 keys each; P^T has 2 NSB
+// 16-key steps).  A QK step (kk, x = sb) adds K[32sb.., 16kk..] x
 // Q^T[16kk.., :] into S^T block sb; a PV step (kk, x = db) adds
 // V^T[32db.., 16kk..] x P^T[16kk.., :] into O^T block db.
 //   mode 0: PV and QK steps alternate, so consecutive MFMAs of one
 //           accumulator are >= 4 steps apart: per group g the order is
 //           PV(g,0) QK(2g,0) PV(g,1) QK(2g,1) PV(g,2) QK(2g+1,0) PV(g,3)
-//           QK(2g+1,1)  (HD 128 only)
+//           QK(2g+1,1)  (HD 128, NSB 2 only)
 //   mode 1: PV only, k-major over the O^T blocks
 //   mode 2: QK only, S^T block 0 first (so it is complete half-way)
 //   mode 3: the QK steps of mode 2, then the PV steps of mode 1
@@ -74,17 +81,20 @@ struct Step {
   bool pv;
   int kk, x;
 };
-__host__ __device__ constexpr Step step_of(int mode, int i, int nkk, int ndb) {
+__host__ __device__ constexpr Step step_of(int mode, int i, int nkk, int ndb, int nsb = 2) {
   return mode == 1   ? Step{true, i / ndb, i % ndb}
          : mode == 2 ? Step{false, i % nkk, i / nkk}
-         : mode == 3 ? (i < 2 * nkk ? Step{false, i % nkk, i / nkk} : Step{true, (i - 2 * nkk) / ndb, (i - 2 * nkk) % ndb})
+         : mode == 3 ? (i < nsb * nkk ? Step{false, i % nkk, i / nkk}
+                                      : Step{true, (i - nsb * nkk) / ndb, (i - nsb * nkk) % ndb})
          : ((i & 7) & 1) == 0 ? Step{true, i >> 3, (i & 7) >> 1}
                               : Step{false, 2 * (i >> 3) + ((i & 7) >> 2), ((i & 7) >> 1) & 1};
 }
-constexpr int steps_of(int mode, int nkk, int ndb) {
-  return mode == 1 ? 4 * ndb : mode == 2 ? 2 * nkk : 2 * nkk + 4 * ndb;
+constexpr int steps_of(int mode, int nkk, int ndb, int nsb = 2) {
+  return mode == 1 ? 2 * nsb * ndb : mode == 2 ? nsb * nkk : nsb * nkk + 2 * nsb * ndb;
 }
-constexpr int reads_of(int mode, int i, int nkk, int ndb) { return step_of(mode, i, nkk, ndb).pv ? 2 : 1; }
+constexpr int reads_of(int mode, int i, int nkk, int ndb, int nsb = 2) {
+  return step_of(mode, i, nkk, ndb, nsb).pv ? 2 : 1;
+}
 
 // kSched: tile schedule; kRing: depth of the fragment prefetch ring of the mma
 // steps (how many steps ahead the LDS reads run); kHD: head dimension.  The
@@ -99,22 +109,35 @@ constexpr int reads_of(int mode, int i, int nkk, int ndb) { return step_of(mode,
 // query head c*g + r / Sq, query row r % Sq, so the g heads that share K/V
 // read each K/V tile once.  It writes the split's O (normalised, fp32) and
 // LSE to the workspace; attn_combine_kernel merges the splits.
-template <int kSched, int kRing, int kHD, bool kSplit = false>
-__global__ __launch_bounds__(64 * waves_of(kSched), waves_of(kSched) == 4 && kHD <= 128 ? 2 : 1)
+//
+// kBN: keys per K/V tile.  64 for every schedule; the serial schedules at HD
+// 128 also run 32 and 128 (a smaller or larger unit of the load / mma /
+// softmax pipeline: with 128 the per-tile fixed costs -- wait, barrier, sum
+// check -- are spread over twice the keys, with 32 the causal diagonal wastes
+// less).  Per tile the softmax runs the same parts over more or fewer scores;
+// a row's results differ from BN 64's only by rounding order.
+template <int kSched, int kRing, int kHD, bool kSplit = false, int kBN = BN>
+__global__ __launch_bounds__(64 * waves_of(kSched), wgs_per_cu(kSched, kHD, kBN))
 void attn_fwd_kernel(Params p) {
-  using G = Geo<kHD>;
+  using G = Geo<kHD, kBN>;
   static_assert(kHD == 128 || kSched == SCHEDULE_SERIAL || kSched == SCHEDULE_SERIAL4,
                 "HD 64 runs the serial schedules");
   static_assert(kHD <= 128 || kSched == SCHEDULE_SERIAL4, "HD 256 runs the SERIAL4 schedule");
   static_assert(!kSplit || kSched == SCHEDULE_SERIAL4, "split-KV mode runs the SERIAL4 schedule");
+  static_assert(kBN == BN || ((kSched == SCHEDULE_SERIAL || kSched == SCHEDULE_SERIAL4) && kHD == 128 && !kSplit),
+                "32- and 128-key tiles: the serial schedules at HD 128");
   constexpr int NW = waves_of(kSched);
-  constexpr int K_SLOTS = k_slots_of(kSched);
+  constexpr int K_SLOTS = k_slots_of(kSched, kBN);
   constexpr int HD = G::HD, NKK = G::NKK, NDB = G::NDB;
-  constexpr int K_ROWB = G::K_ROWB, K_TILEB = G::K_TILEB, K_DMA = G::K_DMA;
+  constexpr int NSB = kBN / 32;  // 32-key blocks of S^T
+  constexpr int NPK = kBN / 16;  // 16-key steps of P^T
+  constexpr int K_ROWB = G::K_ROWB, K_SLOTB = G::K_SLOTB, K_DMA = G::K_DMA;
   constexpr int K_DMA_PER_WAVE = (K_DMA + NW - 1) / NW;  // wave w issues K instructions w, w+NW, ...
   constexpr int V_DMA_PER_WAVE = G::V_DMA / NW;          // wave w issues V instructions w, w+NW, ...
   constexpr int V_ROWB = G::V_ROWB, V_TILEB = G::V_TILEB;
-  __shared__ __attribute__((aligned(1024))) char k_smem[K_SLOTS * K_TILEB];
+  static_assert(wgs_per_cu(kSched, kHD, kBN) * (K_SLOTS * K_SLOTB + V_SLOTS * V_TILEB) <= 160 * 1024,
+                "the rings of the workgroups on a CU fit its 160 KiB LDS");
+  __shared__ __attribute__((aligned(1024))) char k_smem[K_SLOTS * K_SLOTB];
   __shared__ __attribute__((aligned(1024))) char v_smem[V_SLOTS * V_TILEB];
   LDS char* const k_lds = (LDS char*)k_smem;
   LDS char* const v_lds = (LDS char*)v_smem;
@@ -157,8 +180,8 @@ void attn_fwd_kernel(Params p) {
   const int off = p.off;        // causal: query row i attends keys j <= i + off
   const int q0 = t * BM;
   const int qw = q0 + 32 * wq;  // first query row of this wave
-  const int kv_tiles_all = (Sk + BN - 1) / BN;
-  int n_tiles = p.causal ? min(kv_tiles_all, (q0 + off + BM + BN - 1) / BN) : kv_tiles_all;
+  const int kv_tiles_all = (Sk + kBN - 1) / kBN;
+  int n_tiles = p.causal ? min(kv_tiles_all, (q0 + off + BM + kBN - 1) / kBN) : kv_tiles_all;
   int j_lo = 0;  // first key tile
 
   // Split-KV mode: this lane's packed row, its query head and query row, and
@@ -209,12 +232,12 @@ void attn_fwd_kernel(Params p) {
     }
   }
 
-  // ---- K/V staging by direct global -> LDS loads.  K_t and V_t live in slot
-  // t & 1 of their rings.  Wave w issues K instructions w, w+8, w+16 and V
-  // instructions w, w+8 of a tile: 33 per tile over the 8 waves.  The lane
-  // offsets relative to a tile's first row are fixed; rows past the end of
-  // the keys are loaded from row Sk-1 (finite data whose scores and
-  // weights are masked to zero).
+  // ---- K/V staging by direct global -> LDS loads.  K_t and V_t live in slots
+  // t % K_SLOTS and t & 1 of their rings.  Wave w issues K instructions w,
+  // w+NW, ... and V instructions w, w+NW, ... of a tile (HD 128, 64 keys: 33
+  // per tile over 8 waves).  The lane offsets relative to a tile's first row
+  // are fixed; rows past the end of the keys are loaded from row Sk-1 (finite
+  // data whose scores and weights are masked to zero).
   const uint32_t row_bytes = (uint32_t)p.kv_sstride * 2;
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t k_lds_base = (uint32_t)(uintptr_t)k_lds, v_lds_base = (uint32_t)(uintptr_t)v_lds;
@@ -223,9 +246,12 @@ void attn_fwd_kernel(Params p) {
 #pragma unroll
   for (int u = 0; u < K_DMA_PER_WAVE; ++u) {
     const int o = 64 * (wave + NW * u) + lane;  // 16-byte lane slot inside the tile
-    k_row[u] = o / (K_ROWB / 16);
-    const int cb = o - k_row[u] * (K_ROWB / 16);
+    const int row = o / (K_ROWB / 16);
+    const int cb = o - row * (K_ROWB / 16);
     k_col[u] = 16u * (uint32_t)(cb < G::KC ? cb : G::KC - 1);  // padding slot: any in-bounds chunk of the row
+    // a partial last instruction (kBN 32): its surplus lanes land in the slot past the tile, read from any row
+    if constexpr (G::K_SLOTB != G::K_TILEB) k_row[u] = min(row, kBN - 1);
+    else k_row[u] = row;
   }
   const int v_rowl = lane / G::KC;  // row inside the instruction's rows (V_ROWS_PER_DMA * i + v_rowl)
   // chunk stored at slot lane % KC.  The swizzle reads row bits 0..1; the
@@ -237,25 +263,25 @@ void attn_fwd_kernel(Params p) {
     tk = __builtin_amdgcn_readfirstlane(tk);
     tv = __builtin_amdgcn_readfirstlane(tv);
     if (tk < n_tiles) {
-      const char* base = (const char*)kb_ + (int64_t)tk * BN * row_bytes;
-      const bool full = (tk + 1) * BN <= Sk;
+      const char* base = (const char*)kb_ + (int64_t)tk * kBN * row_bytes;
+      const bool full = (tk + 1) * kBN <= Sk;
 #pragma unroll
       for (int u = 0; u < K_DMA_PER_WAVE; ++u) {
         const int i = wave_s + NW * u;
         if (i < K_DMA) {
-          const int row = full ? k_row[u] : min(k_row[u], Sk - 1 - tk * BN);
-          dma16(base, (uint32_t)row * row_bytes + k_col[u], k_lds_base + (tk % K_SLOTS) * K_TILEB + 1024 * i);
+          const int row = full ? k_row[u] : min(k_row[u], Sk - 1 - tk * kBN);
+          dma16(base, (uint32_t)row * row_bytes + k_col[u], k_lds_base + (tk % K_SLOTS) * K_SLOTB + 1024 * i);
         }
       }
     }
     if (tv < n_tiles) {
-      const char* base = (const char*)vb_ + (int64_t)tv * BN * row_bytes;
-      const bool full = (tv + 1) * BN <= Sk;
+      const char* base = (const char*)vb_ + (int64_t)tv * kBN * row_bytes;
+      const bool full = (tv + 1) * kBN <= Sk;
 #pragma unroll
       for (int u = 0; u < V_DMA_PER_WAVE; ++u) {
         const int i = wave_s + NW * u;
         const int row0 = G::V_ROWS_PER_DMA * i + v_rowl;
-        const int row = full ? row0 : min(row0, Sk - 1 - tv * BN);
+        const int row = full ? row0 : min(row0, Sk - 1 - tv * kBN);
         dma16(base, (uint32_t)row * row_bytes + v_col, v_lds_base + (tv & 1) * V_TILEB + 1024 * i);
       }
     }
@@ -287,17 +313,17 @@ void attn_fwd_kernel(Params p) {
   const int qlo_u = __builtin_amdgcn_readfirstlane(q_lo), qhi_u = __builtin_amdgcn_readfirstlane(q_hi);
   const bool wact_u = __builtin_amdgcn_readfirstlane(wave_active ? 1 : 0) != 0;
   auto skip = [&](int j) INL {
-    if constexpr (kSplit) return !wact_u || (p.causal && j * BN > qhi_u + off);
-    else return !active_u || (p.causal && j * BN > qw_u + 31 + off);
+    if constexpr (kSplit) return !wact_u || (p.causal && j * kBN > qhi_u + off);
+    else return !active_u || (p.causal && j * kBN > qw_u + 31 + off);
   };
   auto is_masked = [&](int j) INL {
-    if constexpr (kSplit) return (p.causal && j * BN + BN - 1 > qlo_u + off) || j * BN + BN > Sk;
-    else return (p.causal && j * BN + BN - 1 > qw_u + off) || j * BN + BN > Sk;
+    if constexpr (kSplit) return (p.causal && j * kBN + kBN - 1 > qlo_u + off) || j * kBN + kBN > Sk;
+    else return (p.causal && j * kBN + kBN - 1 > qw_u + off) || j * kBN + kBN > Sk;
   };
 
   // ---- fragments of the mma sTasks
   auto frag_qk = [&](int j, int kk, int sb) INL -> f16x8 {
-    return *(const LDS f16x8*)(k_lds + (j % K_SLOTS) * K_TILEB + k_frag + 32 * sb * K_ROWB + 32 * kk);
+    return *(const LDS f16x8*)(k_lds + (j % K_SLOTS) * K_SLOTB + k_frag + 32 * sb * K_ROWB + 32 * kk);
   };
   auto frag_pv = [&](int j, int kk, int db) INL -> f16x8 {
     const LDS char* a = v_lds + (j & 1) * V_TILEB + v_frag[db] + 16 * kk * V_ROWB;
@@ -312,18 +338,20 @@ void attn_fwd_kernel(Params p) {
   // PV of the previous tile has been accumulated.
   //
   // The work is cut into parts with compile-time indices so that a fused mma
-  // block can place each part between two MFMAs:
-  //   E0..E31 P = 2^(s*cs - m) for score e; every second part also packs an
-  //           earlier pair to fp16 and adds it to the row sum (add_pair_f16),
-  //           one pair behind to hide the exponential's latency
-  //   E32     packs the last pair
-  //   E33     row sum across the lane pair
+  // block can place each part between two MFMAs.  A lane holds NE = 16 NSB
+  // scores of its query (NE = 32 for 64-key tiles):
+  //   E0..E(NE-1)  P = 2^(s*cs - m) for score e; every second part also packs
+  //           an earlier pair to fp16 and adds it to the row sum
+  //           (add_pair_f16), one pair behind to hide the exponential's latency
+  //   E(NE)   packs the last pair
+  //   E(NE+1) row sum across the lane pair
   //   C       the check: does any row's tile sum exceed RS_MAX?  (ballot,
   //           wave-uniform)
   //   F       l = l * alpha + row sum (one fused multiply-add)
   // and, only on a wave's first tile or when C fires, before F:
-  //   X0..X7  tile max: four chains of 8 scores, half a chain per part
-  //   X8, X9  lane-pair max, tile max in log2 units
+  //   X0..X(2NC-1)  tile max: NC = 2 NSB chains of 8 scores, half a chain
+  //           per part
+  //   X(2NC), X(2NC+1)  lane-pair max, tile max in log2 units
   //   D       m = max(m, tile max), alpha = 2^(m_old - m), -m for the exponents
   //   E0..E33 again, with the new m
   // On the first tile this is the textbook online softmax step in order X,
@@ -333,8 +361,10 @@ void attn_fwd_kernel(Params p) {
     bool any;
     float alpha;
   };
+  constexpr int NC = 2 * NSB;    // max chains of 8 scores
+  constexpr int NE = 16 * NSB;   // scores per lane and tile
   struct SmState {
-    float mq[4];     // chain maxima
+    float mq[NC];    // chain maxima
     float sw[2];     // the lane pair's combined maxima after the swap
     float mts;       // tile max, log2 units
     float negm;      // -(running max) used by the exponentials
@@ -344,14 +374,14 @@ void attn_fwd_kernel(Params p) {
     int lim;         // masked tiles: compile-time key offsets below lim are allowed
     Rescale rz;
   };
-  // Key (sb, r) of this lane is j*BN + 32sb + 8(r/4) + 4hh + r%4; it is
+  // Key (sb, r) of this lane is j*kBN + 32sb + 8(r/4) + 4hh + r%4; it is
   // allowed iff it is below end = min(Sk, query + off + 1) (causal) or Sk, i.e. iff
   // the compile-time part 32sb + 8(r/4) + r%4 is below lim.
   auto sm_lim = [&](int j, auto masked, SmState& st) INL {
     if constexpr (decltype(masked)::value) {
       const int query = kSplit ? qidx : qw + n;
       const int end = p.causal ? min(Sk, query + off + 1) : Sk;
-      st.lim = end - j * BN - 4 * hh;
+      st.lim = end - j * kBN - 4 * hh;
     }
   };
   auto sm_start = [&](SmState& st) INL {  // before the E parts
@@ -361,26 +391,31 @@ void attn_fwd_kernel(Params p) {
     st.rz.any = false;
     st.rz.alpha = 1.0f;
   };
-  auto sm_x = [&](auto kc, f32x16 (&sc)[2], auto masked, SmState& st) INL {  // parts X0..X9
+  auto sm_x = [&](auto kc, f32x16 (&sc)[NSB], auto masked, SmState& st) INL {  // parts X0..X(2NC+1)
     constexpr int k = decltype(kc)::value;
     constexpr bool kMasked = decltype(masked)::value;
     auto kept = [&](int sb, int r) INL { return !kMasked || 32 * sb + 8 * (r >> 2) + (r & 3) < st.lim; };
-    if constexpr (k < 8) {
-      constexpr int q = k & 3, half = k >> 2;
+    if constexpr (k < 2 * NC) {
+      constexpr int q = k % NC, half = k / NC;
       if constexpr (half == 0) st.mq[q] = NEG_INF;
 #pragma unroll
       for (int e = 4 * half; e < 4 * half + 4; ++e) {
         const int sb = q >> 1, r = 8 * (q & 1) + e;
         st.mq[q] = fmaxf(st.mq[q], kept(sb, r) ? sc[sb][r] : NEG_INF);
       }
-    } else if constexpr (k == 8) {
-      const float m4 = fmaxf(fmaxf(st.mq[0], st.mq[1]), fmaxf(st.mq[2], st.mq[3]));
+    } else if constexpr (k == 2 * NC) {
+      float m4;  // max of the chains, pairwise
+      if constexpr (NC == 2) m4 = fmaxf(st.mq[0], st.mq[1]);
+      else if constexpr (NC == 4) m4 = fmaxf(fmaxf(st.mq[0], st.mq[1]), fmaxf(st.mq[2], st.mq[3]));
+      else
+        m4 = fmaxf(fmaxf(fmaxf(st.mq[0], st.mq[1]), fmaxf(st.mq[2], st.mq[3])),
+                   fmaxf(fmaxf(st.mq[4], st.mq[5]), fmaxf(st.mq[6], st.mq[7])));
       // lanes l and l^32 hold the same query: combine their partial maxima
       auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(m4), __float_as_uint(m4), false, false);
       st.sw[0] = __uint_as_float(x[0]);
       st.sw[1] = __uint_as_float(x[1]);
     } else {
-      static_assert(k == 9, "max part index");
+      static_assert(k == 2 * NC + 1, "max part index");
       const float mt = fmaxf(st.sw[0], st.sw[1]);
       st.mts = (mt == NEG_INF) ? NEG_INF : mt * cs;
     }
@@ -394,7 +429,7 @@ void attn_fwd_kernel(Params p) {
     st.rz.alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
   };
-  auto sm_e = [&](auto kc, f32x16 (&sc)[2], f16x8 (&pd)[4], auto masked, SmState& st) INL {  // E0..E33
+  auto sm_e = [&](auto kc, f32x16 (&sc)[NSB], f16x8 (&pd)[NPK], auto masked, SmState& st) INL {  // E0..E(NE+1)
     constexpr int e = decltype(kc)::value;
     constexpr bool kMasked = decltype(masked)::value;
     auto kept = [&](int sb, int r) INL { return !kMasked || 32 * sb + 8 * (r >> 2) + (r & 3) < st.lim; };
@@ -404,30 +439,30 @@ void attn_fwd_kernel(Params p) {
       pd[kk][c + 1] = (_Float16)st.t[pp & 1][1];
       add_pair_f16(st.rq[kk & 1], f16x2{pd[kk][c], pd[kk][c + 1]});
     };
-    if constexpr (e < 32) {  // score e = pair e/2, element e%2: (sb, r)
+    if constexpr (e < NE) {  // score e = pair e/2, element e%2: (sb, r)
       constexpr int pair = e >> 1, u = e & 1, sb = pair >> 3, r = 2 * (pair & 7) + u;
       float x = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[sb][r], cs, st.negm));
       if constexpr (kMasked) x = kept(sb, r) ? x : 0.f;
       st.t[pair & 1][u] = x;
       if constexpr (u == 1 && pair >= 1) pack(std::integral_constant<int, pair - 1>{});
-    } else if constexpr (e == 32) {
-      pack(std::integral_constant<int, 15>{});
+    } else if constexpr (e == NE) {
+      pack(std::integral_constant<int, NE / 2 - 1>{});
     } else {
-      static_assert(e == 33, "exp part index");
+      static_assert(e == NE + 1, "exp part index");
       st.rs = pair_sum(st.rq[0] + st.rq[1]);
     }
   };
   // part C; !(rs <= RS_MAX) also catches an infinite sum (m not yet set)
   auto sm_c = [&](SmState& st) INL { return __builtin_amdgcn_ballot_w64(!(st.rs <= RS_MAX)) != 0; };
   auto sm_f = [&](SmState& st) INL { l_run = __builtin_fmaf(l_run, st.rz.alpha, st.rs); };  // part F
-  constexpr int SM_X = 10, SM_E = 34;
+  constexpr int SM_X = 2 * NC + 2, SM_E = NE + 2;
   // X, D, E: the tile with its max (first tile, or C fired)
-  auto sm_full = [&](f32x16 (&sc)[2], f16x8 (&pd)[4], auto masked, SmState& st) INL {
+  auto sm_full = [&](f32x16 (&sc)[NSB], f16x8 (&pd)[NPK], auto masked, SmState& st) INL {
     static_for<SM_X>([&](auto kc) INL { sm_x(kc, sc, masked, st); });
     sm_d(st);
     static_for<SM_E>([&](auto ec) INL { sm_e(ec, sc, pd, masked, st); });
   };
-  auto softmax = [&](int j, f32x16 (&sc)[2], f16x8 (&pd)[4], auto masked, bool first) INL -> Rescale {
+  auto softmax = [&](int j, f32x16 (&sc)[NSB], f16x8 (&pd)[NPK], auto masked, bool first) INL -> Rescale {
     SmState st;
     sm_lim(j, masked, st);
     sm_start(st);
@@ -456,12 +491,12 @@ void attn_fwd_kernel(Params p) {
   // step i + kRing" and nothing moves across steps, so each wave keeps the
   // matrix core, the LDS and the VALU busy together.
   struct NoSoftmax {};
-  auto block = [&](auto mode_c, int jq, f32x16 (&sd)[2], int jv, f16x8 (&ps)[4], auto sm) INL {
+  auto block = [&](auto mode_c, int jq, f32x16 (&sd)[NSB], int jv, f16x8 (&ps)[NPK], auto sm) INL {
     constexpr int mode = decltype(mode_c)::value;
-    constexpr int nsteps = steps_of(mode, NKK, NDB);
+    constexpr int nsteps = steps_of(mode, NKK, NDB, NSB);
     constexpr bool kSoftmax = !std::is_same_v<decltype(sm), NoSoftmax>;
     auto load = [&](auto ic) INL -> f16x8 {
-      constexpr Step st = step_of(mode, decltype(ic)::value, NKK, NDB);
+      constexpr Step st = step_of(mode, decltype(ic)::value, NKK, NDB, NSB);
       if constexpr (st.pv) return frag_pv(jv, st.kk, st.x);
       else return frag_qk(jq, st.kk, st.x);
     };
@@ -469,7 +504,7 @@ void attn_fwd_kernel(Params p) {
     static_for<kRing>([&](auto ic) INL { fr[decltype(ic)::value] = load(ic); });
     auto step = [&](auto ic) INL {
       constexpr int i = decltype(ic)::value;
-      constexpr Step st = step_of(mode, i, NKK, NDB);
+      constexpr Step st = step_of(mode, i, NKK, NDB, NSB);
       const f16x8 a = fr[i % kRing];
       if constexpr (i + kRing < nsteps) fr[i % kRing] = load(std::integral_constant<int, i + kRing>{});
       if constexpr (st.pv)
@@ -482,13 +517,13 @@ void attn_fwd_kernel(Params p) {
     if constexpr (!kSoftmax) {
       static_for<nsteps>(step);
       static_for<kRing>([&](auto ic) INL {
-        __builtin_amdgcn_sched_group_barrier(0x100, reads_of(mode, decltype(ic)::value, NKK, NDB), 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, reads_of(mode, decltype(ic)::value, NKK, NDB, NSB), 0);
       });
       static_for<nsteps>([&](auto ic) INL {
         constexpr int i = decltype(ic)::value;
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         if constexpr (i + kRing < nsteps)
-          __builtin_amdgcn_sched_group_barrier(0x100, reads_of(mode, i + kRing, NKK, NDB), 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, reads_of(mode, i + kRing, NKK, NDB, NSB), 0);
       });
     } else {
       static_for<nsteps>([&](auto ic) INL {
@@ -502,8 +537,8 @@ void attn_fwd_kernel(Params p) {
   using M_PV = std::integral_constant<int, 1>;
   using M_QK = std::integral_constant<int, 2>;
   using M_FUSED = std::integral_constant<int, 3>;
-  f16x8 pf[4];  // P^T of the tile whose softmax ran last
-  f32x16 s[2];  // S^T of the tile whose QK^T ran last
+  f16x8 pf[NPK];  // P^T of the tile whose softmax ran last
+  f32x16 s[NSB];  // S^T of the tile whose QK^T ran last
   auto softmax_tile = [&](int j, bool first) INL {  // first: the wave's first tile
     const Rescale rz = is_masked(j) ? softmax(j, s, pf, std::true_type{}, first)
                                     : softmax(j, s, pf, std::false_type{}, first);
@@ -584,13 +619,13 @@ void attn_fwd_kernel(Params p) {
     // one iteration to the next, so the loops are unrolled twice.  On entry
     // to each loop S^T of the current tile is in sa and P^T of the previous
     // tile in pa; cur holds the softmax state of the current tile.
-    f32x16 sa[2], sb[2];
-    f16x8 pa[4], pb[4];
+    f32x16 sa[NSB], sb[NSB];
+    f16x8 pa[NPK], pb[NPK];
     SmState cur;
     // One iteration.  with_pv / with_qk: whether PV(j-1) / QK(j+1) exist;
     // mask_e / mask_x: whether tile j / tile j+1 need the key mask.
-    auto iter = [&](int j, auto with_pv, auto with_qk, auto mask_e, auto mask_x, f32x16 (&sc)[2],
-                    f32x16 (&sn)[2], f16x8 (&pp)[4], f16x8 (&pc)[4]) INL {
+    auto iter = [&](int j, auto with_pv, auto with_qk, auto mask_e, auto mask_x, f32x16 (&sc)[NSB],
+                    f32x16 (&sn)[NSB], f16x8 (&pp)[NPK], f16x8 (&pc)[NPK]) INL {
       constexpr bool kPV = decltype(with_pv)::value, kQK = decltype(with_qk)::value;
       stage(j + 2, j);
       SmState nx;  // tile j+1
@@ -631,7 +666,7 @@ void attn_fwd_kernel(Params p) {
     // steady-state loop is split so that each loop has one code path.  The
     // first and the last iteration always take the masked path (with no key
     // masked it computes the same values).
-    const int j_ms = min(n_tiles, p.causal ? min(q0 + off, Sk) / BN : Sk / BN);
+    const int j_ms = min(n_tiles, p.causal ? min(q0 + off, Sk) / kBN : Sk / kBN);
     using T = std::true_type;
     using F = std::false_type;
     stage(0, n_tiles);
@@ -731,9 +766,33 @@ hipError_t launch_attn_fwd(const Params& p, hipStream_t stream) {
   if (nb <= 0) return hipErrorInvalidValue;
   const dim3 grid((unsigned)nb), block(64 * waves_of(p.schedule));
 #define LIBATTN_LAUNCH(S, R, H) hipLaunchKernelGGL((attn_fwd_kernel<S, R, H>), grid, block, 0, stream, p)
+#define LIBATTN_LAUNCH_BN(S, R, N) \
+  hipLaunchKernelGGL((attn_fwd_kernel<S, R, 128, false, N>), grid, block, 0, stream, p)
   if (p.ring != 2 && p.ring != 4) return hipErrorInvalidValue;
   const bool r2 = p.ring == 2;
-  if (p.schedule == SCHEDULE_SERIAL4) {
+  if (p.bn != BN) {  // 32- and 128-key tiles: the serial schedules at HD 128
+    if (p.hd != 128 || (p.bn != 32 && p.bn != 128) ||
+        (p.schedule != SCHEDULE_SERIAL && p.schedule != SCHEDULE_SERIAL4))
+      return hipErrorInvalidValue;
+    const bool s4 = p.schedule == SCHEDULE_SERIAL4;
+    if (p.bn == 32) {
+      if (s4) {
+        if (r2) LIBATTN_LAUNCH_BN(SCHEDULE_SERIAL4, 2, 32);
+        else LIBATTN_LAUNCH_BN(SCHEDULE_SERIAL4, 4, 32);
+      } else {
+        if (r2) LIBATTN_LAUNCH_BN(SCHEDULE_SERIAL, 2, 32);
+        else LIBATTN_LAUNCH_BN(SCHEDULE_SERIAL, 4, 32);
+      }
+    } else {
+      if (s4) {
+        if (r2) LIBATTN_LAUNCH_BN(SCHEDULE_SERIAL4, 2, 128);
+        else LIBATTN_LAUNCH_BN(SCHEDULE_SERIAL4, 4, 128);
+      } else {
+        if (r2) LIBATTN_LAUNCH_BN(SCHEDULE_SERIAL, 2, 128);
+        else LIBATTN_LAUNCH_BN(SCHEDULE_SERIAL, 4, 128);
+      }
+    }
+  } else if (p.schedule == SCHEDULE_SERIAL4) {
     if (p.hd == 64) {
       if (r2) LIBATTN_LAUNCH(SCHEDULE_SERIAL4, 2, 64);
       else LIBATTN_LAUNCH(SCHEDULE_SERIAL4, 4, 64);
@@ -763,6 +822,7 @@ hipError_t launch_attn_fwd(const Params& p, hipStream_t stream) {
     else LIBATTN_LAUNCH(SCHEDULE_SERIAL, 4, 128);
   }
 #undef LIBATTN_LAUNCH
+#undef LIBATTN_LAUNCH_BN
   return hipGetLastError();
 }
 

@@ -6,7 +6,7 @@
 
 namespace libattn {
 
-constexpr int BN = 64;           // keys per KV tile
+constexpr int BN = 64;           // keys per KV tile (the serial schedules also run 32 and 128)
 constexpr float NEG_INF = -__builtin_inff();
 constexpr float M_INIT = -1e30f; // finite start for the running max
 constexpr float LN2 = 0.693147180559945309f;
@@ -19,36 +19,40 @@ constexpr float LN2 = 0.693147180559945309f;
 // LSE = m + log2(l) are exact for any m.
 constexpr float RS_MAX = 256.0f;
 
-// LDS layouts (bytes), per head dimension HD (64, 128 or 256).  A tile slot is a
-// run of 1 KiB DMA instructions.
-//  K: 64 key rows of 2*HD + 16 B.  Consecutive keys fall 68 (HD 128), 36
+// LDS layouts (bytes), per head dimension HD (64, 128 or 256) and keys per tile
+// kBN.  A tile slot is a run of 1 KiB DMA instructions; where a K tile is not a
+// whole number of them (kBN 32), its slot is rounded up and the last
+// instruction's surplus lanes land past the tile.
+//  K: kBN key rows of 2*HD + 16 B.  Consecutive keys fall 68 (HD 128), 36
 //    (HD 64) or 132 (HD 256) banks apart, so the 16 keys of a ds_read_b128 pass at one
 //    16-byte column cover all 64 banks once; every K fragment read is a
 //    compile-time offset from one per-lane base.  One 16-byte lane slot per
 //    row lands in the padding.
-//  V: 64 key rows of 2*HD B whose 16-byte chunks are XOR-swizzled: by
+//  V: kBN key rows of 2*HD B whose 16-byte chunks are XOR-swizzled: by
 //    4*(row & 3) for HD 128 and 256, by 4*((row >> 1) & 1) for HD 64.  A
 //    ds_read_b64_tr_b16 group reads 4 consecutive rows x 32 B; with the
 //    swizzle the 4 rows of the two groups of a half-wave (4 rows x 64 B) hit
 //    all 64 banks once.  Across the 32-wide d blocks the per-lane address
 //    changes by an XOR with 64*db.
-template <int kHD>
+template <int kHD, int kBN = BN>
 struct Geo {
   static_assert(kHD == 64 || kHD == 128 || kHD == 256, "head dimension");
+  static_assert(kBN == 32 || kBN == 64 || kBN == 128, "keys per tile");
   static constexpr int HD = kHD;
   static constexpr int KC = kHD / 8;                 // 16-byte chunks per K/V row
   static constexpr int K_ROWB = 2 * kHD + 16;
-  static constexpr int K_TILEB = BN * K_ROWB;        // 17408 | 9216 | 33792
-  static constexpr int K_DMA = K_TILEB / 1024;       // 17 | 9 | 33
+  static constexpr int K_TILEB = kBN * K_ROWB;       // kBN 64: 17408 | 9216 | 33792
+  static constexpr int K_DMA = (K_TILEB + 1023) / 1024;  // kBN 64: 17 | 9 | 33
+  static constexpr int K_SLOTB = 1024 * K_DMA;       // a K ring slot: the tile in whole instructions
 
   static constexpr int V_ROWB = 2 * kHD;
-  static constexpr int V_TILEB = BN * V_ROWB;        // 16384 | 8192 | 32768
-  static constexpr int V_DMA = V_TILEB / 1024;       // 16 | 8 | 32
+  static constexpr int V_TILEB = kBN * V_ROWB;       // kBN 64: 16384 | 8192 | 32768
+  static constexpr int V_DMA = V_TILEB / 1024;       // kBN 64: 16 | 8 | 32
 
   static constexpr int V_ROWS_PER_DMA = 1024 / V_ROWB;
   static constexpr int NKK = kHD / 16;               // 16-wide d steps of QK^T
   static constexpr int NDB = kHD / 32;               // 32-wide d blocks of O^T
-  static_assert(K_TILEB % 1024 == 0 && V_TILEB % 1024 == 0, "tile slots are whole DMA instructions");
+  static_assert(V_TILEB % 1024 == 0, "V tile slots are whole DMA instructions");
   static_assert(V_DMA % 8 == 0, "every wave of 4 or 8 issues the same number of V instructions");
   // physical 16-byte chunk of logical chunk c in V row r is c ^ vswz(r)
   __host__ __device__ static constexpr int vswz(int r) { return kHD == 64 ? 4 * ((r >> 1) & 1) : 4 * (r & 3); }

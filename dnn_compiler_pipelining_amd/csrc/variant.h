@@ -5,8 +5,10 @@
 // A variant is a point of the schedule space that the search in
 // dnn_compiler_pipelining_amd/tune.py explores: the tile schedule, the depth
 // of the fragment prefetch ring, where the softmax parts sit among the MFMAs
-// (64-row schedule), and two workgroup-order switches.  Every variant
-// computes bitwise identical results; they differ only in speed.
+// (64-row schedule), the keys per K/V tile (serial schedules), and two
+// workgroup-order switches.  Variants with the same keys per tile compute
+// bitwise identical results and differ only in speed; another tile size
+// changes the rounding order of the online softmax.
 // PipeThreader searches such a space of task orders with a validity check
 // and profile feedback (page "PipeThreader: Software-Defined Pipelining ...
 // (OSDI 2025)" summary, section "核心方法"); tuned_table.h is the outcome of
@@ -50,12 +52,17 @@ enum Schedule {
 //                held at its step (not sunk to its first use)
 enum Place { PLACE_EVEN = 0, PLACE_FRONT = 1, PLACE_EARLY = 2 };
 
+// Keys per K/V tile of every schedule (BN in the kernels); SERIAL and SERIAL4
+// at head dimension 128 also run 32 and 128.
+constexpr int BN_STD = 64;
+
 struct Variant {
   int schedule;  // Schedule
   int ring;      // fragment prefetch depth of the mma steps: 2 or 4
   int xcd;       // 1: each XCD gets whole (batch, kv head) groups
   int lpt;       // 1: longest causal query tiles of a group first
   int place;     // Place (SCHEDULE_WIDE only; PLACE_EVEN for the others)
+  int bn;        // keys per K/V tile: 64; SERIAL and SERIAL4 also 32 and 128 (head dimension 128)
 };
 
 // One measured shape and the fastest variant found for it.
@@ -70,7 +77,9 @@ struct TunedEntry {
 inline bool variant_valid(const Variant& v) {
   return v.schedule >= SCHEDULE_SERIAL && v.schedule <= SCHEDULE_WIDE && (v.ring == 2 || v.ring == 4) &&
          (v.xcd == 0 || v.xcd == 1) && (v.lpt == 0 || v.lpt == 1) && v.place >= PLACE_EVEN &&
-         v.place <= PLACE_EARLY && (v.schedule == SCHEDULE_WIDE || v.place == PLACE_EVEN);
+         v.place <= PLACE_EARLY && (v.schedule == SCHEDULE_WIDE || v.place == PLACE_EVEN) &&
+         (v.bn == BN_STD || ((v.bn == 32 || v.bn == 128) &&
+                         (v.schedule == SCHEDULE_SERIAL || v.schedule == SCHEDULE_SERIAL4)));
 }
 
 // The variant tuned for the measured shape nearest to (B, Sq, Sk, Hq, Hkv):

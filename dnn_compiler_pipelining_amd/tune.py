@@ -4,10 +4,13 @@ PipeThreader schedules an operator by searching the space of task orders on
 the hardware's units under a resource check, with measured feedback (page
 "PipeThreader: Software-Defined Pipelining ... (OSDI 2025)" summary, section
 "核心方法").  This module does that for libattn's space of kernel variants
-(csrc/variant.h): tile schedule x fragment-prefetch depth x placement of the
-softmax parts among the MFMAs (64-row schedule) (compile time) x two
-workgroup-order switches (run time).  Every variant computes the same bits, so
-the search only trades speed.
+(csrc/variant.h): tile schedule (which also fixes the query rows per wave, 32
+or 64) x fragment-prefetch depth x placement of the softmax parts among the
+MFMAs (64-row schedule) x keys per K/V tile (32, 64 or 128; the serial
+schedules) (compile time) x two workgroup-order switches (run time).  Variants
+with the same tile size compute the same bits; the tile size changes the
+rounding order of the online softmax, and every instance is checked against
+the oracle, so the search only trades speed.
 
     python -m dnn_compiler_pipelining_amd.tune --check
         validity of every compiled variant from the code-object metadata (CPU)
@@ -35,18 +38,38 @@ SCHEDULES = ("serial", "overlap", "pingpong", "serial4", "wide")  # Schedule enu
 PLACES = ("even", "front", "early")  # Place enum order in csrc/variant.h; schedules other than wide: even only
 
 
-def workgroups_per_cu(schedule: str, hd: int) -> int:
-    """serial4 runs two 4-wave workgroups per CU, except at head dimension 256 (one); wide one of 4 waves; the
-    others one of 8 waves."""
-    return 2 if schedule.startswith("serial4") and hd <= 128 else 1
+BNS = (32, 64, 128)  # keys per K/V tile; 32 and 128 for the serial schedules at head dimension 128
 
 
-def waves_per_simd(schedule: str, hd: int) -> int:
-    """wide (64 query rows per wave) and serial4 at head dimension 256 run one wave per SIMD; the others two."""
-    return 1 if schedule == "wide" or (schedule.startswith("serial4") and hd > 128) else 2
+def workgroups_per_cu(schedule: str, hd: int, bn: int = 64) -> int:
+    """serial4 runs two 4-wave workgroups per CU, except at head dimension 256 or with 128-key tiles (one);
+    wide one of 4 waves; the others one of 8 waves."""
+    return 2 if schedule.startswith("serial4") and hd <= 128 and bn <= 64 else 1
+
+
+def waves_per_simd(schedule: str, hd: int, bn: int = 64) -> int:
+    """wide (64 query rows per wave) and serial4 at one workgroup per CU run one wave per SIMD; the others
+    two."""
+    if schedule == "wide":
+        return 1
+    if schedule.startswith("serial4"):
+        return workgroups_per_cu(schedule, hd, bn)
+    return 2
+
+
+def schedule_has(schedule: str, field: str) -> bool:
+    """Whether a schedule has more than one value of a variant field: the placement is the wide schedule's,
+    the tile size the serial schedules'."""
+    if field == "place":
+        return schedule == "wide"
+    if field == "bn":
+        return schedule in ("serial", "serial4")
+    return True
+
+
 RINGS = (2, 4)
 SWITCHES = (0, 1)
-SEED = {"schedule": "serial", "ring": 4, "xcd": 1, "lpt": 1, "place": "even"}
+SEED = {"ring": 4, "xcd": 1, "lpt": 1, "place": "even", "bn": 64}  # the start of each schedule's search
 # A change is kept when it is this much faster.  The median of five timed batches repeats to about
 # 0.2% on one box (repeated same-box pairs of the serial and overlap schedules on the 70B-shaped
 # B = 16 S = 8192 problem differed by 0.3-1.1%, always in the same direction).
@@ -75,7 +98,7 @@ def loop_scratch(text: str, symbol: str) -> int:
 
 
 def kernel_resources(asm_path: str):
-    """{(schedule, ring, hd, place): {vgpr, agpr, vgpr_spill, scratch, lds, loop_scratch}} from the AMDGPU
+    """{(schedule, ring, hd, place, bn): {vgpr, agpr, vgpr_spill, scratch, lds, loop_scratch}} from the AMDGPU
     metadata of a device asm file and the annotated loop structure of its code.
 
     The split-KV instances (attn_fwd_decode) appear under the schedule name "serial4-split".  On gfx950
@@ -84,7 +107,7 @@ def kernel_resources(asm_path: str):
     meta = text[text.index("amdhsa.kernels:"):]
     out = {}
     for block in re.split(r"\n  - ", meta)[1:]:
-        m = re.search(r"\.name:\s+\S*attn_fwd_kernelILi(\d)ELi(\d)ELi(\d+)ELb([01])E", block)
+        m = re.search(r"\.name:\s+\S*attn_fwd_kernelILi(\d)ELi(\d)ELi(\d+)ELb([01])E(?:Li(\d+)E)?", block)
         mw = re.search(r"\.name:\s+\S*attn_wide_kernelILi(\d)ELi(\d)E", block)
         if not m and not mw:
             continue
@@ -94,10 +117,10 @@ def kernel_resources(asm_path: str):
             return int(mm.group(1)) if mm else 0
 
         if mw:  # the wide kernel: head dimension 128, template arguments = prefetch depth, placement
-            key = ("wide", int(mw.group(1)), 128, PLACES[int(mw.group(2))])
+            key = ("wide", int(mw.group(1)), 128, PLACES[int(mw.group(2))], 64)
         else:
             key = (SCHEDULES[int(m.group(1))] + ("-split" if m.group(4) == "1" else ""), int(m.group(2)),
-                   int(m.group(3)), "even")
+                   int(m.group(3)), "even", int(m.group(5) or 64))
         sym = re.search(r"\.name:\s+(\S+)", block).group(1)
         out[key] = dict(
             vgpr=num("vgpr_count"), agpr=num("agpr_count"), vgpr_spill=num("vgpr_spill_count"),
@@ -106,18 +129,18 @@ def kernel_resources(asm_path: str):
     return out
 
 
-def check_valid(res: dict, schedule: str = "serial", hd: int = 128) -> tuple[bool, str]:
+def check_valid(res: dict, schedule: str = "serial", hd: int = 128, bn: int = 64) -> tuple[bool, str]:
     """A variant is valid when its waves per SIMD fit the register file, no spill traffic runs inside its tile
     loop (spill code executed once per workgroup, in the prologue, the epilogue or the last tile's rare
     redo, is allowed: `wide` at 64 query rows per wave has a little), and the LDS of the workgroups that share
     a CU fits it.  Without the loop structure (res without loop_scratch) any spill is invalid."""
-    max_regs = REGISTER_FILE // waves_per_simd(schedule, hd)
+    max_regs = REGISTER_FILE // waves_per_simd(schedule, hd, bn)
     if res["vgpr"] > max_regs:
         return False, "%d VGPRs (AGPRs included) > %d" % (res["vgpr"], max_regs)
     if res.get("loop_scratch", res["vgpr_spill"] or res["scratch"]):
         return False, "spills %d VGPRs / %d B scratch, %s scratch instructions in the tile loop" % (
             res["vgpr_spill"], res["scratch"], res.get("loop_scratch", "?"))
-    wg = workgroups_per_cu(schedule, hd)
+    wg = workgroups_per_cu(schedule, hd, bn)
     if wg * res["lds"] > MAX_LDS:
         return False, "%d x %d B LDS > %d" % (wg, res["lds"], MAX_LDS)
     if res["vgpr_spill"]:
@@ -126,8 +149,8 @@ def check_valid(res: dict, schedule: str = "serial", hd: int = 128) -> tuple[boo
 
 
 def valid_variants(asm_paths=None):
-    """{(schedule, ring, hd): (valid, reason, resources)} for the current sources (device assembly of every
-    attention kernel source, or the given files)."""
+    """{(schedule, ring, hd, place, bn): (valid, reason, resources)} for the current sources (device assembly
+    of every attention kernel source, or the given files)."""
     from dnn_compiler_pipelining_amd import build
 
     if asm_paths is None:
@@ -145,12 +168,12 @@ def valid_variants(asm_paths=None):
     res = {}
     for path in asm_paths:
         res.update(kernel_resources(path))
-    return {k: check_valid(v, k[0], k[2]) + (v,) for k, v in res.items()}
+    return {k: check_valid(v, k[0], k[2], k[4]) + (v,) for k, v in res.items()}
 
 
 def variant_key(pt: dict, hd: int) -> tuple:
     """The valid_variants() key of a search point."""
-    return (pt["schedule"], pt["ring"], hd, pt.get("place", "even"))
+    return (pt["schedule"], pt["ring"], hd, pt.get("place", "even"), pt.get("bn", 64))
 
 
 # ------------------------------------------------------------------ search (GPU)
@@ -179,9 +202,41 @@ def measure(w, point: dict, q, k, v, o, lse) -> float:
     return w.flops / ms / 1e9
 
 
+def greedy_search(rate, is_valid):
+    """Greedy coordinate search per schedule: from the schedule's seed (SEED), change one of its fields at a
+    time, keep a change only when it is more than KEEP_GAIN faster, repeat until nothing improves; the best
+    of the schedules' optima wins.  Searching each schedule on its own keeps the fields that only some
+    schedules have (placement, tile size) in the search whichever schedule is fastest.  `rate(point)` is the
+    measured TFLOP/s of a point, `is_valid(point)` the resource check; returns (best point, its rate)."""
+    fields = [("ring", RINGS), ("xcd", SWITCHES), ("lpt", SWITCHES), ("place", PLACES), ("bn", BNS)]
+    best, best_rate = None, 0.0
+    for sched in SCHEDULES:
+        cur = dict(SEED, schedule=sched)
+        if not is_valid(cur):
+            continue
+        cur_rate = rate(cur)
+        improved = True
+        while improved:
+            improved = False
+            for field, values in fields:
+                if not schedule_has(sched, field):
+                    continue
+                for val in values:
+                    if val == cur[field]:
+                        continue
+                    cand = dict(cur, **{field: val})
+                    if not is_valid(cand):
+                        continue
+                    r = rate(cand)
+                    if r > cur_rate * (1.0 + KEEP_GAIN):
+                        cur, cur_rate, improved = cand, r, True
+        if cur_rate > best_rate:
+            best, best_rate = cur, cur_rate
+    return best, best_rate
+
+
 def search_workload(w, valid, log=print):
-    """Greedy coordinate search from the seed variant: change one field at a time, keep a change only when it
-    is more than KEEP_GAIN faster, repeat until nothing improves."""
+    """greedy_search on one workload, every point timed on the GPU (measure)."""
     from dnn_compiler_pipelining_amd import inputs
 
     q, k, v = inputs.make_inputs(w, "cuda")
@@ -192,45 +247,31 @@ def search_workload(w, valid, log=print):
     seen = {}
 
     def rate(pt):
-        key = (pt["schedule"], pt["ring"], pt["xcd"], pt["lpt"], pt["place"])
+        key = (pt["schedule"], pt["ring"], pt["xcd"], pt["lpt"], pt["place"], pt["bn"])
         if key not in seen:
             seen[key] = measure(w, pt, q, k, v, o, lse)
-            log("  %-26s %-9s ring %d xcd %d lpt %d place %-5s: %7.1f TFLOP/s" % (w.name, *key, seen[key]))
+            log("  %-26s %-9s ring %d xcd %d lpt %d place %-5s bn %3d: %7.1f TFLOP/s" % (w.name, *key, seen[key]))
         return seen[key]
 
-    axes = [("schedule", SCHEDULES), ("ring", RINGS), ("xcd", SWITCHES), ("lpt", SWITCHES), ("place", PLACES)]
-    best = dict(SEED)
-    best_rate = rate(best)
-    improved = True
-    while improved:
-        improved = False
-        for field, values in axes:
-            for val in values:
-                if val == best[field]:
-                    continue
-                cand = dict(best, **{field: val})
-                if not valid.get(variant_key(cand, w.D), (False,))[0]:
-                    continue
-                r = rate(cand)
-                if r > best_rate * (1.0 + KEEP_GAIN):
-                    best, best_rate, improved = cand, r, True
+    best, best_rate = greedy_search(rate, lambda pt: valid.get(variant_key(pt, w.D), (False,))[0])
     del q, k, v, o, lse
     torch.cuda.empty_cache()
     return {"workload": w.name, "B": w.B, "Sq": w.S, "Sk": w.S, "Hq": w.Hq, "Hkv": w.Hkv, "best": best,
             "best_tflops": round(best_rate, 1),
-            "measured": [{"schedule": s, "ring": r, "xcd": x, "lpt": l, "place": pl, "tflops": round(t, 1)}
-                         for (s, r, x, l, pl), t in seen.items()]}
+            "measured": [{"schedule": s, "ring": r, "xcd": x, "lpt": l, "place": pl, "bn": bn, "tflops": round(t, 1)}
+                         for (s, r, x, l, pl, bn), t in seen.items()]}
 
 
 def search(out_dir: str, names=None):
     from dnn_compiler_pipelining_amd import inputs
 
     valid = valid_variants()
-    for (s, r, hd, pl), (ok, why, _) in sorted(valid.items()):
-        print("variant %-13s ring %d hd %3d place %-5s: %s" % (s, r, hd, pl, why), flush=True)
-    rec = {"valid": {"%s/%d/%d/%s" % k: dict(ok=v[0], reason=v[1], **v[2]) for k, v in valid.items()},
-           "rule": "greedy coordinate search from %s; a change is kept when > %.1f%% faster (median of five "
-                   "timed batches)" % (json.dumps(SEED), 100 * KEEP_GAIN),
+    for (s, r, hd, pl, bn), (ok, why, _) in sorted(valid.items()):
+        print("variant %-13s ring %d hd %3d place %-5s bn %3d: %s" % (s, r, hd, pl, bn, why), flush=True)
+    rec = {"valid": {"%s/%d/%d/%s/%d" % k: dict(ok=v[0], reason=v[1], **v[2]) for k, v in valid.items()},
+           "rule": "greedy coordinate search per schedule from %s over the fields the schedule has; a change is "
+                   "kept when > %.1f%% faster (median of five timed batches); the fastest schedule optimum wins"
+                   % (json.dumps(SEED), 100 * KEEP_GAIN),
            "results": []}
     for w in inputs.WORKLOADS:
         if names and w.name not in names:
@@ -256,9 +297,9 @@ def emit(search_json: str, table: str = TABLE, profile: str | None = PROFILE):
              "#pragma once", "static const TunedEntry kTuned[] = {"]
     for r in rec["results"]:
         b = r["best"]
-        lines.append("    {%d, %d, %d, %d, %d, {%s, %d, %d, %d, %s}, %.1f},  // %s" % (
+        lines.append("    {%d, %d, %d, %d, %d, {%s, %d, %d, %d, %s, %d}, %.1f},  // %s" % (
             r["B"], r["Sq"], r["Sk"], r["Hq"], r["Hkv"], enum[b["schedule"]], b["ring"], b["xcd"], b["lpt"],
-            penum[b.get("place", "even")], r["best_tflops"], r["workload"]))
+            penum[b.get("place", "even")], b.get("bn", 64), r["best_tflops"], r["workload"]))
     lines += ["};", "static const int kTunedCount = sizeof(kTuned) / sizeof(kTuned[0]);", ""]
     with open(table, "w") as f:
         f.write("\n".join(lines))
@@ -281,8 +322,8 @@ def main(argv=None):
     if ROOT not in sys.path:
         sys.path.insert(0, ROOT)
     if args.check:
-        for (s, r, hd, pl), (ok, why, res) in sorted(valid_variants().items()):
-            print("%-13s ring %d hd %3d place %-5s: %-5s %s  %s" % (s, r, hd, pl, ok, why, res))
+        for (s, r, hd, pl, bn), (ok, why, res) in sorted(valid_variants().items()):
+            print("%-13s ring %d hd %3d place %-5s bn %3d: %-5s %s  %s" % (s, r, hd, pl, bn, ok, why, res))
     if args.search:
         search(args.search, args.workload)
     if args.emit:

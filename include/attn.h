@@ -44,8 +44,10 @@
  *
  * Kernel variants.  Every entry point runs the variant tuned for the nearest
  * measured shape (a table compiled into the library); attn_fwd_variant names
- * one explicitly.  All variants give bitwise identical results, so each
- * serves as a cross-check of the others.  The library reads no environment.
+ * one explicitly.  Variants with the same keys per K/V tile give bitwise
+ * identical results, so each serves as a cross-check of the others; a tile
+ * size other than 64 keys changes only the rounding order of the online
+ * softmax.  The library reads no environment.
  *
  * Errors: on invalid arguments nothing is launched and a nonzero ATTN_ERR_*
  * code is returned; a failed launch returns ATTN_ERR_HIP.  No exception
@@ -96,7 +98,8 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
  *   SERIAL4   the serial schedule in 4-wave, one-head workgroups, two per CU
  *   WIDE      4-wave workgroups, one wave per SIMD, 64 query rows per wave, the overlap schedule inside
  *             each wave, K/V loaded two tiles ahead (D = 128 only)
- * D = 64 runs SERIAL and SERIAL4, D = 256 SERIAL4, D = 128 all five. */
+ * D = 64 runs SERIAL and SERIAL4, D = 256 SERIAL4, D = 128 all five.  Every schedule stages K/V in tiles of
+ * 64 keys; at D = 128 SERIAL and SERIAL4 also run tiles of 32 and 128 keys. */
 enum {
   ATTN_SCHEDULE_SERIAL = 0,
   ATTN_SCHEDULE_OVERLAP = 1,
@@ -113,20 +116,22 @@ enum { ATTN_PLACE_EVEN = 0, ATTN_PLACE_FRONT = 1, ATTN_PLACE_EARLY = 2 };
 /* attn_fwd_ex with an explicit kernel variant, for schedule search and cross-checks: `schedule` is an
  * ATTN_SCHEDULE_* value, `ring` the fragment prefetch depth (2 or 4), `xcd` 1 to give each XCD whole
  * (batch, KV head) groups, `lpt` 1 to run the longest causal query tiles first, `place` an ATTN_PLACE_*
- * value; -1 in any of them takes the tuned value (place: ATTN_PLACE_EVEN for schedules other than
- * ATTN_SCHEDULE_WIDE).  A value that does not exist, a placement the schedule does not have, or a
- * schedule the head dimension does not run, returns ATTN_ERR_UNSUPPORTED and launches nothing.  Results
- * are bitwise identical for every variant. */
+ * value, `bn` the keys per K/V tile (64; 32 or 128 with SERIAL or SERIAL4 at D = 128); -1 in any of them
+ * takes the tuned value (place: ATTN_PLACE_EVEN for schedules other than ATTN_SCHEDULE_WIDE; bn: 64 where
+ * the schedule or D has no other).  A value that does not exist, a placement or tile size the schedule
+ * does not have, or a schedule the head dimension does not run, returns ATTN_ERR_UNSUPPORTED and launches
+ * nothing.  Results are bitwise identical for every variant of one tile size; another tile size changes the
+ * rounding order of the online softmax. */
 int attn_fwd_variant(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Sq, int Sk, int Hq,
                      int Hkv, int D, int causal, float scale, int schedule, int ring, int xcd, int lpt, int place,
-                     void* stream);
+                     int bn, void* stream);
 
 /* The variant attn_fwd_ex runs for these sizes (ATTN_SCHEDULE_* value, ring depth, xcd and lpt switches,
- * ATTN_PLACE_* value), for reports and cross-checks.  Returns ATTN_OK, ATTN_ERR_NULL for a NULL output
+ * ATTN_PLACE_* value, keys per K/V tile), for reports and cross-checks.  Returns ATTN_OK, ATTN_ERR_NULL for a NULL output
  * pointer, ATTN_ERR_SHAPE for sizes attn_fwd_ex rejects, ATTN_ERR_UNSUPPORTED for a head dimension it does
  * not run.  No HIP call. */
 int attn_tuned_variant(int B, int Sq, int Sk, int Hq, int Hkv, int D, int* schedule, int* ring, int* xcd, int* lpt,
-                       int* place);
+                       int* place, int* bn);
 
 /* Compute-unit count and peak shader clock (kHz) of HIP device `device`, as the runtime reports them: the
  * inputs of a peak-throughput figure (dense fp16 MFMA on gfx950: 4 SIMDs x 1024 FLOP per clock per compute

@@ -74,8 +74,8 @@ def test_chunk_equals_suffix_of_square_bitwise(Sq, Sk):
     q, k, v = cpu_qkv(B, Sq, Sk, Hq, Hkv, seed=41 + Sq)
     pad = inputs.make_tensor(B, Sk - Sq, Hq, D, 43, inputs.Q)
     qfull = torch.cat([pad, q], dim=1).contiguous()
-    o1, l1 = U.run(q.cuda(), k.cuda(), v.cuda(), True, SC)
-    o2, l2 = U.run(qfull.cuda(), k.cuda(), v.cuda(), True, SC)
+    o1, l1 = U.run(q.cuda(), k.cuda(), v.cuda(), True, SC, {"bn": 64})
+    o2, l2 = U.run(qfull.cuda(), k.cuda(), v.cuda(), True, SC, {"bn": 64})
     assert torch.equal(o1, o2[:, Sk - Sq:]) and torch.equal(l1, l2[:, :, Sk - Sq:])
 
 
@@ -92,11 +92,23 @@ def test_rect_schedules_bitwise_identical(B, Sq, Sk, Hq, Hkv, causal):
     U.say(tag)
     st = U.full_parity(q, k, v, bool(causal), SC, tag)
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
-    o1, l1 = U.run(qd, kd, vd, bool(causal), SC)
+    o1, l1 = U.run(qd, kd, vd, bool(causal), SC, {"bn": 64})
     for sched in U.SCHEDULES_D128:
-        o2, l2 = U.run(qd, kd, vd, bool(causal), SC, sched)
+        o2, l2 = U.run(qd, kd, vd, bool(causal), SC, {"schedule": sched, "bn": 64})
         assert torch.equal(o1, o2) and torch.equal(l1, l2), sched
     assert st["finite"]
+
+
+@pytest.mark.parametrize("sched,bn", [(s, bn) for s in ("serial", "serial4") for bn in (32, 128)], ids=str)
+@pytest.mark.parametrize("B,Sq,Sk,Hq,Hkv,causal", RECT, ids=str)
+def test_rect_tile_sizes_against_oracle(B, Sq, Sk, Hq, Hkv, causal, sched, bn):
+    """32- and 128-key tiles of the serial schedules on the rectangular shapes: offsets that are not
+    multiples of the tile, a single partial tile (Sk 40, 63), and Sk 64 (two 32-key tiles, or half of one
+    128-key tile)."""
+    q, k, v = cpu_qkv(B, Sq, Sk, Hq, Hkv, seed=61 + Sq + Sk)
+    tag = "rect %s bn%d B%d Sq%d Sk%d Hq%d Hkv%d causal%d" % (sched, bn, B, Sq, Sk, Hq, Hkv, causal)
+    U.say(tag)
+    U.full_parity(q, k, v, bool(causal), SC, tag, {"schedule": sched, "bn": bn})
 
 
 def test_ex_validation_launches_nothing():

@@ -245,46 +245,53 @@ def test_schedules_bitwise_identical(B, S, Hq, Hkv, causal):
     q, k, v = cpu_qkv(B, S, Hq, Hkv, seed=90 + S)
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
     U.say("schedules B%d S%d Hq%d Hkv%d causal%d" % (B, S, Hq, Hkv, causal))
-    o1, l1 = U.run(qd, kd, vd, bool(causal), SC)
+    o1, l1 = U.run(qd, kd, vd, bool(causal), SC, {"bn": 64})
     for sched in U.SCHEDULES_D128:
-        o2, l2 = U.run(qd, kd, vd, bool(causal), SC, sched)
+        o2, l2 = U.run(qd, kd, vd, bool(causal), SC, {"schedule": sched, "bn": 64})
         assert torch.equal(o1, o2) and torch.equal(l1, l2), sched
 
 
 @pytest.mark.parametrize("B,S,Hq,Hkv,causal", [(1, 700, 8, 2, 1), (2, 257, 12, 3, 0)], ids=str)
 def test_all_variants_bitwise_identical(B, S, Hq, Hkv, causal):
-    """Every point of the searched variant space (schedule x prefetch depth x workgroup order) gives the
-    same bits as the default."""
+    """Every point of the searched variant space of one tile size (schedule x prefetch depth x workgroup
+    order x placement) gives the same bits: 64-key tiles over every schedule, and 32- and 128-key tiles over
+    the serial schedules, each against its own first point."""
     q, k, v = cpu_qkv(B, S, Hq, Hkv, seed=95 + S)
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
-    o1, l1 = U.run(qd, kd, vd, bool(causal), SC)
-    for sched in U.SCHEDULES_D128:
-        for ring in (2, 4):
-            for xcd in (0, 1):
-                for lpt in (0, 1):
-                    for place in (binding.PLACES if sched == "wide" else ("even",)):
-                        var = {"schedule": sched, "ring": ring, "xcd": xcd, "lpt": lpt, "place": place}
-                        o2, l2 = U.run(qd, kd, vd, bool(causal), SC, var)
-                        assert torch.equal(o1, o2) and torch.equal(l1, l2), var
+    for bn in (64, 32, 128):
+        scheds = U.SCHEDULES_D128 if bn == 64 else ("serial", "serial4")
+        o1, l1 = U.run(qd, kd, vd, bool(causal), SC, {"schedule": "serial", "bn": bn})
+        for sched in scheds:
+            for ring in (2, 4):
+                for xcd in (0, 1):
+                    for lpt in (0, 1):
+                        for place in (binding.PLACES if sched == "wide" else ("even",)):
+                            var = {"schedule": sched, "ring": ring, "xcd": xcd, "lpt": lpt, "place": place,
+                                   "bn": bn}
+                            o2, l2 = U.run(qd, kd, vd, bool(causal), SC, var)
+                            assert torch.equal(o1, o2) and torch.equal(l1, l2), var
 
 
-# Every compiled D = 128 kernel instance (schedule x ring depth x softmax placement) on its own against the
-# oracle, causal with ragged tails and non-causal, so a fault confined to one instance is named.
-INSTANCES = [(sched, ring, place) for sched in U.SCHEDULES_D128 for ring in (2, 4)
-             for place in (binding.PLACES if sched == "wide" else ("even",))]
+# Every compiled D = 128 kernel instance (schedule x ring depth x softmax placement x keys per tile) on its
+# own against the oracle, causal with ragged tails and non-causal, so a fault confined to one instance is
+# named.
+INSTANCES = ([(sched, ring, place, 64) for sched in U.SCHEDULES_D128 for ring in (2, 4)
+              for place in (binding.PLACES if sched == "wide" else ("even",))] +
+             [(sched, ring, "even", bn) for sched in ("serial", "serial4") for ring in (2, 4) for bn in (32, 128)])
 
 
-@pytest.mark.parametrize("sched,ring,place", INSTANCES, ids=lambda x: str(x))
+@pytest.mark.parametrize("sched,ring,place,bn", INSTANCES, ids=lambda x: str(x))
 # GQA ratios 4, 3, 2 and 8: the 64-row kernel's workgroups then take 4 heads, 1 head x 256 rows, 2 heads x 128
 # rows, and 4 of 8 heads (two workgroups per KV head)
 @pytest.mark.parametrize("B,S,Hq,Hkv,causal", [(1, 650, 8, 2, 1), (2, 201, 12, 4, 0), (1, 300, 4, 2, 1),
                                                (1, 333, 16, 2, 1)], ids=str)
-def test_every_instance_against_oracle(B, S, Hq, Hkv, causal, sched, ring, place):
-    tag = "instance %s ring%d %s B%d S%d Hq%d Hkv%d causal%d" % (sched, ring, place, B, S, Hq, Hkv, causal)
+def test_every_instance_against_oracle(B, S, Hq, Hkv, causal, sched, ring, place, bn):
+    tag = "instance %s ring%d %s bn%d B%d S%d Hq%d Hkv%d causal%d" % (sched, ring, place, bn, B, S, Hq, Hkv,
+                                                                      causal)
     U.say(tag)
     q, k, v = cpu_qkv(B, S, Hq, Hkv, seed=300 + S + Hq)
     U.full_parity(q, k, v, bool(causal), SC, tag,
-                  {"schedule": sched, "ring": ring, "xcd": 1, "lpt": 1, "place": place})
+                  {"schedule": sched, "ring": ring, "xcd": 1, "lpt": 1, "place": place, "bn": bn})
 
 
 def tuned_entries():
@@ -294,11 +301,12 @@ def tuned_entries():
 
     from dnn_compiler_pipelining_amd import build
     text = open(os.path.join(build.CSRC, "tuned_table.h")).read()
-    rows = re.findall(r"\{(\d+), (\d+), (\d+), (\d+), (\d+), \{SCHEDULE_(\w+), (\d), (\d), (\d), PLACE_(\w+)\}",
-                      text)
+    rows = re.findall(r"\{(\d+), (\d+), (\d+), (\d+), (\d+), \{SCHEDULE_(\w+), (\d), (\d), (\d), PLACE_(\w+), "
+                      r"(\d+)\}", text)
     assert rows
     return [tuple(int(x) for x in r[:5]) + ({"schedule": r[5].lower(), "ring": int(r[6]), "xcd": int(r[7]),
-                                             "lpt": int(r[8]), "place": r[9].lower()},) for r in rows]
+                                             "lpt": int(r[8]), "place": r[9].lower(), "bn": int(r[10])},)
+            for r in rows]
 
 
 @pytest.mark.parametrize("entry", tuned_entries(), ids=lambda e: "B%d_S%d_Hq%d" % (e[0], e[1], e[3]))
