@@ -40,7 +40,8 @@ bool choose_variant(const Request& r, int B, int Sq, int Sk, int Hq, int Hkv, in
   if (r.ring >= 0) v.ring = r.ring;
   if (r.xcd >= 0) v.xcd = r.xcd;
   if (r.lpt >= 0) v.lpt = r.lpt;
-  if (v.schedule != libattn::SCHEDULE_WIDE) v.place = libattn::PLACE_EVEN;  // the only placement they have
+  if (v.schedule != libattn::SCHEDULE_WIDE && v.schedule != libattn::SCHEDULE_OVERLAP)
+    v.place = libattn::PLACE_EVEN;  // the only placement they have
   if (r.place >= 0) v.place = r.place;
   if (D != 128 || (v.schedule != libattn::SCHEDULE_SERIAL && v.schedule != libattn::SCHEDULE_SERIAL4))
     v.bn = libattn::BN_STD;

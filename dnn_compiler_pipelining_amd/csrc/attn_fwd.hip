@@ -96,6 +96,20 @@ constexpr int reads_of(int mode, int i, int nkk, int ndb, int nsb = 2) {
   return step_of(mode, i, nkk, ndb, nsb).pv ? 2 : 1;
 }
 
+// Placement of the ne exponential parts of the overlap schedule among the
+// nsteps MFMAs of its block: the step before whose MFMA part e runs.
+//   PLACE_EVEN : spread evenly over the block
+//   PLACE_FRONT: parts 0..4 before the first MFMA, where the block waits for
+//                its first fragments, the rest spread over steps 1..nsteps-1
+//   PLACE_EARLY: spread over all but the last four steps, so that the sum
+//                check that follows the block has its inputs in time
+// The map is non-decreasing in e, so the parts keep their order.
+constexpr int e_step(int place, int e, int nsteps, int ne) {
+  return place == PLACE_FRONT   ? (e < 5 ? 0 : 1 + (e - 5) * (nsteps - 2) / (ne - 1 - 5))
+         : place == PLACE_EARLY ? e * (nsteps - 5) / (ne - 1)
+                                : e * (nsteps - 1) / (ne - 1);
+}
+
 // kSched: tile schedule; kRing: depth of the fragment prefetch ring of the mma
 // steps (how many steps ahead the LDS reads run); kHD: head dimension.  The
 // overlap and ping-pong schedules are written for HD 128.  A SERIAL4
@@ -116,7 +130,11 @@ constexpr int reads_of(int mode, int i, int nkk, int ndb, int nsb = 2) {
 // check -- are spread over twice the keys, with 32 the causal diagonal wastes
 // less).  Per tile the softmax runs the same parts over more or fewer scores;
 // a row's results differ from BN 64's only by rounding order.
-template <int kSched, int kRing, int kHD, bool kSplit = false, int kBN = BN>
+//
+// kPlace: placement of the softmax parts in the overlap schedule's block
+// (e_step); the other schedules have PLACE_EVEN only.  Every placement runs
+// the same parts in the same order, so the results are the same bits.
+template <int kSched, int kRing, int kHD, bool kSplit = false, int kBN = BN, int kPlace = PLACE_EVEN>
 __global__ __launch_bounds__(64 * waves_of(kSched), wgs_per_cu(kSched, kHD, kBN))
 void attn_fwd_kernel(Params p) {
   using G = Geo<kHD, kBN>;
@@ -126,6 +144,7 @@ void attn_fwd_kernel(Params p) {
   static_assert(!kSplit || kSched == SCHEDULE_SERIAL4, "split-KV mode runs the SERIAL4 schedule");
   static_assert(kBN == BN || ((kSched == SCHEDULE_SERIAL || kSched == SCHEDULE_SERIAL4) && kHD == 128 && !kSplit),
                 "32- and 128-key tiles: the serial schedules at HD 128");
+  static_assert(kPlace == PLACE_EVEN || kSched == SCHEDULE_OVERLAP, "placements: the overlap schedule");
   constexpr int NW = waves_of(kSched);
   constexpr int K_SLOTS = k_slots_of(kSched, kBN);
   constexpr int HD = G::HD, NKK = G::NKK, NDB = G::NDB;
@@ -631,13 +650,13 @@ void attn_fwd_kernel(Params p) {
       SmState nx;  // tile j+1
       if constexpr (kQK) sm_lim(j + 1, mask_x, nx);
       sm_start(cur);
-      // E part e runs before MFMA floor(e * (nsteps - 1) / 33) of the block;
-      // C, the rare X / D / E redo and F follow the block.
+      // E part e runs before MFMA e_step(kPlace, e, nsteps, SM_E) of the
+      // block; C, the rare X / D / E redo and F follow the block.
       constexpr int nsteps = kQK ? steps_of(kPV ? 3 : 2, NKK, NDB) : steps_of(1, NKK, NDB);
       auto sm = [&](auto ic) INL {
         constexpr int i = decltype(ic)::value;
         static_for<SM_E>([&](auto ec) INL {
-          if constexpr (decltype(ec)::value * (nsteps - 1) / (SM_E - 1) == i) sm_e(ec, sc, pc, mask_e, cur);
+          if constexpr (e_step(kPlace, decltype(ec)::value, nsteps, SM_E) == i) sm_e(ec, sc, pc, mask_e, cur);
         });
       };
       if constexpr (kPV && kQK) {
@@ -769,6 +788,8 @@ hipError_t launch_attn_fwd(const Params& p, hipStream_t stream) {
 #define LIBATTN_LAUNCH_BN(S, R, N) \
   hipLaunchKernelGGL((attn_fwd_kernel<S, R, 128, false, N>), grid, block, 0, stream, p)
   if (p.ring != 2 && p.ring != 4) return hipErrorInvalidValue;
+  if (p.place != PLACE_EVEN && (p.schedule != SCHEDULE_OVERLAP || p.bn != BN || p.hd != 128))
+    return hipErrorInvalidValue;
   const bool r2 = p.ring == 2;
   if (p.bn != BN) {  // 32- and 128-key tiles: the serial schedules at HD 128
     if (p.hd != 128 || (p.bn != 32 && p.bn != 128) ||
@@ -812,8 +833,19 @@ hipError_t launch_attn_fwd(const Params& p, hipStream_t stream) {
   } else if (p.hd != 128) {
     return hipErrorInvalidValue;
   } else if (p.schedule == SCHEDULE_OVERLAP) {
-    if (r2) LIBATTN_LAUNCH(SCHEDULE_OVERLAP, 2, 128);
-    else LIBATTN_LAUNCH(SCHEDULE_OVERLAP, 4, 128);
+#define LIBATTN_LAUNCH_PL(R, P) \
+  hipLaunchKernelGGL((attn_fwd_kernel<SCHEDULE_OVERLAP, R, 128, false, BN, P>), grid, block, 0, stream, p)
+    if (p.place == PLACE_FRONT) {
+      if (r2) LIBATTN_LAUNCH_PL(2, PLACE_FRONT);
+      else LIBATTN_LAUNCH_PL(4, PLACE_FRONT);
+    } else if (p.place == PLACE_EARLY) {
+      if (r2) LIBATTN_LAUNCH_PL(2, PLACE_EARLY);
+      else LIBATTN_LAUNCH_PL(4, PLACE_EARLY);
+    } else {
+      if (r2) LIBATTN_LAUNCH(SCHEDULE_OVERLAP, 2, 128);
+      else LIBATTN_LAUNCH(SCHEDULE_OVERLAP, 4, 128);
+    }
+#undef LIBATTN_LAUNCH_PL
   } else if (p.schedule == SCHEDULE_PINGPONG) {
     if (r2) LIBATTN_LAUNCH(SCHEDULE_PINGPONG, 2, 128);
     else LIBATTN_LAUNCH(SCHEDULE_PINGPONG, 4, 128);

@@ -39,7 +39,7 @@ struct Params {
   int xcd;           // 1: give each XCD whole (batch, kv head) groups
   int lpt;           // 1: longest causal query tiles of a group first
   int hpw;           // WIDE: query heads per workgroup (4, 2 or 1; 256 / hpw query rows each)
-  int place;         // WIDE: Place of the softmax parts (variant.h)
+  int place;         // WIDE and OVERLAP: Place of the softmax parts (variant.h)
   int bn;            // keys per K/V tile: 64; SERIAL and SERIAL4 at HD 128 also 32 or 128
   // split-KV mode (attn_fwd_decode): n_qt counts 128-row tiles of the packed
   // (head, query row) rows of a KV group; the keys are cut into n_splits

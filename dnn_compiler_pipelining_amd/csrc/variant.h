@@ -42,14 +42,17 @@ enum Schedule {
   SCHEDULE_WIDE = 4
 };
 
-// Placements of the softmax parts among the MFMAs of the 64-row schedule's
-// fused block (the other schedules have one placement, PLACE_EVEN):
-//   PLACE_EVEN : each half's parts spread evenly over its 32 steps
-//   PLACE_FRONT: query half 0's first five parts before the first MFMA, where
-//                the block waits for its first fragment, the rest spread
-//   PLACE_EARLY: half 1's parts end four steps before the block, so that its
-//                sum check is settled when the block ends; each fp16 pack is
-//                held at its step (not sunk to its first use)
+// Placements of the softmax parts among the MFMAs of the fused block of the
+// 64-row schedule (WIDE) and of the overlap schedule (the other schedules
+// have one placement, PLACE_EVEN):
+//   PLACE_EVEN : the parts spread evenly over the block's steps
+//   PLACE_FRONT: the first five parts (WIDE: of query half 0) before the
+//                first MFMA, where the block waits for its first fragment,
+//                the rest spread
+//   PLACE_EARLY: the parts (WIDE: of half 1) end four steps before the
+//                block, so that the sum check is settled when the block
+//                ends; WIDE also holds each fp16 pack at its step (not sunk
+//                to its first use)
 enum Place { PLACE_EVEN = 0, PLACE_FRONT = 1, PLACE_EARLY = 2 };
 
 // Keys per K/V tile of every schedule (BN in the kernels); SERIAL and SERIAL4
@@ -61,7 +64,7 @@ struct Variant {
   int ring;      // fragment prefetch depth of the mma steps: 2 or 4
   int xcd;       // 1: each XCD gets whole (batch, kv head) groups
   int lpt;       // 1: longest causal query tiles of a group first
-  int place;     // Place (SCHEDULE_WIDE only; PLACE_EVEN for the others)
+  int place;     // Place (SCHEDULE_WIDE and SCHEDULE_OVERLAP; PLACE_EVEN for the others)
   int bn;        // keys per K/V tile: 64; SERIAL and SERIAL4 also 32 and 128 (head dimension 128)
 };
 
@@ -77,7 +80,8 @@ struct TunedEntry {
 inline bool variant_valid(const Variant& v) {
   return v.schedule >= SCHEDULE_SERIAL && v.schedule <= SCHEDULE_WIDE && (v.ring == 2 || v.ring == 4) &&
          (v.xcd == 0 || v.xcd == 1) && (v.lpt == 0 || v.lpt == 1) && v.place >= PLACE_EVEN &&
-         v.place <= PLACE_EARLY && (v.schedule == SCHEDULE_WIDE || v.place == PLACE_EVEN) &&
+         v.place <= PLACE_EARLY &&
+         (v.schedule == SCHEDULE_WIDE || v.schedule == SCHEDULE_OVERLAP || v.place == PLACE_EVEN) &&
          (v.bn == BN_STD || ((v.bn == 32 || v.bn == 128) &&
                          (v.schedule == SCHEDULE_SERIAL || v.schedule == SCHEDULE_SERIAL4)));
 }

@@ -6,7 +6,7 @@ the hardware's units under a resource check, with measured feedback (page
 "核心方法").  This module does that for libattn's space of kernel variants
 (csrc/variant.h): tile schedule (which also fixes the query rows per wave, 32
 or 64) x fragment-prefetch depth x placement of the softmax parts among the
-MFMAs (64-row schedule) x keys per K/V tile (32, 64 or 128; the serial
+MFMAs (64-row and overlap schedules) x keys per K/V tile (32, 64 or 128; the serial
 schedules) (compile time) x two workgroup-order switches (run time).  Variants
 with the same tile size compute the same bits; the tile size changes the
 rounding order of the online softmax, and every instance is checked against
@@ -35,7 +35,7 @@ TABLE = os.path.join(PKG, "csrc", "tuned_table.h")
 PROFILE = os.path.join(ROOT, "profiles", "schedule_search.json")
 
 SCHEDULES = ("serial", "overlap", "pingpong", "serial4", "wide")  # Schedule enum order in csrc/variant.h
-PLACES = ("even", "front", "early")  # Place enum order in csrc/variant.h; schedules other than wide: even only
+PLACES = ("even", "front", "early")  # Place enum order in csrc/variant.h; wide and overlap, the others even only
 
 
 BNS = (32, 64, 128)  # keys per K/V tile; 32 and 128 for the serial schedules at head dimension 128
@@ -58,10 +58,10 @@ def waves_per_simd(schedule: str, hd: int, bn: int = 64) -> int:
 
 
 def schedule_has(schedule: str, field: str) -> bool:
-    """Whether a schedule has more than one value of a variant field: the placement is the wide schedule's,
-    the tile size the serial schedules'."""
+    """Whether a schedule has more than one value of a variant field: the placement is the wide and overlap
+    schedules', the tile size the serial schedules'."""
     if field == "place":
-        return schedule == "wide"
+        return schedule in ("wide", "overlap")
     if field == "bn":
         return schedule in ("serial", "serial4")
     return True
@@ -107,7 +107,8 @@ def kernel_resources(asm_path: str):
     meta = text[text.index("amdhsa.kernels:"):]
     out = {}
     for block in re.split(r"\n  - ", meta)[1:]:
-        m = re.search(r"\.name:\s+\S*attn_fwd_kernelILi(\d)ELi(\d)ELi(\d+)ELb([01])E(?:Li(\d+)E)?", block)
+        m = re.search(r"\.name:\s+\S*attn_fwd_kernelILi(\d)ELi(\d)ELi(\d+)ELb([01])E(?:Li(\d+)E)?(?:Li(\d)E)?",
+                      block)
         mw = re.search(r"\.name:\s+\S*attn_wide_kernelILi(\d)ELi(\d)E", block)
         if not m and not mw:
             continue
@@ -120,7 +121,7 @@ def kernel_resources(asm_path: str):
             key = ("wide", int(mw.group(1)), 128, PLACES[int(mw.group(2))], 64)
         else:
             key = (SCHEDULES[int(m.group(1))] + ("-split" if m.group(4) == "1" else ""), int(m.group(2)),
-                   int(m.group(3)), "even", int(m.group(5) or 64))
+                   int(m.group(3)), PLACES[int(m.group(6) or 0)], int(m.group(5) or 64))
         sym = re.search(r"\.name:\s+(\S+)", block).group(1)
         out[key] = dict(
             vgpr=num("vgpr_count"), agpr=num("agpr_count"), vgpr_spill=num("vgpr_spill_count"),

@@ -108,19 +108,20 @@ enum {
   ATTN_SCHEDULE_WIDE = 4
 };
 
-/* Placement of the softmax work among the MFMAs of ATTN_SCHEDULE_WIDE's main loop: spread evenly,
- * partly before the first MFMA (where the loop waits for its first operands), or ending early (the
- * sum check settled before the loop's next iteration).  The other schedules have ATTN_PLACE_EVEN only. */
+/* Placement of the softmax work among the MFMAs of the main loop of ATTN_SCHEDULE_WIDE and
+ * ATTN_SCHEDULE_OVERLAP: spread evenly, partly before the first MFMA (where the loop waits for its first
+ * operands), or ending early (the sum check settled before the loop's next iteration).  The other
+ * schedules have ATTN_PLACE_EVEN only. */
 enum { ATTN_PLACE_EVEN = 0, ATTN_PLACE_FRONT = 1, ATTN_PLACE_EARLY = 2 };
 
 /* attn_fwd_ex with an explicit kernel variant, for schedule search and cross-checks: `schedule` is an
  * ATTN_SCHEDULE_* value, `ring` the fragment prefetch depth (2 or 4), `xcd` 1 to give each XCD whole
  * (batch, KV head) groups, `lpt` 1 to run the longest causal query tiles first, `place` an ATTN_PLACE_*
  * value, `bn` the keys per K/V tile (64; 32 or 128 with SERIAL or SERIAL4 at D = 128); -1 in any of them
- * takes the tuned value (place: ATTN_PLACE_EVEN for schedules other than ATTN_SCHEDULE_WIDE; bn: 64 where
- * the schedule or D has no other).  A value that does not exist, a placement or tile size the schedule
- * does not have, or a schedule the head dimension does not run, returns ATTN_ERR_UNSUPPORTED and launches
- * nothing.  Results are bitwise identical for every variant of one tile size; another tile size changes the
+ * takes the tuned value (place: ATTN_PLACE_EVEN for schedules other than ATTN_SCHEDULE_WIDE and
+ * ATTN_SCHEDULE_OVERLAP; bn: 64 where the schedule or D has no other).  A value that does not exist, a
+ * placement or tile size the schedule does not have, or a schedule the head dimension does not run,
+ * returns ATTN_ERR_UNSUPPORTED and launches nothing.  Results are bitwise identical for every variant of one tile size; another tile size changes the
  * rounding order of the online softmax. */
 int attn_fwd_variant(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Sq, int Sk, int Hq,
                      int Hkv, int D, int causal, float scale, int schedule, int ring, int xcd, int lpt, int place,

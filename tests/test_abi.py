@@ -226,7 +226,7 @@ def test_tuned_variant_reports_a_runnable_variant(lib):
         v = L.attn_tuned_variant(B, S, S, Hq, Hkv, D)
         assert set(v) == {"schedule", "ring", "xcd", "lpt", "place", "bn"}
         assert v["schedule"] in L.SCHEDULES and v["ring"] in (2, 4) and v["xcd"] in (0, 1) and v["lpt"] in (0, 1)
-        assert v["place"] in L.PLACES and (v["schedule"] == "wide" or v["place"] == "even")
+        assert v["place"] in L.PLACES and (v["schedule"] in ("wide", "overlap") or v["place"] == "even")
         assert v["bn"] == 64 or (v["bn"] in (32, 128) and v["schedule"] in ("serial", "serial4") and D == 128)
         if D != 128:
             assert v["schedule"] in ("serial", "serial4")  # the only schedules D = 64 and 256 run
@@ -252,14 +252,16 @@ def test_static_decode_validates_before_any_hip_call(lib):
     assert L.attn_fwd_decode_static(0, KP, VP, OP, LP, 1, 128, 8192, 64, 8, 256, 1, 0.06, None) == L.ATTN_ERR_NULL
 
 
-def test_variant_placements_outside_the_wide_schedule_are_rejected(lib):
+def test_variant_placements_outside_the_wide_and_overlap_schedules_are_rejected(lib):
     # rejected while choosing the variant, before any HIP call (the pointers are never used)
     def var(schedule, place, D=128, ring=-1):
         return L.attn_fwd_variant(QP, KP, VP, OP, LP, 1, 64, 64, 8, 2, D, 1, 0.088, schedule, ring, -1, -1, place, -1,
                                   None)
-    for sched in ("serial", "overlap", "pingpong", "serial4"):
+    for sched in ("serial", "pingpong", "serial4"):
         for place in ("front", "early"):
             assert var(L.SCHEDULES[sched], L.PLACES[place]) == L.ATTN_ERR_UNSUPPORTED, (sched, place)
+    assert var(L.SCHEDULES["overlap"], 3) == L.ATTN_ERR_UNSUPPORTED
+    assert var(L.SCHEDULES["overlap"], L.PLACES["front"], D=64) == L.ATTN_ERR_UNSUPPORTED
     assert var(L.SCHEDULES["wide"], 3) == L.ATTN_ERR_UNSUPPORTED
     assert var(L.SCHEDULES["wide"], L.PLACES["front"], ring=3) == L.ATTN_ERR_UNSUPPORTED
     assert var(L.SCHEDULES["wide"], L.PLACES["early"], D=64) == L.ATTN_ERR_UNSUPPORTED

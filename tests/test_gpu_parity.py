@@ -265,7 +265,7 @@ def test_all_variants_bitwise_identical(B, S, Hq, Hkv, causal):
             for ring in (2, 4):
                 for xcd in (0, 1):
                     for lpt in (0, 1):
-                        for place in (binding.PLACES if sched == "wide" else ("even",)):
+                        for place in (binding.PLACES if sched in ("wide", "overlap") else ("even",)):
                             var = {"schedule": sched, "ring": ring, "xcd": xcd, "lpt": lpt, "place": place,
                                    "bn": bn}
                             o2, l2 = U.run(qd, kd, vd, bool(causal), SC, var)
@@ -276,7 +276,7 @@ def test_all_variants_bitwise_identical(B, S, Hq, Hkv, causal):
 # own against the oracle, causal with ragged tails and non-causal, so a fault confined to one instance is
 # named.
 INSTANCES = ([(sched, ring, place, 64) for sched in U.SCHEDULES_D128 for ring in (2, 4)
-              for place in (binding.PLACES if sched == "wide" else ("even",))] +
+              for place in (binding.PLACES if sched in ("wide", "overlap") else ("even",))] +
              [(sched, ring, "even", bn) for sched in ("serial", "serial4") for ring in (2, 4) for bn in (32, 128)])
 
 

@@ -18,7 +18,7 @@ def test_every_compiled_variant_is_valid():
     vs = tune.valid_variants()
     rejected = {("serial", r, 128, "even", 128) for r in tune.RINGS}
     assert set(vs) == ({(s, r, 128, "even", 64) for s in tune.SCHEDULES if s != "wide" for r in tune.RINGS} |
-                       {("wide", r, 128, pl, 64) for r in tune.RINGS for pl in tune.PLACES} |
+                       {(s, r, 128, pl, 64) for s in ("wide", "overlap") for r in tune.RINGS for pl in tune.PLACES} |
                        {(s, r, 128, "even", bn) for s in ("serial", "serial4") for r in tune.RINGS
                         for bn in (32, 128)} |
                        {(s, r, 64, "even", 64) for s in ("serial", "serial4") for r in tune.RINGS} |
@@ -80,11 +80,12 @@ def test_check_valid_serial4_with_128_key_tiles_runs_one_workgroup_per_cu():
 
 def test_greedy_search_covers_each_schedules_own_fields():
     """A synthetic rate table: the wide schedule is fastest, but the serial schedules are still searched
-    over their tile sizes and the wide one over its placements; invalid points are never timed."""
+    over their tile sizes and the wide and overlap ones over their placements; invalid points are never
+    timed."""
     def rate_of(pt):
         base = {"serial": 100.0, "overlap": 110.0, "pingpong": 105.0, "serial4": 120.0, "wide": 200.0}[pt["schedule"]]
         base *= {32: 1.1, 64: 1.0, 128: 0.9}[pt["bn"]] if pt["schedule"] in ("serial", "serial4") else 1.0
-        base *= {"even": 1.0, "front": 1.02, "early": 1.05}[pt["place"]] if pt["schedule"] == "wide" else 1.0
+        base *= {"even": 1.0, "front": 1.02, "early": 1.05}[pt["place"]] if pt["schedule"] in ("wide", "overlap") else 1.0
         return base * (1.01 if pt["ring"] == 2 else 1.0)
 
     timed = []
@@ -103,7 +104,9 @@ def test_greedy_search_covers_each_schedules_own_fields():
     for sched in ("serial", "serial4"):
         assert {pt["bn"] for pt in timed if pt["schedule"] == sched} == ({32, 64} if sched == "serial" else {32, 64, 128})
         assert {pt["place"] for pt in timed if pt["schedule"] == sched} == {"even"}
-    assert {pt["place"] for pt in timed if pt["schedule"] == "wide"} == set(tune.PLACES)
+    for sched in ("wide", "overlap"):
+        assert {pt["place"] for pt in timed if pt["schedule"] == sched} == set(tune.PLACES)
+    assert {pt["place"] for pt in timed if pt["schedule"] == "pingpong"} == {"even"}
     assert {pt["bn"] for pt in timed if pt["schedule"] != "serial" and pt["schedule"] != "serial4"} == {64}
 
 
