@@ -45,6 +45,9 @@ fields, with metric FLOPs 2*M*N*K and the fp64 GEMM oracle as cpu_baseline.
 `--workload llama3-70b_decode_b64_s8192` times the split-KV decode path
 (attn_fwd_decode: split kernel + combine kernel per step) and reports HBM
 GB/s (K, V, Q, O and LSE once) against the 8 TB/s HBM roofline.
+`--variants` prints one line per attention variant shape (inputs.VARIANT_SHAPES: non-causal, sequence
+lengths off the tiles, chunked prefill, head dimensions 64 and 256), FLOPs counted exactly as 4*D per
+computed (query, key) pair.
 `--all` prints one line per attention, GEMM and decode workload.  Without --steps / --warmup, and
 under --all, each workload gets at least about 0.25 s of warmup and 0.25 s of timed launches (20
 and 3 for the long ones, more launches for the short ones, reported in the line), so that its
@@ -67,6 +70,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "causal attention fwd TFLOP/s (fp16) + % of MFMA peak, LLaMA3 shapes"
+VARIANT_METRIC = "attention fwd TFLOP/s (fp16), 4*D FLOPs per computed (query, key) pair"
 PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, published
 DEFAULT_WORKLOAD = "llama3-70b_b64_s8192"
 KERNEL_NAME = "attn_fwd_kernel"
@@ -248,6 +252,44 @@ def time_workload(w, steps: int, warmup: int, pmc_copy: int = 0, variant=None):
     ok = bool(torch.isfinite(o[-1, -1]).all().item()) and bool(torch.isfinite(lse[-1, -1]).all().item())
     if pmc_copy:
         calibration_copy(pmc_copy)
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
+    return wall_ms, kernel_ms, ok
+
+
+def time_variant(w, steps: int, warmup: int):
+    """Time one attention variant shape (inputs.VariantShape): HIP events on the launch stream around
+    `steps` launches after `warmup`.  Returns (wall ms, kernel ms per launch, finite output)."""
+    import torch
+
+    from dnn_compiler_pipelining_amd import binding, inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log("[bench] %s: generating seeded inputs" % w.name)
+    q, k, v = inputs.make_variant_inputs(w, dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    torch.cuda.synchronize()
+
+    def step():
+        binding.forward(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    kernel_ms = e0.elapsed_time(e1) / steps
+    ok = bool(torch.isfinite(o).all().item()) and bool(torch.isfinite(lse).all().item())
     del q, k, v, o, lse
     torch.cuda.empty_cache()
     return wall_ms, kernel_ms, ok
@@ -627,6 +669,8 @@ def main():
                     help="untimed launches before them (default: 3, or more for short workloads, about 0.25 s)")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--all", action="store_true", help="one line per workload (parity-test configurations too)")
+    ap.add_argument("--variants", action="store_true",
+                    help="one line per attention variant shape (non-causal, ragged S, chunked prefill, D 64 / 256)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-config", action="store_true",
                     help="time only the named workload (profiling runs: no other configuration's launches)")
@@ -661,11 +705,33 @@ def main():
              [w.name for w in inputs.DECODE_WORKLOADS]) if args.all else [args.workload]
 
     def counts(est_ms: float):
-        return launch_counts(est_ms, args.steps, args.warmup, args.all)
+        return launch_counts(est_ms, args.steps, args.warmup, args.all or args.variants)
 
     peak = mfma_peak()
     log("[bench] dense fp16 MFMA peak: %.1f TFLOP/s = %s (published %.0f)" %
         (peak["tflops"], peak["derivation"], PEAK_TFLOPS))
+    if args.variants:
+        from dnn_compiler_pipelining_amd import binding
+
+        for w in inputs.VARIANT_SHAPES:
+            steps, warmup = counts(w.flops / 8e11)
+            wall_ms, kernel_ms, ok = time_variant(w, steps, warmup)
+            if not ok:
+                log("[bench] non-finite output in %s" % w.name)
+                return 1
+            value = w.flops / (wall_ms * 1e-3) / 1e12
+            achieved = w.flops / (kernel_ms * 1e-3) / 1e12
+            line = {"metric": VARIANT_METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+                    "steps": steps, "warmup": warmup, "ms_per_step": round(wall_ms, 4), "higher_is_better": True,
+                    "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+                    "data": "synthetic: seeded i.i.d. N(0,1) fp16 Q/K/V",
+                    "pct_of_mfma_peak": round(100.0 * value / peak["tflops"], 2), "config": w.describe(),
+                    "kernel_ms": round(kernel_ms, 4), "kernel_tflops": round(achieved, 2),
+                    "flops_per_launch": w.flops,
+                    "variant": binding.attn_tuned_variant(w.B, w.Sq, w.Sk, w.Hq, w.Hkv, w.D),
+                    "device": device_info()}
+            print(json.dumps(line), flush=True)
+        return 0
     for name in names:
         if is_decode(name):
             w = inputs.DECODE_BY_NAME[name]

@@ -232,3 +232,77 @@ def make_decode_inputs(w: DecodeWorkload, device="cpu"):
     """(q, k, v): [B,Sq,Hq,D], [B,Sk,Hkv,D], [B,Sk,Hkv,D] fp16."""
     return (make_tensor(w.B, w.Sq, w.Hq, w.D, w.seed, Q, device), make_tensor(w.B, w.Sk, w.Hkv, w.D, w.seed, K, device),
             make_tensor(w.B, w.Sk, w.Hkv, w.D, w.seed, V, device))
+
+
+# ---------------------------------------------------------------- attention variants at the same boundary
+#
+# Shapes of the variants the same entry points serve beyond the causal square workloads: non-causal,
+# sequence lengths off the tile sizes, chunked prefill (Sq < Sk, bottom-right causal mask) and head
+# dimensions 64 and 256, at the workloads' head counts.  `bench.py --variants` times them; the GPU
+# tests check sampled rows of each against the oracle.  Same recipe as above; the scale is the fp32
+# value of 1/sqrt(D).
+
+def scale_for(D: int) -> float:
+    """fp32 value of 1/sqrt(D) for D in {64, 128, 256}."""
+    return {64: 0.125, 128: SCALE_D128, 256: 0.0625}[D]
+
+
+@dataclass(frozen=True)
+class VariantShape:
+    name: str
+    B: int
+    Sq: int
+    Sk: int
+    Hq: int
+    Hkv: int
+    D: int
+    causal: bool
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        return scale_for(self.D)
+
+    @property
+    def pairs(self) -> int:
+        """(query, key) pairs a (batch, head) computes: Sq * Sk, or under the bottom-right causal mask the
+        sum over rows i of min(Sk, i + Sk - Sq + 1)."""
+        if not self.causal:
+            return self.Sq * self.Sk
+        off = self.Sk - self.Sq
+        return sum(min(self.Sk, i + off + 1) for i in range(self.Sq))
+
+    @property
+    def flops(self) -> float:
+        """4 * D FLOPs per computed (query, key) pair (QK^T and PV), over all batch entries and heads."""
+        return 4.0 * self.D * self.B * self.Hq * self.pairs
+
+    def describe(self) -> dict:
+        return {"workload": self.name, "B": self.B, "Sq": self.Sq, "Sk": self.Sk, "Hq": self.Hq, "Hkv": self.Hkv,
+                "D": self.D, "causal": self.causal, "layout": "[B,S,H,D] fp16 in/out, LSE [B,Hq,Sq] fp32",
+                "scale": self.scale, "seed": self.seed}
+
+
+VARIANT_SHAPES = [
+    VariantShape("llama3-70b_b16_s8192_noncausal", 16, 8192, 8192, 64, 8, 128, False, 61),
+    VariantShape("llama3-70b_b64_s8000", 64, 8000, 8000, 64, 8, 128, True, 62),
+    VariantShape("llama3-8b_b64_s2000", 64, 2000, 2000, 32, 8, 128, True, 63),
+    VariantShape("llama3-70b_b64_chunk2048_of_8192", 64, 2048, 8192, 64, 8, 128, True, 64),
+    VariantShape("d64_b16_s8192", 16, 8192, 8192, 32, 8, 64, True, 65),
+    VariantShape("d64_b16_s8192_noncausal", 16, 8192, 8192, 32, 8, 64, False, 66),
+    VariantShape("d256_b16_s8192", 16, 8192, 8192, 32, 8, 256, True, 67),
+    VariantShape("d256_b16_s8192_noncausal", 16, 8192, 8192, 32, 8, 256, False, 68),
+]
+VARIANT_BY_NAME = {w.name: w for w in VARIANT_SHAPES}
+
+
+def make_variant_inputs(w: VariantShape, device="cpu"):
+    """(q, k, v): [B,Sq,Hq,D], [B,Sk,Hkv,D], [B,Sk,Hkv,D] fp16."""
+    return (make_tensor(w.B, w.Sq, w.Hq, w.D, w.seed, Q, device), make_tensor(w.B, w.Sk, w.Hkv, w.D, w.seed, K, device),
+            make_tensor(w.B, w.Sk, w.Hkv, w.D, w.seed, V, device))
+
+
+def make_variant_batch_cpu(w: VariantShape, b: int):
+    """(q, k, v) of batch entry b on the CPU: [Sq,Hq,D], [Sk,Hkv,D], [Sk,Hkv,D] fp16."""
+    return (make_slice(w.Sq, w.Hq, w.D, w.seed, Q, b), make_slice(w.Sk, w.Hkv, w.D, w.seed, K, b),
+            make_slice(w.Sk, w.Hkv, w.D, w.seed, V, b))

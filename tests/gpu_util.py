@@ -126,6 +126,33 @@ def slice_parity(w: inputs.Workload, q, k, v, o, lse, b: int, h: int, tag=""):
     return st
 
 
+def sampled_parity_shape(w: inputs.VariantShape, q, k, v, o, lse, batches, heads, n_random=64, tag=""):
+    """sampled_parity for a variant shape (Sq query rows against Sk keys): sampled (batch, head, row)
+    outputs of a full-size run against the oracle, which regenerates each batch entry on the CPU from its
+    seed and checks that it is what the GPU read."""
+    rng = np.random.default_rng(w.seed)
+    rows = sample_rows(w.Sq, rng, n_random)
+    hs = np.repeat(np.array(heads, dtype=np.int32), len(rows))
+    rs = np.tile(np.array(rows, dtype=np.int32), len(heads))
+    allst = []
+    for b in batches:
+        qb, kb, vb = inputs.make_variant_batch_cpu(w, b)
+        assert torch.equal(qb, q[b].cpu()) and torch.equal(kb, k[b].cpu()) and torch.equal(vb, v[b].cpu())
+        O, L = oracle_mod.attn_rows(qb.numpy(), kb.numpy(), vb.numpy(), hs, rs, w.causal, w.scale)
+        rows_t = torch.as_tensor(rs, dtype=torch.long, device=o.device)
+        heads_t = torch.as_tensor(hs, dtype=torch.long, device=o.device)
+        allst.append(stats(o[b][rows_t, heads_t].cpu().numpy(), lse[b][heads_t, rows_t].cpu().numpy(), O, L))
+    n = sum(s["n"] for s in allst)
+    worst = max(range(len(allst)), key=lambda x: allst[x]["max_o"])
+    si, d = allst[worst]["argmax_o"] if allst[worst]["argmax_o"] else (0, 0)
+    st = dict(finite=all(s["finite"] for s in allst), max_o=max(s["max_o"] for s in allst),
+              mean_o=sum(s["mean_o"] * s["n"] for s in allst) / n, max_lse=max(s["max_lse"] for s in allst), n=n,
+              p9999_o=max(s["p9999_o"] for s in allst),  # the largest per-batch 99.99th percentile
+              argmax_o=(batches[worst], int(rs[si]), int(hs[si]), int(d)))  # (b, row, head, d)
+    check(st, tag)
+    return st
+
+
 def batch_entries_parity(w: inputs.Workload, q, k, v, o, lse, batches, tag=""):
     """Every output (all rows, heads and d) of the given batch entries of a full-size run against the
     oracle, the bar applied to all of them together.  The oracle regenerates each batch entry on the CPU

@@ -38,3 +38,23 @@ def test_fingerprint_separates_attention_and_gemm_sources():
     fg = bench.kernel_fingerprint("gemm_8k_nt")
     assert len(fa) == 16 and len(fg) == 16 and fa != fg
     assert bench.kernel_fingerprint("llama3-8b_b64_s2048") == fa
+
+
+def test_variant_shape_pairs_match_a_brute_force_mask():
+    """The FLOP count of the variant lines: (query, key) pairs under the bottom-right causal mask (query
+    row i sees keys 0..i + Sk - Sq), counted on an explicit mask, and Sq * Sk without it."""
+    import numpy as np
+
+    from dnn_compiler_pipelining_amd import inputs
+
+    for Sq, Sk in ((1, 1), (1, 64), (7, 200), (100, 100), (129, 700), (300, 301)):
+        i = np.arange(Sq)[:, None]
+        j = np.arange(Sk)[None, :]
+        mask = j <= i + (Sk - Sq)
+        w = inputs.VariantShape("t", 2, Sq, Sk, 8, 2, 128, True, 0)
+        assert w.pairs == int(mask.sum()), (Sq, Sk)
+        assert inputs.VariantShape("t", 2, Sq, Sk, 8, 2, 128, False, 0).pairs == Sq * Sk
+        assert w.flops == 4.0 * 128 * 2 * 8 * int(mask.sum())
+    assert {w.D for w in inputs.VARIANT_SHAPES} == {64, 128, 256}
+    assert any(not w.causal for w in inputs.VARIANT_SHAPES) and any(w.Sq < w.Sk for w in inputs.VARIANT_SHAPES)
+    assert [inputs.scale_for(D) for D in (64, 128, 256)] == [0.125, inputs.SCALE_D128, 0.0625]

@@ -117,6 +117,26 @@ def test_b64_s8192_whole_batch_entry(b):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("name", [w.name for w in inputs.VARIANT_SHAPES])
+def test_variant_shapes_full_size_sampled(name):
+    """The attention variant shapes the bench times (non-causal, sequence lengths off the tiles, chunked
+    prefill, D = 64 and 256), at full size in the tuned launch: every output finite and |O| within
+    max |V|, and sampled rows of every fifth head of the first and last batch entries against the
+    oracle."""
+    w = inputs.VARIANT_BY_NAME[name]
+    U.say("variant shape %s (full size, sampled rows)" % w.name)
+    q, k, v = inputs.make_variant_inputs(w, "cuda")
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full((w.B, w.Hq, w.Sq), float("nan"), dtype=torch.float32, device=q.device)
+    binding.forward(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
+    torch.cuda.synchronize()
+    U.whole_output_sane(o, lse)
+    heads = list(range(0, w.Hq, 5)) + [w.Hq - 1]
+    U.sampled_parity_shape(w, q, k, v, o, lse, [0, w.B - 1], heads, tag=w.name)
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
+
+
 def test_noncausal_full_length_sampled():
     """Non-causal attention at the bench workload's head shape and sequence length (B = 2): every row sees
     all 128 key tiles, the path the causal workloads take only for their last rows.  Sampled rows of every
