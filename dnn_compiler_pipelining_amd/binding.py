@@ -71,7 +71,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
             lib.attn_fwd_ex.restype = i
             lib.attn_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
             lib.attn_fwd_variant.restype = i
-            lib.attn_fwd_variant.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i, i, i, i, i, vp]
+            lib.attn_fwd_variant.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i, i, i, i, i, i, vp]
             lib.attn_fwd_decode_split.restype = i
             lib.attn_fwd_decode_split.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp, ctypes.c_size_t,
                                                   vp]
@@ -87,7 +87,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
             lib.attn_decode_workspace_size.argtypes = [i, i, i, i, i, i]
             ip = ctypes.POINTER(ctypes.c_int)
             lib.attn_tuned_variant.restype = i
-            lib.attn_tuned_variant.argtypes = [i, i, i, i, i, i, ip, ip, ip, ip, ip, ip]
+            lib.attn_tuned_variant.argtypes = [i, i, i, i, i, i, ip, ip, ip, ip, ip, ip, ip]
             lib.attn_device_clock.restype = i
             lib.attn_device_clock.argtypes = [i, ip, ip]
             lib.attn_mfma_ceiling.restype = i
@@ -134,12 +134,12 @@ def attn_fwd_ex(q, k, v, o, lse, B: int, Sq: int, Sk: int, Hq: int, Hkv: int, D:
 
 def attn_fwd_variant(q, k, v, o, lse, B: int, Sq: int, Sk: int, Hq: int, Hkv: int, D: int, causal: int,
                      scale: float, schedule: int, ring: int, xcd: int, lpt: int, place: int, bn: int,
-                     stream) -> int:
+                     hpw: int, stream) -> int:
     """C attn_fwd_variant: attn_fwd_ex with an explicit kernel variant (-1 in a field: the tuned value)."""
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else (stream or 0)
     return load().attn_fwd_variant(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Sq, Sk, Hq, Hkv, D,
                                    int(causal), float(scale), int(schedule), int(ring), int(xcd), int(lpt),
-                                   int(place), int(bn), handle)
+                                   int(place), int(bn), int(hpw), handle)
 
 
 def attn_fwd_decode_static(q, k, v, o, lse, B: int, Sq: int, Sk: int, Hq: int, Hkv: int, D: int, causal: int,
@@ -153,14 +153,14 @@ def attn_fwd_decode_static(q, k, v, o, lse, B: int, Sq: int, Sk: int, Hq: int, H
 
 def attn_tuned_variant(B: int, Sq: int, Sk: int, Hq: int, Hkv: int, D: int) -> dict:
     """C attn_tuned_variant: the variant attn_fwd_ex runs for these sizes, as variant_fields() names it."""
-    out = [ctypes.c_int(-1) for _ in range(6)]
+    out = [ctypes.c_int(-1) for _ in range(7)]
     st = load().attn_tuned_variant(B, Sq, Sk, Hq, Hkv, D, *[ctypes.byref(x) for x in out])
     if st != ATTN_OK:
         raise AttnError(st)
     names = {v: n for n, v in SCHEDULES.items()}
     places = {v: n for n, v in PLACES.items()}
     return {"schedule": names[out[0].value], "ring": out[1].value, "xcd": out[2].value, "lpt": out[3].value,
-            "place": places[out[4].value], "bn": out[5].value}
+            "place": places[out[4].value], "bn": out[5].value, "hpw": out[6].value}
 
 
 def attn_device_clock(device: int = 0) -> tuple[int, int]:
@@ -224,11 +224,11 @@ def attn_decode_workspace_size_split(B: int, Sq: int, Sk: int, Hq: int, Hkv: int
 
 
 def variant_fields(variant) -> tuple:
-    """(schedule, ring, xcd, lpt, place, bn) for attn_fwd_variant from None (all tuned), a schedule name, or a
-    dict with any of the keys schedule (name or number), ring, xcd, lpt, place (name or number), bn (keys per
-    K/V tile); missing fields are -1 (tuned)."""
+    """(schedule, ring, xcd, lpt, place, bn, hpw) for attn_fwd_variant from None (all tuned), a schedule name,
+    or a dict with any of the keys schedule (name or number), ring, xcd, lpt, place (name or number), bn
+    (keys per K/V tile), hpw (heads per workgroup, wide schedule); missing fields are -1 (tuned)."""
     if variant is None:
-        return (-1, -1, -1, -1, -1, -1)
+        return (-1, -1, -1, -1, -1, -1, -1)
     if isinstance(variant, str):
         variant = {"schedule": variant}
     sched = variant.get("schedule", -1)
@@ -238,7 +238,7 @@ def variant_fields(variant) -> tuple:
     if isinstance(place, str):
         place = PLACES[place]
     return (int(sched), int(variant.get("ring", -1)), int(variant.get("xcd", -1)), int(variant.get("lpt", -1)),
-            int(place), int(variant.get("bn", -1)))
+            int(place), int(variant.get("bn", -1)), int(variant.get("hpw", -1)))
 
 
 def attn_status_string(status: int) -> str:

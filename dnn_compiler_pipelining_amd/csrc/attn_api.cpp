@@ -20,9 +20,9 @@ constexpr int kMaxSeq = 1 << 30;  // sequence lengths up to 2^30 keep all tile a
 // state: attn_fwd_variant passes a request explicitly (the schedule search
 // and the tests use it), every other entry point asks for the tuned variant.
 struct Request {
-  int schedule, ring, xcd, lpt, place, bn;
+  int schedule, ring, xcd, lpt, place, bn, hpw;
 };
-constexpr Request kTunedRequest = {-1, -1, -1, -1, -1, -1};
+constexpr Request kTunedRequest = {-1, -1, -1, -1, -1, -1, -1};
 
 // The variant a call runs, or false if the request names a value that does
 // not exist or a schedule the head dimension does not run.  D = 128 runs
@@ -46,6 +46,8 @@ bool choose_variant(const Request& r, int B, int Sq, int Sk, int Hq, int Hkv, in
   if (D != 128 || (v.schedule != libattn::SCHEDULE_SERIAL && v.schedule != libattn::SCHEDULE_SERIAL4))
     v.bn = libattn::BN_STD;
   if (r.bn >= 0) v.bn = r.bn;
+  if (v.schedule != libattn::SCHEDULE_WIDE) v.hpw = 0;  // heads per workgroup: the 64-row schedule's
+  if (r.hpw >= 0) v.hpw = r.hpw;
   if (!libattn::variant_valid(v)) return false;
   if (v.bn != libattn::BN_STD && D != 128) return false;
   if (D == 64) return v.schedule == libattn::SCHEDULE_SERIAL || v.schedule == libattn::SCHEDULE_SERIAL4;
@@ -156,8 +158,10 @@ int forward(const void* q, const void* k, const void* v, void* o, float* lse, in
   hipError_t e;
   if (p.schedule == libattn::SCHEDULE_WIDE) {
     // four heads of a KV group per workgroup at 64 query rows, or two at 128,
-    // or one at 256, whichever divides the GQA ratio
-    p.hpw = p.g % 4 == 0 ? 4 : p.g % 2 == 0 ? 2 : 1;
+    // or one at 256: as the variant names it, else the largest that divides
+    // the GQA ratio (with one that does not, the waves past the last head of
+    // a KV group compute nothing that is stored)
+    p.hpw = var.hpw ? var.hpw : p.g % 4 == 0 ? 4 : p.g % 2 == 0 ? 2 : 1;
     p.pairs = (p.g + p.hpw - 1) / p.hpw;
     const int rows = 256 / p.hpw;
     p.n_qt = (Sq + rows - 1) / rows;
@@ -184,9 +188,9 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
 
 int attn_fwd_variant(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Sq, int Sk, int Hq,
                      int Hkv, int D, int causal, float scale, int schedule, int ring, int xcd, int lpt, int place,
-                     int bn, void* stream) {
+                     int bn, int hpw, void* stream) {
   return forward(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, D, causal, scale,
-                 Request{schedule, ring, xcd, lpt, place, bn}, stream);
+                 Request{schedule, ring, xcd, lpt, place, bn, hpw}, stream);
 }
 
 int attn_fwd_stream(const void* q, const void* k, const void* v, void* o, float* lse, int B, int S, int Hq, int Hkv,
@@ -200,8 +204,8 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
 }
 
 int attn_tuned_variant(int B, int Sq, int Sk, int Hq, int Hkv, int D, int* schedule, int* ring, int* xcd, int* lpt,
-                       int* place, int* bn) {
-  if (!schedule || !ring || !xcd || !lpt || !place || !bn) return ATTN_ERR_NULL;
+                       int* place, int* bn, int* hpw) {
+  if (!schedule || !ring || !xcd || !lpt || !place || !bn || !hpw) return ATTN_ERR_NULL;
   if (B < 1 || Sq < 1 || Sk < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || Sq > kMaxSeq || Sk > kMaxSeq)
     return ATTN_ERR_SHAPE;
   if (D != 64 && D != 128 && D != 256) return ATTN_ERR_UNSUPPORTED;
@@ -213,6 +217,7 @@ int attn_tuned_variant(int B, int Sq, int Sk, int Hq, int Hkv, int D, int* sched
   *lpt = var.lpt;
   *place = var.place;
   *bn = var.bn;
+  *hpw = var.hpw;
   return ATTN_OK;
 }
 

@@ -5,8 +5,9 @@
 // A variant is a point of the schedule space that the search in
 // dnn_compiler_pipelining_amd/tune.py explores: the tile schedule, the depth
 // of the fragment prefetch ring, where the softmax parts sit among the MFMAs
-// (64-row schedule), the keys per K/V tile (serial schedules), and two
-// workgroup-order switches.  Variants with the same keys per tile compute
+// (64-row and overlap schedules), the keys per K/V tile (serial schedules),
+// the query rows per workgroup (64-row schedule) and two workgroup-order
+// switches.  Variants with the same keys per tile compute
 // bitwise identical results and differ only in speed; another tile size
 // changes the rounding order of the online softmax.
 // PipeThreader searches such a space of task orders with a validity check
@@ -66,6 +67,8 @@ struct Variant {
   int lpt;       // 1: longest causal query tiles of a group first
   int place;     // Place (SCHEDULE_WIDE and SCHEDULE_OVERLAP; PLACE_EVEN for the others)
   int bn;        // keys per K/V tile: 64; SERIAL and SERIAL4 also 32 and 128 (head dimension 128)
+  int hpw;       // SCHEDULE_WIDE: query heads per workgroup, 4, 2 or 1 (64, 128 or 256 query rows of
+                 // each), 0 for the largest of them that divides the GQA ratio; 0 for the others
 };
 
 // One measured shape and the fastest variant found for it.
@@ -83,7 +86,8 @@ inline bool variant_valid(const Variant& v) {
          v.place <= PLACE_EARLY &&
          (v.schedule == SCHEDULE_WIDE || v.schedule == SCHEDULE_OVERLAP || v.place == PLACE_EVEN) &&
          (v.bn == BN_STD || ((v.bn == 32 || v.bn == 128) &&
-                         (v.schedule == SCHEDULE_SERIAL || v.schedule == SCHEDULE_SERIAL4)));
+                         (v.schedule == SCHEDULE_SERIAL || v.schedule == SCHEDULE_SERIAL4))) &&
+         (v.hpw == 0 || ((v.hpw == 1 || v.hpw == 2 || v.hpw == 4) && v.schedule == SCHEDULE_WIDE));
 }
 
 // The variant tuned for the measured shape nearest to (B, Sq, Sk, Hq, Hkv):

@@ -7,7 +7,9 @@ the hardware's units under a resource check, with measured feedback (page
 (csrc/variant.h): tile schedule (which also fixes the query rows per wave, 32
 or 64) x fragment-prefetch depth x placement of the softmax parts among the
 MFMAs (64-row and overlap schedules) x keys per K/V tile (32, 64 or 128; the serial
-schedules) (compile time) x two workgroup-order switches (run time).  Variants
+schedules) (compile time) x query heads per workgroup of the 64-row schedule (4,
+2 or 1: 64, 128 or 256 query rows of each) and two workgroup-order switches (run
+time).  Variants
 with the same tile size compute the same bits; the tile size changes the
 rounding order of the online softmax, and every instance is checked against
 the oracle, so the search only trades speed.
@@ -59,9 +61,11 @@ def waves_per_simd(schedule: str, hd: int, bn: int = 64) -> int:
 
 def schedule_has(schedule: str, field: str) -> bool:
     """Whether a schedule has more than one value of a variant field: the placement is the wide and overlap
-    schedules', the tile size the serial schedules'."""
+    schedules', the tile size the serial schedules', the heads per workgroup the wide schedule's."""
     if field == "place":
         return schedule in ("wide", "overlap")
+    if field == "hpw":
+        return schedule == "wide"
     if field == "bn":
         return schedule in ("serial", "serial4")
     return True
@@ -69,7 +73,8 @@ def schedule_has(schedule: str, field: str) -> bool:
 
 RINGS = (2, 4)
 SWITCHES = (0, 1)
-SEED = {"ring": 4, "xcd": 1, "lpt": 1, "place": "even", "bn": 64}  # the start of each schedule's search
+HPWS = (4, 2, 1)  # query heads per workgroup of the wide schedule; 0 = the largest that divides the GQA ratio
+SEED = {"ring": 4, "xcd": 1, "lpt": 1, "place": "even", "bn": 64, "hpw": 0}  # each schedule's search starts here
 # A change is kept when it is this much faster.  The median of five timed batches repeats to about
 # 0.2% on one box (repeated same-box pairs of the serial and overlap schedules on the 70B-shaped
 # B = 16 S = 8192 problem differed by 0.3-1.1%, always in the same direction).
@@ -209,7 +214,8 @@ def greedy_search(rate, is_valid):
     of the schedules' optima wins.  Searching each schedule on its own keeps the fields that only some
     schedules have (placement, tile size) in the search whichever schedule is fastest.  `rate(point)` is the
     measured TFLOP/s of a point, `is_valid(point)` the resource check; returns (best point, its rate)."""
-    fields = [("ring", RINGS), ("xcd", SWITCHES), ("lpt", SWITCHES), ("place", PLACES), ("bn", BNS)]
+    fields = [("ring", RINGS), ("xcd", SWITCHES), ("lpt", SWITCHES), ("place", PLACES), ("bn", BNS),
+              ("hpw", HPWS)]
     best, best_rate = None, 0.0
     for sched in SCHEDULES:
         cur = dict(SEED, schedule=sched)
@@ -247,11 +253,17 @@ def search_workload(w, valid, log=print):
     lse = torch.empty((w.B, w.Hq, w.S), dtype=torch.float32, device=q.device)
     seen = {}
 
+    g = w.Hq // w.Hkv
+    auto_hpw = 4 if g % 4 == 0 else 2 if g % 2 == 0 else 1
+
     def rate(pt):
-        key = (pt["schedule"], pt["ring"], pt["xcd"], pt["lpt"], pt["place"], pt["bn"])
+        # hpw 0 runs the largest divisor of the GQA ratio: the same launch as that value, timed once
+        hpw = pt["hpw"] or (auto_hpw if pt["schedule"] == "wide" else 0)
+        key = (pt["schedule"], pt["ring"], pt["xcd"], pt["lpt"], pt["place"], pt["bn"], hpw)
         if key not in seen:
             seen[key] = measure(w, pt, q, k, v, o, lse)
-            log("  %-26s %-9s ring %d xcd %d lpt %d place %-5s bn %3d: %7.1f TFLOP/s" % (w.name, *key, seen[key]))
+            log("  %-26s %-9s ring %d xcd %d lpt %d place %-5s bn %3d hpw %d: %7.1f TFLOP/s"
+                % (w.name, *key, seen[key]))
         return seen[key]
 
     best, best_rate = greedy_search(rate, lambda pt: valid.get(variant_key(pt, w.D), (False,))[0])
@@ -259,8 +271,8 @@ def search_workload(w, valid, log=print):
     torch.cuda.empty_cache()
     return {"workload": w.name, "B": w.B, "Sq": w.S, "Sk": w.S, "Hq": w.Hq, "Hkv": w.Hkv, "best": best,
             "best_tflops": round(best_rate, 1),
-            "measured": [{"schedule": s, "ring": r, "xcd": x, "lpt": l, "place": pl, "bn": bn, "tflops": round(t, 1)}
-                         for (s, r, x, l, pl, bn), t in seen.items()]}
+            "measured": [{"schedule": s, "ring": r, "xcd": x, "lpt": l, "place": pl, "bn": bn, "hpw": hp,
+                          "tflops": round(t, 1)} for (s, r, x, l, pl, bn, hp), t in seen.items()]}
 
 
 def search(out_dir: str, names=None):
@@ -298,9 +310,9 @@ def emit(search_json: str, table: str = TABLE, profile: str | None = PROFILE):
              "#pragma once", "static const TunedEntry kTuned[] = {"]
     for r in rec["results"]:
         b = r["best"]
-        lines.append("    {%d, %d, %d, %d, %d, {%s, %d, %d, %d, %s, %d}, %.1f},  // %s" % (
+        lines.append("    {%d, %d, %d, %d, %d, {%s, %d, %d, %d, %s, %d, %d}, %.1f},  // %s" % (
             r["B"], r["Sq"], r["Sk"], r["Hq"], r["Hkv"], enum[b["schedule"]], b["ring"], b["xcd"], b["lpt"],
-            penum[b.get("place", "even")], b.get("bn", 64), r["best_tflops"], r["workload"]))
+            penum[b.get("place", "even")], b.get("bn", 64), b.get("hpw", 0), r["best_tflops"], r["workload"]))
     lines += ["};", "static const int kTunedCount = sizeof(kTuned) / sizeof(kTuned[0]);", ""]
     with open(table, "w") as f:
         f.write("\n".join(lines))

@@ -117,22 +117,25 @@ enum { ATTN_PLACE_EVEN = 0, ATTN_PLACE_FRONT = 1, ATTN_PLACE_EARLY = 2 };
 /* attn_fwd_ex with an explicit kernel variant, for schedule search and cross-checks: `schedule` is an
  * ATTN_SCHEDULE_* value, `ring` the fragment prefetch depth (2 or 4), `xcd` 1 to give each XCD whole
  * (batch, KV head) groups, `lpt` 1 to run the longest causal query tiles first, `place` an ATTN_PLACE_*
- * value, `bn` the keys per K/V tile (64; 32 or 128 with SERIAL or SERIAL4 at D = 128); -1 in any of them
- * takes the tuned value (place: ATTN_PLACE_EVEN for schedules other than ATTN_SCHEDULE_WIDE and
- * ATTN_SCHEDULE_OVERLAP; bn: 64 where the schedule or D has no other).  A value that does not exist, a
+ * value, `bn` the keys per K/V tile (64; 32 or 128 with SERIAL or SERIAL4 at D = 128), `hpw` the query
+ * heads per workgroup of ATTN_SCHEDULE_WIDE (4, 2 or 1, i.e. 64, 128 or 256 query rows of each; 0 the
+ * largest that divides Hq / Hkv); -1 in any of them takes the tuned value (place: ATTN_PLACE_EVEN for
+ * schedules other than ATTN_SCHEDULE_WIDE and ATTN_SCHEDULE_OVERLAP; bn: 64 where the schedule or D has no
+ * other; hpw: 0 for schedules other than ATTN_SCHEDULE_WIDE).  A value that does not exist, a
  * placement or tile size the schedule does not have, or a schedule the head dimension does not run,
  * returns ATTN_ERR_UNSUPPORTED and launches nothing.  Results are bitwise identical for every variant of one tile size; another tile size changes the
  * rounding order of the online softmax. */
 int attn_fwd_variant(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Sq, int Sk, int Hq,
                      int Hkv, int D, int causal, float scale, int schedule, int ring, int xcd, int lpt, int place,
-                     int bn, void* stream);
+                     int bn, int hpw, void* stream);
 
 /* The variant attn_fwd_ex runs for these sizes (ATTN_SCHEDULE_* value, ring depth, xcd and lpt switches,
- * ATTN_PLACE_* value, keys per K/V tile), for reports and cross-checks.  Returns ATTN_OK, ATTN_ERR_NULL for a NULL output
+ * ATTN_PLACE_* value, keys per K/V tile, heads per workgroup as requested: 0 = the largest of 4, 2, 1
+ * dividing Hq / Hkv), for reports and cross-checks.  Returns ATTN_OK, ATTN_ERR_NULL for a NULL output
  * pointer, ATTN_ERR_SHAPE for sizes attn_fwd_ex rejects, ATTN_ERR_UNSUPPORTED for a head dimension it does
  * not run.  No HIP call. */
 int attn_tuned_variant(int B, int Sq, int Sk, int Hq, int Hkv, int D, int* schedule, int* ring, int* xcd, int* lpt,
-                       int* place, int* bn);
+                       int* place, int* bn, int* hpw);
 
 /* Compute-unit count and peak shader clock (kHz) of HIP device `device`, as the runtime reports them: the
  * inputs of a peak-throughput figure (dense fp16 MFMA on gfx950: 4 SIMDs x 1024 FLOP per clock per compute

@@ -224,13 +224,14 @@ def test_decode_validation(lib):
 def test_tuned_variant_reports_a_runnable_variant(lib):
     for B, S, Hq, Hkv, D in ((1, 512, 32, 8, 128), (64, 8192, 64, 8, 128), (2, 100, 8, 2, 64), (1, 33, 4, 4, 256)):
         v = L.attn_tuned_variant(B, S, S, Hq, Hkv, D)
-        assert set(v) == {"schedule", "ring", "xcd", "lpt", "place", "bn"}
+        assert set(v) == {"schedule", "ring", "xcd", "lpt", "place", "bn", "hpw"}
+        assert v["hpw"] in (0, 1, 2, 4) and (v["schedule"] == "wide" or v["hpw"] == 0)
         assert v["schedule"] in L.SCHEDULES and v["ring"] in (2, 4) and v["xcd"] in (0, 1) and v["lpt"] in (0, 1)
         assert v["place"] in L.PLACES and (v["schedule"] in ("wide", "overlap") or v["place"] == "even")
         assert v["bn"] == 64 or (v["bn"] in (32, 128) and v["schedule"] in ("serial", "serial4") and D == 128)
         if D != 128:
             assert v["schedule"] in ("serial", "serial4")  # the only schedules D = 64 and 256 run
-    out = [ctypes.c_int(0) for _ in range(6)]
+    out = [ctypes.c_int(0) for _ in range(7)]
     refs = [ctypes.byref(x) for x in out]
     assert lib.attn_tuned_variant(1, 64, 64, 8, 2, 96, *refs) == L.ATTN_ERR_UNSUPPORTED
     assert lib.attn_tuned_variant(1, 64, 64, 6, 4, 128, *refs) == L.ATTN_ERR_SHAPE
@@ -256,7 +257,7 @@ def test_variant_placements_outside_the_wide_and_overlap_schedules_are_rejected(
     # rejected while choosing the variant, before any HIP call (the pointers are never used)
     def var(schedule, place, D=128, ring=-1):
         return L.attn_fwd_variant(QP, KP, VP, OP, LP, 1, 64, 64, 8, 2, D, 1, 0.088, schedule, ring, -1, -1, place, -1,
-                                  None)
+                                  -1, None)
     for sched in ("serial", "pingpong", "serial4"):
         for place in ("front", "early"):
             assert var(L.SCHEDULES[sched], L.PLACES[place]) == L.ATTN_ERR_UNSUPPORTED, (sched, place)
@@ -270,7 +271,8 @@ def test_variant_placements_outside_the_wide_and_overlap_schedules_are_rejected(
 def test_variant_tile_sizes_outside_the_serial_schedules_are_rejected(lib):
     # 32- and 128-key tiles: SERIAL and SERIAL4 at D = 128 only; rejected before any HIP call
     def var(schedule, bn, D=128):
-        return L.attn_fwd_variant(QP, KP, VP, OP, LP, 1, 64, 64, 8, 2, D, 1, 0.088, schedule, -1, -1, -1, -1, bn, None)
+        return L.attn_fwd_variant(QP, KP, VP, OP, LP, 1, 64, 64, 8, 2, D, 1, 0.088, schedule, -1, -1, -1, -1, bn, -1,
+                                  None)
     for sched in ("overlap", "pingpong", "wide"):
         for bn in (32, 128):
             assert var(L.SCHEDULES[sched], bn) == L.ATTN_ERR_UNSUPPORTED, (sched, bn)
@@ -279,6 +281,19 @@ def test_variant_tile_sizes_outside_the_serial_schedules_are_rejected(lib):
             assert var(L.SCHEDULES[sched], bn) == L.ATTN_ERR_UNSUPPORTED, (sched, bn)
         assert var(L.SCHEDULES[sched], 32, D=64) == L.ATTN_ERR_UNSUPPORTED
     assert var(L.SCHEDULES["serial4"], 128, D=256) == L.ATTN_ERR_UNSUPPORTED
+
+
+def test_variant_heads_per_workgroup_outside_the_wide_schedule_are_rejected(lib):
+    # 4, 2 or 1 heads per workgroup (0: the largest dividing Hq / Hkv): the wide schedule only
+    def var(schedule, hpw, D=128):
+        return L.attn_fwd_variant(QP, KP, VP, OP, LP, 1, 64, 64, 8, 2, D, 1, 0.088, schedule, -1, -1, -1, -1, -1, hpw,
+                                  None)
+    for sched in ("serial", "overlap", "pingpong", "serial4"):
+        for hpw in (1, 2, 4):
+            assert var(L.SCHEDULES[sched], hpw) == L.ATTN_ERR_UNSUPPORTED, (sched, hpw)
+    for hpw in (3, 5, 8, 16):
+        assert var(L.SCHEDULES["wide"], hpw) == L.ATTN_ERR_UNSUPPORTED, hpw
+    assert var(L.SCHEDULES["wide"], 2, D=64) == L.ATTN_ERR_UNSUPPORTED
 
 
 def test_mfma_ceiling_validates_before_any_hip_call(lib):

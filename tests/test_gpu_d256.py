@@ -78,7 +78,7 @@ def test_d256_variants_bitwise_identical():
     for sched in sorted(set(binding.SCHEDULES) - set(("serial4",))):
         o = torch.full_like(qd, float("nan"))
         st = binding.attn_fwd_variant(qd, kd, vd, o, None, 1, 700, 700, 8, 2, 256, 1, SC, binding.SCHEDULES[sched],
-                                      -1, -1, -1, -1, -1, None)
+                                      -1, -1, -1, -1, -1, -1, None)
         assert st == binding.ATTN_ERR_UNSUPPORTED, sched
         torch.cuda.synchronize()
         assert bool(torch.isnan(o).all().item()), sched

@@ -286,10 +286,11 @@ def test_all_variants_bitwise_identical(B, S, Hq, Hkv, causal):
                 for xcd in (0, 1):
                     for lpt in (0, 1):
                         for place in (binding.PLACES if sched in ("wide", "overlap") else ("even",)):
-                            var = {"schedule": sched, "ring": ring, "xcd": xcd, "lpt": lpt, "place": place,
-                                   "bn": bn}
-                            o2, l2 = U.run(qd, kd, vd, bool(causal), SC, var)
-                            assert torch.equal(o1, o2) and torch.equal(l1, l2), var
+                            for hpw in ((4, 2, 1) if sched == "wide" else (0,)):
+                                var = {"schedule": sched, "ring": ring, "xcd": xcd, "lpt": lpt, "place": place,
+                                       "bn": bn, "hpw": hpw}
+                                o2, l2 = U.run(qd, kd, vd, bool(causal), SC, var)
+                                assert torch.equal(o1, o2) and torch.equal(l1, l2), var
 
 
 # Every compiled D = 128 kernel instance (schedule x ring depth x softmax placement x keys per tile) on its
@@ -314,6 +315,18 @@ def test_every_instance_against_oracle(B, S, Hq, Hkv, causal, sched, ring, place
                   {"schedule": sched, "ring": ring, "xcd": 1, "lpt": 1, "place": place, "bn": bn})
 
 
+@pytest.mark.parametrize("hpw", [4, 2, 1])
+@pytest.mark.parametrize("B,S,Hq,Hkv,causal", [(1, 650, 8, 2, 1), (2, 201, 12, 4, 0), (1, 333, 16, 2, 1),
+                                               (1, 300, 6, 2, 1)], ids=str)
+def test_wide_heads_per_workgroup_against_oracle(B, S, Hq, Hkv, causal, hpw):
+    """The 64-row kernel with 4, 2 or 1 query heads per workgroup (64, 128 or 256 query rows of each),
+    GQA ratios 4, 3 and 8 (with 3 and hpw 2 or 4, a workgroup's last waves fall past the group's heads)."""
+    tag = "wide hpw%d B%d S%d Hq%d Hkv%d causal%d" % (hpw, B, S, Hq, Hkv, causal)
+    U.say(tag)
+    q, k, v = cpu_qkv(B, S, Hq, Hkv, seed=320 + S + Hq)
+    U.full_parity(q, k, v, bool(causal), SC, tag, {"schedule": "wide", "hpw": hpw})
+
+
 def tuned_entries():
     """(B, Sq, Sk, Hq, Hkv, variant) rows of the compiled-in tuned table."""
     import os
@@ -322,10 +335,11 @@ def tuned_entries():
     from dnn_compiler_pipelining_amd import build
     text = open(os.path.join(build.CSRC, "tuned_table.h")).read()
     rows = re.findall(r"\{(\d+), (\d+), (\d+), (\d+), (\d+), \{SCHEDULE_(\w+), (\d), (\d), (\d), PLACE_(\w+), "
-                      r"(\d+)\}", text)
+                      r"(\d+), (\d)\}", text)
     assert rows
     return [tuple(int(x) for x in r[:5]) + ({"schedule": r[5].lower(), "ring": int(r[6]), "xcd": int(r[7]),
-                                             "lpt": int(r[8]), "place": r[9].lower(), "bn": int(r[10])},)
+                                             "lpt": int(r[8]), "place": r[9].lower(), "bn": int(r[10]),
+                                             "hpw": int(r[11])},)
             for r in rows]
 
 

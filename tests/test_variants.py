@@ -98,7 +98,7 @@ def test_greedy_search_covers_each_schedules_own_fields():
         return not (pt["schedule"] == "serial" and pt["bn"] == 128)
 
     best, r = tune.greedy_search(rate, is_valid)
-    assert best == {"schedule": "wide", "ring": 2, "xcd": 1, "lpt": 1, "place": "early", "bn": 64}
+    assert best == {"schedule": "wide", "ring": 2, "xcd": 1, "lpt": 1, "place": "early", "bn": 64, "hpw": 0}
     assert abs(r - 200.0 * 1.05 * 1.01) < 1e-9
     assert all(is_valid(pt) for pt in timed)
     for sched in ("serial", "serial4"):
@@ -108,6 +108,8 @@ def test_greedy_search_covers_each_schedules_own_fields():
         assert {pt["place"] for pt in timed if pt["schedule"] == sched} == set(tune.PLACES)
     assert {pt["place"] for pt in timed if pt["schedule"] == "pingpong"} == {"even"}
     assert {pt["bn"] for pt in timed if pt["schedule"] != "serial" and pt["schedule"] != "serial4"} == {64}
+    assert {pt["hpw"] for pt in timed if pt["schedule"] == "wide"} == {0, 4, 2, 1}
+    assert {pt["hpw"] for pt in timed if pt["schedule"] != "wide"} == {0}
 
 
 LOOKUP_MAIN = r'''
@@ -117,7 +119,7 @@ int main(int argc, char** argv) {
   int B, Sq, Sk, Hq, Hkv;
   while (std::scanf("%d %d %d %d %d", &B, &Sq, &Sk, &Hq, &Hkv) == 5) {
     libattn::Variant v = libattn::tuned_variant(B, Sq, Sk, Hq, Hkv);
-    std::printf("%d %d %d %d %d %d %d\n", v.schedule, v.ring, v.xcd, v.lpt, v.place, v.bn,
+    std::printf("%d %d %d %d %d %d %d %d\n", v.schedule, v.ring, v.xcd, v.lpt, v.place, v.bn, v.hpw,
                 libattn::variant_valid(v) ? 1 : 0);
   }
   return 0;
@@ -146,11 +148,11 @@ def test_committed_table_picks_its_own_entries(tmp_path):
     enum = {"SCHEDULE_" + name.upper(): value for name, value in binding.SCHEDULES.items()}
     penum = {"PLACE_" + name.upper(): value for name, value in binding.PLACES.items()}
     rows = re.findall(r"\{(\d+), (\d+), (\d+), (\d+), (\d+), \{(SCHEDULE_\w+), (\d), (\d), (\d), (PLACE_\w+), "
-                      r"(\d+)\}", text)
+                      r"(\d+), (\d)\}", text)
     assert rows
     got = lookup(tmp_path, CSRC, [r[:5] for r in rows])
     for r, g in zip(rows, got):
-        assert g == (enum[r[5]], int(r[6]), int(r[7]), int(r[8]), penum[r[9]], int(r[10]), 1), (r, g)
+        assert g == (enum[r[5]], int(r[6]), int(r[7]), int(r[8]), penum[r[9]], int(r[10]), int(r[11]), 1), (r, g)
 
 
 def test_emit_and_nearest_shape(tmp_path):
@@ -164,6 +166,8 @@ def test_emit_and_nearest_shape(tmp_path):
          "best": {"schedule": "wide", "ring": 4, "xcd": 1, "lpt": 1, "place": "early"}},
         {"workload": "short", "B": 4, "Sq": 256, "Sk": 256, "Hq": 8, "Hkv": 8, "best_tflops": 40.0,
          "best": {"schedule": "serial4", "ring": 2, "xcd": 0, "lpt": 0, "place": "even", "bn": 32}},
+        {"workload": "wide2", "B": 2, "Sq": 16384, "Sk": 16384, "Hq": 16, "Hkv": 8, "best_tflops": 900.0,
+         "best": {"schedule": "wide", "ring": 4, "xcd": 1, "lpt": 1, "place": "even", "bn": 64, "hpw": 2}},
     ]}
     js = tmp_path / "search.json"
     js.write_text(json.dumps(rec))
@@ -171,9 +175,10 @@ def test_emit_and_nearest_shape(tmp_path):
     tdir.mkdir()
     tune.emit(str(js), table=str(tdir / "tuned_table.h"), profile=None)
     got = lookup(tmp_path, tdir, [(1, 600, 600, 32, 8), (48, 8192, 8192, 64, 8), (1, 2048, 8192, 64, 8),
-                                  (64, 2000, 2000, 32, 8), (4, 200, 200, 8, 8)])
-    assert got[0] == (1, 2, 0, 1, 0, 64, 1)
-    assert got[1] == (2, 4, 1, 0, 0, 64, 1)
-    assert got[2] in ((1, 2, 0, 1, 0, 64, 1), (2, 4, 1, 0, 0, 64, 1))
-    assert got[3] == (4, 4, 1, 1, 2, 64, 1)
-    assert got[4] == (3, 2, 0, 0, 0, 32, 1)
+                                  (64, 2000, 2000, 32, 8), (4, 200, 200, 8, 8), (2, 16000, 16000, 16, 8)])
+    assert got[0] == (1, 2, 0, 1, 0, 64, 0, 1)
+    assert got[1] == (2, 4, 1, 0, 0, 64, 0, 1)
+    assert got[2] in ((1, 2, 0, 1, 0, 64, 0, 1), (2, 4, 1, 0, 0, 64, 0, 1))
+    assert got[3] == (4, 4, 1, 1, 2, 64, 0, 1)
+    assert got[4] == (3, 2, 0, 0, 0, 32, 0, 1)
+    assert got[5] == (4, 4, 1, 1, 0, 64, 2, 1)
