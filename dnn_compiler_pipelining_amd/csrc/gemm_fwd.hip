@@ -6,27 +6,28 @@
 // Pipelining ... (OSDI 2025)" summary, sections "问题与动机" and "实验与结果")
 // split into a load sTask (A and B tiles, global -> LDS by direct loads into a
 // two-slot ring: prologue / steady state / epilogue, page "AI编译器融合技术 --
-// 5. 并行性与分布式融合", section 5.4.2) and an mma sTask (v_mfma_f32_32x32x16_f16
-// with fragments conformed to the instruction's layout, same page, section
-// 5.2.2).
+// 5. 并行性与分布式融合", section 5.4.2) and an mma sTask (v_mfma_f32_16x16x32_f16
+// with 8 waves, v_mfma_f32_32x32x16_f16 with 4, fragments conformed to the
+// instruction's layout, same page, section 5.2.2).  On random data under the
+// chip's power limit the 16 x 16 x 32 instruction sustains a higher rate than
+// the 32 x 32 x 16 one.
 //
 // One workgroup computes a 256 x 256 tile of C over 64-deep K tiles, with 8
 // waves (two per SIMD) or 4 (one per SIMD, kNW = 4).  Wave (wm, wn) =
 // (w % 2, w / 2) owns rows 128 wm .. +128 of the tile and columns
-// 64 wn .. +64 (8 waves: 4 x 2 accumulators of 32 x 32) or 128 wn .. +128
-// (4 waves: 4 x 4 accumulators, 256 registers that live in AGPRs; a third
-// fewer LDS reads per MFMA, 0.5 against 0.75 with B stored [N][K]).  The MFMA
-// computes
-// the transposed block, D[n][m] = sum_k B^T[n][k] A^T[k][m], so that each lane
-// holds one row m of C and runs of 4 consecutive columns n: the epilogue
-// writes 8-byte runs.
+// 64 wn .. +64 (8 waves: 8 x 4 accumulators of 16 x 16) or 128 wn .. +128
+// (4 waves: 4 x 4 accumulators of 32 x 32, 256 registers that live in AGPRs).
+// The MFMA computes the transposed block, D[n][m] = sum_k B^T[n][k] A^T[k][m],
+// so that each lane holds one row m of C and runs of 4 consecutive columns n:
+// the epilogue writes 8-byte runs.
 //
 // LDS layouts (bytes; one slot of each ring is 32 KiB, both rings 128 KiB):
 //   A tile and B tile stored [N][K]: 256 rows of 64 k = 128 B.  Its 16-byte
-//     chunk c of row r sits at position c ^ ((r >> 1) & 7).  A 32 x 16
-//     fragment is one ds_read_b128 per lane (row l % 32, chunk 2kk + l / 32);
-//     each 16-lane pass of it touches rows r0..r0+15 at one chunk, which
-//     the swizzle spreads over all 64 banks.
+//     chunk c of row r sits at position c ^ ((r >> 1) & 7).  A fragment is
+//     one ds_read_b128 per lane (16 x 32: row l % 16, chunk 4kk + l / 16;
+//     32 x 16: row l % 32, chunk 2kk + l / 32); each 16-lane pass of it
+//     touches rows r0..r0+15 at one chunk, which the swizzle spreads over
+//     all 64 banks.
 //   B tile stored [K][N]: 64 rows of 256 n = 512 B, chunk c of row r at
 //     c ^ (4 * (r & 3)).  A B^T fragment (n rows, k columns) is two
 //     ds_read_b64_tr_b16 of 4 k rows each; a half-wave of such a read covers
@@ -39,6 +40,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "gemm_kernel.h"
 #include "gfx950.h"
 
@@ -49,11 +52,16 @@ constexpr int G_TILEB = 256 * GBK * 2;  // bytes of one A or B slot (32 KiB)
 constexpr int G_BAND = 8;               // output tile rows per raster band
 static_assert(4 * G_TILEB <= 160 * 1024, "two slots of A and B fit the LDS");
 
-template <int kBL, int kNW>  // kBL 0: B stored [K][N]; 1: B stored [N][K].  kNW: waves per workgroup, 8 or 4
+// kBL 0: B stored [K][N]; 1: B stored [N][K].  kNW: waves per workgroup, 8 or 4.  kMI: the MFMA,
+// 32 (v_mfma_f32_32x32x16_f16) or 16 (v_mfma_f32_16x16x32_f16).
+template <int kBL, int kNW, int kMI = 32>
 __global__ __launch_bounds__(64 * kNW, 1) void gemm_kernel(GemmParams p) {
   static_assert(kNW == 8 || kNW == 4, "8 or 4 waves");
+  static_assert(kMI == 32 || kMI == 16, "32 x 32 x 16 or 16 x 16 x 32 MFMAs");
   constexpr int WNX = kNW == 8 ? 64 : 128;  // columns of C per wave
-  constexpr int NFR = WNX / 32;             // 32-column accumulator blocks per wave
+  constexpr int NFR = WNX / kMI;            // accumulator blocks per wave along n
+  constexpr int MFB = 128 / kMI;            // accumulator blocks per wave along m (128 rows)
+  constexpr int NSUB = 64 / (kMI == 32 ? 16 : 32);  // k substeps per 64-deep K tile
   constexpr int UPW = 32 / kNW;             // direct-load instructions per wave per tile, for A and for B
   __shared__ __attribute__((aligned(1024))) char a_smem[2 * G_TILEB];
   __shared__ __attribute__((aligned(1024))) char b_smem[2 * G_TILEB];
@@ -152,68 +160,82 @@ __global__ __launch_bounds__(64 * kNW, 1) void gemm_kernel(GemmParams p) {
     }
   };
 
-  // ---- per-lane fragment offsets (bytes).  Row l % 32 of a 32-row block and
-  // logical chunk 2kk + l/32 of a [row][k] tile, for kk = 0..3:
-  int rk_frag[4];
+  // ---- per-lane fragment offsets (bytes) in a [row][k] tile.  kMI 32: row
+  // l % 32 of a 32-row block and logical chunk 2kk + l/32, kk = 0..3 (the
+  // 32 x 32 x 16 operand: row l % 32, k = 8 (l/32) .. +7).  kMI 16: row l % 16
+  // of a 16-row block and logical chunk 4kk + l/16, kk = 0..1 (the 16 x 16 x 32
+  // operand: row l % 16, k = 8 (l/16) .. +7).  Blocks start at multiples of 16
+  // rows, so the swizzle of row r is that of r % 16.
+  int rk_frag[NSUB];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk)
-    rk_frag[kk] = (lane & 31) * 128 + 16 * ((2 * kk + (lane >> 5)) ^ ((lane >> 1) & 7));
+  for (int kk = 0; kk < NSUB; ++kk)
+    rk_frag[kk] = kMI == 32 ? (lane & 31) * 128 + 16 * ((2 * kk + (lane >> 5)) ^ ((lane >> 1) & 7))
+                            : (lane & 15) * 128 + 16 * ((4 * kk + (lane >> 4)) ^ (((lane & 15) >> 1) & 7));
   // B stored [K][N]: lane (group g = l/16, s = l%16) of a transpose read
-  // addresses k row 8(g/2) + s/4 (+4 for the second read, +16kk per step) and
-  // columns n = WNX wn + 32nf + 16(g%2) + 4(s%4) .. +3.
+  // addresses 4 fp16 of one k row; the read hands lane s of each group the 4
+  // k rows of the group's column s.  kMI 32: k row 8(g/2) + s/4 (+4 for the
+  // second read, +16kk per step) and columns n = WNX wn + 32nf + 16(g%2) +
+  // 4(s%4) .. +3.  kMI 16: k row 8g + s/4 (+4, +32kk) and columns
+  // n = WNX wn + 16nf + 4(s%4) .. +3.
   int kn_frag[NFR];
   {
     const int g = lane >> 4, s = lane & 15;
-    const int row = 8 * (g >> 1) + (s >> 2);
-    const int chunk = (WNX / 8) * wn + 2 * (g & 1) + ((s & 3) >> 1);  // 16-byte chunk for nf = 0
+    const int row = kMI == 32 ? 8 * (g >> 1) + (s >> 2) : 8 * g + (s >> 2);
+    const int chunk = (WNX / 8) * wn + (kMI == 32 ? 2 * (g & 1) : 0) + ((s & 3) >> 1);  // 16-byte chunk, nf = 0
     const int f0 = row * 512 + ((chunk ^ (4 * (s >> 2))) << 4) + ((s & 1) << 3);
-    // nf adds 4nf to the chunk: bits 2..3, which are zero in the nf = 0 chunk and which the swizzle XORs too
+    // nf adds 4nf (kMI 32) or 2nf (kMI 16) to the chunk: bits that are zero in the nf = 0 chunk, so the
+    // sum is an XOR, and XOR commutes with the swizzle
 #pragma unroll
-    for (int nf = 0; nf < NFR; ++nf) kn_frag[nf] = f0 ^ (64 * nf);
+    for (int nf = 0; nf < NFR; ++nf) kn_frag[nf] = f0 ^ ((kMI == 32 ? 64 : 32) * nf);
   }
 
-  auto frag_a = [&](int slot, int kk, int mf) INL -> f16x8 {  // B operand: A^T[k][m], m = 128wm + 32mf + l%32
-    return *(const LDS f16x8*)(a_lds + slot * G_TILEB + (128 * wm + 32 * mf) * 128 + rk_frag[kk]);
+  auto frag_a = [&](int slot, int kk, int mf) INL -> f16x8 {  // B operand: A^T[k][m], m = 128wm + kMI mf + l%kMI
+    return *(const LDS f16x8*)(a_lds + slot * G_TILEB + (128 * wm + kMI * mf) * 128 + rk_frag[kk]);
   };
-  auto frag_b = [&](int slot, int kk, int nf) INL -> f16x8 {  // A operand: B^T[n][k], n = WNX wn + 32nf + l%32
+  auto frag_b = [&](int slot, int kk, int nf) INL -> f16x8 {  // A operand: B^T[n][k], n = WNX wn + kMI nf + l%kMI
     if constexpr (kBL == 1) {
-      return *(const LDS f16x8*)(b_lds + slot * G_TILEB + (WNX * wn + 32 * nf) * 128 + rk_frag[kk]);
+      return *(const LDS f16x8*)(b_lds + slot * G_TILEB + (WNX * wn + kMI * nf) * 128 + rk_frag[kk]);
     } else {
-      const LDS char* a = b_lds + slot * G_TILEB + kn_frag[nf] + 16 * kk * 512;
+      const LDS char* a = b_lds + slot * G_TILEB + kn_frag[nf] + (64 / NSUB) * kk * 512;
       const f16x4 h1 = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS i16x4*)a));
       const f16x4 h2 = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS i16x4*)(a + 4 * 512)));
       return f16x8{h1[0], h1[1], h1[2], h1[3], h2[0], h2[1], h2[2], h2[3]};
     }
   };
 
-  f32x16 acc[4][NFR];
+  using Acc = std::conditional_t<kMI == 32, f32x16, f32x4>;
+  Acc acc[MFB][NFR];
 #pragma unroll
-  for (int mf = 0; mf < 4; ++mf)
+  for (int mf = 0; mf < MFB; ++mf)
 #pragma unroll
-    for (int nf = 0; nf < NFR; ++nf) acc[mf][nf] = f32x16{};
+    for (int nf = 0; nf < NFR; ++nf) acc[mf][nf] = Acc{};
+  auto mma = [&](f16x8 bv, f16x8 av, Acc& c) INL {
+    if constexpr (kMI == 32) c = __builtin_amdgcn_mfma_f32_32x32x16_f16(bv, av, c, 0, 0, 0);
+    else c = __builtin_amdgcn_mfma_f32_16x16x32_f16(bv, av, c, 0, 0, 0);
+  };
 
-  // ---- mma task: a K tile is 4 substeps of 16 k, 4 NFR MFMAs each
-  // (mf-major).  Fragments are double-buffered by substep; the NFR + 4 (or
-  // 2 NFR + 4, with transpose reads) fragment reads of the next substep are
-  // issued one after each of the first MFMAs of the current one (pinned
-  // below), so LDS latency hides behind the matrix core.
-  constexpr int kSteps = 4 * NFR;
-  constexpr int kReads = kBL == 1 ? NFR + 4 : 2 * NFR + 4;
+  // ---- mma task: a K tile is NSUB substeps (4 of 16 k, or 2 of 32 k), MFB
+  // NFR MFMAs each (mf-major).  Fragments are double-buffered by substep; the
+  // NFR + MFB (or 2 NFR + MFB, with transpose reads) fragment reads of the
+  // next substep are issued one after each of the first MFMAs of the current
+  // one (pinned below), so LDS latency hides behind the matrix core.
+  constexpr int kSteps = MFB * NFR;
+  constexpr int kReads = kBL == 1 ? NFR + MFB : 2 * NFR + MFB;
   static_assert(kReads <= kSteps, "one read after each MFMA at most");
-  f16x8 bf[2][NFR], af[2][4];
+  f16x8 bf[2][NFR], af[2][MFB];
   auto load_frags = [&](int slot, auto kc) INL {
     constexpr int kk = decltype(kc)::value;
 #pragma unroll
     for (int nf = 0; nf < NFR; ++nf) bf[kk & 1][nf] = frag_b(slot, kk, nf);
 #pragma unroll
-    for (int mf = 0; mf < 4; ++mf) af[kk & 1][mf] = frag_a(slot, kk, mf);
+    for (int mf = 0; mf < MFB; ++mf) af[kk & 1][mf] = frag_a(slot, kk, mf);
   };
   auto mfmas = [&](auto kc) INL {
     constexpr int kk = decltype(kc)::value;
 #pragma unroll
     for (int j = 0; j < kSteps; ++j) {
       const int mf = j / NFR, nf = j % NFR;
-      acc[mf][nf] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[kk & 1][nf], af[kk & 1][mf], acc[mf][nf], 0, 0, 0);
+      mma(bf[kk & 1][nf], af[kk & 1][mf], acc[mf][nf]);
     }
   };
   auto pin_interleaved = [&]() INL {  // MFMA j, then read j
@@ -224,10 +246,11 @@ __global__ __launch_bounds__(64 * kNW, 1) void gemm_kernel(GemmParams p) {
   };
 
   // ---- K loop, rotated by one substep across the barrier: iteration kt runs
-  // substeps 0..2 of tile kt, waits for tile kt+1's loads and the barrier
-  // that publishes them, then runs substep 3 of tile kt (its fragments are
-  // already in registers) beside the substep-0 reads of tile kt+1, and issues
-  // the loads of tile kt+2 into the slot tile kt has just left.  The matrix
+  // substeps 0..NSUB-2 of tile kt, waits for tile kt+1's loads and the
+  // barrier that publishes them, then runs the last substep of tile kt (its
+  // fragments are already in registers) beside the substep-0 reads of tile
+  // kt+1, and issues the loads of tile kt+2 into the slot tile kt has just
+  // left.  The matrix
   // core stays busy while the waves meet at the barrier and while the first
   // reads of a tile are in flight.
   const int nkt = p.nkt;
@@ -238,8 +261,8 @@ __global__ __launch_bounds__(64 * kNW, 1) void gemm_kernel(GemmParams p) {
   lds_barrier();
   load_frags(0, std::integral_constant<int, 0>{});
   if (nkt > 1) stage(1);
-  auto substeps_012 = [&](int slot) INL {
-    static_for<3>([&](auto kc) INL {
+  auto substeps_012 = [&](int slot) INL {  // substeps 0 .. NSUB-2
+    static_for<NSUB - 1>([&](auto kc) INL {
       constexpr int kk = decltype(kc)::value;
       load_frags(slot, std::integral_constant<int, kk + 1>{});
       mfmas(kc);
@@ -267,7 +290,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void gemm_kernel(GemmParams p) {
   const char* b_run = kBL == 1 ? (const char*)(p.b + (int64_t)n0 * K) + 2 * 2 * GBK
                                : (const char*)(p.b + (int64_t)2 * GBK * N + n0);
   const int64_t b_step = kBL == 1 ? 2 * GBK : (int64_t)2 * GBK * N;  // bytes from one K tile to the next
-  // Substep 3 of tile kt beside the substep-0 reads of tile kt+1 (slot
+  // The last substep of tile kt beside the substep-0 reads of tile kt+1 (slot
   // slot ^ 1), with (kDmaIn) this wave's loads of tile kt+2 into `slot`.
   auto substep3 = [&](int slot, auto dma_in) INL {
     constexpr bool kDmaIn = decltype(dma_in)::value;
@@ -275,9 +298,9 @@ __global__ __launch_bounds__(64 * kNW, 1) void gemm_kernel(GemmParams p) {
     const uint32_t b_m0 = b_lds_base + (uint32_t)slot * G_TILEB + 1024u * (uint32_t)wave_s;
     static_for<kSteps>([&](auto jc) INL {
       constexpr int j = decltype(jc)::value, mf = j / NFR, nf = j % NFR;
-      acc[mf][nf] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[1][nf], af[1][mf], acc[mf][nf], 0, 0, 0);
+      mma(bf[1][nf], af[1][mf], acc[mf][nf]);
       if constexpr (j < NFR) bf[0][j] = frag_b(slot ^ 1, 0, j);
-      else if constexpr (j < NFR + 4) af[0][j - NFR] = frag_a(slot ^ 1, 0, j - NFR);
+      else if constexpr (j < NFR + MFB) af[0][j - NFR] = frag_a(slot ^ 1, 0, j - NFR);
       if constexpr (kDmaIn && j < UPW) dma16_m0_plus<1024u * kNW * j>(a_run, off_a[j], a_m0);
       if constexpr (kDmaIn && j >= UPW && j < 2 * UPW) dma16_m0_plus<1024u * kNW * (j - UPW)>(b_run, off_b[j - UPW], b_m0);
       __builtin_amdgcn_sched_barrier(0);
@@ -287,7 +310,8 @@ __global__ __launch_bounds__(64 * kNW, 1) void gemm_kernel(GemmParams p) {
       b_run += b_step;
     }
   };
-  static_assert(2 * UPW <= kSteps && NFR + 4 <= kSteps, "one load and one fragment read beside each MFMA at most");
+  static_assert(2 * UPW <= kSteps && NFR + MFB <= kSteps, "one load and one fragment read beside each MFMA at most");
+  static_assert((NSUB - 1) % 2 == 1, "the last substep's fragments are in buffer 1");
   // iteration kt: substeps 0..2, the barrier that publishes tile kt+1, substep 3
   auto iteration = [&](int kt, auto dma_in) INL {
     const int slot = kt & 1;
@@ -306,28 +330,49 @@ __global__ __launch_bounds__(64 * kNW, 1) void gemm_kernel(GemmParams p) {
     if (kt + 2 < nkt) stage(kt + 2);
   }
   substeps_012(kt & 1);  // the last tile
-  mfmas(std::integral_constant<int, 3>{});
+  mfmas(std::integral_constant<int, NSUB - 1>{});
 
-  // ---- epilogue: lane l holds C[m][n] for m = m0 + 128wm + 32mf + l%32 and
-  // n = n0 + 64wn + 32nf + 8(r/4) + 4(l/32) + r%4; fp16, round to nearest even.
-  const int h = lane >> 5;
+  if constexpr (kMI == 16) {
+    // ---- epilogue: lane l holds C[m][n] for m = m0 + 128wm + 16mf + l%16 and
+    // n = n0 + WNX wn + 16nf + 4(l/16) + r; fp16, round to nearest even
 #pragma unroll
-  for (int mf = 0; mf < 4; ++mf) {
-    const int m = m0 + 128 * wm + 32 * mf + (lane & 31);
-    if (m >= M) continue;
-    _Float16* crow = p.c + (int64_t)m * N;
+    for (int mf = 0; mf < MFB; ++mf) {
+      const int m = m0 + 128 * wm + 16 * mf + (lane & 15);
+      if (m >= M) continue;
+      _Float16* crow = p.c + (int64_t)m * N;
 #pragma unroll
-    for (int nf = 0; nf < NFR; ++nf)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int n = n0 + WNX * wn + 32 * nf + 8 * r4 + 4 * h;
-        if (n < N) {
+      for (int nf = 0; nf < NFR; ++nf) {
+        const int n = n0 + WNX * wn + 16 * nf + 4 * (lane >> 4);
+        if (n < N) {  // N % 8 == 0 and n % 4 == 0: n .. n+3 lie inside N
           f16x4 hv;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) hv[e] = (_Float16)acc[mf][nf][4 * r4 + e];
+          for (int e = 0; e < 4; ++e) hv[e] = (_Float16)acc[mf][nf][e];
           *reinterpret_cast<f16x4*>(crow + n) = hv;
         }
       }
+    }
+  } else {
+    // ---- epilogue: lane l holds C[m][n] for m = m0 + 128wm + 32mf + l%32 and
+    // n = n0 + WNX wn + 32nf + 8(r/4) + 4(l/32) + r%4; fp16, round to nearest even.
+    const int h = lane >> 5;
+#pragma unroll
+    for (int mf = 0; mf < MFB; ++mf) {
+      const int m = m0 + 128 * wm + 32 * mf + (lane & 31);
+      if (m >= M) continue;
+      _Float16* crow = p.c + (int64_t)m * N;
+#pragma unroll
+      for (int nf = 0; nf < NFR; ++nf)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int n = n0 + WNX * wn + 32 * nf + 8 * r4 + 4 * h;
+          if (n < N) {
+            f16x4 hv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) hv[e] = (_Float16)acc[mf][nf][4 * r4 + e];
+            *reinterpret_cast<f16x4*>(crow + n) = hv;
+          }
+        }
+    }
   }
 }
 
@@ -342,12 +387,13 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t stream) {
   if (nb <= 0 || nb > 0x7fffffff || p.nkt < 1) return hipErrorInvalidValue;
   if (p.waves != 4 && p.waves != 8) return hipErrorInvalidValue;
   const dim3 grid((unsigned)nb), block(64 * p.waves);
+  // 8 waves run 16 x 16 x 32 MFMAs, 4 waves 32 x 32 x 16 (the faster shape of each, measured)
   if (p.b_layout == 0) {
-    if (p.waves == 8) hipLaunchKernelGGL((gemm_kernel<0, 8>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((gemm_kernel<0, 4>), grid, block, 0, stream, p);
+    if (p.waves == 8) hipLaunchKernelGGL((gemm_kernel<0, 8, 16>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((gemm_kernel<0, 4, 32>), grid, block, 0, stream, p);
   } else if (p.b_layout == 1) {
-    if (p.waves == 8) hipLaunchKernelGGL((gemm_kernel<1, 8>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((gemm_kernel<1, 4>), grid, block, 0, stream, p);
+    if (p.waves == 8) hipLaunchKernelGGL((gemm_kernel<1, 8, 16>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((gemm_kernel<1, 4, 32>), grid, block, 0, stream, p);
   } else {
     return hipErrorInvalidValue;
   }

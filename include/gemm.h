@@ -56,8 +56,9 @@ enum { GEMM_B_KN = 0, GEMM_B_NK = 1 };
 int gemm_f16(const void* a, const void* b, void* c, int M, int N, int K, int b_layout, void* stream);
 
 /* gemm_f16 with an explicit workgroup shape, for tuning and cross-checks: `waves` 8 (eight waves of
- * 128 x 64 outputs each, the default), 4 (four waves of 128 x 128, accumulators in AGPRs) or 0 (the
- * default).  Both shapes give bitwise identical results.  Any other value returns ATTN_ERR_UNSUPPORTED
+ * 128 x 64 outputs each on 16 x 16 x 32 MFMAs, the default), 4 (four waves of 128 x 128 on 32 x 32 x 16
+ * MFMAs, accumulators in AGPRs) or 0 (the default).  Both shapes give bitwise identical results (the
+ * products of each output meet its fp32 accumulator in the same order and groups on either MFMA).  Any other value returns ATTN_ERR_UNSUPPORTED
  * after the argument checks above. */
 int gemm_f16_waves(const void* a, const void* b, void* c, int M, int N, int K, int b_layout, int waves,
                    void* stream);

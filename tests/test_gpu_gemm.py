@@ -174,8 +174,9 @@ def test_validation_launches_nothing():
 @pytest.mark.parametrize("layout", [KN, NK], ids=["kn", "nk"])
 @pytest.mark.parametrize("M,N,K", [(300, 264, 136), (513, 520, 520), (1000, 1024, 1000), (64, 8, 4096)], ids=str)
 def test_four_wave_workgroups_give_the_same_bits(M, N, K, layout):
-    """Workgroups of 4 waves (128 x 128 per wave) and of 8 (128 x 64) feed every accumulator the same MFMAs in
-    the same order, so they give the same bits; the 4-wave result also meets the oracle bar."""
+    """Workgroups of 4 waves (128 x 128 per wave, 32 x 32 x 16 MFMAs) and of 8 (128 x 64, 16 x 16 x 32 MFMAs)
+    feed every output the same products in the same k order, and give the same bits; the 4-wave result also
+    meets the oracle bar."""
     a, b = mats(M, N, K, layout, seed=500 + M + K)
     ad, bd = a.cuda(), b.cuda()
     c8 = run(ad, bd, layout, M, N, K, waves=8)
