@@ -179,15 +179,19 @@ def mfma_peak() -> dict:
             (cu, khz / 1e6, MFMA_FP16_FLOP_PER_CU_CLK), "published_tflops": PEAK_TFLOPS}
 
 
-def mfma_ceiling(achieved: float) -> dict:
-    """The box's sustained MFMA-only rate on random operands, measured after the timed region (context for
-    `achieved`: under the power limit it varies from box to box and sits well below the published peak)."""
+def mfma_ceiling(achieved: float, shape: int = 32) -> dict:
+    """The box's sustained MFMA-only rate on random operands for the instruction the kernel runs (`shape` 32:
+    v_mfma_f32_32x32x16_f16, the attention kernels; 16: v_mfma_f32_16x16x32_f16, the GEMM), measured after
+    the timed region (context for `achieved`: under the power limit it varies from box to box and sits well
+    below the published peak)."""
     from dnn_compiler_pipelining_amd import binding
 
-    tf = binding.attn_mfma_ceiling(200000)
+    tf = binding.attn_mfma_ceiling_shape(shape, 200000)
+    name = "v_mfma_f32_32x32x16_f16" if shape == 32 else "v_mfma_f32_16x16x32_f16"
     return {"tflops": round(tf, 1), "frac": round(achieved / tf, 4),
-            "method": "attn_mfma_ceiling: back-to-back v_mfma_f32_32x32x16_f16 on random fp16 operands, one wave per "
-                      "SIMD on every CU, timed with HIP events in this run after the timed region"}
+            "method": "attn_mfma_ceiling_shape(%d): back-to-back %s (the kernel's MFMA) on random fp16 operands, one "
+                      "wave per SIMD on every CU, timed with HIP events in this run after the timed region"
+                      % (shape, name)}
 
 
 def cpu_model() -> str | None:
@@ -803,7 +807,7 @@ def main():
             # the other attention configurations, each timed under the --all warmup rule, in the same run
             line["per_config"] = per_config(w.name, args.schedule, peak)
         if not args.all and not args.no_per_config:
-            line["mfma_ceiling"] = mfma_ceiling(achieved)
+            line["mfma_ceiling"] = mfma_ceiling(achieved, 16 if gemm else 32)
         if not args.no_cpu_baseline and not args.all:
             line["cpu_baseline"] = (cpu_baseline_gemm if gemm else cpu_baseline)(w, args.cpu_seconds)
             line["cpu_baseline"]["cpu_model"] = cpu_model()

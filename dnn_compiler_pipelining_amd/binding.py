@@ -33,7 +33,7 @@ ATTN_STATIC_WORKSPACE_BYTES = 64 << 20  # the library's own split-KV workspace p
 
 EXPORTS = ("attn_fwd", "attn_fwd_stream", "attn_fwd_ex", "attn_fwd_variant", "attn_fwd_decode",
            "attn_fwd_decode_split", "attn_fwd_decode_static", "attn_decode_workspace_size", "attn_decode_workspace_size_split",
-           "attn_status_string", "attn_version", "attn_tuned_variant", "attn_device_clock", "attn_mfma_ceiling", "gemm_f16",
+           "attn_status_string", "attn_version", "attn_tuned_variant", "attn_device_clock", "attn_mfma_ceiling", "attn_mfma_ceiling_shape", "gemm_f16",
            "gemm_f16_waves")
 
 # Tile schedules (ATTN_SCHEDULE_* in include/attn.h), by name
@@ -92,6 +92,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
             lib.attn_device_clock.argtypes = [i, ip, ip]
             lib.attn_mfma_ceiling.restype = i
             lib.attn_mfma_ceiling.argtypes = [i, vp, ctypes.POINTER(ctypes.c_double)]
+            lib.attn_mfma_ceiling_shape.restype = i
+            lib.attn_mfma_ceiling_shape.argtypes = [i, i, vp, ctypes.POINTER(ctypes.c_double)]
             lib.attn_status_string.restype = ctypes.c_char_p
             lib.attn_status_string.argtypes = [i]
             lib.attn_version.restype = i
@@ -178,6 +180,16 @@ def attn_mfma_ceiling(iters: int = 200000, stream=None) -> float:
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else (stream or 0)
     out = ctypes.c_double(0.0)
     st = load().attn_mfma_ceiling(int(iters), handle, ctypes.byref(out))
+    if st != ATTN_OK:
+        raise AttnError(st)
+    return out.value
+
+
+def attn_mfma_ceiling_shape(shape: int, iters: int = 200000, stream=None) -> float:
+    """C attn_mfma_ceiling_shape: attn_mfma_ceiling for `shape` 32 (32x32x16) or 16 (16x16x32)."""
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else (stream or 0)
+    out = ctypes.c_double(0.0)
+    st = load().attn_mfma_ceiling_shape(int(shape), int(iters), handle, ctypes.byref(out))
     if st != ATTN_OK:
         raise AttnError(st)
     return out.value

@@ -192,6 +192,12 @@ int attn_fwd_decode_static(const void* q, const void* k, const void* v, void* o,
  * only); about 0.07 s per launch at iters = 200000 on MI355X. */
 int attn_mfma_ceiling(int iters, void* stream, double* tflops);
 
+/* attn_mfma_ceiling for a given instruction: `shape` 32 (v_mfma_f32_32x32x16_f16, what attn_mfma_ceiling
+ * times) or 16 (v_mfma_f32_16x16x32_f16, 32 per iteration: the same FLOPs).  ATTN_ERR_UNSUPPORTED for
+ * another shape, nothing launched; otherwise as attn_mfma_ceiling.  On random data the 16 x 16 x 32
+ * instruction sustains the higher rate under the power limit. */
+int attn_mfma_ceiling_shape(int shape, int iters, void* stream, double* tflops);
+
 /* Static, NUL-terminated description of a status code ("unknown status" for others). */
 const char* attn_status_string(int status);
 

@@ -303,4 +303,8 @@ def test_mfma_ceiling_validates_before_any_hip_call(lib):
     assert lib.attn_mfma_ceiling(-5, None, ctypes.byref(out)) == L.ATTN_ERR_SHAPE
     assert lib.attn_mfma_ceiling(10000001, None, ctypes.byref(out)) == L.ATTN_ERR_SHAPE
     assert lib.attn_mfma_ceiling(100, None, None) == L.ATTN_ERR_NULL
+    for shape in (0, 8, 17, 31, 64):
+        assert lib.attn_mfma_ceiling_shape(shape, 100, None, ctypes.byref(out)) == L.ATTN_ERR_UNSUPPORTED, shape
+    assert lib.attn_mfma_ceiling_shape(16, 0, None, ctypes.byref(out)) == L.ATTN_ERR_SHAPE
+    assert lib.attn_mfma_ceiling_shape(16, 100, None, None) == L.ATTN_ERR_NULL
     assert out.value == -1.0

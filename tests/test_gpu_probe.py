@@ -29,9 +29,23 @@ def test_rate_is_plausible_on_null_and_side_stream():
     assert 400.0 < tf2 <= PEAK_TFLOPS, tf2
 
 
+def test_both_instruction_shapes():
+    """Both shapes give a plausible rate; the 32 x 32 x 16 one is what attn_mfma_ceiling times (same box, so
+    the two agree within a few per cent of clock drift)."""
+    U.say("mfma ceiling by shape")
+    r32 = binding.attn_mfma_ceiling_shape(32, 20000)
+    r16 = binding.attn_mfma_ceiling_shape(16, 20000)
+    r = binding.attn_mfma_ceiling(20000)
+    U.say("  32x32x16 %.1f, 16x16x32 %.1f, attn_mfma_ceiling %.1f TFLOP/s" % (r32, r16, r))
+    for tf in (r32, r16, r):
+        assert 400.0 < tf <= PEAK_TFLOPS, (r32, r16, r)
+    assert abs(r - r32) <= 0.1 * r32
+
+
 def test_bad_arguments_launch_nothing():
     lib = binding.load()
     out = ctypes.c_double(-1.0)
     assert lib.attn_mfma_ceiling(0, None, ctypes.byref(out)) == binding.ATTN_ERR_SHAPE
     assert lib.attn_mfma_ceiling(7, None, None) == binding.ATTN_ERR_NULL
+    assert lib.attn_mfma_ceiling_shape(24, 7, None, ctypes.byref(out)) == binding.ATTN_ERR_UNSUPPORTED
     assert out.value == -1.0
