@@ -37,7 +37,7 @@ EXPORTS = ("attn_fwd", "attn_fwd_stream", "attn_fwd_ex", "attn_fwd_variant", "at
            "gemm_f16_waves")
 
 # Tile schedules (ATTN_SCHEDULE_* in include/attn.h), by name
-SCHEDULES = {"serial": 0, "overlap": 1, "pingpong": 2, "serial4": 3, "wide": 4}
+SCHEDULES = {"serial": 0, "overlap": 1, "pingpong": 2, "serial4": 3, "wide": 4, "serial4_16": 5}
 # Placements of the softmax work in the 64-row schedule (ATTN_PLACE_* in include/attn.h), by name
 PLACES = {"even": 0, "front": 1, "early": 2}
 

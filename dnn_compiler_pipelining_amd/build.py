@@ -14,8 +14,8 @@ LIB = os.path.join(PKG, "libattn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 WIDE_SOURCES = [os.path.join(CSRC, "attn_wide_%s.hip" % p) for p in ("even", "front", "early")]
-ATTN_SOURCES = [os.path.join(CSRC, "attn_fwd.hip"), *WIDE_SOURCES, os.path.join(CSRC, "attn_api.cpp"),
-                os.path.join(CSRC, "attn_static_ws.hip")]
+ATTN_SOURCES = [os.path.join(CSRC, "attn_fwd.hip"), *WIDE_SOURCES, os.path.join(CSRC, "attn_s16.hip"),
+                os.path.join(CSRC, "attn_api.cpp"), os.path.join(CSRC, "attn_static_ws.hip")]
 GEMM_SOURCES = [os.path.join(CSRC, "gemm_fwd.hip"), os.path.join(CSRC, "gemm_api.cpp")]
 # measurement aid (attn_mfma_ceiling), outside the attention and GEMM paths
 PROBE_SOURCES = [os.path.join(CSRC, "mfma_ceiling.hip")]

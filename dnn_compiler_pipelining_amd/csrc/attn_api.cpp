@@ -52,7 +52,7 @@ bool choose_variant(const Request& r, int B, int Sq, int Sk, int Hq, int Hkv, in
   if (v.bn != libattn::BN_STD && D != 128) return false;
   if (D == 64) return v.schedule == libattn::SCHEDULE_SERIAL || v.schedule == libattn::SCHEDULE_SERIAL4;
   if (D == 256) return v.schedule == libattn::SCHEDULE_SERIAL4;
-  return true;
+  return true;  // D = 128 runs every schedule
 }
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
@@ -167,6 +167,11 @@ int forward(const void* q, const void* k, const void* v, void* o, float* lse, in
     p.n_qt = (Sq + rows - 1) / rows;
     if (libattn::grid_blocks_wide(p) < 0) return ATTN_ERR_SHAPE;
     e = libattn::launch_attn_wide(p, static_cast<hipStream_t>(stream));
+  } else if (p.schedule == libattn::SCHEDULE_SERIAL4_16) {
+    p.n_qt = (Sq + 127) / 128;
+    p.pairs = p.g;  // one query head per workgroup
+    if (libattn::grid_blocks_s16(p) < 0) return ATTN_ERR_SHAPE;
+    e = libattn::launch_attn_s16(p, static_cast<hipStream_t>(stream));
   } else {
     p.n_qt = (Sq + 127) / 128;
     // query heads per workgroup: a pair (two wave groups), or one for SERIAL4

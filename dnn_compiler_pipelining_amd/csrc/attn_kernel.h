@@ -70,4 +70,10 @@ hipError_t launch_attn_fwd(const Params& p, hipStream_t stream);
 int64_t grid_blocks_wide(const Params& p);
 hipError_t launch_attn_wide(const Params& p, hipStream_t stream);
 
+// Grid size and launch of the SERIAL4_16 schedule's kernel (attn_s16.hip; head
+// dimension 128, 64-key tiles): p.pairs = g one-head workgroups per KV head,
+// p.n_qt query tiles of 128 rows, prefetch depth p.ring.
+int64_t grid_blocks_s16(const Params& p);
+hipError_t launch_attn_s16(const Params& p, hipStream_t stream);
+
 }  // namespace libattn

@@ -35,12 +35,16 @@ namespace libattn {
 //             K/V fragment read from LDS feeds two MFMAs, the overlap
 //             schedule inside each wave, K/V loaded two tiles ahead
 //             (head dimension 128)
+//   SERIAL4_16: SERIAL4 on 16 x 16 x 32 MFMAs (attn_s16.hip; head dimension
+//             128, 64-key tiles); same values up to rounding order, not the
+//             same bits
 enum Schedule {
   SCHEDULE_SERIAL = 0,
   SCHEDULE_OVERLAP = 1,
   SCHEDULE_PINGPONG = 2,
   SCHEDULE_SERIAL4 = 3,
-  SCHEDULE_WIDE = 4
+  SCHEDULE_WIDE = 4,
+  SCHEDULE_SERIAL4_16 = 5
 };
 
 // Placements of the softmax parts among the MFMAs of the fused block of the
@@ -81,7 +85,7 @@ struct TunedEntry {
 #include "tuned_table.h"  // kTuned[], kTunedCount
 
 inline bool variant_valid(const Variant& v) {
-  return v.schedule >= SCHEDULE_SERIAL && v.schedule <= SCHEDULE_WIDE && (v.ring == 2 || v.ring == 4) &&
+  return v.schedule >= SCHEDULE_SERIAL && v.schedule <= SCHEDULE_SERIAL4_16 && (v.ring == 2 || v.ring == 4) &&
          (v.xcd == 0 || v.xcd == 1) && (v.lpt == 0 || v.lpt == 1) && v.place >= PLACE_EVEN &&
          v.place <= PLACE_EARLY &&
          (v.schedule == SCHEDULE_WIDE || v.schedule == SCHEDULE_OVERLAP || v.place == PLACE_EVEN) &&

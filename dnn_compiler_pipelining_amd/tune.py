@@ -36,7 +36,7 @@ ROOT = os.path.dirname(PKG)
 TABLE = os.path.join(PKG, "csrc", "tuned_table.h")
 PROFILE = os.path.join(ROOT, "profiles", "schedule_search.json")
 
-SCHEDULES = ("serial", "overlap", "pingpong", "serial4", "wide")  # Schedule enum order in csrc/variant.h
+SCHEDULES = ("serial", "overlap", "pingpong", "serial4", "wide", "serial4_16")  # Schedule enum order in csrc/variant.h
 PLACES = ("even", "front", "early")  # Place enum order in csrc/variant.h; wide and overlap, the others even only
 
 
@@ -115,7 +115,8 @@ def kernel_resources(asm_path: str):
         m = re.search(r"\.name:\s+\S*attn_fwd_kernelILi(\d)ELi(\d)ELi(\d+)ELb([01])E(?:Li(\d+)E)?(?:Li(\d)E)?",
                       block)
         mw = re.search(r"\.name:\s+\S*attn_wide_kernelILi(\d)ELi(\d)E", block)
-        if not m and not mw:
+        ms = re.search(r"\.name:\s+\S*attn_s16_kernelILi(\d)E", block)
+        if not m and not mw and not ms:
             continue
 
         def num(key):
@@ -124,6 +125,8 @@ def kernel_resources(asm_path: str):
 
         if mw:  # the wide kernel: head dimension 128, template arguments = prefetch depth, placement
             key = ("wide", int(mw.group(1)), 128, PLACES[int(mw.group(2))], 64)
+        elif ms:  # the 16 x 16 x 32 serial4 kernel: head dimension 128, 64-key tiles; template argument = depth
+            key = ("serial4_16", int(ms.group(1)), 128, "even", 64)
         else:
             key = (SCHEDULES[int(m.group(1))] + ("-split" if m.group(4) == "1" else ""), int(m.group(2)),
                    int(m.group(3)), PLACES[int(m.group(6) or 0)], int(m.group(5) or 64))

@@ -98,14 +98,16 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
  *   SERIAL4   the serial schedule in 4-wave, one-head workgroups, two per CU
  *   WIDE      4-wave workgroups, one wave per SIMD, 64 query rows per wave, the overlap schedule inside
  *             each wave, K/V loaded two tiles ahead (D = 128 only)
- * D = 64 runs SERIAL and SERIAL4, D = 256 SERIAL4, D = 128 all five.  Every schedule stages K/V in tiles of
+ *   SERIAL4_16  SERIAL4 on 16 x 16 x 32 MFMAs (D = 128, 64-key tiles); same values up to rounding order
+ * D = 64 runs SERIAL and SERIAL4, D = 256 SERIAL4, D = 128 all six.  Every schedule stages K/V in tiles of
  * 64 keys; at D = 128 SERIAL and SERIAL4 also run tiles of 32 and 128 keys. */
 enum {
   ATTN_SCHEDULE_SERIAL = 0,
   ATTN_SCHEDULE_OVERLAP = 1,
   ATTN_SCHEDULE_PINGPONG = 2,
   ATTN_SCHEDULE_SERIAL4 = 3,
-  ATTN_SCHEDULE_WIDE = 4
+  ATTN_SCHEDULE_WIDE = 4,
+  ATTN_SCHEDULE_SERIAL4_16 = 5
 };
 
 /* Placement of the softmax work among the MFMAs of the main loop of ATTN_SCHEDULE_WIDE and

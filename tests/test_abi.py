@@ -258,7 +258,7 @@ def test_variant_placements_outside_the_wide_and_overlap_schedules_are_rejected(
     def var(schedule, place, D=128, ring=-1):
         return L.attn_fwd_variant(QP, KP, VP, OP, LP, 1, 64, 64, 8, 2, D, 1, 0.088, schedule, ring, -1, -1, place, -1,
                                   -1, None)
-    for sched in ("serial", "pingpong", "serial4"):
+    for sched in ("serial", "pingpong", "serial4", "serial4_16"):
         for place in ("front", "early"):
             assert var(L.SCHEDULES[sched], L.PLACES[place]) == L.ATTN_ERR_UNSUPPORTED, (sched, place)
     assert var(L.SCHEDULES["overlap"], 3) == L.ATTN_ERR_UNSUPPORTED
@@ -273,7 +273,7 @@ def test_variant_tile_sizes_outside_the_serial_schedules_are_rejected(lib):
     def var(schedule, bn, D=128):
         return L.attn_fwd_variant(QP, KP, VP, OP, LP, 1, 64, 64, 8, 2, D, 1, 0.088, schedule, -1, -1, -1, -1, bn, -1,
                                   None)
-    for sched in ("overlap", "pingpong", "wide"):
+    for sched in ("overlap", "pingpong", "wide", "serial4_16"):
         for bn in (32, 128):
             assert var(L.SCHEDULES[sched], bn) == L.ATTN_ERR_UNSUPPORTED, (sched, bn)
     for sched in ("serial", "serial4"):
@@ -288,12 +288,21 @@ def test_variant_heads_per_workgroup_outside_the_wide_schedule_are_rejected(lib)
     def var(schedule, hpw, D=128):
         return L.attn_fwd_variant(QP, KP, VP, OP, LP, 1, 64, 64, 8, 2, D, 1, 0.088, schedule, -1, -1, -1, -1, -1, hpw,
                                   None)
-    for sched in ("serial", "overlap", "pingpong", "serial4"):
+    for sched in ("serial", "overlap", "pingpong", "serial4", "serial4_16"):
         for hpw in (1, 2, 4):
             assert var(L.SCHEDULES[sched], hpw) == L.ATTN_ERR_UNSUPPORTED, (sched, hpw)
     for hpw in (3, 5, 8, 16):
         assert var(L.SCHEDULES["wide"], hpw) == L.ATTN_ERR_UNSUPPORTED, hpw
     assert var(L.SCHEDULES["wide"], 2, D=64) == L.ATTN_ERR_UNSUPPORTED
+
+
+def test_sixteen_by_sixteen_schedule_runs_head_dimension_128_only(lib):
+    def var(schedule, D):
+        return L.attn_fwd_variant(QP, KP, VP, OP, LP, 1, 64, 64, 8, 2, D, 1, 0.088, schedule, -1, -1, -1, -1, -1, -1,
+                                  None)
+    for D in (64, 256):
+        assert var(L.SCHEDULES["serial4_16"], D) == L.ATTN_ERR_UNSUPPORTED, D
+    assert var(6, 128) == L.ATTN_ERR_UNSUPPORTED  # no such schedule
 
 
 def test_mfma_ceiling_validates_before_any_hip_call(lib):

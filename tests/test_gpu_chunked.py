@@ -99,7 +99,8 @@ def test_rect_schedules_bitwise_identical(B, Sq, Sk, Hq, Hkv, causal):
     assert st["finite"]
 
 
-@pytest.mark.parametrize("sched,bn", [(s, bn) for s in ("serial", "serial4") for bn in (32, 128)], ids=str)
+@pytest.mark.parametrize("sched,bn", [(s, bn) for s in ("serial", "serial4") for bn in (32, 128)] +
+                         [("serial4_16", 64)], ids=str)
 @pytest.mark.parametrize("B,Sq,Sk,Hq,Hkv,causal", RECT, ids=str)
 def test_rect_tile_sizes_against_oracle(B, Sq, Sk, Hq, Hkv, causal, sched, bn):
     """32- and 128-key tiles of the serial schedules on the rectangular shapes: offsets that are not

@@ -70,6 +70,7 @@ def eager_noise():
     (2, 333, 12, 3, 1, {"schedule": "serial4", "bn": 32}),
     (1, 650, 8, 2, 1, {"schedule": "overlap", "place": "front"}),
     (1, 257, 8, 1, 1, {"schedule": "pingpong"}),
+    (2, 300, 8, 2, 1, {"schedule": "serial4_16"}),
 ], ids=str)
 def test_forward_graph_replays(B, S, Hq, Hkv, causal, variant):
     tag = "forward B%d S%d Hq%d Hkv%d causal%d %s" % (B, S, Hq, Hkv, causal, variant)

@@ -274,13 +274,16 @@ def test_schedules_bitwise_identical(B, S, Hq, Hkv, causal):
 @pytest.mark.parametrize("B,S,Hq,Hkv,causal", [(1, 700, 8, 2, 1), (2, 257, 12, 3, 0)], ids=str)
 def test_all_variants_bitwise_identical(B, S, Hq, Hkv, causal):
     """Every point of the searched variant space of one tile size (schedule x prefetch depth x workgroup
-    order x placement) gives the same bits: 64-key tiles over every schedule, and 32- and 128-key tiles over
-    the serial schedules, each against its own first point."""
+    order x placement x heads per workgroup) gives the same bits: 64-key tiles over every 32 x 32 x 16
+    schedule, 32- and 128-key tiles over the serial schedules, and the 16 x 16 x 32 schedule's variants,
+    each group against its own first point."""
     q, k, v = cpu_qkv(B, S, Hq, Hkv, seed=95 + S)
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
-    for bn in (64, 32, 128):
-        scheds = U.SCHEDULES_D128 if bn == 64 else ("serial", "serial4")
-        o1, l1 = U.run(qd, kd, vd, bool(causal), SC, {"schedule": "serial", "bn": bn})
+    for bn, scheds in ((64, U.SCHEDULES_D128), (32, ("serial", "serial4")), (128, ("serial", "serial4")),
+                       (64, ("serial4_16",))):
+        # the 16 x 16 x 32 schedule rounds differently: its variants are compared among themselves
+        first = "serial4_16" if scheds == ("serial4_16",) else "serial"
+        o1, l1 = U.run(qd, kd, vd, bool(causal), SC, {"schedule": first, "bn": bn})
         for sched in scheds:
             for ring in (2, 4):
                 for xcd in (0, 1):
@@ -298,7 +301,8 @@ def test_all_variants_bitwise_identical(B, S, Hq, Hkv, causal):
 # named.
 INSTANCES = ([(sched, ring, place, 64) for sched in U.SCHEDULES_D128 for ring in (2, 4)
               for place in (binding.PLACES if sched in ("wide", "overlap") else ("even",))] +
-             [(sched, ring, "even", bn) for sched in ("serial", "serial4") for ring in (2, 4) for bn in (32, 128)])
+             [(sched, ring, "even", bn) for sched in ("serial", "serial4") for ring in (2, 4) for bn in (32, 128)] +
+             [("serial4_16", ring, "even", 64) for ring in (2, 4)])
 
 
 @pytest.mark.parametrize("sched,ring,place,bn", INSTANCES, ids=lambda x: str(x))

@@ -17,8 +17,10 @@ def test_every_compiled_variant_is_valid():
     registers and it spills inside the tile loop, so the check takes it out of the search."""
     vs = tune.valid_variants()
     rejected = {("serial", r, 128, "even", 128) for r in tune.RINGS}
-    assert set(vs) == ({(s, r, 128, "even", 64) for s in tune.SCHEDULES if s != "wide" for r in tune.RINGS} |
+    assert set(vs) == ({(s, r, 128, "even", 64) for s in tune.SCHEDULES if s not in ("wide", "serial4_16")
+                        for r in tune.RINGS} |
                        {(s, r, 128, pl, 64) for s in ("wide", "overlap") for r in tune.RINGS for pl in tune.PLACES} |
+                       {("serial4_16", r, 128, "even", 64) for r in tune.RINGS} |
                        {(s, r, 128, "even", bn) for s in ("serial", "serial4") for r in tune.RINGS
                         for bn in (32, 128)} |
                        {(s, r, 64, "even", 64) for s in ("serial", "serial4") for r in tune.RINGS} |
@@ -83,7 +85,8 @@ def test_greedy_search_covers_each_schedules_own_fields():
     over their tile sizes and the wide and overlap ones over their placements; invalid points are never
     timed."""
     def rate_of(pt):
-        base = {"serial": 100.0, "overlap": 110.0, "pingpong": 105.0, "serial4": 120.0, "wide": 200.0}[pt["schedule"]]
+        base = {"serial": 100.0, "overlap": 110.0, "pingpong": 105.0, "serial4": 120.0, "wide": 200.0,
+                "serial4_16": 118.0}[pt["schedule"]]
         base *= {32: 1.1, 64: 1.0, 128: 0.9}[pt["bn"]] if pt["schedule"] in ("serial", "serial4") else 1.0
         base *= {"even": 1.0, "front": 1.02, "early": 1.05}[pt["place"]] if pt["schedule"] in ("wide", "overlap") else 1.0
         return base * (1.01 if pt["ring"] == 2 else 1.0)
