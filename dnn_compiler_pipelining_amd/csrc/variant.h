@@ -20,7 +20,8 @@
 
 namespace libattn {
 
-// Tile schedules (see attn_fwd.hip).  All compute bitwise identical results.
+// Tile schedules (see attn_fwd.hip).  The first five compute bitwise identical
+// results at 64-key tiles; SERIAL4_16 the same values up to rounding order.
 //   SERIAL  : per tile, one wave runs QK^T, softmax and PV back to back; the
 //             two waves that share a SIMD overlap each other's MFMA and VALU
 //             work
