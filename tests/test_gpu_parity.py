@@ -331,6 +331,19 @@ def test_wide_heads_per_workgroup_against_oracle(B, S, Hq, Hkv, causal, hpw):
     U.full_parity(q, k, v, bool(causal), SC, tag, {"schedule": "wide", "hpw": hpw})
 
 
+@pytest.mark.parametrize("sched,bn", [("serial4_16", 64), ("serial4", 32), ("serial", 32), ("serial4", 128)],
+                         ids=str)
+@pytest.mark.parametrize("scale", [-SC, 0.0, 1.0], ids=["neg", "zero", "one"])
+def test_other_instances_at_edge_scales(sched, bn, scale):
+    """The instances whose rounding differs from the 64-key 32 x 32 x 16 schedules, at a negative scale
+    (Q negated in the kernel), zero (uniform weights) and 1 (sharply peaked rows: the rescale path runs
+    many times per row), against the oracle."""
+    tag = "%s bn%d scale %.4g" % (sched, bn, scale)
+    U.say("edge scale " + tag)
+    q, k, v = cpu_qkv(1, 700, 8, 2, seed=330)
+    U.full_parity(q, k, v, True, scale, tag, {"schedule": sched, "bn": bn})
+
+
 def tuned_entries():
     """(B, Sq, Sk, Hq, Hkv, variant) rows of the compiled-in tuned table."""
     import os
