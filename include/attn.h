@@ -44,10 +44,11 @@
  *
  * Kernel variants.  Every entry point runs the variant tuned for the nearest
  * measured shape (a table compiled into the library); attn_fwd_variant names
- * one explicitly.  Variants with the same keys per K/V tile give bitwise
- * identical results, so each serves as a cross-check of the others; a tile
- * size other than 64 keys changes only the rounding order of the online
- * softmax.  The library reads no environment.
+ * one explicitly.  Variants on the 32 x 32 x 16 MFMA with the same keys per
+ * K/V tile give bitwise identical results, so each serves as a cross-check of
+ * the others; a tile size other than 64 keys, or ATTN_SCHEDULE_SERIAL4_16 (the
+ * 16 x 16 x 32 MFMA), changes only the rounding order.  The library reads no
+ * environment.
  *
  * Errors: on invalid arguments nothing is launched and a nonzero ATTN_ERR_*
  * code is returned; a failed launch returns ATTN_ERR_HIP.  No exception
@@ -125,8 +126,8 @@ enum { ATTN_PLACE_EVEN = 0, ATTN_PLACE_FRONT = 1, ATTN_PLACE_EARLY = 2 };
  * schedules other than ATTN_SCHEDULE_WIDE and ATTN_SCHEDULE_OVERLAP; bn: 64 where the schedule or D has no
  * other; hpw: 0 for schedules other than ATTN_SCHEDULE_WIDE).  A value that does not exist, a
  * placement or tile size the schedule does not have, or a schedule the head dimension does not run,
- * returns ATTN_ERR_UNSUPPORTED and launches nothing.  Results are bitwise identical for every variant of one tile size; another tile size changes the
- * rounding order of the online softmax. */
+ * returns ATTN_ERR_UNSUPPORTED and launches nothing.  Results are bitwise identical for every variant of one
+ * tile size except ATTN_SCHEDULE_SERIAL4_16; another tile size, or that schedule, changes the rounding order. */
 int attn_fwd_variant(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Sq, int Sk, int Hq,
                      int Hkv, int D, int causal, float scale, int schedule, int ring, int xcd, int lpt, int place,
                      int bn, int hpw, void* stream);
