@@ -317,3 +317,30 @@ def test_mfma_ceiling_validates_before_any_hip_call(lib):
     assert lib.attn_mfma_ceiling_shape(16, 0, None, ctypes.byref(out)) == L.ATTN_ERR_SHAPE
     assert lib.attn_mfma_ceiling_shape(16, 100, None, None) == L.ATTN_ERR_NULL
     assert out.value == -1.0
+
+
+def header_constants():
+    """Every `ATTN_NAME = value` of the enums in include/*.h, and ATTN_STATIC_WORKSPACE_BYTES."""
+    consts = {}
+    for path in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(path).read(), flags=re.S)
+        for name, val in re.findall(r"\b(ATTN_[A-Z0-9_]+)\s*=\s*(\d+)", text):
+            consts[name] = int(val)
+        for name, expr in re.findall(r"#define\s+(ATTN_[A-Z0-9_]+)\s+([^\n]+)", text):
+            m = re.search(r"(\d+)\s*<<\s*(\d+)", expr)  # ((size_t)64 << 20)
+            if m:
+                consts[name] = int(m.group(1)) << int(m.group(2))
+    return consts
+
+
+def test_binding_constants_match_the_header():
+    """The binding's status codes, schedule and placement numbers and static workspace size are the
+    header's: a drift would pass a different schedule, or misname a status, without any error."""
+    h = header_constants()
+    codes = {n: v for n, v in h.items() if n == "ATTN_OK" or n.startswith("ATTN_ERR_")}
+    assert codes and all(getattr(L, n) == v for n, v in codes.items()), codes
+    scheds = {n[len("ATTN_SCHEDULE_"):].lower(): v for n, v in h.items() if n.startswith("ATTN_SCHEDULE_")}
+    assert scheds == L.SCHEDULES
+    places = {n[len("ATTN_PLACE_"):].lower(): v for n, v in h.items() if n.startswith("ATTN_PLACE_")}
+    assert places == L.PLACES
+    assert h.get("ATTN_STATIC_WORKSPACE_BYTES") == L.ATTN_STATIC_WORKSPACE_BYTES
