@@ -185,3 +185,14 @@ def test_emit_and_nearest_shape(tmp_path):
     assert got[3] == (4, 4, 1, 1, 2, 64, 0, 1)
     assert got[4] == (3, 2, 0, 0, 0, 32, 0, 1)
     assert got[5] == (4, 4, 1, 1, 0, 64, 2, 1)
+
+
+def test_committed_table_is_what_the_committed_search_emits(tmp_path):
+    """tuned_table.h is generated: emitting the committed search record gives the committed file byte for byte,
+    so the table the library compiles in is the one the recorded measurements chose."""
+    from dnn_compiler_pipelining_amd import tune
+
+    out = tmp_path / "tuned_table.h"
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    tune.emit(os.path.join(root, "profiles", "schedule_search.json"), table=str(out), profile=None)
+    assert out.read_text() == open(os.path.join(CSRC, "tuned_table.h")).read()
